@@ -1,0 +1,152 @@
+"""CPU oracle for paged decode attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import this package.
+It shares no code with the HIP library (``paged_kv_cache_458_amd``) and neither imports the other.
+
+Two independent routes compute the same plain definition, softmax(scale * q . K^T) . V over each sequence's
+logically ordered K/V (vLLM PagedAttention, page 1 section 3.2: a block table maps logical positions to
+physical blocks of a [num_blocks, block_size, heads, head_dim] pool):
+
+* ``decode`` -- fp64 C (``pa_oracle.c``), forward gather through the block table, OpenMP over rows;
+* ``brute.decode`` -- numpy, builds the inverse map physical slot -> logical position by scanning the pool.
+
+``reshape_and_cache``, ``copy_blocks`` and ``gather`` apply the cache write, the block copy and the logical
+gather to host copies of the pools, byte for byte.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+F32, BF16 = 0, 1
+_lib = None
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the C oracle with gcc (-O2, no fast-math: sums keep their written order)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        _lib = _bind(ctypes.CDLL(build()))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_decode.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_double, i32, i32, i32,
+                                  i32, i32, i64, i32, P, i64]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32]
+    lib.oracle_reshape_and_cache.restype = ctypes.c_int
+    lib.oracle_copy_blocks.argtypes = [P, P, P, i32, i64, i64]
+    lib.oracle_copy_blocks.restype = ctypes.c_int
+    lib.oracle_gather.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i32, i32]
+    lib.oracle_gather.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return BF16
+    raise TypeError(f"oracle takes float32 arrays or uint16 bf16 bit patterns, got {a.dtype}")
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())
+
+
+def decode(query, key_cache, value_cache, block_tables, context_lens, scale, *, rows=None, lib=None):
+    """fp64 decode attention.
+
+    query [B, Hq, D] and the pools [NB, bs, Hkv, D] are float32 arrays or uint16 arrays of bf16 bits.
+    Returns float64 [B, Hq, D]; with ``rows`` (int array [n, 2] of (seq, head)) only those rows are computed
+    and the rest are NaN.
+    """
+    lib = lib or load()
+    q = np.ascontiguousarray(query)
+    kc = np.ascontiguousarray(key_cache)
+    vc = np.ascontiguousarray(value_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = kc.shape
+    if D2 != D or vc.shape != kc.shape or bt.shape[0] != B or cl.shape != (B,):
+        raise ValueError("shape mismatch")
+    out = np.full((B, Hq, D), np.nan if rows is not None else 0.0, dtype=np.float64)
+    rw = None
+    n = 0
+    if rows is not None:
+        rw = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        n = rw.shape[0]
+    rc = lib.oracle_decode(_ptr(out), _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(bt),
+                           _ptr(cl), float(scale), bs, B, Hq, Hkv, D, NB, bt.shape[1],
+                           _ptr(rw) if rw is not None else None, n)
+    if rc != 0:
+        raise ValueError(f"oracle_decode rejected its input (status {rc})")
+    return out
+
+
+def reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, *, lib=None):
+    """Apply the slot-mapped write to host pools in place (arrays of any dtype, raw bytes)."""
+    lib = lib or load()
+    for a in (key_cache, value_cache):
+        if not a.flags.c_contiguous:
+            raise ValueError("pools must be C-contiguous")
+    k = np.ascontiguousarray(key)
+    v = np.ascontiguousarray(value)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    NB, bs, Hkv, D = key_cache.shape
+    rc = lib.oracle_reshape_and_cache(_ptr(key_cache), _ptr(value_cache), _ptr(k), _ptr(v), _ptr(sm), sm.size, Hkv,
+                                      D, bs, NB, key_cache.itemsize)
+    if rc != 0:
+        raise ValueError(f"oracle_reshape_and_cache rejected its input (status {rc})")
+
+
+def copy_blocks(key_cache, value_cache, pairs, *, lib=None):
+    """Apply block copies (src -> dst, in order) to host pools in place."""
+    lib = lib or load()
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    NB = key_cache.shape[0]
+    block_bytes = key_cache[0].nbytes
+    rc = lib.oracle_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(pr), pr.shape[0], block_bytes, NB)
+    if rc != 0:
+        raise ValueError(f"oracle_copy_blocks rejected its input (status {rc})")
+
+
+def gather(cache, block_tables, context_lens, *, lib=None):
+    """Logical-order rows [sum(L), Hkv, D] of one pool, raw bytes."""
+    lib = lib or load()
+    c = np.ascontiguousarray(cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    NB, bs, Hkv, D = c.shape
+    out = np.empty((int(cl.astype(np.int64).sum()), Hkv, D), dtype=c.dtype)
+    rc = lib.oracle_gather(_ptr(out), _ptr(c), _ptr(bt), _ptr(cl), cl.size, bs, Hkv, D, NB, bt.shape[1], c.itemsize)
+    if rc != 0:
+        raise ValueError(f"oracle_gather rejected its input (status {rc})")
+    return out

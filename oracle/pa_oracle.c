@@ -1,0 +1,230 @@
+/*
+ * Plain fp64 CPU oracle for paged decode attention, the slot-mapped cache write and the block copy.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's CPU-baseline leg load this
+ * file's library. It shares no code, header or table with the HIP library and must never be used as a
+ * fallback for it. It is deliberately slow and written to be checked by eye against the pages:
+ *
+ *  - vLLM PagedAttention, page 1 ("LLM inference framework evaluation ... PagedAttention"), section 3.2: the KV
+ *    cache is split into fixed-size blocks held in one global pool laid out as
+ *    [num_blocks, block_size, num_heads, head_dim]; a sequence's tokens live in non-contiguous physical blocks
+ *    and a per-sequence block table maps each logical position to its physical place. Page 3 (vLLM
+ *    architecture), section 2.2, gives the example "logical block 0 -> physical block 7".
+ *  - page 2 ("vLLM-v0.11.0 ... how much memory does PagedAttention save"), section 4.2: a sequence of
+ *    length L occupies ceil(L / block_size) blocks.
+ *  - page 1 section 3.1 and page 3 section 2.1: each decode step the new token reads the K and V of all
+ *    previous tokens, and after sampling the new token's K/V is appended to the cache.
+ *  - page 1 section 3.2 (sharing and copy-on-write): sequences may share physical blocks; a shared block is
+ *    copied before it is written.
+ *
+ * Paging changes where K and V live, never what is attended, so decode attention is the plain definition
+ * softmax(scale * q . K^T) . V over the logically ordered keys and values, computed here in fp64 after an
+ * exact decode of every stored element (bf16 bits << 16 give the fp32 value; fp32 widens exactly to fp64).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* One stored element, decoded exactly to fp64. */
+static double elem(const void *base, int64_t index, int dtype) {
+    if (dtype == ORACLE_F32) {
+        return (double)((const float *)base)[index];
+    }
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[index] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Decode attention for the (sequence, query head) rows listed in `rows` (pairs s, h), or for every row when
+ * rows == NULL. out is [num_seqs, num_q_heads, head_dim] fp64; rows not listed are left untouched.
+ *
+ * For each row: G = num_q_heads / num_kv_heads query heads share KV head g = h / G (consecutive grouping);
+ * position t of the sequence sits in physical block block_tables[s][t / block_size] at offset
+ * t % block_size; z_t = scale * sum_d q[d] k_t[d] (d ascending); m = max z; w_t = exp(z_t - m);
+ * out = sum_t w_t v_t / sum_t w_t. A context of length 0 gives a zero row.
+ *
+ * Returns 0, or -1 on a bad shape, -2 when a length exceeds the table width, -3 when a table entry that the
+ * length makes live is not a valid block id, -4 when memory runs out.
+ */
+int oracle_decode(double *out, const void *query, int q_dtype, const void *key_cache, const void *value_cache,
+                  int kv_dtype, const int32_t *block_tables, const int32_t *context_lens, double scale,
+                  int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, const int32_t *rows,
+                  int64_t num_rows) {
+    if (block_size <= 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0) {
+        return -1;
+    }
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int64_t L = context_lens[s];
+        if (L < 0 || (L + block_size - 1) / block_size > max_blocks_per_seq) {
+            return -2;
+        }
+        for (int64_t j = 0; j < (L + block_size - 1) / block_size; ++j) {
+            int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + j];
+            if (b < 0 || b >= num_blocks) {
+                return -3;
+            }
+        }
+    }
+    const int32_t G = num_q_heads / num_kv_heads;
+    const int64_t total = rows ? num_rows : (int64_t)num_seqs * num_q_heads;
+    int status = 0;
+
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < total; ++r) {
+        int32_t s, h;
+        if (rows) {
+            s = rows[2 * r];
+            h = rows[2 * r + 1];
+        } else {
+            s = (int32_t)(r / num_q_heads);
+            h = (int32_t)(r % num_q_heads);
+        }
+        double *o = out + ((int64_t)s * num_q_heads + h) * head_dim;
+        const int64_t L = context_lens[s];
+        const int32_t g = h / G;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            o[d] = 0.0;
+        }
+        if (L == 0) {
+            continue;
+        }
+        double *q = malloc(sizeof(double) * head_dim);
+        double *k = malloc(sizeof(double) * L * head_dim);
+        double *v = malloc(sizeof(double) * L * head_dim);
+        double *z = malloc(sizeof(double) * L);
+        if (!q || !k || !v || !z) {
+            free(q); free(k); free(v); free(z);
+#pragma omp atomic write
+            status = -4;
+            continue;
+        }
+        const int64_t q_base = ((int64_t)s * num_q_heads + h) * head_dim;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            q[d] = elem(query, q_base + d, q_dtype);
+        }
+        /* reassemble this head's K and V in logical order through the block table */
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+            const int64_t off = t % block_size;
+            const int64_t base = ((phys * block_size + off) * num_kv_heads + g) * head_dim;
+            for (int32_t d = 0; d < head_dim; ++d) {
+                k[t * head_dim + d] = elem(key_cache, base + d, kv_dtype);
+                v[t * head_dim + d] = elem(value_cache, base + d, kv_dtype);
+            }
+        }
+        double m = -INFINITY;
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = 0.0;
+            for (int32_t d = 0; d < head_dim; ++d) {
+                acc += q[d] * k[t * head_dim + d];
+            }
+            z[t] = scale * acc;
+            if (z[t] > m) {
+                m = z[t];
+            }
+        }
+        double sum = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            z[t] = exp(z[t] - m); /* z now holds the unnormalised weight w_t */
+            sum += z[t];
+        }
+        for (int64_t t = 0; t < L; ++t) {
+            for (int32_t d = 0; d < head_dim; ++d) {
+                o[d] += z[t] * v[t * head_dim + d];
+            }
+        }
+        for (int32_t d = 0; d < head_dim; ++d) {
+            o[d] /= sum;
+        }
+        free(q); free(k); free(v); free(z);
+    }
+    return status;
+}
+
+/*
+ * The new token's K/V goes into its slot: for token n with slot = slot_mapping[n] >= 0, physical block
+ * slot / block_size, offset slot % block_size receives key[n] (all KV heads, all dims), likewise value.
+ * Slots < 0 are skipped. Bytes are copied unchanged. Returns 0, or -1 when a slot is beyond the pool.
+ */
+int oracle_reshape_and_cache(void *key_cache, void *value_cache, const void *key, const void *value,
+                             const int32_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t elem_bytes) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim * elem_bytes;
+    for (int32_t n = 0; n < num_tokens; ++n) {
+        const int64_t slot = slot_mapping[n];
+        if (slot < 0) {
+            continue;
+        }
+        if (slot >= num_blocks * block_size) {
+            return -1;
+        }
+        const int64_t block = slot / block_size;
+        const int64_t off = slot % block_size;
+        const int64_t dst = (block * block_size + off) * row;
+        memcpy((char *)key_cache + dst, (const char *)key + n * row, (size_t)row);
+        memcpy((char *)value_cache + dst, (const char *)value + n * row, (size_t)row);
+    }
+    return 0;
+}
+
+/*
+ * Copy-on-write of shared blocks: for each pair (src, dst), the whole dst block of both pools becomes a byte
+ * copy of the src block. Pairs are applied in order. Returns 0, or -1 on an id outside the pool.
+ */
+int oracle_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int32_t num_pairs,
+                       int64_t block_bytes, int64_t num_blocks) {
+    for (int32_t p = 0; p < num_pairs; ++p) {
+        const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) {
+            return -1;
+        }
+        memmove((char *)key_cache + dst * block_bytes, (const char *)key_cache + src * block_bytes,
+                (size_t)block_bytes);
+        memmove((char *)value_cache + dst * block_bytes, (const char *)value_cache + src * block_bytes,
+                (size_t)block_bytes);
+    }
+    return 0;
+}
+
+/*
+ * Logical-order gather of one pool: out[(sum of earlier lengths) + t] = cache row of position t of each
+ * sequence, all KV heads, raw bytes. out has sum(context_lens) rows of num_kv_heads*head_dim*elem_bytes.
+ * Returns 0, or -3 on a live table entry outside the pool.
+ */
+int oracle_gather(void *out, const void *cache, const int32_t *block_tables, const int32_t *context_lens,
+                  int32_t num_seqs, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                  int64_t num_blocks, int32_t max_blocks_per_seq, int32_t elem_bytes) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim * elem_bytes;
+    int64_t r = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        for (int64_t t = 0; t < context_lens[s]; ++t) {
+            const int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+            if (phys < 0 || phys >= num_blocks) {
+                return -3;
+            }
+            memcpy((char *)out + r * row, (const char *)cache + (phys * block_size + t % block_size) * row,
+                   (size_t)row);
+            ++r;
+        }
+    }
+    return 0;
+}
