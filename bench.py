@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+A step is one decode step of a batch over its paged KV pool: copy-on-write block copies (the workload with a
+shared prefix), the slot-mapped write of every sequence's new K/V, then paged decode attention over the whole
+context (single pass, or split-context partitions plus the log-sum-exp reduce). Inputs are seeded synthetic
+tensors already resident in HBM; consecutive steps read different replicas of the pools so that no step can
+be served from the 256 MB last-level cache left warm by the previous one.
+
+Prints one JSON line: whole-step achieved GB/s (algorithmic bytes / step time), decode queries/s, a roofline
+entry for the attention call (HIP events on the stream it runs on) and the CPU oracle's rate on the host cores.
+
+    python bench.py [--workload llama2_7b] [--steps 100] [--warmup 10]
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "paged decode attention achieved HBM GB/s (% of peak) + decode queries/sec"
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_458_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Counter-measured HBM bytes per attention call, if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--replicas", type=int, default=2, help="pool replicas cycled by consecutive steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle timing budget (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py runs on one GPU only: this library has no multi-GPU path (each GPU would run the "
+                  "same kernels on its own share of sequences or KV heads); use --gpus 1", flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_458_amd as pa
+    from workloads import CONFIG_NAMES, algorithmic_bytes, build_structure, materialize
+
+    if args.workload not in CONFIG_NAMES:
+        ap.error(f"--workload must be one of {CONFIG_NAMES}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+
+    st = build_structure(args.workload)
+    part = st.partition_size if args.partition_size is None else args.partition_size
+    B, Hq, Hkv, D, bs = st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size
+    kv_code = pa.PA_BF16 if st.dtype == "bf16" else pa.PA_F32
+    launched_part = pa.partition_size_for(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+
+    t = materialize(st, dev, include_new_token=False)
+    pools = [(t["key_cache"], t["value_cache"])]
+    for _ in range(1, max(1, args.replicas)):
+        pools.append((t["key_cache"].clone(), t["value_cache"].clone()))
+    log(f"{args.workload}: {len(pools)} pool replicas of {2 * t['key_cache'].nbytes / 2**30:.2f} GiB")
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    tables, lens, slots = i32(st.block_tables), i32(st.context_lens), i32(st.slot_mapping)
+    pairs = i32(st.copy_pairs) if len(st.copy_pairs) else None
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws_bytes = pa.workspace_bytes(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        kc, vc = pools[i % len(pools)]
+        if pairs is not None:
+            pa.copy_blocks(kc, vc, pairs)
+        pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.paged_attention_decode(out, t["query"], kc, vc, tables, lens, st.scale, bs,
+                                  max_context_len=st.max_context_len, partition_size=part, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = start.elapsed_time(end) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_ms = float(np.mean(attn_ms))
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us "
+        f"(median {np.median(attn_ms) * 1e3:.1f}, min {np.min(attn_ms) * 1e3:.1f})")
+
+    ab = algorithmic_bytes(st)
+    row_bytes = Hkv * D * st.esize
+    cache_write_bytes = 2 * 2 * int((st.slot_mapping >= 0).sum()) * row_bytes  # read + write, K and V
+    copy_bytes = 2 * 2 * len(st.copy_pairs) * bs * row_bytes
+    step_bytes = ab["total"] + cache_write_bytes + copy_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    attn_gbs = ab["total"] / (attn_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": st.dtype,
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": B,
+            "num_q_heads": Hq,
+            "num_kv_heads": Hkv,
+            "head_dim": D,
+            "block_size": bs,
+            "context_len_mean": float(st.context_lens.mean()),
+            "context_len_max": int(st.context_lens.max()),
+            "partition_size": launched_part,
+            "pool_blocks": st.num_blocks,
+            "replicas": len(pools),
+            "seed": st.seed,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "decode_queries_per_s": round(B / (ms_step * 1e-3), 1),
+        "attention": {
+            "us_mean": round(attn_avg_ms * 1e3, 2),
+            "us_median": round(float(np.median(attn_ms)) * 1e3, 2),
+            "us_min": round(float(np.min(attn_ms)) * 1e3, 2),
+            "gb_per_s": round(attn_gbs, 1),
+            "queries_per_s": round(B / (attn_avg_ms * 1e-3), 1),
+            "bytes_per_call": ab["total"],
+            "kv_unique_bytes": ab["kv_unique"],
+        },
+        "step_bytes": step_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (partition kernel + log-sum-exp reduce when split)",
+            "achieved": round(attn_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+
+    if args.cpu_seconds > 0:
+        import oracle
+
+        kc, vc = pools[0]
+        host = {}
+        for name, tt in (("query", t["query"]), ("key_cache", kc), ("value_cache", vc)):
+            tt = tt.contiguous().cpu()
+            host[name] = tt.view(torch.int16).numpy().view(np.uint16) if tt.dtype == torch.bfloat16 else tt.numpy()
+        lib = oracle.load()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.decode(host["query"], host["key_cache"], host["value_cache"], st.block_tables, st.context_lens,
+                          st.scale, lib=lib)
+            reps += 1
+            el = time.perf_counter() - t0
+            log(f"cpu oracle call {reps}: {el:.1f} s")
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        rec["cpu_baseline"] = {
+            "value": round(B * reps / el, 2),
+            "unit": "decode queries/s",
+            "gb_per_s": round(ab["total"] * reps / el / 1e9, 3),
+            "cores": oracle.num_threads(lib),
+            "kind": "oracle",
+            "sample": f"the whole {args.workload} batch ({B} sequences x {Hq} heads, fp64 C oracle with OpenMP), "
+                      f"{reps} call(s) in {el:.1f} s",
+        }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

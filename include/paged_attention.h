@@ -1,0 +1,161 @@
+/*
+ * paged_attention.h -- C ABI of libpagedattn.so, the MI355X (gfx950) paged decode attention library.
+ *
+ * The paged KV cache (vLLM PagedAttention, page 1 "LLM inference framework evaluation ...", section 3.2):
+ * keys and values live in two global block pools, each laid out as
+ *     [num_blocks][block_size][num_kv_heads][head_dim]        (row-major, contiguous)
+ * and each sequence owns a row of a block table that maps its logical block j (positions j*block_size ..
+ * (j+1)*block_size-1) to a physical block id (page 3, section 2.2: logical block 0 may sit in physical block
+ * 7). A sequence of length L uses its first ceil(L / block_size) table entries (page 2, section 4.2).
+ *
+ * Conventions for every call below:
+ *  - Tensor arguments are DEVICE pointers into caller-owned memory (for instance PyTorch allocations),
+ *    row-major and contiguous. The library allocates no device memory, keeps no per-call state and is
+ *    reentrant; split-context scratch comes only from the caller's workspace.
+ *  - dtype codes: PA_F32 (IEEE fp32) and PA_BF16 (bfloat16). Attention output is always fp32.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it and the call returns
+ *    without synchronising; results are valid once the caller synchronises that stream.
+ *  - Every argument the host can check is checked before anything is launched; on failure the call
+ *    returns a negative status and launches nothing. A launch failure returns PA_ERR_HIP.
+ *  - Device-side contents (table entries, lengths, slots, copy pairs) are caller contracts, not checked on
+ *    the host. The kernels still never touch memory outside the pools for them: a table entry outside
+ *    [0, num_blocks) turns that (sequence, head) output row into NaN, a length is clamped to
+ *    max_context_len, and out-of-range slots or copy pairs are skipped.
+ *  - Pointers must be 16-byte aligned (PA_ERR_ALIGN otherwise).
+ */
+#ifndef PAGED_ATTENTION_H
+#define PAGED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+/* dtype codes */
+#define PA_F32 0
+#define PA_BF16 1
+
+/* status codes */
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PA_ERR_SHAPE (-2)       /* a size is negative or zero where it must be positive, or sizes disagree */
+#define PA_ERR_DTYPE (-3)       /* unknown dtype code or unsupported (query, cache) dtype pair */
+#define PA_ERR_UNSUPPORTED (-4) /* head_dim, block_size or grid size outside what the kernels implement */
+#define PA_ERR_WORKSPACE (-5)   /* the split-context path needs a larger workspace */
+#define PA_ERR_HIP (-6)         /* a HIP launch or runtime call failed */
+#define PA_ERR_ALIGN (-7)       /* a pointer is not 16-byte aligned */
+
+/* PA_ABI_VERSION of the loaded library. */
+int pa_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *pa_strerror(int status);
+
+/*
+ * Partition size (in tokens) that paged_attention_decode uses for a given `partition_size` argument:
+ * 0 stays 0 (single pass), a positive value is returned unchanged, -1 is replaced by the library's choice
+ * for these sizes. Returns a negative status for an invalid request.
+ */
+int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t kv_dtype, int32_t partition_size);
+
+/*
+ * Bytes of workspace paged_attention_decode needs for these sizes (0 when the call runs single pass).
+ * Arguments as in paged_attention_decode. Returns 0 as well for invalid sizes (the decode call reports them).
+ */
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t kv_dtype, int32_t partition_size);
+
+/*
+ * Decode attention over the paged cache: for every sequence s and query head h,
+ *     out[s][h][:] = softmax_t( scale * query[s][h][:] . K_t ) . V_t ,  t = 0 .. L-1,  L = context_lens[s],
+ * where K_t / V_t are row (block_tables[s][t / block_size], t % block_size, h / G) of the pools and
+ * G = num_q_heads / num_kv_heads query heads share one KV head (consecutive grouping). Each new token reads
+ * every earlier K/V of its sequence (page 1 section 3.1); paging changes only where those rows live. A
+ * length-0 context gives a zero row.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim] fp32, written; must not alias any input
+ *   query          [num_seqs][num_q_heads][head_dim] q_dtype
+ *   key_cache      [num_blocks][block_size][num_kv_heads][head_dim] kv_dtype
+ *   value_cache    same layout as key_cache
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; only entries j < ceil(L / block_size) are read
+ *   context_lens   int32 [num_seqs]; 0 <= L <= max_context_len (longer lengths are clamped)
+ *   scale          multiplies q . k before the softmax (1/sqrt(head_dim) in the usual models)
+ *   block_size     tokens per block: 16, 32, 64, 128 or 256
+ *   head_dim       64 or 128
+ *   num_q_heads    a multiple of num_kv_heads
+ *   max_context_len  upper bound of context_lens, <= max_blocks_per_seq * block_size
+ *   (q_dtype, kv_dtype)  (PA_F32, PA_F32) or (PA_BF16, PA_BF16); accumulation is fp32 either way
+ *   partition_size 0 = one pass over each context; > 0 = split each context into partitions of this many
+ *                  tokens (a multiple of 16) and merge the partial softmax states with a log-sum-exp
+ *                  reduction; -1 = the library chooses (paged_attention_partition_size)
+ *   workspace      device scratch of at least paged_attention_workspace_bytes(...) bytes when that is
+ *                  non-zero (may be NULL otherwise); contents need no initialisation and are clobbered
+ *   stream         hipStream_t
+ * num_seqs == 0 is a no-op returning PA_OK.
+ */
+int paged_attention_decode(float *out, const void *query, const void *key_cache, const void *value_cache,
+                           const int32_t *block_tables, const int32_t *context_lens, float scale,
+                           int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int32_t q_dtype, int32_t kv_dtype, int32_t partition_size,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Append each new token's K/V to its cache slot (page 3 section 2.1: every decode step updates the KV cache
+ * after sampling; page 1 section 3.2: a slot is a (physical block, offset) pair):
+ *     key_cache[slot / block_size][slot % block_size][:][:] = key[n][:][:]   (likewise value)
+ * for n < num_tokens with slot = slot_mapping[n]. Bytes are copied unchanged. Slots < 0 (padding) and slots
+ * >= num_blocks * block_size are skipped. Slots must be distinct (otherwise the surviving write is not
+ * specified).
+ *
+ *   key, value               [num_tokens][num_kv_heads][head_dim] kv_dtype
+ *   key_cache, value_cache   [num_blocks][block_size][num_kv_heads][head_dim] kv_dtype, updated in place
+ *   slot_mapping             int32 [num_tokens]
+ * num_tokens == 0 is a no-op returning PA_OK.
+ */
+int reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
+                      const int32_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t kv_dtype, void *stream);
+
+/*
+ * Copy-on-write of shared blocks (page 1 section 3.2: sequences share physical blocks until one of them
+ * writes; then the block is copied): for each pair p, block block_pairs[p][1] (dst) of both pools becomes a
+ * byte copy of block block_pairs[p][0] (src). Destinations must be distinct and no block may be both a
+ * source and a destination (pairs are then independent and run concurrently). Pairs with an id outside
+ * [0, num_blocks) are skipped.
+ *
+ *   key_cache, value_cache   pools as above, updated in place
+ *   block_pairs              int32 [num_pairs][2] = {src, dst}, device memory
+ * num_pairs == 0 is a no-op returning PA_OK.
+ */
+int copy_blocks(void *key_cache, void *value_cache, const int32_t *block_pairs, int32_t num_pairs,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t kv_dtype,
+                void *stream);
+
+/*
+ * Logical-order gather through the block table, with the same device address arithmetic that
+ * paged_attention_decode uses (exported so that tests can check that indexing byte for byte):
+ *     out_key[s][t][:][:] = key_cache[block_tables[s][t / block_size]][t % block_size][:][:]   (likewise V)
+ * for t < min(context_lens[s], max_context_len). Rows t >= L of out_key/out_value are left untouched; a row
+ * whose table entry is outside [0, num_blocks) is left untouched too.
+ *
+ *   out_key, out_value  [num_seqs][max_context_len][num_kv_heads][head_dim] kv_dtype
+ *   other arguments as in paged_attention_decode
+ */
+int paged_gather(void *out_key, void *out_value, const void *key_cache, const void *value_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, int32_t block_size, int32_t num_seqs,
+                 int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                 int32_t max_context_len, int32_t kv_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H */

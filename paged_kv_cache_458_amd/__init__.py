@@ -1,0 +1,212 @@
+"""MI355X (gfx950) paged decode attention.
+
+A thin Python binding over ``libpagedattn.so`` (the C ABI in ``include/paged_attention.h``). It only checks and
+marshals arguments -- every step of the decode path runs in the library's HIP kernels. There is no fallback:
+if the library is missing or fails to load, every call raises.
+
+The functions take torch tensors that already live on the GPU (PyTorch supplies device memory and streams),
+and launch on the current stream of the tensors' device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libpagedattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention.h")
+
+PA_F32, PA_BF16 = 0, 1
+PA_OK = 0
+ABI_VERSION = 1
+
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {strerror(status)} (status {status})")
+
+
+def load_library(path: str | None = None):
+    """Load libpagedattn.so and declare its signatures. Raises if it is missing or its ABI differs."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is not built; run `python -m paged_kv_cache_458_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.pa_abi_version.argtypes, lib.pa_abi_version.restype = [], ctypes.c_int
+    lib.pa_strerror.argtypes, lib.pa_strerror.restype = [ctypes.c_int], ctypes.c_char_p
+    sizes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_attention_partition_size.argtypes, lib.paged_attention_partition_size.restype = sizes, i32
+    lib.paged_attention_workspace_bytes.argtypes, lib.paged_attention_workspace_bytes.restype = sizes, sz
+    lib.paged_attention_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, i32, i32, i32, i32, i32, i64, i32, i32,
+                                           i32, i32, i32, P, sz, P]
+    lib.paged_attention_decode.restype = ctypes.c_int
+    lib.reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32, P]
+    lib.reshape_and_cache.restype = ctypes.c_int
+    lib.copy_blocks.argtypes = [P, P, P, i32, i32, i32, i32, i64, i32, P]
+    lib.copy_blocks.restype = ctypes.c_int
+    lib.paged_gather.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i64, i32, i32, i32, P]
+    lib.paged_gather.restype = ctypes.c_int
+    if lib.pa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{p}: ABI version {lib.pa_abi_version()} != {ABI_VERSION}")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().pa_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != PA_OK:
+        raise PagedAttentionError(fn, status)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; the kernels take float32 or bfloat16")
+
+
+def _dev(*tensors):
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device != dev or t.device.type != "cuda":
+            raise ValueError("all tensors must live on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(dev, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _int32(t, name):
+    if t.dtype != _torch().int32:
+        raise TypeError(f"{name} must be int32")
+
+
+def partition_size_for(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
+                       partition_size=-1) -> int:
+    """Partition size the decode call launches with (0 = single pass)."""
+    r = load_library().paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                      max_context_len, kv_dtype, partition_size)
+    _check("paged_attention_partition_size", r if r < 0 else 0)
+    return int(r)
+
+
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
+                    partition_size=-1) -> int:
+    return int(load_library().paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                              block_size, max_context_len, kv_dtype, partition_size))
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                           block_size: int | None = None, *, max_context_len: int | None = None,
+                           partition_size: int = -1, workspace=None, stream=None):
+    """out[s, h] = softmax(scale * query[s, h] . K^T) . V over sequence s's paged K/V (see the C header).
+
+    out: fp32 [B, Hq, D]; query: [B, Hq, D]; key_cache/value_cache: [NB, bs, Hkv, D] (same dtype as query);
+    block_tables: int32 [B, MB]; context_lens: int32 [B]. max_context_len defaults to MB * bs (an upper bound
+    needs no device sync). A workspace is allocated with torch when the split path needs one and none is given.
+    """
+    torch = _torch()
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+    if out.dtype != torch.float32:
+        raise TypeError("out must be float32")
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    B, Hq, D = query.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    if block_size is not None and block_size != bs:
+        raise ValueError("block_size disagrees with key_cache.shape[1]")
+    if D2 != D or value_cache.shape != key_cache.shape or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("shape mismatch between out, query and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    MB = block_tables.shape[1]
+    mcl = MB * bs if max_context_len is None else int(max_context_len)
+    qd, kd = _dtype_code(query), _dtype_code(key_cache)
+    lib = load_library()
+    need = lib.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl, kd, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.paged_attention_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                                    block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, B, Hq, Hkv,
+                                    D, NB, MB, mcl, qd, kd, int(partition_size), ws_ptr, ws_len,
+                                    _stream(dev, stream))
+    _check("paged_attention_decode", st)
+    return out
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, stream=None):
+    """key_cache[slot // bs, slot % bs] = key[n] (and value) for every n with slot = slot_mapping[n] >= 0."""
+    dev = _dev(key, value, key_cache, value_cache, slot_mapping)
+    _int32(slot_mapping, "slot_mapping")
+    N, Hkv, D = key.shape
+    NB, bs, Hkv2, D2 = key_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or value.shape != key.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if key.dtype != key_cache.dtype or value.dtype != value_cache.dtype or key.dtype != value.dtype:
+        raise TypeError("key/value must match the cache dtype")
+    if tuple(slot_mapping.shape) != (N,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = load_library().reshape_and_cache(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                          value_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB,
+                                          _dtype_code(key_cache), _stream(dev, stream))
+    _check("reshape_and_cache", st)
+
+
+def copy_blocks(key_cache, value_cache, block_pairs, *, stream=None):
+    """Copy-on-write: block dst of both pools becomes a copy of block src for each (src, dst) row of block_pairs."""
+    dev = _dev(key_cache, value_cache, block_pairs)
+    _int32(block_pairs, "block_pairs")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [P, 2]")
+    NB, bs, Hkv, D = key_cache.shape
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache must agree")
+    st = load_library().copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), block_pairs.data_ptr(),
+                                    block_pairs.shape[0], bs, Hkv, D, NB, _dtype_code(key_cache),
+                                    _stream(dev, stream))
+    _check("copy_blocks", st)
+
+
+def paged_gather(out_key, out_value, key_cache, value_cache, block_tables, context_lens, *, stream=None):
+    """out_key[s, t] = key_cache row of position t of sequence s (t < L), through the kernels' addressing."""
+    dev = _dev(out_key, out_value, key_cache, value_cache, block_tables, context_lens)
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    NB, bs, Hkv, D = key_cache.shape
+    B, mcl = out_key.shape[0], out_key.shape[1]
+    if tuple(out_key.shape) != (B, mcl, Hkv, D) or out_value.shape != out_key.shape:
+        raise ValueError("out_key/out_value must be [B, max_context_len, Hkv, D]")
+    if out_key.dtype != key_cache.dtype:
+        raise TypeError("gather output must match the cache dtype")
+    st = load_library().paged_gather(out_key.data_ptr(), out_value.data_ptr(), key_cache.data_ptr(),
+                                     value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), bs, B,
+                                     Hkv, D, NB, block_tables.shape[1], mcl, _dtype_code(key_cache),
+                                     _stream(dev, stream))
+    _check("paged_gather", st)

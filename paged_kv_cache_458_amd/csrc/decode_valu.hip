@@ -1,0 +1,248 @@
+// Paged decode attention on the vector ALUs of gfx950: one wave64 per (sequence, query head, partition).
+//
+// What it computes (vLLM PagedAttention, page 1 sections 3.1-3.2): the new token of each sequence attends
+// over all earlier K/V of that sequence, which the block table scatters through the block pools. The
+// softmax is taken in one streaming pass with a running maximum and sum (online softmax), so K and V are
+// read from HBM exactly once.
+//
+// Lane layout. A 16-byte load covers 8 bf16 or 4 fp32 elements, so one head's row (head_dim elements) spans
+// kRowLanes lanes and one wave-wide load covers kRows consecutive slots of a block; a 16-token tile takes
+// kLoads loads for K and as many for V. Every lane consumes exactly the bytes it loaded -- there is no reuse
+// to stage through LDS. Each group of kRowLanes lanes ("row group") owns the tile rows r, r + kRows, ... and
+// keeps its own running (max, sum, accumulator); the groups are merged once at the end with the same
+// log-sum-exp rule the split-context reduce uses. The dot product of a row is finished with DPP adds inside
+// the row group, so a score never leaves its 16 lanes.
+//
+// Pipelining. Tile j+1 is loaded into a second register set while tile j is consumed; the block id of a
+// tile comes from a scalar load of the table, so address generation stays on the scalar unit.
+#include "pa_device.h"
+#include "pa_kernels.h"
+#include "../../include/paged_attention.h"
+
+namespace pa {
+namespace {
+
+template <int KV, int D>
+struct Shape {
+  static constexpr int kEsize = KV == PA_BF16 ? 2 : 4;
+  static constexpr int kEpl = 16 / kEsize;        // elements per lane per 16-byte load
+  static constexpr int kRowLanes = D / kEpl;      // lanes holding one head's row
+  static constexpr int kRows = kWave / kRowLanes; // slots per wave-wide load
+  static constexpr int kLoads = kTile / kRows;    // loads per 16-token tile (per K and per V)
+};
+
+template <int KV>
+__device__ __forceinline__ float dot_chunk(const U4& q, const U4& k);
+
+template <>
+__device__ __forceinline__ float dot_chunk<PA_BF16>(const U4& q, const U4& k) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  float d = 0.f;
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), d, false);
+  return d;
+}
+
+template <>
+__device__ __forceinline__ float dot_chunk<PA_F32>(const U4& q, const U4& k) {
+  float d = __uint_as_float(q.x) * __uint_as_float(k.x);
+  d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
+  d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
+  d = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
+  return d;
+}
+
+template <int KV>
+__device__ __forceinline__ void axpy_chunk(float* acc, float p, const U4& v) {
+  if constexpr (KV == PA_BF16) {
+    acc[0] = fmaf(p, bf16_lo(v.x), acc[0]);
+    acc[1] = fmaf(p, bf16_hi(v.x), acc[1]);
+    acc[2] = fmaf(p, bf16_lo(v.y), acc[2]);
+    acc[3] = fmaf(p, bf16_hi(v.y), acc[3]);
+    acc[4] = fmaf(p, bf16_lo(v.z), acc[4]);
+    acc[5] = fmaf(p, bf16_hi(v.z), acc[5]);
+    acc[6] = fmaf(p, bf16_lo(v.w), acc[6]);
+    acc[7] = fmaf(p, bf16_hi(v.w), acc[7]);
+  } else {
+    acc[0] = fmaf(p, __uint_as_float(v.x), acc[0]);
+    acc[1] = fmaf(p, __uint_as_float(v.y), acc[1]);
+    acc[2] = fmaf(p, __uint_as_float(v.z), acc[2]);
+    acc[3] = fmaf(p, __uint_as_float(v.w), acc[3]);
+  }
+}
+
+constexpr int kWavesPerGroup = 4;  // waves (query heads) per workgroup
+
+template <int KV, int D>
+__global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(const DecodeArgs a) {
+  using S = Shape<KV, D>;
+  constexpr int NL = S::kLoads;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int h = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int part = blockIdx.y;
+  const int s = blockIdx.z;
+  if (h >= a.num_q_heads) return;
+
+  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  const int t0 = part * a.partition;
+  if (part > 0 && t0 >= L) return;  // this sequence has fewer partitions
+  const int t1 = min(L, t0 + a.partition);
+  const int g = h / a.group;
+  const int r = lane / S::kRowLanes;  // row group
+  const int c = lane % S::kRowLanes;  // 16-byte chunk of the head's row
+
+  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
+  uint32_t lane_off[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    lane_off[i] = (uint32_t)((i * S::kRows + r) * row_bytes + (int64_t)g * D * S::kEsize + c * 16);
+
+  const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
+  const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
+  const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const U4 q = *reinterpret_cast<const U4*>(static_cast<const char*>(a.query) +
+                                            ((int64_t)s * a.num_q_heads + h) * D * S::kEsize + c * 16);
+
+  float m = -INFINITY, l = 0.f;
+  float acc[S::kEpl];
+#pragma unroll
+  for (int e = 0; e < S::kEpl; ++e) acc[e] = 0.f;
+  bool bad = false;
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+
+  U4 kA[NL], vA[NL], kB[NL], vB[NL];
+  // Loads of a tile index past the end re-read the last tile (cache hits): the loads stay unconditional so
+  // the wait counters of the two register sets never merge across a branch.
+  auto issue = [&](U4* kb, U4* vb, int tile) {
+    const int t = t0 + min(tile, ntiles - 1) * kTile;
+    const int64_t base = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
+    const char* kp = kbase + base;
+    const char* vp = vbase + base;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      kb[i] = *reinterpret_cast<const U4*>(kp + lane_off[i]);
+      vb[i] = *reinterpret_cast<const U4*>(vp + lane_off[i]);
+    }
+  };
+  auto consume = [&](const U4* kb, const U4* vb, int tile) {
+    const int t = t0 + tile * kTile;
+    const bool full = t + kTile <= t1;
+    float sc[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      sc[i] = group_sum<S::kRowLanes>(dot_chunk<KV>(q, kb[i])) * a.scale_log2;
+      if (!full && t + i * S::kRows + r >= t1) sc[i] = -INFINITY;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) mt = fmaxf(mt, sc[i]);
+    const float mn = fmaxf(m, mt);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float p = fast_exp2(sc[i] - mref);
+      l += p;
+      U4 v = vb[i];
+      if (!full && t + i * S::kRows + r >= t1) v = U4{0u, 0u, 0u, 0u};  // a past-the-end slot may hold NaN
+      axpy_chunk<KV>(acc, p, v);
+    }
+    m = mn;
+  };
+
+  if (ntiles > 0) {
+    issue(kA, vA, 0);
+    int j = 0;
+    for (; j + 2 <= ntiles; j += 2) {
+      issue(kB, vB, j + 1);
+      consume(kA, vA, j);
+      issue(kA, vA, j + 2);
+      consume(kB, vB, j + 1);
+    }
+    if (j < ntiles) consume(kA, vA, j);
+  }
+
+  // merge the row groups: lanes l, l ^ kRowLanes, ... hold the same dims of different token subsets
+#pragma unroll
+  for (int off = S::kRowLanes; off < kWave; off <<= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    const float M = fmaxf(m, mo);
+    const float Mr = M == -INFINITY ? 0.f : M;
+    const float fa = fast_exp2(m - Mr), fb = fast_exp2(mo - Mr);
+    l = l * fa + lo * fb;
+#pragma unroll
+    for (int e = 0; e < S::kEpl; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], off) * fb;
+    m = M;
+  }
+
+  if (r == 0) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float poison = __uint_as_float(0x7fc00000u);
+    float res[S::kEpl];
+#pragma unroll
+    for (int e = 0; e < S::kEpl; ++e) res[e] = bad ? poison : acc[e] * inv;
+    float* dst;
+    if (!a.split || L <= a.partition) {
+      dst = a.out + ((int64_t)s * a.num_q_heads + h) * D + c * S::kEpl;
+    } else {
+      const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + part;
+      dst = a.ws_o + row * D + c * S::kEpl;
+      if (c == 0) {
+        a.ws_ml[2 * row] = bad ? poison : m;
+        a.ws_ml[2 * row + 1] = l;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < S::kEpl; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(res[e], res[e + 1], res[e + 2], res[e + 3]);
+  }
+}
+
+// Merge of split-context partials: with partition p giving running max m_p (log2 units), sum l_p and
+// normalised output o_p, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p).
+__global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  if (L <= a.partition) return;  // single partition: written by the partition kernel
+  const int np = (L + a.partition - 1) / a.partition;
+  const int64_t row0 = ((int64_t)s * a.num_q_heads + h) * a.max_partitions;
+  const float* __restrict__ ml = a.ws_ml + 2 * row0;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  float wsum = 0.f;
+  for (int p = 0; p < np; ++p) wsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  const float inv = 1.0f / wsum;
+  for (int d = threadIdx.x; d < a.head_dim; d += kWave) {
+    float acc = 0.f;
+    for (int p = 0; p < np; ++p) acc += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) * a.ws_o[(row0 + p) * a.head_dim + d];
+    a.out[((int64_t)s * a.num_q_heads + h) * a.head_dim + d] = acc * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.split ? a.max_partitions : 1,
+                  a.num_seqs);
+  const dim3 block(kWave * kWavesPerGroup);
+  if (kv_dtype == PA_BF16 && a.head_dim == 128) decode_valu_kernel<PA_BF16, 128><<<grid, block, 0, stream>>>(a);
+  else if (kv_dtype == PA_BF16 && a.head_dim == 64) decode_valu_kernel<PA_BF16, 64><<<grid, block, 0, stream>>>(a);
+  else if (kv_dtype == PA_F32 && a.head_dim == 128) decode_valu_kernel<PA_F32, 128><<<grid, block, 0, stream>>>(a);
+  else if (kv_dtype == PA_F32 && a.head_dim == 64) decode_valu_kernel<PA_F32, 64><<<grid, block, 0, stream>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
+  lse_reduce_kernel<<<dim3(a.num_q_heads, a.num_seqs), dim3(kWave), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,250 @@
+// C ABI of libpagedattn.so: host-side argument checks, launch planning (single pass or split context,
+// VALU or MFMA variant, workspace layout) and the launches themselves. Every check runs before any HIP call,
+// so an invalid call returns its status without touching the device.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/paged_attention.h"
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int kTileTokens = 16;
+constexpr int kMaxGridYZ = 65535;
+
+int esize_of(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 0; }
+
+int log2_pow2(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return k;
+}
+
+bool supported_block_size(int bs) { return bs >= 16 && bs <= 256 && log2_pow2(bs) >= 0; }
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Plan {
+  int status = PA_OK;
+  int32_t partition = 0;       // tokens per partition as launched
+  int32_t max_partitions = 1;  // partitions of the longest context
+  bool split = false;
+  size_t ws_bytes = 0;
+  size_t ws_ml_offset = 0;
+};
+
+// Library choice of partition size. Long contexts are cut so that the grid has many more partition
+// workgroups than the chip has slots for (load balance across 256 CUs), while a partition still streams
+// enough K/V that the partial write and the reduce stay a small fraction of the traffic.
+int32_t pick_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
+  (void)num_seqs;
+  (void)num_q_heads;
+  (void)num_kv_heads;
+  if (max_context_len <= 256) return 0;
+  return 256;
+}
+
+Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+               int32_t max_context_len, int32_t kv_dtype, int32_t partition_size) {
+  Plan p;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_context_len < 0 || num_q_heads % num_kv_heads != 0) {
+    p.status = PA_ERR_SHAPE;
+    return p;
+  }
+  if (esize_of(kv_dtype) == 0) {
+    p.status = PA_ERR_DTYPE;
+    return p;
+  }
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || num_seqs > kMaxGridYZ) {
+    p.status = PA_ERR_UNSUPPORTED;
+    return p;
+  }
+  if (partition_size < -1 || (partition_size > 0 && partition_size % kTileTokens != 0)) {
+    p.status = PA_ERR_SHAPE;
+    return p;
+  }
+  int32_t part = partition_size == -1 ? pick_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len)
+                                      : partition_size;
+  const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
+  if (part == 0 || part >= whole) {
+    p.partition = (int32_t)(whole > INT32_MAX ? INT32_MAX : whole);
+    p.max_partitions = 1;
+    p.split = false;
+    return p;
+  }
+  const int64_t pm = (max_context_len + (int64_t)part - 1) / part;
+  if (pm > kMaxGridYZ) {
+    p.status = PA_ERR_UNSUPPORTED;
+    return p;
+  }
+  p.partition = part;
+  p.max_partitions = (int32_t)pm;
+  p.split = true;
+  const size_t o_bytes = pa::ws_o_elems(num_seqs, num_q_heads, pm, head_dim) * sizeof(float);
+  p.ws_ml_offset = round_up(o_bytes, 256);
+  p.ws_bytes = p.ws_ml_offset + pa::ws_ml_elems(num_seqs, num_q_heads, pm) * sizeof(float);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid or inconsistent sizes";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unsupported dtype or dtype pair";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size or grid size not implemented";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch or runtime call failed";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t kv_dtype, int32_t partition_size) {
+  const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
+                           partition_size);
+  if (p.status != PA_OK) return p.status;
+  return p.split ? p.partition : 0;
+}
+
+size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t kv_dtype, int32_t partition_size) {
+  const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
+                           partition_size);
+  return p.status == PA_OK ? p.ws_bytes : 0;
+}
+
+int paged_attention_decode(float* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int32_t q_dtype, int32_t kv_dtype, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                              kv_dtype, partition_size);
+  if (plan.status != PA_OK) return plan.status;
+  if (q_dtype != kv_dtype || esize_of(q_dtype) == 0) return PA_ERR_DTYPE;
+  if (num_blocks <= 0 || num_blocks > INT32_MAX || max_blocks_per_seq <= 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens))
+    return PA_ERR_ALIGN;
+  if (plan.split) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_o = plan.split ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = plan.split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.group = num_q_heads / num_kv_heads;
+  a.bs_log2 = log2_pow2(block_size);
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.partition = plan.partition;
+  a.max_partitions = plan.max_partitions;
+  a.split = plan.split ? 1 : 0;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (a.group > 1 && pa::gqa_mfma_supported(kv_dtype, head_dim, a.group))
+    err = pa::launch_decode_gqa_mfma(a, st);
+  else
+    err = pa::launch_decode_valu(a, kv_dtype, st);
+  if (err != hipSuccess) return PA_ERR_HIP;
+  if (plan.split && pa::launch_lse_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, int32_t kv_dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (esize_of(kv_dtype) == 0) return PA_ERR_DTYPE;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * esize_of(kv_dtype);
+  if (row_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(slot_mapping))
+    return PA_ERR_ALIGN;
+  if (num_tokens > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  return pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens, row_bytes,
+                                      block_size, num_blocks, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs, int32_t num_pairs,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t kv_dtype,
+                void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (esize_of(kv_dtype) == 0) return PA_ERR_DTYPE;
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * esize_of(kv_dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_pairs) return PA_ERR_NULL;
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned4(block_pairs)) return PA_ERR_ALIGN;
+  const int64_t per_wg = 256 * 4 * 16;
+  if ((block_bytes + per_wg - 1) / per_wg > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  return pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs, block_bytes, num_blocks,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int paged_gather(void* out_key, void* out_value, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int32_t block_size, int32_t num_seqs,
+                 int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                 int32_t max_context_len, int32_t kv_dtype, void* stream) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || num_blocks > INT32_MAX ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return PA_ERR_SHAPE;
+  if (esize_of(kv_dtype) == 0) return PA_ERR_DTYPE;
+  if (!supported_block_size(block_size) || num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * esize_of(kv_dtype);
+  if (row_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (!out_key || !out_value || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out_key) || !aligned16(out_value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(block_tables) || !aligned4(context_lens))
+    return PA_ERR_ALIGN;
+  return pa::launch_paged_gather(out_key, out_value, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                                 log2_pow2(block_size), num_blocks, max_blocks_per_seq, max_context_len, row_bytes,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+}  // extern "C"

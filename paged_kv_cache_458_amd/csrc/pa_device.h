@@ -1,0 +1,57 @@
+// Device helpers shared by the gfx950 kernels of libpagedattn: block-table address arithmetic, bf16 decode,
+// wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kTile = 16;  // tokens per tile; a tile never straddles a block because block_size >= 16
+
+struct alignas(16) U4 {
+  uint32_t x, y, z, w;
+};
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------------------------------------
+// Paged addressing (vLLM PagedAttention, page 1 section 3.2; page 3 section 2.2). Pools are
+// [num_blocks][block_size][num_kv_heads][head_dim]; one "row" is a slot: all KV heads of one position,
+// row_bytes = num_kv_heads * head_dim * element size. Position t of a sequence sits in slot
+// block_table_row[t >> bs_log2] * block_size + (t & (block_size - 1)).
+//
+// Byte offset of the slot holding position t (t a multiple of kTile, so the kTile positions t .. t+15 are
+// consecutive slots of one block). A table entry outside [0, num_blocks) is replaced by block 0 -- always a
+// valid address -- and reported through `bad` so the caller can poison its result instead of faulting.
+__device__ __forceinline__ int64_t tile_slot_bytes(const int32_t* __restrict__ table_row, int t, int bs_log2,
+                                                   int64_t num_blocks, int64_t row_bytes, bool& bad) {
+  const int32_t phys = table_row[t >> bs_log2];
+  const bool ok = (uint32_t)phys < (uint64_t)num_blocks;
+  bad |= !ok;
+  const int64_t block = ok ? (int64_t)phys : 0;
+  return ((block << bs_log2) + (t & ((1 << bs_log2) - 1))) * row_bytes;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Sum over aligned groups of N lanes (N = 4, 8 or 16), result in every lane of the group, via DPP
+// (quad_perm swaps, then half-row and row mirrors: each step adds the partner's partial sum).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));  // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));  // lane ^ 2
+  if constexpr (N >= 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // 8-mirror
+  if constexpr (N >= 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // 16-mirror
+  if constexpr (N == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa
