@@ -136,6 +136,28 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention {attn_avg_ms * 1e3:.1f} us "
         f"(median {np.median(attn_ms) * 1e3:.1f}, min {np.min(attn_ms) * 1e3:.1f})")
 
+    # the practical ceiling: a plain streaming read (same 16-byte loads) and copy over 4 GiB on this device
+    big = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    big2 = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    sink = torch.empty(pa.STREAM_SINK_FLOATS, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        pa.stream_read(big, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        pa.stream_read(big, sink)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    read_gbs = 10 * big.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    e0.record(stream)
+    for _ in range(10):
+        pa.stream_copy(big2, big[: big2.numel()])
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    copy_gbs = 10 * 2 * big2.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big, big2
+    log(f"streaming read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s (read + write)")
+
     ab = algorithmic_bytes(st)
     row_bytes = Hkv * D * st.esize
     cache_write_bytes = 2 * 2 * int((st.slot_mapping >= 0).sum()) * row_bytes  # read + write, K and V
@@ -185,6 +207,8 @@ def main() -> int:
             "kv_unique_bytes": ab["kv_unique"],
         },
         "step_bytes": step_bytes,
+        "device_stream_read_gbs": round(read_gbs, 1),
+        "device_stream_copy_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attention_decode (partition kernel + log-sum-exp reduce when split)",

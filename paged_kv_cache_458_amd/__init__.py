@@ -16,6 +16,8 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libpagedattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention.h")
+DIAG_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention_diag.h")
+STREAM_SINK_FLOATS = 8192
 
 PA_F32, PA_BF16 = 0, 1
 PA_OK = 0
@@ -54,6 +56,8 @@ def load_library(path: str | None = None):
     lib.copy_blocks.restype = ctypes.c_int
     lib.paged_gather.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i64, i32, i32, i32, P]
     lib.paged_gather.restype = ctypes.c_int
+    lib.pa_stream_read.argtypes, lib.pa_stream_read.restype = [P, sz, P, P], ctypes.c_int
+    lib.pa_stream_copy.argtypes, lib.pa_stream_copy.restype = [P, P, sz, P], ctypes.c_int
     if lib.pa_abi_version() != ABI_VERSION:
         raise ImportError(f"{p}: ABI version {lib.pa_abi_version()} != {ABI_VERSION}")
     if path is None:
@@ -210,3 +214,24 @@ def paged_gather(out_key, out_value, key_cache, value_cache, block_tables, conte
                                      Hkv, D, NB, block_tables.shape[1], mcl, _dtype_code(key_cache),
                                      _stream(dev, stream))
     _check("paged_gather", st)
+
+
+def stream_read(src, sink, *, stream=None):
+    """Diagnostic: read every byte of ``src`` once (HBM read-rate probe); ``sink`` is fp32 with at least
+    STREAM_SINK_FLOATS elements."""
+    dev = _dev(src, sink)
+    if sink.dtype != _torch().float32 or sink.numel() < STREAM_SINK_FLOATS:
+        raise ValueError("sink must be float32 with at least STREAM_SINK_FLOATS elements")
+    st = load_library().pa_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                       _stream(dev, stream))
+    _check("pa_stream_read", st)
+
+
+def stream_copy(dst, src, *, stream=None):
+    """Diagnostic: copy ``src`` into ``dst`` (same byte size) with the library's streaming copy kernel."""
+    dev = _dev(dst, src)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src must have the same byte size")
+    st = load_library().pa_stream_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(dev, stream))
+    _check("pa_stream_copy", st)

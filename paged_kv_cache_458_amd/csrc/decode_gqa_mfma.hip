@@ -1,10 +1,250 @@
-// Grouped-query decode on the MFMA units (placeholder until the kernel lands: every case runs on VALU).
+// Grouped-query paged decode on the MFMA units of gfx950: one wave64 per (sequence, KV head, partition).
+//
+// When G = num_q_heads / num_kv_heads query heads share one KV head, every K/V row read from HBM serves G
+// dot products and G axpys; at G = 8 that would keep the vector ALUs busier than the memory system, so the
+// two products run as small dense contractions on v_mfma_f32_16x16x32_bf16 (bf16 inputs, fp32 accumulate):
+//
+//   S^T[32 tokens x 16]  = K_tile[32 x D] . Q^T[D x 16]      (the G heads padded to 16 columns)
+//   O^T[D x 16]         += V_tile^T[D x 32] . P^T[32 x 16]
+//
+// Operand layouts. K rows are the A operand of the first product and are loaded straight from the pool in
+// MFMA layout (lane (n, j) = (lane % 16, lane / 16) reads row n, bytes 64c + 16j of each 16-row half).
+// The result leaves lane (n, j) with the scores of head n for tokens 4j..4j+3 of both halves; those eight
+// probabilities are exactly that lane's B operand of the second product once the contraction index k = 8j + e
+// is mapped to token (e < 4 ? 4j + e : 16 + 4j + e - 4) -- no data moves between lanes. V^T needs eight
+// tokens of one dim per lane, the transpose of the pool's layout, so each wave stages its V tile in its own
+// LDS slice (rows padded by 16 bytes, which spreads the four token groups over distinct banks) and reads it
+// back as 16-bit elements. The accumulator of the second product leaves lane (n, j) with head n, the same
+// head as its softmax state, so the online-softmax rescale is a per-lane multiply.
+//
+// K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
+// loads of the block table (one per 16-token half). Scores use the exp2 domain (scale * log2 e folded in).
+#include "pa_device.h"
 #include "pa_kernels.h"
+#include "../../include/paged_attention.h"
 
 namespace pa {
+namespace {
 
-bool gqa_mfma_supported(int, int, int) { return false; }
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-hipError_t launch_decode_gqa_mfma(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
+constexpr int kWaves = 4;      // waves (KV heads) per workgroup
+constexpr int kTileTok = 32;   // tokens per tile: two 16-row halves
+
+__device__ __forceinline__ f32x4 mfma(const U4& a, const U4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const DecodeArgs a) {
+  constexpr int kChunks = D / 32;          // 32-dim k-chunks of the QK product
+  constexpr int kNt = D / 16;              // 16-dim column tiles of the PV product
+  constexpr int kPitch = D * 2 + 16;       // LDS bytes per V row
+  constexpr int kSlice = kTileTok * kPitch;
+  constexpr int kVLanes = D * 2 / 16;      // lanes covering one V row with 16-byte loads
+  constexpr int kVRows = kWave / kVLanes;  // V rows per wave-wide load
+  constexpr int kVLoads = kTile / kVRows;  // V loads per 16-row half
+  __shared__ __attribute__((aligned(16))) char lds[kWaves * kSlice];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int g = blockIdx.x * kWaves + w;
+  const int part = blockIdx.y;
+  const int s = blockIdx.z;
+  if (g >= a.num_kv_heads) return;  // no workgroup barriers below: each wave owns its LDS slice
+
+  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  const int t0 = part * a.partition;
+  if (part > 0 && t0 >= L) return;
+  const int t1 = min(L, t0 + a.partition);
+  const int G = a.group;
+  const int n = lane & 15;  // MFMA column: query head within the group (valid when n < G)
+  const int j = lane >> 4;  // 0..3
+  const int vr = lane / kVLanes;  // V staging: row within a load
+  const int vc = lane % kVLanes;  //            16-byte chunk within the row
+  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * 2;
+  const int64_t head_off = (int64_t)g * D * 2;
+  char* const slice = lds + w * kSlice;
+
+  // Q^T (B operand of S^T = K Q^T): lane (n, j) holds q[g*G + n][32c + 8j .. 32c + 8j + 7]; padding heads are 0.
+  const bool head_ok = n < G;
+  const char* qrow = static_cast<const char*>(a.query) +
+                     ((int64_t)s * a.num_q_heads + (int64_t)g * G + (head_ok ? n : 0)) * D * 2;
+  U4 qb[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const U4 v = *reinterpret_cast<const U4*>(qrow + c * 64 + j * 16);
+    qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
+  }
+
+  // per-lane byte offsets inside a 16-row half tile
+  uint32_t koff[kChunks], voff[kVLoads];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) koff[c] = (uint32_t)(n * row_bytes + head_off + c * 64 + j * 16);
+#pragma unroll
+  for (int i = 0; i < kVLoads; ++i) voff[i] = (uint32_t)((vr + kVRows * i) * row_bytes + head_off + vc * 16);
+
+  const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
+  const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
+  const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[kNt];
+#pragma unroll
+  for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+  const int ntiles = (t1 - t0 + kTileTok - 1) / kTileTok;
+  const int last_half = ntiles > 0 ? ((t1 - 1) & ~(kTile - 1)) : t0;  // start of the last live 16-token half
+
+  U4 kA[2][kChunks], vA[2][kVLoads], kB[2][kChunks], vB[2][kVLoads];
+  auto issue = [&](U4 (*kb)[kChunks], U4 (*vb)[kVLoads], int tile) {
+    const int t = t0 + min(tile, ntiles - 1) * kTileTok;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int th = min(t + h2 * kTile, last_half);  // a half past the end re-reads a live one (masked)
+      const int64_t base = tile_slot_bytes(table, th, a.bs_log2, a.num_blocks, row_bytes, bad);
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) kb[h2][c] = *reinterpret_cast<const U4*>(kbase + base + koff[c]);
+#pragma unroll
+      for (int i = 0; i < kVLoads; ++i) vb[h2][i] = *reinterpret_cast<const U4*>(vbase + base + voff[i]);
+    }
+  };
+
+  // LDS addresses: V row r at slice + r * kPitch; this lane writes rows vr + kVRows*i (+16 for the second half)
+  // at column vc * 16 bytes and reads the 16-bit element of dim 16nt + n from rows token(8j + e).
+  char* const wbase = slice + vr * kPitch + vc * 16;
+  const char* const rbase = slice + 4 * j * kPitch + n * 2;
+
+  auto consume = [&](U4 (*kb)[kChunks], U4 (*vb)[kVLoads], int tile) {
+    const int t = t0 + tile * kTileTok;
+    const bool full = t + kTileTok <= t1;
+    // stage V (rows past the end are zeroed: their slots may hold NaN); the previous tile's reads come first
+    wave_lds_sync();
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < kVLoads; ++i) {
+        U4 v = vb[h2][i];
+        if (!full && t + h2 * kTile + vr + kVRows * i >= t1) v = U4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<U4*>(wbase + (h2 * kTile + kVRows * i) * kPitch) = v;
+      }
+    wave_lds_sync();
+    // scores
+    f32x4 sc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) sc[h2] = mfma(kb[h2][c], qb[c], sc[h2]);
+    }
+    float sv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = sc[h2][i] * a.scale_log2;
+        if (!full && t + h2 * kTile + 4 * j + i >= t1) x = -INFINITY;
+        sv[h2 * 4 + i] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    m = mn;
+    // probabilities, rounded to bf16 for the MFMA; the running sum adds the rounded values
+    uint32_t pw[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t lo = bf16_bits(fast_exp2(sv[e] - mref));
+      const uint32_t hi = bf16_bits(fast_exp2(sv[e + 1] - mref));
+      psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+      pw[e / 2] = lo | (hi << 16);
+    }
+    l = l * alpha + psum;
+    const U4 pb{pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) {
+      // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4)
+      const char* r = rbase + nt * 32;
+      uint32_t d[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int r0 = (e < 4 ? e : kTile + e - 4) * kPitch;
+        const int r1 = (e + 1 < 4 ? e + 1 : kTile + e + 1 - 4) * kPitch;
+        d[e / 2] = (uint32_t)*reinterpret_cast<const uint16_t*>(r + r0) |
+                   ((uint32_t)*reinterpret_cast<const uint16_t*>(r + r1) << 16);
+      }
+      f32x4 acc = o[nt];
+      acc[0] *= alpha;
+      acc[1] *= alpha;
+      acc[2] *= alpha;
+      acc[3] *= alpha;
+      o[nt] = mfma(U4{d[0], d[1], d[2], d[3]}, pb, acc);
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(kA, vA, 0);
+    int tj = 0;
+    for (; tj + 2 <= ntiles; tj += 2) {
+      issue(kB, vB, tj + 1);
+      consume(kA, vA, tj);
+      issue(kA, vA, tj + 2);
+      consume(kB, vB, tj + 1);
+    }
+    if (tj < ntiles) consume(kA, vA, tj);
+  }
+
+  // each lane summed the probabilities of its own token group j; the max is already shared
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!head_ok) return;
+  const int h = g * G + n;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float poison = __uint_as_float(0x7fc00000u);
+  float* dst;
+  if (!a.split || L <= a.partition) {
+    dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
+  } else {
+    const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + part;
+    dst = a.ws_o + row * D;
+    if (j == 0) {
+      a.ws_ml[2 * row] = bad ? poison : m;
+      a.ws_ml[2 * row + 1] = l;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < kNt; ++nt) {
+    const f32x4 v = o[nt];
+    *reinterpret_cast<float4*>(dst + nt * 16 + 4 * j) =
+        bad ? make_float4(poison, poison, poison, poison)
+            : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  }
+}
+
+}  // namespace
+
+bool gqa_mfma_supported(int kv_dtype, int head_dim, int group) {
+  return kv_dtype == PA_BF16 && (head_dim == 128 || head_dim == 64) && group >= 2 && group <= 16;
+}
+
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((a.num_kv_heads + kWaves - 1) / kWaves, a.split ? a.max_partitions : 1, a.num_seqs);
+  const dim3 block(kWave * kWaves);
+  if (a.head_dim == 128) decode_gqa_mfma_kernel<128><<<grid, block, 0, stream>>>(a);
+  else if (a.head_dim == 64) decode_gqa_mfma_kernel<64><<<grid, block, 0, stream>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 }  // namespace pa

@@ -205,25 +205,63 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
 }
 
 // Merge of split-context partials: with partition p giving running max m_p (log2 units), sum l_p and
-// normalised output o_p, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p).
+// normalised output o_p, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p). One wave per
+// (sequence, head): lane p owns partition p's weight, and every lane accumulates its own head_dim / 64 dims,
+// so the loads of all partitions are independent and in flight together.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <int D>
 __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
+  constexpr int kDpl = D / kWave;  // dims per lane
+  const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   if (L <= a.partition) return;  // single partition: written by the partition kernel
   const int np = (L + a.partition - 1) / a.partition;
   const int64_t row0 = ((int64_t)s * a.num_q_heads + h) * a.max_partitions;
-  const float* __restrict__ ml = a.ws_ml + 2 * row0;
+  const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
   float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[p].x);
+  M = wave_max(M);
+  float acc[kDpl];
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  for (int p = 0; p < np; ++p) wsum += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-  const float inv = 1.0f / wsum;
-  for (int d = threadIdx.x; d < a.head_dim; d += kWave) {
-    float acc = 0.f;
-    for (int p = 0; p < np; ++p) acc += ml[2 * p + 1] * fast_exp2(ml[2 * p] - M) * a.ws_o[(row0 + p) * a.head_dim + d];
-    a.out[((int64_t)s * a.num_q_heads + h) * a.head_dim + d] = acc * inv;
+  for (int p0 = 0; p0 < np; p0 += kWave) {
+    float w = 0.f;
+    if (p0 + lane < np) {
+      const float2 v = ml[p0 + lane];
+      w = v.y * fast_exp2(v.x - M);
+    }
+    wsum += w;
+    const int n = min(kWave, np - p0);
+    const float* __restrict__ o = a.ws_o + (row0 + p0) * D + lane * kDpl;
+    for (int k0 = 0; k0 < n; k0 += 8) {  // eight partitions' loads in flight at a time
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int k = k0 + kk;
+        if (k < n) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+          for (int e = 0; e < kDpl; ++e) acc[e] = fmaf(wk, o[(int64_t)k * D + e], acc[e]);
+        }
+      }
+    }
   }
+  const float inv = 1.0f / wave_sum(wsum);
+  float* dst = a.out + ((int64_t)s * a.num_q_heads + h) * D + lane * kDpl;
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) dst[e] = acc[e] * inv;
 }
 
 }  // namespace
@@ -241,7 +279,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t str
 }
 
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
-  lse_reduce_kernel<<<dim3(a.num_q_heads, a.num_seqs), dim3(kWave), 0, stream>>>(a);
+  const dim3 grid(a.num_q_heads, a.num_seqs);
+  if (a.head_dim == 128) lse_reduce_kernel<128><<<grid, dim3(kWave), 0, stream>>>(a);
+  else if (a.head_dim == 64) lse_reduce_kernel<64><<<grid, dim3(kWave), 0, stream>>>(a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -54,4 +54,13 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders one wave's LDS accesses when lanes exchange data through LDS: everything before it (in every lane) is
+// visible to everything after it. Without it the compiler may move a lane's read of another lane's data
+// above that lane's own earlier write, since a single lane sees no dependence between the two.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace pa

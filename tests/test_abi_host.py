@@ -17,7 +17,7 @@ FAKE = 1 << 20  # a 16-byte-aligned address that is never dereferenced: validati
 
 
 def header_functions():
-    text = open(pa.HEADER_PATH).read()
+    text = open(pa.HEADER_PATH).read() + open(pa.DIAG_HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"paged_attention_decode", "reshape_and_cache", "copy_blocks", "paged_gather",
             "paged_attention_workspace_bytes", "paged_attention_partition_size", "pa_strerror",
-            "pa_abi_version"} <= set(names)
+            "pa_abi_version", "pa_stream_read", "pa_stream_copy"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert lib.pa_abi_version() == pa.ABI_VERSION
@@ -152,3 +152,12 @@ def test_gather_rejects():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         pa.load_library(str(tmp_path / "nope.so"))
+
+
+def test_stream_diagnostics_reject():
+    lib = pa.load_library()
+    assert lib.pa_stream_read(FAKE, 100, FAKE, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_read(None, 1024, FAKE, None) == PA_ERR_NULL
+    assert lib.pa_stream_read(FAKE + 8, 1024, FAKE, None) == PA_ERR_ALIGN
+    assert lib.pa_stream_copy(FAKE, FAKE, 0, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_copy(FAKE + 4, FAKE, 1024, None) == PA_ERR_ALIGN
