@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   const int vr = lane / kVLanes;  // V staging: row within a load
   const int vc = lane % kVLanes;  //            16-byte chunk within the row
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * 2;
+  const uint32_t tile_bytes = (uint32_t)(kTile * row_bytes);  // 16 rows; the host keeps this below 2^31
   const int64_t head_off = (int64_t)g * D * 2;
   char* const slice = lds + w * kSlice;
 
@@ -109,10 +110,12 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
     for (int h2 = 0; h2 < 2; ++h2) {
       const int th = min(t + h2 * kTile, last_half);  // a half past the end re-reads a live one (masked)
       const int64_t base = tile_slot_bytes(table, th, a.bs_log2, a.num_blocks, row_bytes, bad);
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, tile_bytes);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, tile_bytes);
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) kb[h2][c] = *reinterpret_cast<const U4*>(kbase + base + koff[c]);
+      for (int c = 0; c < kChunks; ++c) kb[h2][c] = load16<kPolShared>(kr, koff[c]);
 #pragma unroll
-      for (int i = 0; i < kVLoads; ++i) vb[h2][i] = *reinterpret_cast<const U4*>(vbase + base + voff[i]);
+      for (int i = 0; i < kVLoads; ++i) vb[h2][i] = load16<kPolShared>(vr, voff[i]);
     }
   };
 

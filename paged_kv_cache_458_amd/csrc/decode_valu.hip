@@ -94,6 +94,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int c = lane % S::kRowLanes;  // 16-byte chunk of the head's row
 
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
+  const uint32_t tile_bytes = (uint32_t)(kTile * row_bytes);  // the host keeps this below 2^31
   uint32_t lane_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i)
@@ -118,12 +119,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   auto issue = [&](U4* kb, U4* vb, int tile) {
     const int t = t0 + min(tile, ntiles - 1) * kTile;
     const int64_t base = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
-    const char* kp = kbase + base;
-    const char* vp = vbase + base;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, tile_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, tile_bytes);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      kb[i] = *reinterpret_cast<const U4*>(kp + lane_off[i]);
-      vb[i] = *reinterpret_cast<const U4*>(vp + lane_off[i]);
+      kb[i] = load16<kPolStream>(kr, lane_off[i]);
+      vb[i] = load16<kPolStream>(vr, lane_off[i]);
     }
   };
   auto consume = [&](const U4* kb, const U4* vb, int tile) {

@@ -9,7 +9,7 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // 16-byte loads in flight per lane per iteration
+constexpr int kUnroll = 8;  // 16-byte loads in flight per lane per iteration
 
 // Workgroups take contiguous chunks of kThreads * kUnroll words; each lane's kUnroll loads are issued
 // before any is used. The xor of everything a lane read is folded per workgroup and stored in sink so that
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const U4* __restr
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      v[u] = i < words ? src[i] : U4{0u, 0u, 0u, 0u};
+      v[u] = i < words ? load_stream(reinterpret_cast<const char*>(src + i)) : U4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void stream_copy_kernel(U4* __restrict__ 
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < words) v[u] = src[i];
+      if (i < words) v[u] = load_stream(reinterpret_cast<const char*>(src + i));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {

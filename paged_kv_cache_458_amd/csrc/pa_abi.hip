@@ -59,7 +59,10 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
     p.status = PA_ERR_DTYPE;
     return p;
   }
-  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || num_seqs > kMaxGridYZ) {
+  // a 16-row tile is addressed through one buffer descriptor, whose size field is a signed 32-bit count
+  const int64_t tile_bytes = (int64_t)kTileTokens * num_kv_heads * head_dim * esize_of(kv_dtype);
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || num_seqs > kMaxGridYZ ||
+      tile_bytes > INT32_MAX) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }

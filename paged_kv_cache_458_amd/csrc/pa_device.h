@@ -14,6 +14,37 @@ struct alignas(16) U4 {
   uint32_t x, y, z, w;
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Cache-policy bits of a vector memory instruction on gfx950 (the `aux` operand of the buffer builtins).
+constexpr int kPolSc0 = 1;  // sc0
+constexpr int kPolNt = 2;   // nt: non-temporal, the line is not kept for reuse
+constexpr int kPolSc1 = 16; // sc1
+
+// Policy of the K/V loads in kernels whose rows are read once per call (no row serves two waves).
+constexpr int kPolStream = kPolNt;
+// Policy of the K/V loads in kernels where several waves may read the same rows (shared prefix blocks).
+constexpr int kPolShared = 0;
+
+// Buffer resource over `bytes` bytes at a wave-uniform base (gfx9 raw buffer: stride 0, 32-bit dwords).
+// Loads beyond `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte load at byte `off` of a buffer resource with cache policy POL.
+template <int POL>
+__device__ __forceinline__ U4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL);
+  return U4{v.x, v.y, v.z, v.w};
+}
+
+// 16-byte non-temporal load through a flat pointer (diagnostic streaming kernels).
+__device__ __forceinline__ U4 load_stream(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return U4{v.x, v.y, v.z, v.w};
+}
+
 // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
