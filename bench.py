@@ -42,16 +42,88 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+TRAFFIC_TAG = "<!-- traffic "
+COPY_BYTES = 1 << 31  # bytes the calibration copy reads and writes per dispatch (stream_copy over 2 GiB)
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+
+
 def load_traffic(workload: str):
     """Counter-measured HBM bytes per attention call, if taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
+    rec = None
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+        for line in f:
+            if line.startswith(TRAFFIC_TAG):
+                rec = json.loads(line[len(TRAFFIC_TAG):].rsplit("-->", 1)[0])
+    if rec is None or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_call")
+
+
+def _counter_means(db: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3 database."""
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, dispatch_id, sum(value) from counters_collection where counter_name = ? "
+                       "group by kernel_name, dispatch_id", (counter,)).fetchall()
+    con.close()
+    acc = {}
+    for name, _, v in rows:
+        acc.setdefault(name, []).append(float(v))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch: str, cmd_write: str) -> str:
+    """Turn the FETCH_SIZE and WRITE_SIZE runs of this benchmark into bytes per attention call.
+
+    Each counter is scaled by what it reads for the streaming copy kernel, whose traffic is known exactly
+    (COPY_BYTES read and COPY_BYTES written per dispatch). The attention call is the decode kernel plus, when
+    the context is split, the log-sum-exp merge kernel: their per-dispatch means are added.
+    """
+    fetch, write = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
+
+    def pick(d, key):
+        hits = [k for k in d if key in k]
+        return hits[0] if hits else None
+
+    copy_f, copy_w = pick(fetch, "stream_copy_kernel"), pick(write, "stream_copy_kernel")
+    f_scale, w_scale = COPY_BYTES / fetch[copy_f][0], COPY_BYTES / write[copy_w][0]
+    rows, fb, wb = [], 0.0, 0.0
+    for key in ("decode_valu_kernel", "decode_gqa_mfma_kernel", "lse_reduce_kernel"):
+        kf, kw = pick(fetch, key), pick(write, key)
+        if kf is None:
+            continue
+        f, w = fetch[kf][0] * f_scale, write[kw][0] * w_scale
+        fb, wb = fb + f, wb + w
+        rows.append((kf, fetch[kf][1], fetch[kf][0], write[kw][0], f, w))
+    from workloads import algorithmic_bytes, build_structure
+
+    alg = algorithmic_bytes(build_structure(workload))["total"]
+    lines = [f"# HBM traffic per attention call: {workload}", "",
+             "Two counter runs of the benchmark (run from the repository root on one MI355X):", "", "```",
+             cmd_fetch, cmd_write, "```", "",
+             f"Calibration: the streaming copy kernel moves {COPY_BYTES} B each way per dispatch; it reads "
+             f"FETCH_SIZE = {fetch[copy_f][0]:.0f} and WRITE_SIZE = {write[copy_w][0]:.0f} per dispatch, so the "
+             f"scale factors are {f_scale:.3f} B per FETCH_SIZE unit and {w_scale:.3f} B per WRITE_SIZE unit.", "",
+             "| kernel | dispatches | FETCH_SIZE | WRITE_SIZE | fetched B | written B |", "|---|---|---|---|---|---|"]
+    for k, n, f0, w0, f, w in rows:
+        lines.append(f"| `{k[:90]}` | {n} | {f0:.0f} | {w0:.0f} | {f:.4g} | {w:.4g} |")
+    lines += ["", f"Per call: {fb + wb:.4g} B of HBM traffic against {alg} algorithmic bytes "
+                  f"(ratio {(fb + wb) / alg:.3f}).", "",
+              TRAFFIC_TAG + json.dumps({"kernel_source_hash": kernel_source_hash(), "fetch_bytes_per_call": round(fb),
+                                        "write_bytes_per_call": round(wb), "bytes_per_call": round(fb + wb),
+                                        "algorithmic_bytes": alg}) + " -->"]
+    path = traffic_path(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 
 
 def main() -> int:
@@ -63,7 +135,15 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--replicas", type=int, default=2, help="pool replicas cycled by consecutive steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle timing budget (0 = skip)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="summarise two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) of this benchmark "
+                         "into profiles/traffic_<workload>.md and exit")
+    ap.add_argument("--traffic-cmds", nargs=2, default=("", ""), help="the two profiling commands, for the record")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        print(write_traffic_summary(args.workload, *args.traffic_from, *args.traffic_cmds))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         if int(os.environ.get("RANK", "0")) == 0:
