@@ -296,10 +296,52 @@ def pin_gather(lib):
     assert r == g.shape[0]
 
 
+def _log_sum_exp_scores(h, st, s, hh, t0, t1):
+    """log of sum_t exp(scale * q . k_t) over positions t0..t1-1 of sequence s, head hh (numpy, fp64)."""
+    g = hh // (st.num_q_heads // st.num_kv_heads)
+    q = f64(h["query"][s, hh])
+    ks = []
+    for t in range(t0, t1):
+        b = st.block_tables_pre[s, t // st.block_size]
+        ks.append(f64(h["key_cache"][b, t % st.block_size, g]))
+    z = st.scale * (np.array(ks) @ q)
+    zmax = z.max()
+    return zmax + math.log(np.exp(z - zmax).sum())
+
+
+def pin_split_merge(lib):
+    # Cutting a context into partitions and merging the partitions' normalised outputs o_p with weights
+    # w_p = exp(lse_p), lse_p = log sum_{t in p} exp(z_t), is exact in real arithmetic. The partition outputs
+    # come from the oracle itself over block-aligned sub-contexts (the table shifted by t0 / block_size); the
+    # weights from an independent numpy sum of the same scores.
+    st, h = small_case(31, [70, 16, 33, 1], 4, 2, 8, 4, "bf16", scale=0.4)
+    full = oracle.decode(h["query"], h["key_cache"], h["value_cache"], st.block_tables_pre, st.context_lens,
+                         st.scale, lib=lib)
+    for part in (4, 8, 32):
+        for s, L in enumerate(st.context_lens):
+            L = int(L)
+            bounds = [(t0, min(L, t0 + part)) for t0 in range(0, L, part)]
+            for hh in range(st.num_q_heads):
+                outs, lses = [], []
+                for t0, t1 in bounds:
+                    tbl = np.zeros((1, st.max_blocks_per_seq), np.int32)
+                    shifted = st.block_tables_pre[s, t0 // st.block_size:]
+                    tbl[0, : shifted.size] = shifted
+                    o = oracle.decode(h["query"][s:s + 1], h["key_cache"], h["value_cache"], tbl,
+                                      np.array([t1 - t0], np.int32), st.scale, rows=np.array([[0, hh]]), lib=lib)
+                    outs.append(o[0, hh])
+                    lses.append(_log_sum_exp_scores(h, st, s, hh, t0, t1))
+                lse = np.array(lses)
+                w = np.exp(lse - lse.max())
+                merged = (w[:, None] * np.array(outs)).sum(0) / w.sum()
+                np.testing.assert_allclose(merged, full[s, hh], rtol=0, atol=1e-12,
+                                           err_msg=f"partition {part}, seq {s}, head {hh}")
+
+
 PINS = [pin_golden_decode, pin_golden_cache_ops, pin_brute_force, pin_paged_equals_contiguous,
         pin_permutation_invariance, pin_shared_equals_copied, pin_single_token, pin_identical_keys_and_positions,
         pin_gqa_replication, pin_block_size_invariance, pin_one_hot, pin_cache_write, pin_copy_on_write,
-        pin_gather]
+        pin_gather, pin_split_merge]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
