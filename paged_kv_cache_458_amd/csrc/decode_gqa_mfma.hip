@@ -69,7 +69,6 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   const int vr = lane / kVLanes;  // V staging: row within a load
   const int vc = lane % kVLanes;  //            16-byte chunk within the row
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * 2;
-  const uint32_t tile_bytes = (uint32_t)(kTile * row_bytes);  // 16 rows; the host keeps this below 2^31
   const int64_t head_off = (int64_t)g * D * 2;
   char* const slice = lds + w * kSlice;
 
@@ -108,10 +107,13 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
     const int t = t0 + min(tile, ntiles - 1) * kTileTok;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int th = min(t + h2 * kTile, last_half);  // a half past the end re-reads a live one (masked)
+      // the table is read at a live half; rows past the partition end read as zero without touching memory
+      const int th = min(t + h2 * kTile, last_half);
       const int64_t base = tile_slot_bytes(table, th, a.bs_log2, a.num_blocks, row_bytes, bad);
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, tile_bytes);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, tile_bytes);
+      const int rows = min(kTile, t1 - (t0 + tile * kTileTok + h2 * kTile));
+      const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) kb[h2][c] = load16<kPolShared>(kr, koff[c]);
 #pragma unroll

@@ -94,7 +94,6 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int c = lane % S::kRowLanes;  // 16-byte chunk of the head's row
 
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
-  const uint32_t tile_bytes = (uint32_t)(kTile * row_bytes);  // the host keeps this below 2^31
   uint32_t lane_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i)
@@ -114,13 +113,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
   U4 kA[NL], vA[NL], kB[NL], vB[NL];
-  // Loads of a tile index past the end re-read the last tile (cache hits): the loads stay unconditional so
-  // the wait counters of the two register sets never merge across a branch.
+  // The loads stay unconditional, so the wait counters of the two register sets never merge across a branch:
+  // the descriptor covers only the tile's rows below the partition end, and rows past it (a tile index past
+  // the end: all of them) read as zero without touching memory.
   auto issue = [&](U4* kb, U4* vb, int tile) {
     const int t = t0 + min(tile, ntiles - 1) * kTile;
     const int64_t base = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, tile_bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, tile_bytes);
+    const uint32_t live = tile < ntiles ? (uint32_t)min(kTile, t1 - t) * (uint32_t)row_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       kb[i] = load16<kPolStream>(kr, lane_off[i]);
@@ -207,8 +208,10 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
 
 // Merge of split-context partials: with partition p giving running max m_p (log2 units), sum l_p and
 // normalised output o_p, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p). One wave per
-// (sequence, head): lane p owns partition p's weight, and every lane accumulates its own head_dim / 64 dims,
-// so the loads of all partitions are independent and in flight together.
+// (sequence, head): lane p owns partition p's weight, and every lane accumulates its own head_dim / 64 dims.
+// The kernel is latency-bound, so the (max, sum) pairs and the first kSpec partitions' outputs are loaded
+// before the context length is known (slots past the row's partition count hold stale values and are never
+// combined: the loops below stop at the count).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -220,19 +223,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int kSpec = 16;  // partitions whose outputs are loaded up front
+
 template <int D>
 __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   constexpr int kDpl = D / kWave;  // dims per lane
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
-  if (L <= a.partition) return;  // single partition: written by the partition kernel
-  const int np = (L + a.partition - 1) / a.partition;
-  const int64_t row0 = ((int64_t)s * a.num_q_heads + h) * a.max_partitions;
+  const int pm = a.max_partitions;
+  const int64_t row0 = ((int64_t)s * a.num_q_heads + h) * pm;
   const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
-  float M = -INFINITY;
-  for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[p].x);
+  const float* __restrict__ o = a.ws_o + row0 * D + lane * kDpl;
+
+  // indexes clamped to the row's last slot keep every speculative load inside the workspace without a branch
+  const float2 v0 = ml[min(lane, pm - 1)];
+  float ov[kSpec][kDpl];
+#pragma unroll
+  for (int k = 0; k < kSpec; ++k)
+#pragma unroll
+    for (int e = 0; e < kDpl; ++e) ov[k][e] = o[(int64_t)min(k, pm - 1) * D + e];
+
+  // a row with a single partition was written by the partition kernel: it is merged as one partition here
+  // (no early exit, which would let the compiler sink the loads above behind the length) and not stored
+  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  const bool merge = L > a.partition;
+  const int np = merge ? (L + a.partition - 1) / a.partition : 1;
+
+  float M = lane < np ? v0.x : -INFINITY;
+  for (int p = lane + kWave; p < np; p += kWave) M = fmaxf(M, ml[p].x);
   M = wave_max(M);
   float acc[kDpl];
 #pragma unroll
@@ -241,25 +260,38 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   for (int p0 = 0; p0 < np; p0 += kWave) {
     float w = 0.f;
     if (p0 + lane < np) {
-      const float2 v = ml[p0 + lane];
+      const float2 v = p0 == 0 ? v0 : ml[p0 + lane];
       w = v.y * fast_exp2(v.x - M);
     }
     wsum += w;
     const int n = min(kWave, np - p0);
-    const float* __restrict__ o = a.ws_o + (row0 + p0) * D + lane * kDpl;
-    for (int k0 = 0; k0 < n; k0 += 8) {  // eight partitions' loads in flight at a time
+    int k0 = 0;
+    if (p0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kSpec; ++k) {
+        if (k < n) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+          for (int e = 0; e < kDpl; ++e) acc[e] = fmaf(wk, ov[k][e], acc[e]);
+        }
+      }
+      k0 = kSpec;
+    }
+    const float* __restrict__ op = o + (int64_t)p0 * D;
+    for (; k0 < n; k0 += 8) {  // eight partitions' loads in flight at a time
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int k = k0 + kk;
         if (k < n) {
           const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-          for (int e = 0; e < kDpl; ++e) acc[e] = fmaf(wk, o[(int64_t)k * D + e], acc[e]);
+          for (int e = 0; e < kDpl; ++e) acc[e] = fmaf(wk, op[(int64_t)k * D + e], acc[e]);
         }
       }
     }
   }
   const float inv = 1.0f / wave_sum(wsum);
+  if (!merge) return;
   float* dst = a.out + ((int64_t)s * a.num_q_heads + h) * D + lane * kDpl;
 #pragma unroll
   for (int e = 0; e < kDpl; ++e) dst[e] = acc[e] * inv;
