@@ -73,7 +73,8 @@ __device__ __forceinline__ void axpy_chunk(float* acc, float p, const U4& v) {
   }
 }
 
-constexpr int kWavesPerGroup = 4;  // waves (query heads) per workgroup
+constexpr int kWavesPerGroup = 2;  // waves (query heads) per workgroup
+constexpr int kStages = 3;         // 16-token tiles in flight per wave
 
 template <int KV, int D>
 __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(const DecodeArgs a) {
@@ -112,11 +113,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   bool bad = false;
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
-  U4 kA[NL], vA[NL], kB[NL], vB[NL];
+  U4 kb[kStages][NL], vb[kStages][NL];
   // The loads stay unconditional, so the wait counters of the two register sets never merge across a branch:
   // the descriptor covers only the tile's rows below the partition end, and rows past it (a tile index past
   // the end: all of them) read as zero without touching memory.
-  auto issue = [&](U4* kb, U4* vb, int tile) {
+  auto issue = [&](U4* kq, U4* vq, int tile) {
     const int t = t0 + min(tile, ntiles - 1) * kTile;
     const int64_t base = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
     const uint32_t live = tile < ntiles ? (uint32_t)min(kTile, t1 - t) * (uint32_t)row_bytes : 0u;
@@ -124,17 +125,17 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      kb[i] = load16<kPolStream>(kr, lane_off[i]);
-      vb[i] = load16<kPolStream>(vr, lane_off[i]);
+      kq[i] = load16<kPolStream>(kr, lane_off[i]);
+      vq[i] = load16<kPolStream>(vr, lane_off[i]);
     }
   };
-  auto consume = [&](const U4* kb, const U4* vb, int tile) {
+  auto consume = [&](const U4* kq, const U4* vq, int tile) {
     const int t = t0 + tile * kTile;
     const bool full = t + kTile <= t1;
     float sc[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      sc[i] = group_sum<S::kRowLanes>(dot_chunk<KV>(q, kb[i])) * a.scale_log2;
+      sc[i] = group_sum<S::kRowLanes>(dot_chunk<KV>(q, kq[i])) * a.scale_log2;
       if (!full && t + i * S::kRows + r >= t1) sc[i] = -INFINITY;
     }
     float mt = sc[0];
@@ -150,23 +151,28 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
     for (int i = 0; i < NL; ++i) {
       const float p = fast_exp2(sc[i] - mref);
       l += p;
-      U4 v = vb[i];
+      U4 v = vq[i];
       if (!full && t + i * S::kRows + r >= t1) v = U4{0u, 0u, 0u, 0u};  // a past-the-end slot may hold NaN
       axpy_chunk<KV>(acc, p, v);
     }
     m = mn;
   };
 
+  // kStages register sets in a ring: tile j + kStages - 1 is in flight while tile j is consumed
   if (ntiles > 0) {
-    issue(kA, vA, 0);
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) issue(kb[i], vb[i], i);
     int j = 0;
-    for (; j + 2 <= ntiles; j += 2) {
-      issue(kB, vB, j + 1);
-      consume(kA, vA, j);
-      issue(kA, vA, j + 2);
-      consume(kB, vB, j + 1);
+    for (; j + kStages <= ntiles; j += kStages) {
+#pragma unroll
+      for (int i = 0; i < kStages; ++i) {
+        issue(kb[(i + kStages - 1) % kStages], vb[(i + kStages - 1) % kStages], j + i + kStages - 1);
+        consume(kb[i], vb[i], j + i);
+      }
     }
-    if (j < ntiles) consume(kA, vA, j);
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (j + i < ntiles) consume(kb[i], vb[i], j + i);
   }
 
   // merge the row groups: lanes l, l ^ kRowLanes, ... hold the same dims of different token subsets
