@@ -13,8 +13,8 @@
 // probabilities are exactly that lane's B operand of the second product once the contraction index k = 8j + e
 // is mapped to token (e < 4 ? 4j + e : 16 + 4j + e - 4) -- no data moves between lanes. V^T needs eight
 // tokens of one dim per lane, the transpose of the pool's layout, so each wave stages its V tile in its own
-// LDS slice (rows padded by 16 bytes, which spreads the four token groups over distinct banks) and reads it
-// back as 16-bit elements. The accumulator of the second product leaves lane (n, j) with head n, the same
+// LDS slice (rows padded by 16 bytes) and reads it back with gfx950's transposing LDS reads, two 8-byte reads
+// per 16-dim column tile. The accumulator of the second product leaves lane (n, j) with head n, the same
 // head as its softmax state, so the online-softmax rescale is a per-lane multiply.
 //
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
@@ -35,6 +35,16 @@ constexpr int kTileTok = 32;   // tokens per tile: two 16-row halves
 __device__ __forceinline__ f32x4 mfma(const U4& a, const U4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte transposing LDS read (gfx950 ds_read_b64_tr_b16).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -122,9 +132,13 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   };
 
   // LDS addresses: V row r at slice + r * kPitch; this lane writes rows vr + kVRows*i (+16 for the second half)
-  // at column vc * 16 bytes and reads the 16-bit element of dim 16nt + n from rows token(8j + e).
+  // at column vc * 16 bytes.
   char* const wbase = slice + vr * kPitch + vc * 16;
-  const char* const rbase = slice + 4 * j * kPitch + n * 2;
+  // Transposed reads (ds_read_b64_tr_b16): within each 16-lane group, lane l receives element l % 4 of the
+  // 8-byte rows addressed by lanes (l % 16) / 4 + 4e, e = 0..3. So lane (q, r) = ((l%16)/4, l%4) of group j
+  // addresses token row 4j + q at dims 16nt + 4r .. 16nt + 4r + 3, and every lane ends up with its own dim
+  // 16nt + n of the group's four token rows.
+  const char* const rbase = slice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
 
   auto consume = [&](U4 (*kb)[kChunks], U4 (*vb)[kVLoads], int tile) {
     const int t = t0 + tile * kTileTok;
@@ -180,21 +194,15 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
       // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4)
-      const char* r = rbase + nt * 32;
-      uint32_t d[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int r0 = (e < 4 ? e : kTile + e - 4) * kPitch;
-        const int r1 = (e + 1 < 4 ? e + 1 : kTile + e + 1 - 4) * kPitch;
-        d[e / 2] = (uint32_t)*reinterpret_cast<const uint16_t*>(r + r0) |
-                   ((uint32_t)*reinterpret_cast<const uint16_t*>(r + r1) << 16);
-      }
+      // two transposed reads give this lane dim 16nt + n of tokens 4j..4j+3 and 16+4j..16+4j+3
+      const u32x2 lo = lds_read_tr16(rbase + nt * 32);
+      const u32x2 hi = lds_read_tr16(rbase + kTile * kPitch + nt * 32);
       f32x4 acc = o[nt];
       acc[0] *= alpha;
       acc[1] *= alpha;
       acc[2] *= alpha;
       acc[3] *= alpha;
-      o[nt] = mfma(U4{d[0], d[1], d[2], d[3]}, pb, acc);
+      o[nt] = mfma(U4{lo.x, lo.y, hi.x, hi.y}, pb, acc);
     }
   };
 
