@@ -7,14 +7,17 @@
 //   S^T[32 tokens x 16]  = K_tile[32 x D] . Q^T[D x 16]      (the G heads padded to 16 columns)
 //   O^T[D x 16]         += V_tile^T[D x 32] . P^T[32 x 16]
 //
-// Operand layouts. K rows are the A operand of the first product and are loaded straight from the pool in
-// MFMA layout (lane (n, j) = (lane % 16, lane / 16) reads row n, bytes 64c + 16j of each 16-row half).
-// The result leaves lane (n, j) with the scores of head n for tokens 4j..4j+3 of both halves; those eight
-// probabilities are exactly that lane's B operand of the second product once the contraction index k = 8j + e
-// is mapped to token (e < 4 ? 4j + e : 16 + 4j + e - 4) -- no data moves between lanes. V^T needs eight
-// tokens of one dim per lane, the transpose of the pool's layout, so each wave stages its V tile in its own
-// LDS slice (rows padded by 16 bytes) and reads it back with gfx950's transposing LDS reads, two 8-byte reads
-// per 16-dim column tile. The accumulator of the second product leaves lane (n, j) with head n, the same
+// Loads. K and V rows are read from the pool with every wave-wide load covering kRows whole 256-byte head
+// rows (full cache lines, non-temporal: each row is read once per call); both go through a per-wave LDS slice
+// (rows padded by 16 bytes). Loading K straight into the MFMA operand layout instead (16 rows x 64 bytes per
+// load, each line split across two loads) costs about 12% of bandwidth with non-temporal loads.
+//
+// Operand layouts. K rows are the A operand of the first product: lane (n, j) = (lane % 16, lane / 16) reads
+// row n, bytes 64c + 16j of each 16-row half from LDS. The result leaves lane (n, j) with the scores of head n
+// for tokens 4j..4j+3 of both halves; those eight probabilities are exactly that lane's B operand of the
+// second product once the contraction index k = 8j + e is mapped to token (e < 4 ? 4j + e : 16 + 4j + e - 4)
+// -- no data moves between lanes. V^T needs eight tokens of one dim per lane, the transpose of the pool's
+// layout: gfx950's transposing LDS reads give it with two 8-byte reads per 16-dim column tile. The accumulator of the second product leaves lane (n, j) with head n, the same
 // head as its softmax state, so the online-softmax rescale is a per-lane multiply.
 //
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
@@ -55,12 +58,13 @@ template <int D>
 __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / 32;          // 32-dim k-chunks of the QK product
   constexpr int kNt = D / 16;              // 16-dim column tiles of the PV product
-  constexpr int kPitch = D * 2 + 16;       // LDS bytes per V row
-  constexpr int kSlice = kTileTok * kPitch;
-  constexpr int kVLanes = D * 2 / 16;      // lanes covering one V row with 16-byte loads
-  constexpr int kVRows = kWave / kVLanes;  // V rows per wave-wide load
-  constexpr int kVLoads = kTile / kVRows;  // V loads per 16-row half
-  __shared__ __attribute__((aligned(16))) char lds[kWaves * kSlice];
+  constexpr int kPitch = D * 2 + 16;       // LDS bytes per K or V row
+  constexpr int kSlice = kTileTok * kPitch;  // one 32-row tile of K or of V
+  constexpr int kRowLanes = D * 2 / 16;    // lanes covering one row with 16-byte loads
+  constexpr int kRows = kWave / kRowLanes; // rows per wave-wide load
+  constexpr int kLoads = kTile / kRows;    // loads per 16-row half, for K and for V (== kChunks)
+  static_assert(kLoads == kChunks, "one load per 32-dim chunk");
+  __shared__ __attribute__((aligned(16))) char lds[kWaves * 2 * kSlice];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
@@ -76,11 +80,12 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   const int G = a.group;
   const int n = lane & 15;  // MFMA column: query head within the group (valid when n < G)
   const int j = lane >> 4;  // 0..3
-  const int vr = lane / kVLanes;  // V staging: row within a load
-  const int vc = lane % kVLanes;  //            16-byte chunk within the row
+  const int rr = lane / kRowLanes;  // loads: row within a wave-wide load
+  const int rc = lane % kRowLanes;  //        16-byte chunk within the row
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * 2;
   const int64_t head_off = (int64_t)g * D * 2;
-  char* const slice = lds + w * kSlice;
+  char* const kslice = lds + w * 2 * kSlice;
+  char* const vslice = kslice + kSlice;
 
   // Q^T (B operand of S^T = K Q^T): lane (n, j) holds q[g*G + n][32c + 8j .. 32c + 8j + 7]; padding heads are 0.
   const bool head_ok = n < G;
@@ -93,12 +98,11 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
     qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
   }
 
-  // per-lane byte offsets inside a 16-row half tile
-  uint32_t koff[kChunks], voff[kVLoads];
+  // per-lane byte offsets inside a 16-row half tile: each wave-wide load covers kRows whole 256-byte head rows
+  // (full cache lines), for K as for V
+  uint32_t off[kLoads];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) koff[c] = (uint32_t)(n * row_bytes + head_off + c * 64 + j * 16);
-#pragma unroll
-  for (int i = 0; i < kVLoads; ++i) voff[i] = (uint32_t)((vr + kVRows * i) * row_bytes + head_off + vc * 16);
+  for (int i = 0; i < kLoads; ++i) off[i] = (uint32_t)((rr + kRows * i) * row_bytes + head_off + rc * 16);
 
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
@@ -112,8 +116,8 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   const int ntiles = (t1 - t0 + kTileTok - 1) / kTileTok;
   const int last_half = ntiles > 0 ? ((t1 - 1) & ~(kTile - 1)) : t0;  // start of the last live 16-token half
 
-  U4 kA[2][kChunks], vA[2][kVLoads], kB[2][kChunks], vB[2][kVLoads];
-  auto issue = [&](U4 (*kb)[kChunks], U4 (*vb)[kVLoads], int tile) {
+  U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
+  auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
     const int t = t0 + min(tile, ntiles - 1) * kTileTok;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -125,33 +129,36 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) kb[h2][c] = load16<kPolShared>(kr, koff[c]);
-#pragma unroll
-      for (int i = 0; i < kVLoads; ++i) vb[h2][i] = load16<kPolShared>(vr, voff[i]);
+      for (int i = 0; i < kLoads; ++i) {
+        kb[h2][i] = load16<kPolStream>(kr, off[i]);
+        vb[h2][i] = load16<kPolStream>(vr, off[i]);
+      }
     }
   };
 
-  // LDS addresses: V row r at slice + r * kPitch; this lane writes rows vr + kVRows*i (+16 for the second half)
-  // at column vc * 16 bytes.
-  char* const wbase = slice + vr * kPitch + vc * 16;
+  // LDS: row r of the tile at slice + r * kPitch, K and V each in their own slice. This lane writes rows
+  // rr + kRows*i (+16 for the second half) at column rc * 16 bytes of both slices.
+  const int wofs = rr * kPitch + rc * 16;
+  // K is read back in the A-operand layout of S^T = K Q^T: lane (n, j) takes row n, bytes 64c + 16j.
+  const char* const kread = kslice + n * kPitch + j * 16;
   // Transposed reads (ds_read_b64_tr_b16): within each 16-lane group, lane l receives element l % 4 of the
   // 8-byte rows addressed by lanes (l % 16) / 4 + 4e, e = 0..3. So lane (q, r) = ((l%16)/4, l%4) of group j
   // addresses token row 4j + q at dims 16nt + 4r .. 16nt + 4r + 3, and every lane ends up with its own dim
   // 16nt + n of the group's four token rows.
-  const char* const rbase = slice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
+  const char* const rbase = vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
 
-  auto consume = [&](U4 (*kb)[kChunks], U4 (*vb)[kVLoads], int tile) {
+  auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
     const int t = t0 + tile * kTileTok;
     const bool full = t + kTileTok <= t1;
-    // stage V (rows past the end are zeroed: their slots may hold NaN); the previous tile's reads come first
+    // stage K and V (rows past the partition end were loaded as zeros); the previous tile's reads come first
     wave_lds_sync();
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int i = 0; i < kVLoads; ++i) {
-        U4 v = vb[h2][i];
-        if (!full && t + h2 * kTile + vr + kVRows * i >= t1) v = U4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<U4*>(wbase + (h2 * kTile + kVRows * i) * kPitch) = v;
+      for (int i = 0; i < kLoads; ++i) {
+        const int r = (h2 * kTile + kRows * i) * kPitch + wofs;
+        *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
+        *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
       }
     wave_lds_sync();
     // scores
@@ -160,7 +167,8 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
     for (int h2 = 0; h2 < 2; ++h2) {
       sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) sc[h2] = mfma(kb[h2][c], qb[c], sc[h2]);
+      for (int c = 0; c < kChunks; ++c)
+        sc[h2] = mfma(*reinterpret_cast<const U4*>(kread + h2 * kTile * kPitch + c * 64), qb[c], sc[h2]);
     }
     float sv[8];
     float mt = -INFINITY;
