@@ -32,7 +32,6 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kWaves = 4;      // waves (KV heads) per workgroup
 constexpr int kTileTok = 32;   // tokens per tile: two 16-row halves
 
 __device__ __forceinline__ f32x4 mfma(const U4& a, const U4& b, f32x4 c) {
@@ -54,8 +53,9 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-template <int D>
-__global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const DecodeArgs a) {
+// W waves (KV heads of one sequence) per workgroup: they stream the same slots of the pool side by side.
+template <int D, int W>
+__global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const DecodeArgs a) {
   constexpr int kChunks = D / 32;          // 32-dim k-chunks of the QK product
   constexpr int kNt = D / 16;              // 16-dim column tiles of the PV product
   constexpr int kPitch = D * 2 + 16;       // LDS bytes per K or V row
@@ -64,19 +64,21 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   constexpr int kRows = kWave / kRowLanes; // rows per wave-wide load
   constexpr int kLoads = kTile / kRows;    // loads per 16-row half, for K and for V (== kChunks)
   static_assert(kLoads == kChunks, "one load per 32-dim chunk");
-  __shared__ __attribute__((aligned(16))) char lds[kWaves * 2 * kSlice];
+  __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
-  const int g = blockIdx.x * kWaves + w;
-  const int part = blockIdx.y;
+  const int g = blockIdx.x * W + w;
   const int s = blockIdx.z;
   if (g >= a.num_kv_heads) return;  // no workgroup barriers below: each wave owns its LDS slice
 
+  // The wave covers parts_per_wave consecutive partitions, [u0, u1), in one load pipeline and leaves one
+  // partial result per partition (partition boundaries fall on 32-token tiles whenever parts_per_wave > 1).
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
-  const int t0 = part * a.partition;
-  if (part > 0 && t0 >= L) return;
-  const int t1 = min(L, t0 + a.partition);
+  const int span = a.partition * a.parts_per_wave;
+  const int u0 = blockIdx.y * span;
+  if (blockIdx.y > 0 && u0 >= L) return;
+  const int u1 = min(L, u0 + span);
   const int G = a.group;
   const int n = lane & 15;  // MFMA column: query head within the group (valid when n < G)
   const int j = lane >> 4;  // 0..3
@@ -113,18 +115,18 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
 #pragma unroll
   for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
-  const int ntiles = (t1 - t0 + kTileTok - 1) / kTileTok;
-  const int last_half = ntiles > 0 ? ((t1 - 1) & ~(kTile - 1)) : t0;  // start of the last live 16-token half
+  const int ntiles = (u1 - u0 + kTileTok - 1) / kTileTok;
+  const int last_half = ntiles > 0 ? ((u1 - 1) & ~(kTile - 1)) : u0;  // start of the last live 16-token half
 
   U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
   auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-    const int t = t0 + min(tile, ntiles - 1) * kTileTok;
+    const int t = u0 + min(tile, ntiles - 1) * kTileTok;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      // the table is read at a live half; rows past the partition end read as zero without touching memory
+      // the table is read at a live half; rows past the range end read as zero without touching memory
       const int th = min(t + h2 * kTile, last_half);
       const int64_t base = tile_slot_bytes(table, th, a.bs_log2, a.num_blocks, row_bytes, bad);
-      const int rows = min(kTile, t1 - (t0 + tile * kTileTok + h2 * kTile));
+      const int rows = min(kTile, u1 - (u0 + tile * kTileTok + h2 * kTile));
       const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
@@ -147,9 +149,44 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
   // 16nt + n of the group's four token rows.
   const char* const rbase = vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
 
+  // end of a partition: normalise this wave's G rows and write them (the output itself when the sequence has
+  // one partition, else partial p of the split workspace), then start the next partition afresh
+  const float poison = __uint_as_float(0x7fc00000u);
+  auto flush = [&](int p) {
+    // each lane summed the probabilities of its own token group j; the max is already shared
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (head_ok) {
+      const int h = g * G + n;
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      float* dst;
+      if (!a.split || L <= a.partition) {
+        dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
+      } else {
+        const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + p;
+        dst = a.ws_o + row * D;
+        if (j == 0) {
+          a.ws_ml[2 * row] = bad ? poison : m;
+          a.ws_ml[2 * row + 1] = lt;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) {
+        const f32x4 v = o[nt];
+        *reinterpret_cast<float4*>(dst + nt * 16 + 4 * j) =
+            bad ? make_float4(poison, poison, poison, poison)
+                : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      }
+    }
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
   auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-    const int t = t0 + tile * kTileTok;
-    const bool full = t + kTileTok <= t1;
+    const int t = u0 + tile * kTileTok;
+    const bool full = t + kTileTok <= u1;
     // stage K and V (rows past the partition end were loaded as zeros); the previous tile's reads come first
     wave_lds_sync();
 #pragma unroll
@@ -177,7 +214,7 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = sc[h2][i] * a.scale_log2;
-        if (!full && t + h2 * kTile + 4 * j + i >= t1) x = -INFINITY;
+        if (!full && t + h2 * kTile + 4 * j + i >= u1) x = -INFINITY;
         sv[h2 * 4 + i] = x;
         mt = fmaxf(mt, x);
       }
@@ -212,6 +249,7 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
       acc[3] *= alpha;
       o[nt] = mfma(U4{lo.x, lo.y, hi.x, hi.y}, pb, acc);
     }
+    if (t + kTileTok >= u1 || (t + kTileTok - u0) % a.partition == 0) flush(t / a.partition);
   };
 
   if (ntiles > 0) {
@@ -224,32 +262,8 @@ __global__ __launch_bounds__(kWave * kWaves) void decode_gqa_mfma_kernel(const D
       consume(kB, vB, tj + 1);
     }
     if (tj < ntiles) consume(kA, vA, tj);
-  }
-
-  // each lane summed the probabilities of its own token group j; the max is already shared
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!head_ok) return;
-  const int h = g * G + n;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const float poison = __uint_as_float(0x7fc00000u);
-  float* dst;
-  if (!a.split || L <= a.partition) {
-    dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
   } else {
-    const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + part;
-    dst = a.ws_o + row * D;
-    if (j == 0) {
-      a.ws_ml[2 * row] = bad ? poison : m;
-      a.ws_ml[2 * row + 1] = l;
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < kNt; ++nt) {
-    const f32x4 v = o[nt];
-    *reinterpret_cast<float4*>(dst + nt * 16 + 4 * j) =
-        bad ? make_float4(poison, poison, poison, poison)
-            : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    flush(0);  // an empty context: its output row is zero
   }
 }
 
@@ -259,13 +273,27 @@ bool gqa_mfma_supported(int kv_dtype, int head_dim, int group) {
   return kv_dtype == PA_BF16 && (head_dim == 128 || head_dim == 64) && group >= 2 && group <= 16;
 }
 
-hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((a.num_kv_heads + kWaves - 1) / kWaves, a.split ? a.max_partitions : 1, a.num_seqs);
-  const dim3 block(kWave * kWaves);
-  if (a.head_dim == 128) decode_gqa_mfma_kernel<128><<<grid, block, 0, stream>>>(a);
-  else if (a.head_dim == 64) decode_gqa_mfma_kernel<64><<<grid, block, 0, stream>>>(a);
-  else return hipErrorInvalidValue;
+template <int D, int W>
+hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
+  const int groups = a.split ? (a.max_partitions + a.parts_per_wave - 1) / a.parts_per_wave : 1;
+  const dim3 grid((a.num_kv_heads + W - 1) / W, groups, a.num_seqs);
+  decode_gqa_mfma_kernel<D, W><<<grid, dim3(kWave * W), 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  // a workgroup takes up to 8 KV heads of a sequence; the LDS slices of 8 waves fit one CU (8 x 17 KB at D 128)
+  if (a.num_kv_heads >= 8) return launch_w<D, 8>(a, stream);
+  if (a.num_kv_heads >= 4) return launch_w<D, 4>(a, stream);
+  if (a.num_kv_heads >= 2) return launch_w<D, 2>(a, stream);
+  return launch_w<D, 1>(a, stream);
+}
+
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -31,20 +31,32 @@ struct Plan {
   int status = PA_OK;
   int32_t partition = 0;       // tokens per partition as launched
   int32_t max_partitions = 1;  // partitions of the longest context
+  int32_t parts_per_wave = 1;  // consecutive partitions one wave covers
   bool split = false;
   size_t ws_bytes = 0;
   size_t ws_ml_offset = 0;
 };
 
-// Library choice of partition size. Long contexts are cut so that the grid has many more partition
-// workgroups than the chip has slots for (load balance across 256 CUs), while a partition still streams
-// enough K/V that the partial write and the reduce stay a small fraction of the traffic.
-int32_t pick_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_q_heads;
-  (void)num_kv_heads;
-  if (max_context_len <= 256) return 0;
-  return 256;
+// Library choice of partition size. A partition is the unit of work of one wave (the GQA kernel may take
+// several): long enough that the partial writes and the merge stay a small fraction of the traffic and that
+// per-wave start-up is amortised, short enough that the grid holds a few waves per slot of the chip so the
+// load is balanced. Measured on MI355X: 512 tokens for the single-head kernel and 1024 for the grouped-query
+// kernel, halved while the grid would hold fewer than kMinWaves waves.
+constexpr int64_t kMinWaves = 4096;
+
+int32_t pick_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                       bool gqa) {
+  int32_t part = gqa ? 1024 : 512;
+  const int64_t rows = (int64_t)num_seqs * (gqa ? num_kv_heads : num_q_heads);
+  while (part > 64 && rows * ((max_context_len + part - 1) / part) < kMinWaves) part /= 2;
+  return max_context_len <= part ? 0 : part;
+}
+
+// Consecutive partitions one wave of the GQA kernel covers: enough to stream about 1024 tokens per wave when
+// the caller asks for shorter partitions. Needs partitions made of whole 32-token tiles.
+int32_t gqa_parts_per_wave(int32_t partition) {
+  if (partition <= 0 || partition % pa::kGqaTileTokens != 0) return 1;
+  return partition >= 1024 ? 1 : 1024 / partition;
 }
 
 Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -70,7 +82,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
     p.status = PA_ERR_SHAPE;
     return p;
   }
-  int32_t part = partition_size == -1 ? pick_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len)
+  const bool gqa = num_q_heads > num_kv_heads && pa::gqa_mfma_supported(kv_dtype, head_dim,
+                                                                       num_q_heads / num_kv_heads);
+  int32_t part = partition_size == -1 ? pick_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len, gqa)
                                       : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
   if (part == 0 || part >= whole) {
@@ -86,6 +100,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
   }
   p.partition = part;
   p.max_partitions = (int32_t)pm;
+  p.parts_per_wave = gqa ? gqa_parts_per_wave(part) : 1;
   p.split = true;
   const size_t o_bytes = pa::ws_o_elems(num_seqs, num_q_heads, pm, head_dim) * sizeof(float);
   p.ws_ml_offset = round_up(o_bytes, 256);
@@ -174,6 +189,7 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
   a.max_context_len = max_context_len;
   a.partition = plan.partition;
   a.max_partitions = plan.max_partitions;
+  a.parts_per_wave = plan.parts_per_wave;
   a.split = plan.split ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -22,6 +22,7 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq, max_context_len;
   int32_t partition;           // tokens per partition (split) or >= max_context_len rounded to 16 (single)
   int32_t max_partitions;      // PM
+  int32_t parts_per_wave;      // consecutive partitions one wave covers (GQA kernel; the others take 1)
   int32_t split;               // 0: every sequence is one partition, written straight to out
 };
 
@@ -32,6 +33,7 @@ inline size_t ws_ml_elems(int64_t B, int64_t Hq, int64_t PM) { return B * Hq * P
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group);
+constexpr int kGqaTileTokens = 32;  // tokens per tile of the GQA kernel
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
