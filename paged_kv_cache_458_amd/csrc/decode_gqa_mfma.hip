@@ -72,8 +72,8 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   const int s = blockIdx.z;
   if (g >= a.num_kv_heads) return;  // no workgroup barriers below: each wave owns its LDS slice
 
-  // The wave covers parts_per_wave consecutive partitions, [u0, u1), in one load pipeline and leaves one
-  // partial result per partition (partition boundaries fall on 32-token tiles whenever parts_per_wave > 1).
+  // The wave covers parts_per_wave (1 or 2) consecutive partitions, [u0, u1), in one load pipeline and leaves
+  // one partial result per partition (partition boundaries fall on 32-token tiles whenever parts_per_wave is 2).
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   const int span = a.partition * a.parts_per_wave;
   const int u0 = blockIdx.y * span;
@@ -149,39 +149,55 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   // 16nt + n of the group's four token rows.
   const char* const rbase = vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
 
-  // end of a partition: normalise this wave's G rows and write them (the output itself when the sequence has
-  // one partition, else partial p of the split workspace), then start the next partition afresh
-  const float poison = __uint_as_float(0x7fc00000u);
-  auto flush = [&](int p) {
-    // each lane summed the probabilities of its own token group j; the max is already shared
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
-    if (head_ok) {
-      const int h = g * G + n;
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-      float* dst;
-      if (!a.split || L <= a.partition) {
-        dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
-      } else {
-        const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + p;
-        dst = a.ws_o + row * D;
-        if (j == 0) {
-          a.ws_ml[2 * row] = bad ? poison : m;
-          a.ws_ml[2 * row + 1] = lt;
-        }
-      }
+  // A wave covers at most two partitions. Finishing the first one mid-range only parks its state in
+  // registers: any store inside the load loop would leave the compiler unable to count outstanding memory
+  // operations, and it would then drain the load pipeline on every tile. Both partials are written after
+  // the loop.
+  const int cut = min(u0 + a.partition, u1);  // end of the wave's first partition
+  const int p0 = u0 / a.partition;            // its index
+  float m_first = -INFINITY, l_first = 0.f;
+  f32x4 o_first[kNt];
 #pragma unroll
-      for (int nt = 0; nt < kNt; ++nt) {
-        const f32x4 v = o[nt];
-        *reinterpret_cast<float4*>(dst + nt * 16 + 4 * j) =
-            bad ? make_float4(poison, poison, poison, poison)
-                : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-      }
-    }
+  for (int nt = 0; nt < kNt; ++nt) o_first[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto park_first = [&]() {
+    m_first = m;
+    l_first = l;
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) o_first[nt] = o[nt];
     m = -INFINITY;
     l = 0.f;
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // Normalise one partition's G rows and write them: the output itself when the sequence has a single
+  // partition, else partial p of the split workspace.
+  const float poison = __uint_as_float(0x7fc00000u);
+  auto write_rows = [&](int p, float mp, float lp, const f32x4* op) {
+    // each lane summed the probabilities of its own token group j; the max is already shared
+    float lt = lp + __shfl_xor(lp, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!head_ok) return;
+    const int h = g * G + n;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    float* dst;
+    if (!a.split || L <= a.partition) {
+      dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
+    } else {
+      const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + p;
+      dst = a.ws_o + row * D;
+      if (j == 0) {
+        a.ws_ml[2 * row] = bad ? poison : mp;
+        a.ws_ml[2 * row + 1] = lt;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) {
+      const f32x4 v = op[nt];
+      *reinterpret_cast<float4*>(dst + nt * 16 + 4 * j) =
+          bad ? make_float4(poison, poison, poison, poison)
+              : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    }
   };
 
   auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
       acc[3] *= alpha;
       o[nt] = mfma(U4{lo.x, lo.y, hi.x, hi.y}, pb, acc);
     }
-    if (t + kTileTok >= u1 || (t + kTileTok - u0) % a.partition == 0) flush(t / a.partition);
+    if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
   };
 
   if (ntiles > 0) {
@@ -262,8 +278,13 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
       consume(kB, vB, tj + 1);
     }
     if (tj < ntiles) consume(kA, vA, tj);
+  }
+  // an empty context writes a zero row (l = 0)
+  if (cut < u1) {
+    write_rows(p0, m_first, l_first, o_first);
+    write_rows(p0 + 1, m, l, o);
   } else {
-    flush(0);  // an empty context: its output row is zero
+    write_rows(p0, m, l, o);
   }
 }
 

@@ -40,23 +40,23 @@ struct Plan {
 // Library choice of partition size. A partition is the unit of work of one wave (the GQA kernel may take
 // several): long enough that the partial writes and the merge stay a small fraction of the traffic and that
 // per-wave start-up is amortised, short enough that the grid holds a few waves per slot of the chip so the
-// load is balanced. Measured on MI355X: 512 tokens for the single-head kernel and 1024 for the grouped-query
-// kernel, halved while the grid would hold fewer than kMinWaves waves.
-constexpr int64_t kMinWaves = 4096;
-
+// load is balanced. Measured on MI355X: 512 tokens for the single-head kernel, halved while its grid would
+// hold fewer than 4096 waves (two per wave slot), and 1024 for the grouped-query kernel, halved while its grid
+// would hold fewer than 2048 waves (one per slot: its waves run longest when they all start together).
 int32_t pick_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
                        bool gqa) {
   int32_t part = gqa ? 1024 : 512;
+  const int64_t min_waves = gqa ? 2048 : 4096;
   const int64_t rows = (int64_t)num_seqs * (gqa ? num_kv_heads : num_q_heads);
-  while (part > 64 && rows * ((max_context_len + part - 1) / part) < kMinWaves) part /= 2;
+  while (part > 64 && rows * ((max_context_len + part - 1) / part) < min_waves) part /= 2;
   return max_context_len <= part ? 0 : part;
 }
 
-// Consecutive partitions one wave of the GQA kernel covers: enough to stream about 1024 tokens per wave when
-// the caller asks for shorter partitions. Needs partitions made of whole 32-token tiles.
+// Consecutive partitions one wave of the GQA kernel covers (1 or 2): two when the caller asks for partitions
+// of 512..1023 tokens, so that a wave still streams about 1024 tokens. Needs partitions made of whole
+// 32-token tiles.
 int32_t gqa_parts_per_wave(int32_t partition) {
-  if (partition <= 0 || partition % pa::kGqaTileTokens != 0) return 1;
-  return partition >= 1024 ? 1 : 1024 / partition;
+  return partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
 }
 
 Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
