@@ -17,6 +17,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libpagedattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention.h")
 DIAG_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention_diag.h")
+BM_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_block_manager.h")
 STREAM_SINK_FLOATS = 8192
 
 PA_F32, PA_BF16 = 0, 1

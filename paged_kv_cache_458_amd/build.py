@@ -29,7 +29,8 @@ FLAGS = [
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    """HIP sources (device and host code) and C++ sources (host code only)."""
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:
@@ -48,6 +49,8 @@ def device_asm(out_dir: str) -> list[str]:
     os.makedirs(out_dir, exist_ok=True)
     outs = []
     for src in sources():
+        if not src.endswith(".hip"):
+            continue
         out = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".s"))
         flags = [f for f in FLAGS if f not in ("-shared",)]
         subprocess.run([HIPCC, *flags, "-I", os.path.join(ROOT, "include"), "-S", "--cuda-device-only", src, "-o",

@@ -1,0 +1,157 @@
+"""A multi-step decode loop over the paged KV cache: the native block manager decides where every token goes,
+the HIP kernels move and read the bytes.
+
+Each step appends one token to every running sequence (vLLM PagedAttention, page 3 section 2.1: forward,
+sample, update the KV cache, forward again): the block manager hands out the new tokens' slots and any
+copy-on-write pairs; copy_blocks applies the copies, reshape_and_cache writes the new K/V, and
+paged_attention_decode attends over each sequence's whole cache. Sequences join (with a prompt whose full
+blocks may be shared with earlier prompts), fork (sharing every block, page 1 section 3.2) and finish
+(their blocks return to the pool) between steps.
+
+K/V values are synthetic. A prompt token's K/V is a fixed function of the prompt up to and including it, so
+two prompts with a common prefix would write identical rows there -- which is what makes sharing their
+blocks correct. Generated tokens get fresh random K/V from the device generator.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import PA_BF16, PA_F32, copy_blocks, paged_attention_decode, reshape_and_cache, workspace_bytes
+from .block_manager import BlockManager
+
+
+def _prefix_seed(seed: int, tokens: np.ndarray) -> int:
+    """A 63-bit seed determined by the token prefix (FNV-1a over the ids)."""
+    h = 1469598103934665603 ^ (seed & 0xFFFFFFFF)
+    for t in tokens.tolist():
+        h = ((h ^ (t & 0xFFFFFFFF)) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h & 0x7FFFFFFFFFFFFFFF
+
+
+class DecodeLoop:
+    """Paged KV pools on one GPU plus the block manager that fills them.
+
+    The pools hold `num_blocks` blocks; the last one is never handed out and pads the block tables. Every slot
+    that holds no token is NaN, so a kernel that reads one shows it.
+    """
+
+    def __init__(self, *, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 max_blocks_per_seq: int, dtype: str = "bf16", device="cuda", seed: int = 0, scale=None,
+                 partition_size: int = -1, record: bool = False):
+        import torch
+
+        self.torch = torch
+        self.dev = torch.device(device)
+        self.dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.kv_code = PA_BF16 if dtype == "bf16" else PA_F32
+        self.bs, self.hq, self.hkv, self.d = block_size, num_q_heads, num_kv_heads, head_dim
+        self.mbs = max_blocks_per_seq
+        self.pad_block = num_blocks - 1
+        self.seed = seed
+        self.scale = float(scale) if scale is not None else head_dim ** -0.5
+        self.partition_size = partition_size
+        self.bm = BlockManager(num_blocks, block_size, max_blocks_per_seq, reserved_block=self.pad_block)
+        shape = (num_blocks, block_size, num_kv_heads, head_dim)
+        self.key_cache = torch.full(shape, float("nan"), dtype=self.dt, device=self.dev)
+        self.value_cache = torch.full(shape, float("nan"), dtype=self.dt, device=self.dev)
+        self.gen = torch.Generator(device=self.dev)
+        self.gen.manual_seed(seed)
+        self.running: list[int] = []
+        self.lengths: dict[int, int] = {}
+        self._ws = None
+        # with record=True every cache write and copy is kept on the host so that a test can rebuild the pools
+        self.log: list | None = [] if record else None
+
+    # ------------------------------------------------------------------------------------------------------
+    def _rows(self, n: int):
+        t = self.torch
+        k = t.randn((n, self.hkv, self.d), generator=self.gen, device=self.dev, dtype=t.float32).to(self.dt)
+        v = t.randn((n, self.hkv, self.d), generator=self.gen, device=self.dev, dtype=t.float32).to(self.dt)
+        return k, v
+
+    def prompt_rows(self, tokens: np.ndarray):
+        """K/V of every prompt position: row t depends only on tokens[: t + 1] (host numpy, then the device)."""
+        t = self.torch
+        n = len(tokens)
+        k = np.empty((n, self.hkv, self.d), np.float32)
+        v = np.empty((n, self.hkv, self.d), np.float32)
+        for i in range(n):
+            rng = np.random.default_rng(_prefix_seed(self.seed, tokens[: i + 1]))
+            k[i] = rng.standard_normal((self.hkv, self.d), dtype=np.float32)
+            v[i] = rng.standard_normal((self.hkv, self.d), dtype=np.float32)
+        return (t.from_numpy(k).to(self.dev).to(self.dt), t.from_numpy(v).to(self.dev).to(self.dt))
+
+    def _write(self, k, v, slots: np.ndarray):
+        t = self.torch
+        sm = t.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to(self.dev)
+        reshape_and_cache(k, v, self.key_cache, self.value_cache, sm)
+        if self.log is not None:
+            self.log.append(("write", slots.copy(), k.cpu(), v.cpu()))
+
+    def _apply_copies(self):
+        pairs = self.bm.take_copies()
+        if len(pairs):
+            copy_blocks(self.key_cache, self.value_cache, self.torch.from_numpy(pairs).to(self.dev))
+            if self.log is not None:
+                self.log.append(("copy", pairs.copy()))
+        return pairs
+
+    # ------------------------------------------------------------------------------------------------------
+    def add_sequence(self, seq_id: int, tokens) -> np.ndarray:
+        """Admit a sequence with its prompt; returns the prompt slots (-1 where a shared block already has it)."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = self.bm.add_sequence(seq_id, len(tokens), tokens)
+        fresh = slots >= 0
+        if fresh.any():
+            k, v = self.prompt_rows(tokens)
+            idx = self.torch.from_numpy(np.nonzero(fresh)[0]).to(self.dev)
+            self._write(k[idx].contiguous(), v[idx].contiguous(), slots[fresh])
+        self.running.append(seq_id)
+        self.lengths[seq_id] = len(tokens)
+        return slots
+
+    def fork(self, parent_id: int, child_id: int):
+        self.bm.fork(parent_id, child_id)
+        self.running.append(child_id)
+        self.lengths[child_id] = self.lengths[parent_id]
+
+    def finish(self, seq_id: int):
+        self.bm.free_sequence(seq_id)
+        self.running.remove(seq_id)
+        del self.lengths[seq_id]
+
+    def step(self, query=None, new_kv=None):
+        """One decode step for every running sequence; returns (seq_ids, out [n, Hq, D] fp32, copy pairs).
+
+        query defaults to random rows; new_kv (k, v) of shape [n, Hkv, D] to random rows.
+        """
+        t = self.torch
+        ids = list(self.running)
+        n = len(ids)
+        if n == 0:
+            return ids, None, np.zeros((0, 2), np.int32)
+        slots = self.bm.append_slots(ids)
+        pairs = self._apply_copies()  # copy-on-write before the new tokens land in the copies
+        k, v = self._rows(n) if new_kv is None else new_kv
+        self._write(k, v, slots)
+        for s in ids:
+            self.lengths[s] += 1
+        if query is None:
+            query = t.randn((n, self.hq, self.d), generator=self.gen, device=self.dev,
+                            dtype=t.float32).to(self.dt)
+        tables, lens = self.bm.block_tables(ids)
+        mcl = int(lens.max())
+        need = workspace_bytes(n, self.hq, self.hkv, self.d, self.bs, mcl, self.kv_code, self.partition_size)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = t.empty(need, dtype=t.uint8, device=self.dev)
+        out = t.empty((n, self.hq, self.d), dtype=t.float32, device=self.dev)
+        paged_attention_decode(out, query, self.key_cache, self.value_cache,
+                               t.from_numpy(tables).to(self.dev), t.from_numpy(lens).to(self.dev), self.scale,
+                               self.bs, max_context_len=mcl, partition_size=self.partition_size,
+                               workspace=self._ws if need else None)
+        self.last_query = query
+        return ids, out, pairs
+
+    def stats(self) -> dict:
+        return self.bm.stats()

@@ -17,7 +17,7 @@ FAKE = 1 << 20  # a 16-byte-aligned address that is never dereferenced: validati
 
 
 def header_functions():
-    text = open(pa.HEADER_PATH).read() + open(pa.DIAG_HEADER_PATH).read()
+    text = "".join(open(p).read() for p in (pa.HEADER_PATH, pa.DIAG_HEADER_PATH, pa.BM_HEADER_PATH))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"paged_attention_decode", "reshape_and_cache", "copy_blocks", "paged_gather",
             "paged_attention_workspace_bytes", "paged_attention_partition_size", "pa_strerror",
-            "pa_abi_version", "pa_stream_read", "pa_stream_copy"} <= set(names)
+            "pa_abi_version", "pa_stream_read", "pa_stream_copy", "pa_bm_create", "pa_bm_append_slots"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert lib.pa_abi_version() == pa.ABI_VERSION
