@@ -11,6 +11,7 @@ Prints one JSON line: whole-step achieved GB/s (algorithmic bytes / step time), 
 entry for the attention call (HIP events on the stream it runs on) and the CPU oracle's rate on the host cores.
 
     python bench.py [--workload llama2_7b] [--steps 100] [--warmup 10]
+    python bench.py --workload decode_loop --steps 100 --warmup 50   (continuous batching, block manager)
 """
 
 from __future__ import annotations
@@ -126,6 +127,128 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
     return path
 
 
+def run_decode_loop(args) -> int:
+    """Continuous-batching decode over a request stream: the block manager places every token, the kernels
+    move and read them. Llama-2-7B-shaped attention (32 heads x 128, bf16, 16-token blocks), up to 256
+    sequences, prompts of the mixed-length workload (30% of the long ones open with a shared 1024-token
+    system prompt), 32..256 new tokens each, 5% of requests sampled twice (a fork). Finished sequences free
+    their blocks and are replaced at once. A step is one decode step of every running sequence, host
+    bookkeeping included; the timed steps run after the batch has filled."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_458_amd as pa
+    from paged_kv_cache_458_amd.block_manager import PA_ERR_NOMEM
+    from paged_kv_cache_458_amd.decode_loop import DecodeLoop
+    from workloads import request_stream
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    max_batch, hq, hkv, d, bs, max_len = 256, 32, 32, 128, 16, 4096 + 256
+    num_blocks = 40000  # about 1.6x what 256 sequences of the mix hold on average; plus the padding block
+    loop = DecodeLoop(num_blocks=num_blocks, block_size=bs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      max_blocks_per_seq=-(-max_len // bs), dtype="bf16", seed=6, prompt_kv="random",
+                      partition_size=-1 if args.partition_size is None else args.partition_size)
+    stream = request_stream(6)
+    remaining: dict[int, int] = {}
+    pending = []
+    next_id = 0
+    admitted = finished = deferred = 0
+
+    def refill():
+        nonlocal next_id, admitted, deferred
+        while len(loop.running) < max_batch:
+            req = pending.pop() if pending else next(stream)
+            try:
+                loop.add_sequence(next_id, req.prompt)
+            except pa.PagedAttentionError as e:
+                if e.status != PA_ERR_NOMEM:
+                    raise
+                pending.append(req)
+                deferred += 1
+                return
+            remaining[next_id] = req.max_new_tokens
+            next_id += 1
+            admitted += 1
+            if req.parallel > 1 and len(loop.running) < max_batch:
+                loop.fork(next_id - 1, next_id)
+                remaining[next_id] = req.max_new_tokens
+                next_id += 1
+
+    def step():
+        nonlocal finished
+        refill()
+        ids, _, _ = loop.step()
+        for s in ids:
+            remaining[s] -= 1
+            if remaining[s] == 0:
+                loop.finish(s)
+                del remaining[s]
+                finished += 1
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize(dev)
+    loop.attention_events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    events = loop.attention_events
+    loop.attention_events = None
+    stats = []  # occupancy, sampled over further steps outside the timed region
+    for _ in range(min(args.steps, 20)):
+        step()
+        stats.append(loop.stats())
+    row = hkv * d * 2
+    attn_s, attn_bytes, stepped = 0.0, 0, 0
+    for (e0, e1), lens in events:
+        attn_s += e0.elapsed_time(e1) * 1e-3
+        nb = int(((lens.astype(np.int64) + bs - 1) // bs).sum())
+        attn_bytes += int(lens.astype(np.int64).sum()) * row * 2 + len(lens) * hq * d * (2 + 4) + nb * 4 + 4 * len(lens)
+        stepped += len(lens)
+    frag = float(np.mean([s["internal_fragmentation"] for s in stats]))
+    contiguous_slots = float(np.mean([s["sequences"] for s in stats])) * max_len
+    rec = {
+        "metric": METRIC,
+        "value": round(attn_bytes / wall / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode_loop", "max_batch": max_batch, "num_q_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": d, "block_size": bs, "pool_blocks": num_blocks, "seed": 6},
+        "decode_queries_per_s": round(stepped / wall, 1),
+        "attention": {"us_mean": round(attn_s / len(events) * 1e6, 2),
+                      "gb_per_s": round(attn_bytes / attn_s / 1e9, 1),
+                      "share_of_step": round(attn_s / wall, 3)},
+        "decode_loop": {
+            "admitted": admitted, "finished": finished, "deferred_for_memory": deferred,
+            "mean_running": round(stepped / len(events), 1),
+            "internal_fragmentation": round(frag, 4),
+            "used_slots_vs_contiguous_max_len": round(float(np.mean([s["slots_in_used_blocks"] for s in stats]))
+                                                      / contiguous_slots, 4),
+            "shared_blocks_mean": round(float(np.mean([s["shared_blocks"] for s in stats])), 1),
+            "cow_copies": stats[-1]["cow_copies"],
+        },
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode within the loop", "achieved":
+                     round(attn_bytes / attn_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(attn_bytes / attn_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,8 +280,10 @@ def main() -> int:
     import paged_kv_cache_458_amd as pa
     from workloads import CONFIG_NAMES, algorithmic_bytes, build_structure, materialize
 
+    if args.workload == "decode_loop":
+        return run_decode_loop(args)
     if args.workload not in CONFIG_NAMES:
-        ap.error(f"--workload must be one of {CONFIG_NAMES}")
+        ap.error(f"--workload must be one of {CONFIG_NAMES} or decode_loop")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.load_library()

@@ -38,7 +38,7 @@ class DecodeLoop:
 
     def __init__(self, *, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  max_blocks_per_seq: int, dtype: str = "bf16", device="cuda", seed: int = 0, scale=None,
-                 partition_size: int = -1, record: bool = False):
+                 partition_size: int = -1, record: bool = False, prompt_kv: str = "prefix"):
         import torch
 
         self.torch = torch
@@ -62,6 +62,13 @@ class DecodeLoop:
         self._ws = None
         # with record=True every cache write and copy is kept on the host so that a test can rebuild the pools
         self.log: list | None = [] if record else None
+        # "prefix": prompt K/V is a function of the token prefix (host generator, for checking shared blocks);
+        # "random": fresh device-generated rows (for timing, where only the access pattern matters)
+        if prompt_kv not in ("prefix", "random"):
+            raise ValueError("prompt_kv must be 'prefix' or 'random'")
+        self.prompt_kv = prompt_kv
+        # a list to collect ((start, end) HIP events, context lengths) of every attention call, or None
+        self.attention_events: list | None = None
 
     # ------------------------------------------------------------------------------------------------------
     def _rows(self, n: int):
@@ -82,9 +89,13 @@ class DecodeLoop:
             v[i] = rng.standard_normal((self.hkv, self.d), dtype=np.float32)
         return (t.from_numpy(k).to(self.dev).to(self.dt), t.from_numpy(v).to(self.dev).to(self.dt))
 
+    def _to_device(self, a: np.ndarray):
+        # through pinned memory without blocking: the host can prepare the next step while the GPU works, and
+        # torch's pinned-memory allocator does not hand the staging buffer out again before the copy has run
+        return self.torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(self.dev, non_blocking=True)
+
     def _write(self, k, v, slots: np.ndarray):
-        t = self.torch
-        sm = t.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to(self.dev)
+        sm = self._to_device(np.asarray(slots, dtype=np.int32))
         reshape_and_cache(k, v, self.key_cache, self.value_cache, sm)
         if self.log is not None:
             self.log.append(("write", slots.copy(), k.cpu(), v.cpu()))
@@ -92,7 +103,7 @@ class DecodeLoop:
     def _apply_copies(self):
         pairs = self.bm.take_copies()
         if len(pairs):
-            copy_blocks(self.key_cache, self.value_cache, self.torch.from_numpy(pairs).to(self.dev))
+            copy_blocks(self.key_cache, self.value_cache, self._to_device(pairs))
             if self.log is not None:
                 self.log.append(("copy", pairs.copy()))
         return pairs
@@ -104,9 +115,13 @@ class DecodeLoop:
         slots = self.bm.add_sequence(seq_id, len(tokens), tokens)
         fresh = slots >= 0
         if fresh.any():
-            k, v = self.prompt_rows(tokens)
-            idx = self.torch.from_numpy(np.nonzero(fresh)[0]).to(self.dev)
-            self._write(k[idx].contiguous(), v[idx].contiguous(), slots[fresh])
+            if self.prompt_kv == "random":
+                k, v = self._rows(int(fresh.sum()))
+            else:
+                k, v = self.prompt_rows(tokens)
+                idx = self._to_device(np.nonzero(fresh)[0])
+                k, v = k[idx].contiguous(), v[idx].contiguous()
+            self._write(k, v, slots[fresh])
         self.running.append(seq_id)
         self.lengths[seq_id] = len(tokens)
         return slots
@@ -146,10 +161,17 @@ class DecodeLoop:
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = t.empty(need, dtype=t.uint8, device=self.dev)
         out = t.empty((n, self.hq, self.d), dtype=t.float32, device=self.dev)
+        ev = None
+        if self.attention_events is not None:
+            ev = (t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
+            ev[0].record(t.cuda.current_stream(self.dev))
         paged_attention_decode(out, query, self.key_cache, self.value_cache,
-                               t.from_numpy(tables).to(self.dev), t.from_numpy(lens).to(self.dev), self.scale,
+                               self._to_device(tables), self._to_device(lens), self.scale,
                                self.bs, max_context_len=mcl, partition_size=self.partition_size,
                                workspace=self._ws if need else None)
+        if ev is not None:
+            ev[1].record(t.cuda.current_stream(self.dev))
+            self.attention_events.append((ev, lens.copy()))
         self.last_query = query
         return ids, out, pairs
 

@@ -14,3 +14,4 @@ from .decode import (  # noqa: F401
     materialize,
     algorithmic_bytes,
 )
+from .requests import Request, request_stream  # noqa: F401,E402
