@@ -25,7 +25,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
-F32, BF16 = 0, 1
+F32, BF16, E4M3 = 0, 1, 2
 _lib = None
 
 
@@ -50,8 +50,14 @@ def load(path: str | None = None):
 def _bind(lib):
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
-    lib.oracle_decode.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, P, P, ctypes.c_double, i32, i32, i32,
-                                  i32, i32, i64, i32, P, i64]
+    lib.oracle_decode.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_double, ctypes.c_double, P, P,
+                                  ctypes.c_double, i32, i32, i32, i32, i32, i64, i32, P, i64]
+    lib.oracle_e4m3_values.argtypes, lib.oracle_e4m3_values.restype = [P], None
+    lib.oracle_quantize_e4m3.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_float]
+    lib.oracle_quantize_e4m3.restype = ctypes.c_int
+    lib.oracle_reshape_and_cache_e4m3.argtypes = [P, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i64,
+                                                  ctypes.c_float, ctypes.c_float]
+    lib.oracle_reshape_and_cache_e4m3.restype = ctypes.c_int
     lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32]
     lib.oracle_reshape_and_cache.restype = ctypes.c_int
@@ -73,17 +79,21 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:  # bf16 bit patterns
         return BF16
-    raise TypeError(f"oracle takes float32 arrays or uint16 bf16 bit patterns, got {a.dtype}")
+    if a.dtype == np.uint8:  # OCP FP8 E4M3 codes
+        return E4M3
+    raise TypeError(f"oracle takes float32 arrays, uint16 bf16 bit patterns or uint8 E4M3 codes, got {a.dtype}")
 
 
 def num_threads(lib=None) -> int:
     return int((lib or load()).oracle_num_threads())
 
 
-def decode(query, key_cache, value_cache, block_tables, context_lens, scale, *, rows=None, lib=None):
+def decode(query, key_cache, value_cache, block_tables, context_lens, scale, *, rows=None, k_scale=1.0,
+           v_scale=1.0, lib=None):
     """fp64 decode attention.
 
-    query [B, Hq, D] and the pools [NB, bs, Hkv, D] are float32 arrays or uint16 arrays of bf16 bits.
+    query [B, Hq, D] and the pools [NB, bs, Hkv, D] are float32 arrays, uint16 arrays of bf16 bits or (pools
+    only) uint8 arrays of E4M3 codes, whose decoded values are multiplied by k_scale and v_scale.
     Returns float64 [B, Hq, D]; with ``rows`` (int array [n, 2] of (seq, head)) only those rows are computed
     and the rest are NaN.
     """
@@ -103,7 +113,8 @@ def decode(query, key_cache, value_cache, block_tables, context_lens, scale, *, 
     if rows is not None:
         rw = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
         n = rw.shape[0]
-    rc = lib.oracle_decode(_ptr(out), _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(bt),
+    rc = lib.oracle_decode(_ptr(out), _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc),
+                           float(k_scale), float(v_scale), _ptr(bt),
                            _ptr(cl), float(scale), bs, B, Hq, Hkv, D, NB, bt.shape[1],
                            _ptr(rw) if rw is not None else None, n)
     if rc != 0:
@@ -150,3 +161,40 @@ def gather(cache, block_tables, context_lens, *, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_gather rejected its input (status {rc})")
     return out
+
+
+def e4m3_values(lib=None) -> np.ndarray:
+    """float64 [256]: the value of every OCP FP8 E4M3 code (NaN for 0x7F and 0xFF)."""
+    lib = lib or load()
+    out = np.empty(256, dtype=np.float64)
+    lib.oracle_e4m3_values(_ptr(out))
+    return out
+
+
+def quantize_e4m3(x, scale: float, *, lib=None) -> np.ndarray:
+    """uint8 E4M3 codes of x / scale (fp32 division), saturated to +-448, ties to even; NaN -> 0x7F."""
+    lib = lib or load()
+    src = np.ascontiguousarray(x)
+    dst = np.empty(src.shape, dtype=np.uint8)
+    rc = lib.oracle_quantize_e4m3(_ptr(dst), _ptr(src), _dtype_code(src), src.size, float(scale))
+    if rc != 0:
+        raise ValueError("quantize_e4m3 takes float32 or bf16 input")
+    return dst
+
+
+def reshape_and_cache_e4m3(key_cache, value_cache, key, value, slot_mapping, k_scale, v_scale, *, lib=None):
+    """The FP8 cache write on host pools (uint8 [NB, bs, Hkv, D]): quantise key/value rows into their slots."""
+    lib = lib or load()
+    for a in (key_cache, value_cache):
+        if a.dtype != np.uint8 or not a.flags.c_contiguous:
+            raise ValueError("E4M3 pools must be C-contiguous uint8 arrays")
+    k = np.ascontiguousarray(key)
+    v = np.ascontiguousarray(value)
+    if k.dtype != v.dtype:
+        raise TypeError("key and value must share a dtype")
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    NB, bs, Hkv, D = key_cache.shape
+    rc = lib.oracle_reshape_and_cache_e4m3(_ptr(key_cache), _ptr(value_cache), _ptr(k), _ptr(v), _dtype_code(k),
+                                           _ptr(sm), sm.size, Hkv, D, bs, NB, float(k_scale), float(v_scale))
+    if rc != 0:
+        raise ValueError(f"oracle_reshape_and_cache_e4m3 rejected its input (status {rc})")

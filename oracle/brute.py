@@ -13,16 +13,31 @@ from __future__ import annotations
 import numpy as np
 
 
+def _e4m3_as_f32(c: np.ndarray) -> np.ndarray:
+    """E4M3 codes rebuilt as fp32 bit patterns: the exponent is re-biased (7 -> 127) and the 3 mantissa bits
+    moved to the top of the fp32 mantissa; subnormals (exponent 0) are m / 512, which numpy computes exactly;
+    exponent 15 with mantissa 7 is NaN."""
+    c = c.astype(np.uint32)
+    sign, e, m = c >> 7, (c >> 3) & 15, c & 7
+    normal = ((sign << 31) | ((e + 120) << 23) | (m << 20)).view(np.float32)
+    sub = np.where(sign == 1, -1.0, 1.0).astype(np.float32) * (m.astype(np.float32) / np.float32(512.0))
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (m == 7), np.float32(np.nan), out)
+
+
 def to_f64(a: np.ndarray) -> np.ndarray:
-    """float32 arrays widen exactly; uint16 arrays are bf16 bit patterns (the high half of an fp32)."""
+    """float32 arrays widen exactly; uint16 arrays are bf16 bit patterns (the high half of an fp32); uint8
+    arrays are OCP FP8 E4M3 codes."""
     if a.dtype == np.float32:
         return a.astype(np.float64)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype == np.uint8:
+        return _e4m3_as_f32(a).astype(np.float64)
     raise TypeError(a.dtype)
 
 
-def dense_kv(key_cache, value_cache, block_table_row, length):
+def dense_kv(key_cache, value_cache, block_table_row, length, k_scale=1.0, v_scale=1.0):
     """Dense [L, Hkv, D] K and V of one sequence, rebuilt by scanning every physical block of the pool."""
     NB, bs, Hkv, D = key_cache.shape
     nblk = -(-int(length) // bs)
@@ -35,15 +50,15 @@ def dense_kv(key_cache, value_cache, block_table_row, length):
             for off in range(bs):
                 t = int(j) * bs + off
                 if t < length:
-                    k[t] = to_f64(key_cache[b, off])
-                    v[t] = to_f64(value_cache[b, off])
+                    k[t] = to_f64(key_cache[b, off]) * k_scale
+                    v[t] = to_f64(value_cache[b, off]) * v_scale
                     seen[t] = True
     if not seen.all():
         raise ValueError("a live logical position maps to no physical block of the pool")
     return k, v
 
 
-def decode(query, key_cache, value_cache, block_tables, context_lens, scale):
+def decode(query, key_cache, value_cache, block_tables, context_lens, scale, k_scale=1.0, v_scale=1.0):
     q = to_f64(np.asarray(query))
     B, Hq, D = q.shape
     Hkv = key_cache.shape[2]
@@ -53,7 +68,7 @@ def decode(query, key_cache, value_cache, block_tables, context_lens, scale):
         L = int(context_lens[s])
         if L == 0:
             continue
-        k, v = dense_kv(key_cache, value_cache, block_tables[s], L)
+        k, v = dense_kv(key_cache, value_cache, block_tables[s], L, k_scale, v_scale)
         for h in range(Hq):
             z = (k[:, h // G, :] @ q[s, h]) * scale
             w = np.exp(z - z.max())

@@ -31,16 +31,81 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_E4M3 2 /* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities */
+
+/*
+ * Value of an OCP FP8 E4M3 code, from the format's definition: exponent field 15 with mantissa 7 is NaN;
+ * exponent field 0 is subnormal, m * 2^-9; otherwise (1 + m / 8) * 2^(e - 7). Largest finite value 448.
+ */
+static double e4m3_value(uint8_t c) {
+    const int e = (c >> 3) & 0xF, m = c & 7;
+    const double sign = (c & 0x80) ? -1.0 : 1.0;
+    if (e == 15 && m == 7) {
+        return NAN;
+    }
+    if (e == 0) {
+        return sign * ldexp((double)m, -9);
+    }
+    return sign * ldexp(1.0 + m / 8.0, e - 7);
+}
 
 /* One stored element, decoded exactly to fp64. */
 static double elem(const void *base, int64_t index, int dtype) {
     if (dtype == ORACLE_F32) {
         return (double)((const float *)base)[index];
     }
+    if (dtype == ORACLE_E4M3) {
+        return e4m3_value(((const uint8_t *)base)[index]);
+    }
     uint32_t bits = (uint32_t)((const uint16_t *)base)[index] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/*
+ * Quantisation of the FP8 cache write: y = x / scale as an fp32 division (correctly rounded), saturated to
+ * [-448, 448] (infinities included), then rounded to the nearest E4M3 value, ties to an even mantissa; NaN
+ * becomes code 0x7F. Exact: the scalings below are by powers of two, and nearbyint rounds ties to even in the
+ * default rounding mode.
+ */
+static uint8_t e4m3_quantize(float x, float scale) {
+    const float y = x / scale;
+    if (isnan(y)) {
+        return 0x7F;
+    }
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs((double)y);
+    if (a > 448.0) {
+        a = 448.0;
+    }
+    if (a < ldexp(1.0, -6)) { /* below the smallest normal: units of 2^-9, and 8 units is that normal */
+        return sign | (uint8_t)nearbyint(ldexp(a, 9));
+    }
+    int e = ilogb(a); /* 2^e <= a < 2^(e+1), e in [-6, 8] */
+    double q = nearbyint(ldexp(a, 3 - e)); /* in [8, 16] */
+    if (q == 16.0) {
+        q = 8.0;
+        ++e;
+    }
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+void oracle_e4m3_values(double *out) {
+    for (int c = 0; c < 256; ++c) {
+        out[c] = e4m3_value((uint8_t)c);
+    }
+}
+
+/* dst[i] = quantised src[i] (src float32 or bf16 bits) for i < n. */
+int oracle_quantize_e4m3(uint8_t *dst, const void *src, int src_dtype, int64_t n, float scale) {
+    if (src_dtype != ORACLE_F32 && src_dtype != ORACLE_BF16) {
+        return -1;
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        dst[i] = e4m3_quantize((float)elem(src, i, src_dtype), scale);
+    }
+    return 0;
 }
 
 int oracle_num_threads(void) {
@@ -55,6 +120,9 @@ int oracle_num_threads(void) {
  * Decode attention for the (sequence, query head) rows listed in `rows` (pairs s, h), or for every row when
  * rows == NULL. out is [num_seqs, num_q_heads, head_dim] fp64; rows not listed are left untouched.
  *
+ * Stored K and V elements are multiplied by k_scale and v_scale after decoding (1 for float32 / bf16 caches;
+ * the dequantisation scales of an FP8 cache).
+ *
  * For each row: G = num_q_heads / num_kv_heads query heads share KV head g = h / G (consecutive grouping);
  * position t of the sequence sits in physical block block_tables[s][t / block_size] at offset
  * t % block_size; z_t = scale * sum_d q[d] k_t[d] (d ascending); m = max z; w_t = exp(z_t - m);
@@ -64,7 +132,8 @@ int oracle_num_threads(void) {
  * length makes live is not a valid block id, -4 when memory runs out.
  */
 int oracle_decode(double *out, const void *query, int q_dtype, const void *key_cache, const void *value_cache,
-                  int kv_dtype, const int32_t *block_tables, const int32_t *context_lens, double scale,
+                  int kv_dtype, double k_scale, double v_scale, const int32_t *block_tables,
+                  const int32_t *context_lens, double scale,
                   int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, const int32_t *rows,
                   int64_t num_rows) {
@@ -127,8 +196,8 @@ int oracle_decode(double *out, const void *query, int q_dtype, const void *key_c
             const int64_t off = t % block_size;
             const int64_t base = ((phys * block_size + off) * num_kv_heads + g) * head_dim;
             for (int32_t d = 0; d < head_dim; ++d) {
-                k[t * head_dim + d] = elem(key_cache, base + d, kv_dtype);
-                v[t * head_dim + d] = elem(value_cache, base + d, kv_dtype);
+                k[t * head_dim + d] = k_scale * elem(key_cache, base + d, kv_dtype);
+                v[t * head_dim + d] = v_scale * elem(value_cache, base + d, kv_dtype);
             }
         }
         double m = -INFINITY;
@@ -224,6 +293,31 @@ int oracle_gather(void *out, const void *cache, const int32_t *block_tables, con
             memcpy((char *)out + r * row, (const char *)cache + (phys * block_size + t % block_size) * row,
                    (size_t)row);
             ++r;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The FP8 cache write: the new token's K/V rows (float32 or bf16) are quantised (e4m3_quantize with k_scale,
+ * v_scale) into slot slot_mapping[n] of the E4M3 pools. Slots < 0 are skipped; -1 for a slot past the pool.
+ */
+int oracle_reshape_and_cache_e4m3(uint8_t *key_cache, uint8_t *value_cache, const void *key, const void *value,
+                                  int src_dtype, const int32_t *slot_mapping, int32_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  float k_scale, float v_scale) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    for (int32_t n = 0; n < num_tokens; ++n) {
+        const int64_t slot = slot_mapping[n];
+        if (slot < 0) {
+            continue;
+        }
+        if (slot >= num_blocks * block_size) {
+            return -1;
+        }
+        for (int64_t i = 0; i < row; ++i) {
+            key_cache[slot * row + i] = e4m3_quantize((float)elem(key, n * row + i, src_dtype), k_scale);
+            value_cache[slot * row + i] = e4m3_quantize((float)elem(value, n * row + i, src_dtype), v_scale);
         }
     }
     return 0;

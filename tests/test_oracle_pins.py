@@ -375,7 +375,7 @@ MUTANTS = {
     "dropped_scale": ("z[t] = scale * acc;", "z[t] = acc;"),
     "wrong_kv_head": ("const int32_t g = h / G;", "const int32_t g = h % num_kv_heads;"),
     "offset_off_by_one": ("const int64_t off = t % block_size;", "const int64_t off = (t + 1) % block_size;"),
-    "k_v_swapped": ("k[t * head_dim + d] = elem(key_cache", "k[t * head_dim + d] = elem(value_cache"),
+    "k_v_swapped": ("k[t * head_dim + d] = k_scale * elem(key_cache", "k[t * head_dim + d] = k_scale * elem(value_cache"),
     "bf16_misdecoded": ("<< 16;", "<< 15;"),
     "no_normalisation": ("o[d] /= sum;", "o[d] /= 1.0;"),
     "table_row_stride": ("block_tables[(int64_t)s * max_blocks_per_seq + t / block_size]",
