@@ -291,7 +291,7 @@ def main() -> int:
     st = build_structure(args.workload)
     part = st.partition_size if args.partition_size is None else args.partition_size
     B, Hq, Hkv, D, bs = st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size
-    kv_code = pa.PA_BF16 if st.dtype == "bf16" else pa.PA_F32
+    kv_code = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
     launched_part = pa.partition_size_for(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
 
     t = materialize(st, dev, include_new_token=False)
@@ -314,11 +314,12 @@ def main() -> int:
         kc, vc = pools[i % len(pools)]
         if pairs is not None:
             pa.copy_blocks(kc, vc, pairs)
-        pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots)
+        pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots, k_scale=st.k_scale, v_scale=st.v_scale)
         if ev is not None:
             ev[0].record(stream)
         pa.paged_attention_decode(out, t["query"], kc, vc, tables, lens, st.scale, bs,
-                                  max_context_len=st.max_context_len, partition_size=part, workspace=ws)
+                                  max_context_len=st.max_context_len, partition_size=part, workspace=ws,
+                                  k_scale=st.k_scale, v_scale=st.v_scale)
         if ev is not None:
             ev[1].record(stream)
 
@@ -365,7 +366,8 @@ def main() -> int:
 
     ab = algorithmic_bytes(st)
     row_bytes = Hkv * D * st.esize
-    cache_write_bytes = 2 * 2 * int((st.slot_mapping >= 0).sum()) * row_bytes  # read + write, K and V
+    # K and V: read the new row (query dtype), write it into the cache (cache dtype)
+    cache_write_bytes = 2 * int((st.slot_mapping >= 0).sum()) * Hkv * D * (st.q_esize + st.esize)
     copy_bytes = 2 * 2 * len(st.copy_pairs) * bs * row_bytes
     step_bytes = ab["total"] + cache_write_bytes + copy_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -383,7 +385,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": st.dtype,
+        # an E4M3 cache is widened to bf16 for the products: the arithmetic is bf16 x bf16 -> f32
+        "dtype": "bf16" if st.dtype == "fp8" else st.dtype,
         "accumulate": "f32",
         "data": "synthetic",
         "config": {
@@ -393,6 +396,7 @@ def main() -> int:
             "num_kv_heads": Hkv,
             "head_dim": D,
             "block_size": bs,
+            "kv_cache_dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[st.dtype],
             "context_len_mean": float(st.context_lens.mean()),
             "context_len_max": int(st.context_lens.max()),
             "partition_size": launched_part,
@@ -433,12 +437,17 @@ def main() -> int:
         host = {}
         for name, tt in (("query", t["query"]), ("key_cache", kc), ("value_cache", vc)):
             tt = tt.contiguous().cpu()
-            host[name] = tt.view(torch.int16).numpy().view(np.uint16) if tt.dtype == torch.bfloat16 else tt.numpy()
+            if tt.dtype == torch.bfloat16:
+                host[name] = tt.view(torch.int16).numpy().view(np.uint16)
+            elif tt.dtype == torch.float8_e4m3fn:
+                host[name] = tt.view(torch.uint8).numpy()
+            else:
+                host[name] = tt.numpy()
         lib = oracle.load()
         reps, t0 = 0, time.perf_counter()
         while True:
             oracle.decode(host["query"], host["key_cache"], host["value_cache"], st.block_tables, st.context_lens,
-                          st.scale, lib=lib)
+                          st.scale, k_scale=st.k_scale, v_scale=st.v_scale, lib=lib)
             reps += 1
             el = time.perf_counter() - t0
             log(f"cpu oracle call {reps}: {el:.1f} s")

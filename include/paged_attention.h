@@ -12,7 +12,8 @@
  *  - Tensor arguments are DEVICE pointers into caller-owned memory (for instance PyTorch allocations),
  *    row-major and contiguous. The library allocates no device memory, keeps no per-call state and is
  *    reentrant; split-context scratch comes only from the caller's workspace.
- *  - dtype codes: PA_F32 (IEEE fp32) and PA_BF16 (bfloat16). Attention output is always fp32.
+ *  - dtype codes: PA_F32 (IEEE fp32), PA_BF16 (bfloat16) and, for caches, PA_FP8_E4M3. Attention
+ *    output is always fp32.
  *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it and the call returns
  *    without synchronising; results are valid once the caller synchronises that stream.
  *  - Every argument the host can check is checked before anything is launched; on failure the call
@@ -38,6 +39,7 @@ extern "C" {
 /* dtype codes */
 #define PA_F32 0
 #define PA_BF16 1
+#define PA_FP8_E4M3 2 /* OCP 8-bit float E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; max 448) */
 
 /* status codes */
 #define PA_OK 0
@@ -91,7 +93,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *   head_dim       64 or 128
  *   num_q_heads    a multiple of num_kv_heads
  *   max_context_len  upper bound of context_lens, <= max_blocks_per_seq * block_size
- *   (q_dtype, kv_dtype)  (PA_F32, PA_F32) or (PA_BF16, PA_BF16); accumulation is fp32 either way
+ *   (q_dtype, kv_dtype)  (PA_F32, PA_F32) or (PA_BF16, PA_BF16); accumulation is fp32 either way (FP8
+ *                  caches: paged_attention_decode_scaled)
  *   partition_size 0 = one pass over each context; > 0 = split each context into partitions of this many
  *                  tokens (a multiple of 16) and merge the partial softmax states with a log-sum-exp
  *                  reduction; -1 = the library chooses (paged_attention_partition_size)
@@ -106,6 +109,38 @@ int paged_attention_decode(float *out, const void *query, const void *key_cache,
                            int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_context_len, int32_t q_dtype, int32_t kv_dtype, int32_t partition_size,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode over caches whose stored elements are multiplied by a per-pool scale:
+ *     K_t = k_scale * key_cache row,  V_t = v_scale * value_cache row,
+ * the dequantisation of an FP8 KV cache (a quantised cache halves the bytes of a bandwidth-bound path;
+ * page 1 section 4.1 and page 3 section 2.3 name FP8 among the quantised formats). Arguments as in
+ * paged_attention_decode, plus k_scale and v_scale (finite, non-zero); the (q_dtype, kv_dtype) pairs are
+ * (PA_F32, PA_F32), (PA_BF16, PA_BF16) and (PA_BF16, PA_FP8_E4M3). Every E4M3 code is exactly a bf16 value, so
+ * the arithmetic after the load is that of the bf16 cache: k_scale folds into `scale` and v_scale into the
+ * output. paged_attention_decode(...) is this call with k_scale = v_scale = 1.
+ */
+int paged_attention_decode_scaled(float *out, const void *query, const void *key_cache, const void *value_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                  float k_scale, float v_scale, int32_t block_size, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+                                  int32_t kv_dtype, int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * Quantising cache write into PA_FP8_E4M3 pools: like reshape_and_cache, with every element of key[n]
+ * (value[n]) stored as the E4M3 code of x / k_scale (x / v_scale): an fp32 division, saturated to +-448,
+ * rounded to nearest with ties to an even mantissa; NaN is stored as 0x7F.
+ *
+ *   key, value               [num_tokens][num_kv_heads][head_dim] src_dtype (PA_F32 or PA_BF16)
+ *   key_cache, value_cache   [num_blocks][block_size][num_kv_heads][head_dim] E4M3 codes, updated in place
+ *   k_scale, v_scale         finite, non-zero
+ */
+int reshape_and_cache_fp8(const void *key, const void *value, void *key_cache, void *value_cache,
+                          const int32_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, int32_t src_dtype, float k_scale, float v_scale,
+                          void *stream);
 
 /*
  * Append each new token's K/V to its cache slot (page 3 section 2.1: every decode step updates the KV cache

@@ -20,7 +20,7 @@ DIAG_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_atte
 BM_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_block_manager.h")
 STREAM_SINK_FLOATS = 8192
 
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_OK = 0
 ABI_VERSION = 1
 
@@ -51,6 +51,12 @@ def load_library(path: str | None = None):
     lib.paged_attention_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, i32, i32, i32, i32, i32, i64, i32, i32,
                                            i32, i32, i32, P, sz, P]
     lib.paged_attention_decode.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.paged_attention_decode_scaled.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i64, i32,
+                                                  i32, i32, i32, i32, P, sz, P]
+    lib.paged_attention_decode_scaled.restype = ctypes.c_int
+    lib.reshape_and_cache_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32, f32, f32, P]
+    lib.reshape_and_cache_fp8.restype = ctypes.c_int
     lib.reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32, P]
     lib.reshape_and_cache.restype = ctypes.c_int
     lib.copy_blocks.argtypes = [P, P, P, i32, i32, i32, i32, i64, i32, P]
@@ -87,7 +93,9 @@ def _dtype_code(t) -> int:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; the kernels take float32 or bfloat16")
+    if t.dtype == torch.float8_e4m3fn:
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}; the kernels take float32, bfloat16 or float8_e4m3fn (cache)")
 
 
 def _dev(*tensors):
@@ -128,12 +136,14 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, m
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
                            block_size: int | None = None, *, max_context_len: int | None = None,
-                           partition_size: int = -1, workspace=None, stream=None):
+                           partition_size: int = -1, workspace=None, stream=None, k_scale: float = 1.0,
+                           v_scale: float = 1.0):
     """out[s, h] = softmax(scale * query[s, h] . K^T) . V over sequence s's paged K/V (see the C header).
 
-    out: fp32 [B, Hq, D]; query: [B, Hq, D]; key_cache/value_cache: [NB, bs, Hkv, D] (same dtype as query);
-    block_tables: int32 [B, MB]; context_lens: int32 [B]. max_context_len defaults to MB * bs (an upper bound
-    needs no device sync). A workspace is allocated with torch when the split path needs one and none is given.
+    out: fp32 [B, Hq, D]; query: [B, Hq, D]; key_cache/value_cache: [NB, bs, Hkv, D] (same dtype as query, or
+    float8_e4m3fn under a bfloat16 query, read as code value x k_scale / v_scale); block_tables: int32 [B, MB];
+    context_lens: int32 [B]. max_context_len defaults to MB * bs (an upper bound needs no device sync). A
+    workspace is allocated with torch when the split path needs one and none is given.
     """
     torch = _torch()
     dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens)
@@ -158,26 +168,47 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.paged_attention_decode(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-                                    block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, B, Hq, Hkv,
-                                    D, NB, MB, mcl, qd, kd, int(partition_size), ws_ptr, ws_len,
-                                    _stream(dev, stream))
-    _check("paged_attention_decode", st)
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache must have the same dtype")
+    ptrs = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+            context_lens.data_ptr())
+    tail = (bs, B, Hq, Hkv, D, NB, MB, mcl, qd, kd, int(partition_size), ws_ptr, ws_len, _stream(dev, stream))
+    if kd == PA_FP8_E4M3 or k_scale != 1.0 or v_scale != 1.0:
+        st = lib.paged_attention_decode_scaled(*ptrs, float(scale), float(k_scale), float(v_scale), *tail)
+        _check("paged_attention_decode_scaled", st)
+    else:
+        st = lib.paged_attention_decode(*ptrs, float(scale), *tail)
+        _check("paged_attention_decode", st)
     return out
 
 
-def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, stream=None):
-    """key_cache[slot // bs, slot % bs] = key[n] (and value) for every n with slot = slot_mapping[n] >= 0."""
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, stream=None, k_scale: float = 1.0,
+                      v_scale: float = 1.0):
+    """key_cache[slot // bs, slot % bs] = key[n] (and value) for every n with slot = slot_mapping[n] >= 0.
+
+    Into a float8_e4m3fn cache from float32/bfloat16 rows, the values are quantised: code = E4M3(x / scale) with
+    round-to-nearest-even, saturating to +-448, NaN to 0x7F (k_scale for keys, v_scale for values).
+    """
     dev = _dev(key, value, key_cache, value_cache, slot_mapping)
     _int32(slot_mapping, "slot_mapping")
     N, Hkv, D = key.shape
     NB, bs, Hkv2, D2 = key_cache.shape
     if (Hkv2, D2) != (Hkv, D) or value.shape != key.shape or value_cache.shape != key_cache.shape:
         raise ValueError("shape mismatch")
-    if key.dtype != key_cache.dtype or value.dtype != value_cache.dtype or key.dtype != value.dtype:
-        raise TypeError("key/value must match the cache dtype")
     if tuple(slot_mapping.shape) != (N,):
         raise ValueError("slot_mapping must be [num_tokens]")
+    if value_cache.dtype != key_cache.dtype or key.dtype != value.dtype:
+        raise TypeError("key/value and the two caches must agree in dtype")
+    torch = _torch()
+    if key_cache.dtype == torch.float8_e4m3fn and key.dtype != key_cache.dtype:
+        st = load_library().reshape_and_cache_fp8(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                                  value_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB,
+                                                  _dtype_code(key), float(k_scale), float(v_scale),
+                                                  _stream(dev, stream))
+        _check("reshape_and_cache_fp8", st)
+        return
+    if key.dtype != key_cache.dtype:
+        raise TypeError("key/value must match the cache dtype")
     st = load_library().reshape_and_cache(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
                                           value_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB,
                                           _dtype_code(key_cache), _stream(dev, stream))

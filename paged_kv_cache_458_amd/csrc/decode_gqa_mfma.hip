@@ -22,6 +22,10 @@
 //
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
 // loads of the block table (one per 16-token half). Scores use the exp2 domain (scale * log2 e folded in).
+//
+// An FP8 (OCP E4M3) cache is read at one byte per element and widened to bf16 while being staged into LDS
+// (every E4M3 value is exactly a bf16 value); from the LDS slices on, both caches take the same path. The
+// cache's scales enter as k_scale folded into the score scale and v_scale into the final normalisation.
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "../../include/paged_attention.h"
@@ -49,21 +53,33 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// 16 E4M3 codes -> 16 bf16 values (32 bytes) at p
+__device__ __forceinline__ void stage_e4m3(char* p, const U4& c) {
+  U4 lo, hi;
+  e4m3x4_to_bf16x4(c.x, lo.x, lo.y);
+  e4m3x4_to_bf16x4(c.y, lo.z, lo.w);
+  e4m3x4_to_bf16x4(c.z, hi.x, hi.y);
+  e4m3x4_to_bf16x4(c.w, hi.z, hi.w);
+  reinterpret_cast<U4*>(p)[0] = lo;
+  reinterpret_cast<U4*>(p)[1] = hi;
+}
+
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // W waves (KV heads of one sequence) per workgroup: they stream the same slots of the pool side by side.
-template <int D, int W>
+template <int KV, int D, int W>
 __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const DecodeArgs a) {
+  constexpr int kEsize = KV == PA_BF16 ? 2 : 1;  // bytes per cached element
   constexpr int kChunks = D / 32;          // 32-dim k-chunks of the QK product
   constexpr int kNt = D / 16;              // 16-dim column tiles of the PV product
-  constexpr int kPitch = D * 2 + 16;       // LDS bytes per K or V row
+  constexpr int kPitch = D * 2 + 16;       // LDS bytes per K or V row (bf16 in LDS for both caches)
   constexpr int kSlice = kTileTok * kPitch;  // one 32-row tile of K or of V
-  constexpr int kRowLanes = D * 2 / 16;    // lanes covering one row with 16-byte loads
+  constexpr int kRowLanes = D * kEsize / 16; // lanes covering one head row with 16-byte loads
   constexpr int kRows = kWave / kRowLanes; // rows per wave-wide load
-  constexpr int kLoads = kTile / kRows;    // loads per 16-row half, for K and for V (== kChunks)
-  static_assert(kLoads == kChunks, "one load per 32-dim chunk");
+  constexpr int kLoads = kTile / kRows;    // loads per 16-row half, for K and for V
+  static_assert(kLoads * kRows == kTile, "whole rows per load");
   __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -84,8 +100,8 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   const int j = lane >> 4;  // 0..3
   const int rr = lane / kRowLanes;  // loads: row within a wave-wide load
   const int rc = lane % kRowLanes;  //        16-byte chunk within the row
-  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * 2;
-  const int64_t head_off = (int64_t)g * D * 2;
+  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
+  const int64_t head_off = (int64_t)g * D * kEsize;
   char* const kslice = lds + w * 2 * kSlice;
   char* const vslice = kslice + kSlice;
 
@@ -100,8 +116,8 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
     qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
   }
 
-  // per-lane byte offsets inside a 16-row half tile: each wave-wide load covers kRows whole 256-byte head rows
-  // (full cache lines), for K as for V
+  // per-lane byte offsets inside a 16-row half tile: each wave-wide load covers kRows whole head rows (full
+  // cache lines: 256 bytes of bf16 or 128 of E4M3 at D = 128), for K as for V
   uint32_t off[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) off[i] = (uint32_t)((rr + kRows * i) * row_bytes + head_off + rc * 16);
@@ -139,8 +155,8 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   };
 
   // LDS: row r of the tile at slice + r * kPitch, K and V each in their own slice. This lane writes rows
-  // rr + kRows*i (+16 for the second half) at column rc * 16 bytes of both slices.
-  const int wofs = rr * kPitch + rc * 16;
+  // rr + kRows*i (+16 for the second half) at bf16 column rc * 16 / kEsize of both slices.
+  const int wofs = rr * kPitch + rc * 16 * (2 / kEsize);
   // K is read back in the A-operand layout of S^T = K Q^T: lane (n, j) takes row n, bytes 64c + 16j.
   const char* const kread = kslice + n * kPitch + j * 16;
   // Transposed reads (ds_read_b64_tr_b16): within each 16-lane group, lane l receives element l % 4 of the
@@ -179,7 +195,7 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
     lt += __shfl_xor(lt, 32);
     if (!head_ok) return;
     const int h = g * G + n;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     float* dst;
     if (!a.split || L <= a.partition) {
       dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
@@ -210,8 +226,13 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int r = (h2 * kTile + kRows * i) * kPitch + wofs;
-        *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
-        *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
+        if constexpr (KV == PA_BF16) {
+          *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
+          *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
+        } else {
+          stage_e4m3(kslice + r, kb[h2][i]);
+          stage_e4m3(vslice + r, vb[h2][i]);
+        }
       }
     wave_lds_sync();
     // scores
@@ -291,29 +312,32 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 }  // namespace
 
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group) {
-  return kv_dtype == PA_BF16 && (head_dim == 128 || head_dim == 64) && group >= 2 && group <= 16;
+  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && (head_dim == 128 || head_dim == 64) && group >= 2 &&
+         group <= 16;
 }
 
-template <int D, int W>
+template <int KV, int D, int W>
 hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
   const int groups = a.split ? (a.max_partitions + a.parts_per_wave - 1) / a.parts_per_wave : 1;
   const dim3 grid((a.num_kv_heads + W - 1) / W, groups, a.num_seqs);
-  decode_gqa_mfma_kernel<D, W><<<grid, dim3(kWave * W), 0, stream>>>(a);
+  decode_gqa_mfma_kernel<KV, D, W><<<grid, dim3(kWave * W), 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int KV, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   // a workgroup takes up to 8 KV heads of a sequence; the LDS slices of 8 waves fit one CU (8 x 17 KB at D 128)
-  if (a.num_kv_heads >= 8) return launch_w<D, 8>(a, stream);
-  if (a.num_kv_heads >= 4) return launch_w<D, 4>(a, stream);
-  if (a.num_kv_heads >= 2) return launch_w<D, 2>(a, stream);
-  return launch_w<D, 1>(a, stream);
+  if (a.num_kv_heads >= 8) return launch_w<KV, D, 8>(a, stream);
+  if (a.num_kv_heads >= 4) return launch_w<KV, D, 4>(a, stream);
+  if (a.num_kv_heads >= 2) return launch_w<KV, D, 2>(a, stream);
+  return launch_w<KV, D, 1>(a, stream);
 }
 
-hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_d<128>(a, stream);
-  if (a.head_dim == 64) return launch_d<64>(a, stream);
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  if (kv_dtype == PA_BF16 && a.head_dim == 128) return launch_d<PA_BF16, 128>(a, stream);
+  if (kv_dtype == PA_BF16 && a.head_dim == 64) return launch_d<PA_BF16, 64>(a, stream);
+  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128) return launch_d<PA_FP8_E4M3, 128>(a, stream);
+  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64) return launch_d<PA_FP8_E4M3, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -24,47 +24,86 @@ namespace {
 
 template <int KV, int D>
 struct Shape {
-  static constexpr int kEsize = KV == PA_BF16 ? 2 : 4;
+  static constexpr int kEsize = KV == PA_F32 ? 4 : KV == PA_BF16 ? 2 : 1;
   static constexpr int kEpl = 16 / kEsize;        // elements per lane per 16-byte load
   static constexpr int kRowLanes = D / kEpl;      // lanes holding one head's row
   static constexpr int kRows = kWave / kRowLanes; // slots per wave-wide load
   static constexpr int kLoads = kTile / kRows;    // loads per 16-token tile (per K and per V)
+  static constexpr int kQEsize = KV == PA_F32 ? 4 : 2;  // the query is bf16 over an E4M3 cache
+  static constexpr int kQWords = kEpl * kQEsize / 16;   // 16-byte words of query per lane chunk
 };
 
+template <int N>
+struct Words {
+  U4 w[N];
+};
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ float dot2(uint32_t q, uint32_t k, float d) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q), __builtin_bit_cast(bf16x2, k), d, false);
+}
+
 template <int KV>
-__device__ __forceinline__ float dot_chunk(const U4& q, const U4& k);
+__device__ __forceinline__ float dot_chunk(const Words<Shape<KV, 64>::kQWords>& q, const U4& k);
 
 template <>
-__device__ __forceinline__ float dot_chunk<PA_BF16>(const U4& q, const U4& k) {
-  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-  float d = 0.f;
-  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), d, false);
-  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), d, false);
-  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), d, false);
-  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), d, false);
-  return d;
+__device__ __forceinline__ float dot_chunk<PA_BF16>(const Words<1>& q, const U4& k) {
+  float d = dot2(q.w[0].x, k.x, 0.f);
+  d = dot2(q.w[0].y, k.y, d);
+  d = dot2(q.w[0].z, k.z, d);
+  return dot2(q.w[0].w, k.w, d);
 }
 
 template <>
-__device__ __forceinline__ float dot_chunk<PA_F32>(const U4& q, const U4& k) {
-  float d = __uint_as_float(q.x) * __uint_as_float(k.x);
-  d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
-  d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
-  d = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
+__device__ __forceinline__ float dot_chunk<PA_F32>(const Words<1>& q, const U4& k) {
+  float d = __uint_as_float(q.w[0].x) * __uint_as_float(k.x);
+  d = fmaf(__uint_as_float(q.w[0].y), __uint_as_float(k.y), d);
+  d = fmaf(__uint_as_float(q.w[0].z), __uint_as_float(k.z), d);
+  d = fmaf(__uint_as_float(q.w[0].w), __uint_as_float(k.w), d);
   return d;
+}
+
+// E4M3 keys: each word of four codes becomes two bf16 pairs, dotted with the matching bf16 query words
+template <>
+__device__ __forceinline__ float dot_chunk<PA_FP8_E4M3>(const Words<2>& q, const U4& k) {
+  uint32_t a, b;
+  float d = 0.f;
+  e4m3x4_to_bf16x4(k.x, a, b);
+  d = dot2(q.w[0].x, a, d);
+  d = dot2(q.w[0].y, b, d);
+  e4m3x4_to_bf16x4(k.y, a, b);
+  d = dot2(q.w[0].z, a, d);
+  d = dot2(q.w[0].w, b, d);
+  e4m3x4_to_bf16x4(k.z, a, b);
+  d = dot2(q.w[1].x, a, d);
+  d = dot2(q.w[1].y, b, d);
+  e4m3x4_to_bf16x4(k.w, a, b);
+  d = dot2(q.w[1].z, a, d);
+  return dot2(q.w[1].w, b, d);
+}
+
+__device__ __forceinline__ void axpy_bf16x2(float* acc, float p, uint32_t v) {
+  acc[0] = fmaf(p, bf16_lo(v), acc[0]);
+  acc[1] = fmaf(p, bf16_hi(v), acc[1]);
 }
 
 template <int KV>
 __device__ __forceinline__ void axpy_chunk(float* acc, float p, const U4& v) {
   if constexpr (KV == PA_BF16) {
-    acc[0] = fmaf(p, bf16_lo(v.x), acc[0]);
-    acc[1] = fmaf(p, bf16_hi(v.x), acc[1]);
-    acc[2] = fmaf(p, bf16_lo(v.y), acc[2]);
-    acc[3] = fmaf(p, bf16_hi(v.y), acc[3]);
-    acc[4] = fmaf(p, bf16_lo(v.z), acc[4]);
-    acc[5] = fmaf(p, bf16_hi(v.z), acc[5]);
-    acc[6] = fmaf(p, bf16_lo(v.w), acc[6]);
-    acc[7] = fmaf(p, bf16_hi(v.w), acc[7]);
+    axpy_bf16x2(acc + 0, p, v.x);
+    axpy_bf16x2(acc + 2, p, v.y);
+    axpy_bf16x2(acc + 4, p, v.z);
+    axpy_bf16x2(acc + 6, p, v.w);
+  } else if constexpr (KV == PA_FP8_E4M3) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t a, b;
+      e4m3x4_to_bf16x4(w[i], a, b);
+      axpy_bf16x2(acc + 4 * i, p, a);
+      axpy_bf16x2(acc + 4 * i + 2, p, b);
+    }
   } else {
     acc[0] = fmaf(p, __uint_as_float(v.x), acc[0]);
     acc[1] = fmaf(p, __uint_as_float(v.y), acc[1]);
@@ -103,8 +142,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
   const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const U4 q = *reinterpret_cast<const U4*>(static_cast<const char*>(a.query) +
-                                            ((int64_t)s * a.num_q_heads + h) * D * S::kEsize + c * 16);
+  Words<S::kQWords> q;
+  {
+    const char* qp = static_cast<const char*>(a.query) + ((int64_t)s * a.num_q_heads + h) * D * S::kQEsize +
+                     c * 16 * S::kQWords;
+#pragma unroll
+    for (int i = 0; i < S::kQWords; ++i) q.w[i] = reinterpret_cast<const U4*>(qp)[i];
+  }
 
   float m = -INFINITY, l = 0.f;
   float acc[S::kEpl];
@@ -190,7 +234,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   }
 
   if (r == 0) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const float poison = __uint_as_float(0x7fc00000u);
     float res[S::kEpl];
 #pragma unroll
@@ -313,6 +357,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t str
   else if (kv_dtype == PA_BF16 && a.head_dim == 64) decode_valu_kernel<PA_BF16, 64><<<grid, block, 0, stream>>>(a);
   else if (kv_dtype == PA_F32 && a.head_dim == 128) decode_valu_kernel<PA_F32, 128><<<grid, block, 0, stream>>>(a);
   else if (kv_dtype == PA_F32 && a.head_dim == 64) decode_valu_kernel<PA_F32, 64><<<grid, block, 0, stream>>>(a);
+  else if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128)
+    decode_valu_kernel<PA_FP8_E4M3, 128><<<grid, block, 0, stream>>>(a);
+  else if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64)
+    decode_valu_kernel<PA_FP8_E4M3, 64><<<grid, block, 0, stream>>>(a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -12,7 +12,8 @@ namespace {
 constexpr int kTileTokens = 16;
 constexpr int kMaxGridYZ = 65535;
 
-int esize_of(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 0; }
+int esize_of(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : dtype == PA_FP8_E4M3 ? 1 : 0; }
+bool finite_nonzero(float x) { return x == x && x != 0.f && x - x == 0.f; }
 
 int log2_pow2(int v) {
   if (v <= 0 || (v & (v - 1))) return -1;
@@ -151,10 +152,27 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
                            int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_context_len, int32_t q_dtype, int32_t kv_dtype, int32_t partition_size,
                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_dtype == PA_FP8_E4M3) return PA_ERR_DTYPE;  // a quantised cache needs its scales
+  return paged_attention_decode_scaled(out, query, key_cache, value_cache, block_tables, context_lens, scale, 1.f,
+                                       1.f, block_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                       max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size,
+                                       workspace, workspace_bytes, stream);
+}
+
+int paged_attention_decode_scaled(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                  float k_scale, float v_scale, int32_t block_size, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+                                  int32_t kv_dtype, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
                               kv_dtype, partition_size);
   if (plan.status != PA_OK) return plan.status;
-  if (q_dtype != kv_dtype || esize_of(q_dtype) == 0) return PA_ERR_DTYPE;
+  const bool pair_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) || (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
+                       (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
+  if (!pair_ok) return PA_ERR_DTYPE;
+  if (!finite_nonzero(k_scale) || !finite_nonzero(v_scale)) return PA_ERR_SHAPE;
   if (num_blocks <= 0 || num_blocks > INT32_MAX || max_blocks_per_seq <= 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return PA_ERR_SHAPE;
@@ -177,7 +195,8 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
   a.context_lens = context_lens;
   a.ws_o = plan.split ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = plan.split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -195,7 +214,7 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (a.group > 1 && pa::gqa_mfma_supported(kv_dtype, head_dim, a.group))
-    err = pa::launch_decode_gqa_mfma(a, st);
+    err = pa::launch_decode_gqa_mfma(a, kv_dtype, st);
   else
     err = pa::launch_decode_valu(a, kv_dtype, st);
   if (err != hipSuccess) return PA_ERR_HIP;
@@ -219,6 +238,28 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
   if (num_tokens > INT32_MAX) return PA_ERR_UNSUPPORTED;
   return pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens, row_bytes,
                                       block_size, num_blocks, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int reshape_and_cache_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, int32_t src_dtype, float k_scale, float v_scale,
+                          void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (src_dtype != PA_F32 && src_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (!finite_nonzero(k_scale) || !finite_nonzero(v_scale)) return PA_ERR_SHAPE;
+  const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+  if (row_elems % 16 != 0) return PA_ERR_UNSUPPORTED;  // rows are written as whole 16-byte words
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned4(slot_mapping))
+    return PA_ERR_ALIGN;
+  return pa::launch_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, num_tokens, row_elems,
+                                          block_size, num_blocks, src_dtype, k_scale, v_scale,
+                                          static_cast<hipStream_t>(stream)) == hipSuccess
              ? PA_OK
              : PA_ERR_HIP;
 }

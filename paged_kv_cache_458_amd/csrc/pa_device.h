@@ -45,6 +45,13 @@ __device__ __forceinline__ U4 load_stream(const char* p) {
   return U4{v.x, v.y, v.z, v.w};
 }
 
+// Four OCP E4M3 codes (a word, first code in the lowest byte) -> two words of two bf16 each, exactly: every
+// E4M3 value is a bf16 value (gfx950 v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+}
+
 // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

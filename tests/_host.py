@@ -10,12 +10,15 @@ from workloads import custom_structure, materialize
 
 
 def to_host(t: torch.Tensor) -> np.ndarray:
-    """float32 tensors become float32 arrays; bfloat16 tensors become uint16 arrays of their bit patterns."""
+    """float32 tensors become float32 arrays; bfloat16 tensors uint16 arrays of their bit patterns; float8_e4m3fn
+    tensors uint8 arrays of their codes."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.float32:
         return t.numpy().copy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().copy()
     if t.dtype == torch.int32:
         return t.numpy().copy()
     raise TypeError(t.dtype)

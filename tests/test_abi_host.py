@@ -27,7 +27,8 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"paged_attention_decode", "reshape_and_cache", "copy_blocks", "paged_gather",
             "paged_attention_workspace_bytes", "paged_attention_partition_size", "pa_strerror",
-            "pa_abi_version", "pa_stream_read", "pa_stream_copy", "pa_bm_create", "pa_bm_append_slots"} <= set(names)
+            "pa_abi_version", "pa_stream_read", "pa_stream_copy", "pa_bm_create", "pa_bm_append_slots",
+            "paged_attention_decode_scaled", "reshape_and_cache_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert lib.pa_abi_version() == pa.ABI_VERSION
@@ -74,6 +75,56 @@ def decode_call(**over):
 ])
 def test_decode_rejects_before_launch(over, status):
     assert decode_call(**over) == status
+
+
+def scaled_call(**over):
+    args = dict(out=FAKE, query=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE, context_lens=FAKE,
+                scale=0.1, k_scale=0.5, v_scale=0.25, block_size=16, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, num_blocks=100, max_blocks_per_seq=8, max_context_len=128, q_dtype=pa.PA_BF16,
+                kv_dtype=pa.PA_FP8_E4M3, partition_size=0, workspace=None, workspace_bytes=0, stream=None)
+    args.update(over)
+    return pa.load_library().paged_attention_decode_scaled(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q_dtype=pa.PA_F32), PA_ERR_DTYPE),  # an E4M3 cache takes a bf16 query
+    (dict(q_dtype=pa.PA_FP8_E4M3), PA_ERR_DTYPE),
+    (dict(q_dtype=pa.PA_F32, kv_dtype=pa.PA_BF16), PA_ERR_DTYPE),
+    (dict(k_scale=0.0), PA_ERR_SHAPE),
+    (dict(v_scale=float("nan")), PA_ERR_SHAPE),
+    (dict(k_scale=float("inf")), PA_ERR_SHAPE),
+    (dict(head_dim=96), PA_ERR_UNSUPPORTED),
+    (dict(partition_size=32), PA_ERR_WORKSPACE),
+    (dict(out=None), PA_ERR_NULL),
+])
+def test_scaled_decode_rejects_before_launch(over, status):
+    assert scaled_call(**over) == status
+
+
+def test_unscaled_decode_refuses_an_fp8_cache():
+    assert decode_call(kv_dtype=pa.PA_FP8_E4M3) == PA_ERR_DTYPE
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(src_dtype=pa.PA_FP8_E4M3), PA_ERR_DTYPE),
+    (dict(src_dtype=7), PA_ERR_DTYPE),
+    (dict(k_scale=0.0), PA_ERR_SHAPE),
+    (dict(v_scale=float("-inf")), PA_ERR_SHAPE),
+    (dict(num_kv_heads=1, head_dim=8), PA_ERR_UNSUPPORTED),
+    (dict(num_tokens=-1), PA_ERR_SHAPE),
+    (dict(value_cache=None), PA_ERR_NULL),
+    (dict(key_cache=FAKE + 8), PA_ERR_ALIGN),
+])
+def test_fp8_cache_write_rejects(over, status):
+    args = dict(key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE, slot_mapping=FAKE, num_tokens=4,
+                num_kv_heads=2, head_dim=64, block_size=16, num_blocks=10, src_dtype=pa.PA_BF16, k_scale=0.1,
+                v_scale=0.1, stream=None)
+    args.update(over)
+    assert pa.load_library().reshape_and_cache_fp8(*args.values()) == status
+    if over.get("num_tokens", 4) > 0:
+        args.update(num_tokens=0, key=None, value=None, key_cache=None, value_cache=None, slot_mapping=None)
+        expect_noop = status in (PA_ERR_NULL, PA_ERR_ALIGN)
+        assert (pa.load_library().reshape_and_cache_fp8(*args.values()) == 0) == expect_noop
 
 
 def test_decode_with_no_sequences_is_a_no_op():

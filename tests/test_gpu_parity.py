@@ -1,8 +1,9 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same seeded inputs.
 
-Bar: bit-exact for reshape_and_cache, copy_blocks and the block-table gather (whole pools compared byte for
-byte, so untouched blocks, NaN-poisoned free slots and tails are covered); attention within 1e-5 absolute for
-fp32 and within 2e-3 absolute + 1e-2 relative for bf16 K/V (fp32 accumulation), element by element.
+Bar: bit-exact for reshape_and_cache (also its quantising FP8 form), copy_blocks and the block-table gather
+(whole pools compared byte for byte, so untouched blocks, NaN-poisoned free slots and tails are covered);
+attention within 1e-5 absolute for fp32 and within 2e-3 absolute + 1e-2 relative for bf16 or E4M3 K/V under a
+bf16 query (fp32 accumulation), element by element.
 """
 
 from __future__ import annotations
@@ -35,7 +36,7 @@ def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: s
     err = np.abs(gpu.astype(np.float64) - ref)
     if dtype == "f32":
         bad = err > 1e-5
-    else:
+    else:  # bf16, or fp8 (E4M3 caches, bf16 query): both multiply bf16 operands with fp32 accumulation
         bad = err > 2e-3 + 1e-2 * np.abs(ref)
     assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.3e}"
     return float(err.max())
@@ -50,14 +51,31 @@ def decode(st, t, tables, partition_size, context_lens=None, max_context_len=Non
     cl = st.context_lens if context_lens is None else context_lens
     pa.paged_attention_decode(out, t["query"], t["key_cache"], t["value_cache"], dev_i32(tables), dev_i32(cl),
                               st.scale, st.block_size, partition_size=partition_size,
-                              max_context_len=st.max_context_len if max_context_len is None else max_context_len)
+                              max_context_len=st.max_context_len if max_context_len is None else max_context_len,
+                              k_scale=st.k_scale, v_scale=st.v_scale)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
 def oracle_decode(st, h, tables, context_lens=None, rows=None):
     cl = st.context_lens if context_lens is None else context_lens
-    return oracle.decode(h["query"], h["key_cache"], h["value_cache"], tables, cl, st.scale, rows=rows)
+    return oracle.decode(h["query"], h["key_cache"], h["value_cache"], tables, cl, st.scale, rows=rows,
+                         k_scale=st.k_scale, v_scale=st.v_scale)
+
+
+def step_writes(st, t, h):
+    """The step's cache update on the device pools and on their host copies: copy-on-write pairs, then the
+    new token's K/V (quantised into an E4M3 cache)."""
+    if len(st.copy_pairs):
+        pa.copy_blocks(t["key_cache"], t["value_cache"], dev_i32(st.copy_pairs))
+        oracle.copy_blocks(h["key_cache"], h["value_cache"], st.copy_pairs)
+    pa.reshape_and_cache(t["new_key"], t["new_value"], t["key_cache"], t["value_cache"], dev_i32(st.slot_mapping),
+                         k_scale=st.k_scale, v_scale=st.v_scale)
+    if st.dtype == "fp8":
+        oracle.reshape_and_cache_e4m3(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"],
+                                      st.slot_mapping, st.k_scale, st.v_scale)
+    else:
+        oracle.reshape_and_cache(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"], st.slot_mapping)
 
 
 # --------------------------------------------------------------------------------------------------------
@@ -74,6 +92,11 @@ SMALL = [
     (207, [90, 33, 257, 16], 8, 2, 64, 32, "bf16"),
     (208, [600, 129, 64, 3], 16, 1, 128, 128, "bf16"),
     (209, [100, 45, 1, 65], 6, 3, 64, 64, "f32"),
+    (210, [5, 17, 300, 64, 1030], 8, 8, 128, 16, "fp8"),
+    (211, [100, 1, 65, 513], 4, 4, 64, 16, "fp8"),
+    (212, [700, 1200, 45, 1], 32, 8, 128, 16, "fp8"),
+    (213, [90, 33, 257, 16], 8, 2, 64, 32, "fp8"),
+    (214, [2050, 999, 513, 300], 64, 8, 128, 256, "fp8"),
 ]
 
 
@@ -90,21 +113,54 @@ def test_small_attention_parity(case):
         assert_attention_close(gpu, ref, dt, f"partition {part}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
 def test_small_cache_ops_bit_exact(dt):
     st = custom_structure("ops", 301, [65, 77, 96, 100, 130, 81], 8, 2, 64, 16, dt, shared_prefix_blocks=4,
                           cow_seqs=3, pool_factor=1.5)
     t = materialize(st, DEV, include_new_token=False)
     h = {k: to_host(v) for k, v in t.items()}
-    pa.copy_blocks(t["key_cache"], t["value_cache"], dev_i32(st.copy_pairs))
-    pa.reshape_and_cache(t["new_key"], t["new_value"], t["key_cache"], t["value_cache"], dev_i32(st.slot_mapping))
+    step_writes(st, t, h)
     torch.cuda.synchronize()
-    oracle.copy_blocks(h["key_cache"], h["value_cache"], st.copy_pairs)
-    oracle.reshape_and_cache(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"], st.slot_mapping)
     np.testing.assert_array_equal(to_host(t["key_cache"]).view(np.uint8), h["key_cache"].view(np.uint8))
     np.testing.assert_array_equal(to_host(t["value_cache"]).view(np.uint8), h["value_cache"].view(np.uint8))
     gpu = decode(st, t, st.block_tables, -1)
     assert_attention_close(gpu, oracle_decode(st, h, st.block_tables), dt)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_fp8_quantiser_special_values_bit_exact(src):
+    # every E4M3 code value, the midpoints between neighbours (ties to even), values past the largest finite
+    # code (saturation), NaN, infinities, signed zeros, tiny values, then random data, at several scales
+    vals = oracle.e4m3_values()
+    fin = vals[~np.isnan(vals)]
+    pos = np.sort(vals[(vals >= 0) & ~np.isnan(vals)])
+    special = np.concatenate([fin, (pos[:-1] + pos[1:]) / 2, -(pos[:-1] + pos[1:]) / 2,
+                              [464.0, 479.0, 480.0, 1e6, -1e6, np.inf, -np.inf, np.nan, -np.nan, 0.0, -0.0, 1e-30,
+                               -1e-30, 2.0 ** -10, 3 * 2.0 ** -11]])
+    rng = np.random.default_rng(501)
+    x = np.concatenate([special, rng.standard_normal(4096) * rng.choice([1e-3, 1.0, 100.0, 1e4], 4096)])
+    x = x.astype(np.float32)
+    hkv, d = 2, 32
+    x = np.concatenate([x, np.zeros((-x.size) % (hkv * d), np.float32)]).reshape(-1, hkv, d)
+    n = x.shape[0]
+    src_t = torch.from_numpy(x)
+    if src == "bf16":
+        src_t = src_t.to(torch.bfloat16)
+    host_src = to_host(src_t)
+    nb, bs = -(-n // 16) + 1, 16
+    slots = np.random.default_rng(502).permutation(nb * bs)[:n].astype(np.int32)
+    for ks, vs in ((1.0, 1.0), (0.0125, 3.0), (2.0 ** -6, 0.3)):
+        kc = torch.full((nb, bs, hkv, d), float("nan"), device=DEV).to(torch.float8_e4m3fn)
+        vc = kc.clone()
+        k_dev = src_t.to(DEV)
+        v_dev = (-src_t).to(DEV)
+        pa.reshape_and_cache(k_dev, v_dev, kc, vc, dev_i32(slots), k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+        hk = np.full((nb, bs, hkv, d), 0x7F, np.uint8)
+        hv = hk.copy()
+        oracle.reshape_and_cache_e4m3(hk, hv, host_src, to_host(-src_t), slots, ks, vs)
+        np.testing.assert_array_equal(to_host(kc), hk, err_msg=f"k_scale {ks}")
+        np.testing.assert_array_equal(to_host(vc), hv, err_msg=f"v_scale {vs}")
 
 
 def test_reshape_skips_padding_and_out_of_pool_slots():
@@ -123,13 +179,13 @@ def test_reshape_skips_padding_and_out_of_pool_slots():
     np.testing.assert_array_equal(to_host(t["value_cache"]), before_v)
 
 
-@pytest.mark.parametrize("bs,dt", [(16, "bf16"), (256, "bf16"), (32, "f32")])
+@pytest.mark.parametrize("bs,dt", [(16, "bf16"), (256, "bf16"), (32, "f32"), (16, "fp8")])
 def test_gather_bit_exact(bs, dt):
     st = custom_structure("gather", 303, [1, 15, 16, 17, 300, 513], 8, 4, 128, bs, dt)
     t = materialize(st, DEV)
     mcl = st.max_context_len
-    ok = torch.full((st.num_seqs, mcl, st.num_kv_heads, st.head_dim), float("nan"), dtype=t["key_cache"].dtype,
-                    device=DEV)
+    ok = torch.full((st.num_seqs, mcl, st.num_kv_heads, st.head_dim), float("nan"),
+                    device=DEV).to(t["key_cache"].dtype)
     ov = ok.clone()
     pa.paged_gather(ok, ov, t["key_cache"], t["value_cache"], dev_i32(st.block_tables_pre), dev_i32(st.context_lens))
     torch.cuda.synchronize()
@@ -141,7 +197,10 @@ def test_gather_bit_exact(bs, dt):
     for s, L in enumerate(st.context_lens):
         np.testing.assert_array_equal(gk[s, :L].view(np.uint8), rk[r:r + L].view(np.uint8))
         np.testing.assert_array_equal(gv[s, :L].view(np.uint8), rv[r:r + L].view(np.uint8))
-        assert np.isnan(f64(gk[s, L:])).all()  # rows past the length untouched
+        if dt == "fp8":
+            assert (gk[s, L:] == 0x7F).all()  # rows past the length untouched (the NaN code)
+        else:
+            assert np.isnan(f64(gk[s, L:])).all()  # rows past the length untouched
         r += L
 
 
@@ -167,11 +226,14 @@ def test_permutation_and_determinism_bit_identical():
 
 
 def test_single_token_is_exact_value_row():
-    for dt, hq, hkv in (("f32", 4, 4), ("bf16", 32, 32), ("bf16", 32, 8), ("bf16", 64, 8)):
+    for dt, hq, hkv in (("f32", 4, 4), ("bf16", 32, 32), ("bf16", 32, 8), ("bf16", 64, 8), ("fp8", 32, 32),
+                        ("fp8", 32, 8)):
         st = custom_structure("one", 411, [1, 1, 1], hq, hkv, 128, 16, dt)
         t = materialize(st, DEV)
         gpu = decode(st, t, st.block_tables_pre, -1)
-        v = f64(to_host(t["value_cache"]))
+        hv = to_host(t["value_cache"])
+        # with a power-of-two v_scale the output row is code value x v_scale exactly
+        v = oracle.e4m3_values()[hv] * st.v_scale if dt == "fp8" else f64(hv)
         G = hq // hkv
         for s in range(3):
             b = st.block_tables_pre[s, 0]
@@ -222,13 +284,8 @@ def test_full_workload_step(name):
     st = build_structure(name)
     t = materialize(st, DEV, include_new_token=False)
     h = {k: to_host(v) for k, v in t.items()}
-    if len(st.copy_pairs):
-        pa.copy_blocks(t["key_cache"], t["value_cache"], dev_i32(st.copy_pairs))
-    pa.reshape_and_cache(t["new_key"], t["new_value"], t["key_cache"], t["value_cache"], dev_i32(st.slot_mapping))
+    step_writes(st, t, h)
     gpu = decode(st, t, st.block_tables, st.partition_size)
-    if len(st.copy_pairs):
-        oracle.copy_blocks(h["key_cache"], h["value_cache"], st.copy_pairs)
-    oracle.reshape_and_cache(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"], st.slot_mapping)
     gk, gv = to_host(t["key_cache"]), to_host(t["value_cache"])
     assert np.array_equal(gk.view(np.uint8), h["key_cache"].view(np.uint8)), "key pool differs after the step"
     assert np.array_equal(gv.view(np.uint8), h["value_cache"].view(np.uint8)), "value pool differs after the step"

@@ -7,6 +7,11 @@ of shape [num_blocks, block_size, num_kv_heads, head_dim], with a per-sequence t
 to a physical block id (page 3 section 2.2 gives the example logical 0 -> physical 7). A sequence of length L
 uses ceil(L / block_size) blocks (page 2 section 4.2, the block-per-sequence loop of its pseudocode).
 
+With dtype "fp8" the caches hold OCP FP8 E4M3 codes (torch.float8_e4m3fn) read as code value x k_scale
+(keys) and x v_scale (values); the query and the step's new rows stay bfloat16. The codes are torch's
+float8 rounding of N(0, 1) / scale draws (clamped to the format's +-448), the scales 1/64 (a power of two, so
+that N(0, 1) data spans most of the E4M3 range without saturating).
+
 Every slot that holds no live token -- free blocks, the unused tail of a sequence's last block, a dedicated
 poison block that pads the tables -- is filled with NaN, so a kernel that reads a slot it should not read
 produces a NaN that a parity test sees.
@@ -16,14 +21,17 @@ Nothing in here computes attention, writes a cache slot or copies a block.
 
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass, field
 
 import numpy as np
 
-CONFIG_NAMES = ("tiny_fp32", "llama2_7b", "mixed_len", "mistral_gqa_prefix", "llama2_70b_gqa")
+CONFIG_NAMES = ("tiny_fp32", "llama2_7b", "mixed_len", "mistral_gqa_prefix", "llama2_70b_gqa", "llama2_7b_fp8",
+                "llama2_70b_gqa_fp8")
 
-_ESIZE = {"f32": 4, "bf16": 2}
+_ESIZE = {"f32": 4, "bf16": 2, "fp8": 1}
+FP8_KV_SCALE = 1.0 / 64
 
 
 @dataclass
@@ -37,7 +45,7 @@ class DecodeStructure:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    dtype: str  # dtype of query, key cache and value cache: "f32" or "bf16"; the output is always fp32
+    dtype: str  # "f32" or "bf16" (query and caches), or "fp8" (bf16 query, E4M3 caches); the output is fp32
     scale: float
     max_context_len: int
     max_blocks_per_seq: int
@@ -50,10 +58,18 @@ class DecodeStructure:
     copy_pairs: np.ndarray  # int32 [num_pairs, 2] = (src, dst)
     partition_size: int  # 0 = single pass, -1 = library default, > 0 = split-context partition in tokens
     notes: dict = field(default_factory=dict)
+    k_scale: float = 1.0  # dequantisation scales of an E4M3 cache (1.0 otherwise)
+    v_scale: float = 1.0
 
     @property
     def esize(self) -> int:
+        """Bytes per cached K/V element."""
         return _ESIZE[self.dtype]
+
+    @property
+    def q_esize(self) -> int:
+        """Bytes per query element (and per element of the step's new K/V rows)."""
+        return 2 if self.dtype == "fp8" else _ESIZE[self.dtype]
 
     @property
     def group_size(self) -> int:
@@ -154,8 +170,11 @@ def custom_structure(
         if L > 0:
             slots[s] = tables[s, (L - 1) // bs] * bs + (L - 1) % bs
 
+    if dtype not in _ESIZE:
+        raise ValueError(f"dtype must be one of {tuple(_ESIZE)}")
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
+    kv_scale = FP8_KV_SCALE if dtype == "fp8" else 1.0
     return DecodeStructure(
         name=name, seed=seed, num_seqs=num_seqs, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
         head_dim=head_dim, block_size=bs, dtype=dtype, scale=float(scale), max_context_len=max_len,
@@ -163,15 +182,21 @@ def custom_structure(
         context_lens=lens.astype(np.int32), block_tables=tables.astype(np.int32),
         block_tables_pre=tables_pre.astype(np.int32), slot_mapping=slots.astype(np.int32),
         copy_pairs=pairs.astype(np.int32), partition_size=partition_size,
-        notes={"need_blocks": need, "shared_prefix_blocks": shared_prefix_blocks},
+        notes={"need_blocks": need, "shared_prefix_blocks": shared_prefix_blocks}, k_scale=kv_scale,
+        v_scale=kv_scale,
     )
 
 
 def build_structure(name: str, seed: int | None = None) -> DecodeStructure:
-    """The five synthetic decode workloads at their full sizes (seeds 1..5 by default)."""
+    """The synthetic decode workloads at their full sizes (seeds 1..7 by default). A name ending in "_fp8" is
+    the structure of the workload without the suffix (same seed, same lengths and tables) over E4M3 caches."""
     if name not in CONFIG_NAMES:
         raise KeyError(f"unknown workload {name!r}; known: {CONFIG_NAMES}")
     idx = CONFIG_NAMES.index(name)
+    if name.endswith("_fp8"):
+        base = build_structure(name[: -len("_fp8")], seed)
+        return dataclasses.replace(base, name=name, seed=idx + 1 if seed is None else seed, dtype="fp8",
+                                   k_scale=FP8_KV_SCALE, v_scale=FP8_KV_SCALE)
     seed = idx + 1 if seed is None else seed
     rng = np.random.default_rng(seed)
     if name == "tiny_fp32":
@@ -226,7 +251,8 @@ def materialize(st: DecodeStructure, device="cpu", include_new_token: bool = Tru
 
     Returns a dict with ``query`` [B, Hq, D], ``key_cache`` / ``value_cache`` [NB, bs, Hkv, D], ``new_key`` /
     ``new_value`` [B, Hkv, D] (the step's new token), all in the structure's dtype, N(0, 1) then rounded to the
-    dtype, and NaN in every slot that is not live. With ``include_new_token`` True the position-(L-1) slots
+    dtype, and NaN in every slot that is not live. For "fp8" the query and new rows are bfloat16 and the caches
+    float8_e4m3fn codes of N(0, 1) / scale (NaN code 0x7F in the slots that are not live). With ``include_new_token`` True the position-(L-1) slots
     already hold random values (attention-only use, read through ``block_tables_pre``); with False they hold
     NaN and the caller writes ``new_key``/``new_value`` there and copies the copy-on-write pairs before
     attending through ``block_tables``.
@@ -234,6 +260,7 @@ def materialize(st: DecodeStructure, device="cpu", include_new_token: bool = Tru
     import torch
 
     dt = torch.float32 if st.dtype == "f32" else torch.bfloat16
+    fp8 = st.dtype == "fp8"
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
     gen.manual_seed(int(st.seed))
@@ -249,13 +276,17 @@ def materialize(st: DecodeStructure, device="cpu", include_new_token: bool = Tru
     mask = torch.from_numpy(live_slot_mask(st, include_new_token)).to(dev)
     nan = float("nan")
     caches = []
-    for _ in range(2):
-        cache = torch.empty((NB, bs, Hkv, D), dtype=dt, device=dev)
+    for scale in (st.k_scale, st.v_scale):
+        cache = torch.empty((NB, bs, Hkv, D), dtype=torch.float8_e4m3fn if fp8 else dt, device=dev)
         for b0 in range(0, NB, chunk_blocks):
             b1 = min(NB, b0 + chunk_blocks)
-            part = draw((b1 - b0, bs, Hkv, D))
+            if fp8:
+                part = torch.randn((b1 - b0, bs, Hkv, D), generator=gen, device=dev, dtype=torch.float32)
+                part = (part / scale).clamp_(-448.0, 448.0)
+            else:
+                part = draw((b1 - b0, bs, Hkv, D))
             part[~mask[b0:b1]] = nan
-            cache[b0:b1] = part
+            cache[b0:b1] = part.to(cache.dtype)
         caches.append(cache)
     return {"query": query, "key_cache": caches[0], "value_cache": caches[1], "new_key": new_key,
             "new_value": new_value}
@@ -267,7 +298,7 @@ def algorithmic_bytes(st: DecodeStructure) -> dict:
     lens = st.context_lens.astype(np.int64)
     row = st.num_kv_heads * st.head_dim * st.esize
     kv = int(lens.sum()) * row * 2
-    q = st.num_seqs * st.num_q_heads * st.head_dim * st.esize
+    q = st.num_seqs * st.num_q_heads * st.head_dim * st.q_esize
     out = st.num_seqs * st.num_q_heads * st.head_dim * 4
     tbl = int(st.blocks_per_seq().sum()) * 4 + 4 * st.num_seqs
     shared = st.notes.get("shared_prefix_blocks", 0)
