@@ -17,7 +17,6 @@ entry for the attention call (HIP events on the stream it runs on) and the CPU o
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -35,9 +34,14 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# the sources that define or launch the attention kernels whose HBM traffic is counted (partition kernels, the
+# log-sum-exp reduce, the launch plan); a change to any of them makes stored counter readings stale
+ATTENTION_SOURCES = ("decode_valu.hip", "decode_gqa_mfma.hip", "pa_device.h", "pa_kernels.h", "pa_abi.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_458_amd", "csrc", "*"))):
+    for p in sorted(os.path.join(ROOT, "paged_kv_cache_458_amd", "csrc", f) for f in ATTENTION_SOURCES):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode() + f.read())
     return h.hexdigest()[:16]
