@@ -89,7 +89,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *   block_tables   int32 [num_seqs][max_blocks_per_seq]; only entries j < ceil(L / block_size) are read
  *   context_lens   int32 [num_seqs]; 0 <= L <= max_context_len (longer lengths are clamped)
  *   scale          multiplies q . k before the softmax (1/sqrt(head_dim) in the usual models)
- *   block_size     tokens per block: 16, 32, 64, 128 or 256
+ *   block_size     tokens per block: 8, 16, 32, 64, 128 or 256 (page 1 section 5 suggests 8 for short
+ *                  sequences; 8 needs head rows of at least 128 bytes, so not E4M3 at head_dim 64)
  *   head_dim       64 or 128
  *   num_q_heads    a multiple of num_kv_heads
  *   max_context_len  upper bound of context_lens, <= max_blocks_per_seq * block_size

@@ -144,15 +144,17 @@ __global__ __launch_bounds__(kThreads) void paged_gather_kernel(char* __restrict
                                                                 int32_t bs_log2, int64_t num_blocks,
                                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
                                                                 int64_t row_bytes) {
+  // one workgroup per tile of min(16, block_size) positions: a tile never leaves its block
+  const int tile = min(kTile, 1 << bs_log2);
   const int s = blockIdx.y;
-  const int t = blockIdx.x * kTile;
+  const int t = blockIdx.x * tile;
   const int L = min(max(context_lens[s], 0), max_context_len);
   if (t >= L) return;
   bool bad = false;
   const int64_t base = tile_slot_bytes(block_tables + (int64_t)s * max_blocks_per_seq, t, bs_log2, num_blocks,
                                        row_bytes, bad);
   if (bad) return;
-  const int rows = min(kTile, L - t);
+  const int rows = min(tile, L - t);
   const int64_t row_u4 = row_bytes / 16;
   const int64_t obase = ((int64_t)s * max_context_len + t) * row_bytes;
   for (int64_t i = threadIdx.x; i < rows * row_u4; i += kThreads) {
@@ -206,7 +208,8 @@ hipError_t launch_paged_gather(void* out_key, void* out_value, const void* key_c
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t bs_log2, int64_t num_blocks, int32_t max_blocks_per_seq,
                                int32_t max_context_len, int64_t row_bytes, hipStream_t stream) {
-  const dim3 grid((max_context_len + kTile - 1) / kTile, num_seqs);
+  const int tile = min(kTile, 1 << bs_log2);
+  const dim3 grid((max_context_len + tile - 1) / tile, num_seqs);
   paged_gather_kernel<<<grid, dim3(kThreads), 0, stream>>>(
       static_cast<char*>(out_key), static_cast<char*>(out_value), static_cast<const char*>(key_cache),
       static_cast<const char*>(value_cache), block_tables, context_lens, bs_log2, num_blocks, max_blocks_per_seq,

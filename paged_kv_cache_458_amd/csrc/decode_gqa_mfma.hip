@@ -132,24 +132,36 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
   const int ntiles = (u1 - u0 + kTileTok - 1) / kTileTok;
-  const int last_half = ntiles > 0 ? ((u1 - 1) & ~(kTile - 1)) : u0;  // start of the last live 16-token half
+  const int last8 = ntiles > 0 ? ((u1 - 1) & ~(kTile / 2 - 1)) : u0;  // start of the last live 8-token group
+  // a load of at most 8 rows stays inside one 8-row quarter; 16-row loads (E4M3 at head_dim 64) take a whole
+  // half through the even quarter's descriptor (the host refuses 8-slot blocks for them)
+  constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
 
   U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
   auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
     const int t = u0 + min(tile, ntiles - 1) * kTileTok;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      // the table is read at a live half; rows past the range end read as zero without touching memory
-      const int th = min(t + h2 * kTile, last_half);
-      const int64_t base = tile_slot_bytes(table, th, a.bs_log2, a.num_blocks, row_bytes, bad);
-      const int rows = min(kTile, u1 - (u0 + tile * kTileTok + h2 * kTile));
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // 8-row quarter q4 of the tile (rows 8 q4 .. 8 q4 + 7): the table is read at a live position, and the
+      // quarter's rows past the range end read as zero without touching memory. Quarters of one 16-row half
+      // share a block unless blocks hold 8 slots.
+      const int h2 = q4 >> 1;
+      const int64_t base = (q4 & 1) == 0 || a.bs_log2 == 3
+                               ? tile_slot_bytes(table, min(t + q4 * (kTile / 2), last8), a.bs_log2, a.num_blocks,
+                                                 row_bytes, bad)
+                               : tile_slot_bytes(table, min(t + h2 * kTile, last8), a.bs_log2, a.num_blocks,
+                                                 row_bytes, bad) + (kTile / 2) * row_bytes;
+      const int rows = min(kQuarterRows, u1 - (u0 + tile * kTileTok + q4 * (kTile / 2)));
       const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
+      const uint32_t qoff = (uint32_t)((q4 & 1) * (kTile / 2) * row_bytes);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        kb[h2][i] = load16<kPolStream>(kr, off[i]);
-        vb[h2][i] = load16<kPolStream>(vr, off[i]);
+        if ((kRows * i < kTile / 2) == ((q4 & 1) == 0)) {
+          kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
+          vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
+        }
       }
     }
   };

@@ -159,18 +159,35 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
 
   U4 kb[kStages][NL], vb[kStages][NL];
   // The loads stay unconditional, so the wait counters of the two register sets never merge across a branch:
-  // the descriptor covers only the tile's rows below the partition end, and rows past it (a tile index past
-  // the end: all of them) read as zero without touching memory.
+  // each 8-row half of the tile has a descriptor that covers only its rows below the partition end, and rows
+  // past it (a tile index past the end: all of them) read as zero without touching memory. The halves lie in
+  // one block unless blocks hold 8 slots; a wave-wide load of at most 8 rows never straddles them. Shapes with
+  // 16 rows per load (E4M3 at head_dim 64) take the whole tile through the first descriptor: the host refuses
+  // 8-slot blocks for them.
+  constexpr bool kHalves = S::kRows <= kTile / 2;
+  const int last8 = (t1 - 1) & ~(kTile / 2 - 1);  // start of the last live 8-row group
   auto issue = [&](U4* kq, U4* vq, int tile) {
     const int t = t0 + min(tile, ntiles - 1) * kTile;
-    const int64_t base = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
-    const uint32_t live = tile < ntiles ? (uint32_t)min(kTile, t1 - t) * (uint32_t)row_bytes : 0u;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
+    const int64_t base0 = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
+    const int64_t base1 = a.bs_log2 == 3
+                              ? tile_slot_bytes(table, min(t + kTile / 2, last8), a.bs_log2, a.num_blocks,
+                                                row_bytes, bad)
+                              : base0 + (kTile / 2) * row_bytes;
+    const int rows = tile < ntiles ? min(kTile, t1 - t) : 0;
+    const uint32_t live0 = (uint32_t)(kHalves ? min(rows, kTile / 2) : rows) * (uint32_t)row_bytes;
+    const uint32_t live1 = (uint32_t)max(rows - kTile / 2, 0) * (uint32_t)row_bytes;
+    const __amdgpu_buffer_rsrc_t kr0 = make_rsrc(kbase + base0, live0), kr1 = make_rsrc(kbase + base1, live1);
+    const __amdgpu_buffer_rsrc_t vr0 = make_rsrc(vbase + base0, live0), vr1 = make_rsrc(vbase + base1, live1);
+    const uint32_t half_off = (uint32_t)((kTile / 2) * row_bytes);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      kq[i] = load16<kPolStream>(kr, lane_off[i]);
-      vq[i] = load16<kPolStream>(vr, lane_off[i]);
+      if (i * S::kRows < kTile / 2) {
+        kq[i] = load16<kPolStream>(kr0, lane_off[i]);
+        vq[i] = load16<kPolStream>(vr0, lane_off[i]);
+      } else {
+        kq[i] = load16<kPolStream>(kr1, lane_off[i] - half_off);
+        vq[i] = load16<kPolStream>(vr1, lane_off[i] - half_off);
+      }
     }
   };
   auto consume = [&](const U4* kq, const U4* vq, int tile) {

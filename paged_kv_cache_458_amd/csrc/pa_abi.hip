@@ -22,7 +22,7 @@ int log2_pow2(int v) {
   return k;
 }
 
-bool supported_block_size(int bs) { return bs >= 16 && bs <= 256 && log2_pow2(bs) >= 0; }
+bool supported_block_size(int bs) { return bs >= 8 && bs <= 256 && log2_pow2(bs) >= 0; }
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -76,6 +76,12 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
   const int64_t tile_bytes = (int64_t)kTileTokens * num_kv_heads * head_dim * esize_of(kv_dtype);
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || num_seqs > kMaxGridYZ ||
       tile_bytes > INT32_MAX) {
+    p.status = PA_ERR_UNSUPPORTED;
+    return p;
+  }
+  // a wave-wide load covers 64 x 16 bytes of whole head rows and must stay inside one 8-slot block: E4M3 rows
+  // of 64 dims would put 16 slots in one load
+  if (block_size == 8 && head_dim * esize_of(kv_dtype) < 128) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }

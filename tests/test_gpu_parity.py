@@ -97,6 +97,12 @@ SMALL = [
     (212, [700, 1200, 45, 1], 32, 8, 128, 16, "fp8"),
     (213, [90, 33, 257, 16], 8, 2, 64, 32, "fp8"),
     (214, [2050, 999, 513, 300], 64, 8, 128, 256, "fp8"),
+    # 8-slot blocks (page 1 section 5): a 16-token tile spans two blocks
+    (215, [5, 17, 100, 64, 300, 8], 8, 8, 128, 8, "bf16"),
+    (216, [90, 33, 257, 16, 1], 16, 4, 64, 8, "bf16"),
+    (217, [700, 45, 513, 9], 32, 8, 128, 8, "fp8"),
+    (218, [33, 64, 7, 200], 4, 4, 64, 8, "f32"),
+    (219, [1100, 24, 520], 64, 8, 128, 8, "bf16"),
 ]
 
 
@@ -113,9 +119,10 @@ def test_small_attention_parity(case):
         assert_attention_close(gpu, ref, dt, f"partition {part}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
-def test_small_cache_ops_bit_exact(dt):
-    st = custom_structure("ops", 301, [65, 77, 96, 100, 130, 81], 8, 2, 64, 16, dt, shared_prefix_blocks=4,
+@pytest.mark.parametrize("dt,bs", [("f32", 16), ("bf16", 16), ("fp8", 16), ("bf16", 8), ("fp8", 8)])
+def test_small_cache_ops_bit_exact(dt, bs):
+    d = 128 if (dt, bs) == ("fp8", 8) else 64  # E4M3 rows of 64 dims need blocks of >= 16 slots
+    st = custom_structure("ops", 301, [65, 77, 96, 100, 130, 81], 8, 2, d, bs, dt, shared_prefix_blocks=4,
                           cow_seqs=3, pool_factor=1.5)
     t = materialize(st, DEV, include_new_token=False)
     h = {k: to_host(v) for k, v in t.items()}
@@ -179,7 +186,7 @@ def test_reshape_skips_padding_and_out_of_pool_slots():
     np.testing.assert_array_equal(to_host(t["value_cache"]), before_v)
 
 
-@pytest.mark.parametrize("bs,dt", [(16, "bf16"), (256, "bf16"), (32, "f32"), (16, "fp8")])
+@pytest.mark.parametrize("bs,dt", [(16, "bf16"), (256, "bf16"), (32, "f32"), (16, "fp8"), (8, "bf16"), (8, "fp8")])
 def test_gather_bit_exact(bs, dt):
     st = custom_structure("gather", 303, [1, 15, 16, 17, 300, 513], 8, 4, 128, bs, dt)
     t = materialize(st, DEV)
