@@ -91,7 +91,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *   scale          multiplies q . k before the softmax (1/sqrt(head_dim) in the usual models)
  *   block_size     tokens per block: 8, 16, 32, 64, 128 or 256 (page 1 section 5 suggests 8 for short
  *                  sequences; 8 needs head rows of at least 128 bytes, so not E4M3 at head_dim 64)
- *   head_dim       64 or 128
+ *   head_dim       64, 80, 96, 112, 128, 192 or 256 (grouped heads run on the matrix cores at 64 and 128
+ *                  with bf16 or E4M3 caches, on the vector ALUs otherwise)
  *   num_q_heads    a multiple of num_kv_heads
  *   max_context_len  upper bound of context_lens, <= max_blocks_per_seq * block_size
  *   (q_dtype, kv_dtype)  (PA_F32, PA_F32) or (PA_BF16, PA_BF16); accumulation is fp32 either way (FP8

@@ -5,9 +5,10 @@
 // softmax is taken in one streaming pass with a running maximum and sum (online softmax), so K and V are
 // read from HBM exactly once.
 //
-// Lane layout. A 16-byte load covers 8 bf16 or 4 fp32 elements, so one head's row (head_dim elements) spans
-// kRowLanes lanes and one wave-wide load covers kRows consecutive slots of a block; a 16-token tile takes
-// kLoads loads for K and as many for V. Every lane consumes exactly the bytes it loaded -- there is no reuse
+// Lane layout. A 16-byte load covers 16 E4M3, 8 bf16 or 4 fp32 elements, so one head's row (head_dim
+// elements) spans kHeadLanes lanes, padded to a power of two kRowLanes (the padding lanes read zeros through an
+// out-of-range offset and store nothing), and one wave-wide load covers kRows consecutive slots of a block; a
+// tile of kTileTok tokens takes kLoads (at most 4) loads for K and as many for V. Every lane consumes exactly the bytes it loaded -- there is no reuse
 // to stage through LDS. Each group of kRowLanes lanes ("row group") owns the tile rows r, r + kRows, ... and
 // keeps its own running (max, sum, accumulator); the groups are merged once at the end with the same
 // log-sum-exp rule the split-context reduce uses. The dot product of a row is finished with DPP adds inside
@@ -22,13 +23,19 @@
 namespace pa {
 namespace {
 
+constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2); }
+
 template <int KV, int D>
 struct Shape {
   static constexpr int kEsize = KV == PA_F32 ? 4 : KV == PA_BF16 ? 2 : 1;
-  static constexpr int kEpl = 16 / kEsize;        // elements per lane per 16-byte load
-  static constexpr int kRowLanes = D / kEpl;      // lanes holding one head's row
-  static constexpr int kRows = kWave / kRowLanes; // slots per wave-wide load
-  static constexpr int kLoads = kTile / kRows;    // loads per 16-token tile (per K and per V)
+  static constexpr int kEpl = 16 / kEsize;               // elements per lane per 16-byte load
+  static constexpr int kHeadLanes = D / kEpl;            // lanes holding one head's row
+  static constexpr int kRowLanes = next_pow2(kHeadLanes);  // lanes per row group (the rest of them idle)
+  static constexpr int kRows = kWave / kRowLanes;        // slots per wave-wide load
+  // tokens per tile: at most 4 loads per lane for K (and for V), at most 16 tokens
+  static constexpr int kTileTok = kRows * 4 < kTile ? kRows * 4 : kTile;
+  static constexpr int kLoads = kTileTok / kRows;        // loads per tile (per K and per V)
+  static_assert(D % kEpl == 0 && kRowLanes <= kWave, "head_dim must fill whole 16-byte chunks");
   static constexpr int kQEsize = KV == PA_F32 ? 4 : 2;  // the query is bf16 over an E4M3 cache
   static constexpr int kQWords = kEpl * kQEsize / 16;   // 16-byte words of query per lane chunk
 };
@@ -119,6 +126,7 @@ template <int KV, int D>
 __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(const DecodeArgs a) {
   using S = Shape<KV, D>;
   constexpr int NL = S::kLoads;
+  constexpr int TT = S::kTileTok;
   const int lane = threadIdx.x & (kWave - 1);
   const int h = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   const int part = blockIdx.y;
@@ -132,12 +140,17 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int g = h / a.group;
   const int r = lane / S::kRowLanes;  // row group
   const int c = lane % S::kRowLanes;  // 16-byte chunk of the head's row
+  const bool lane_ok = c < S::kHeadLanes;  // false for the padding lanes of a row group
 
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
+  // padding lanes load at an offset above every descriptor's size (at most 16 rows < 2^30 bytes), so they read
+  // zeros without touching memory
+  constexpr uint32_t kNowhere = 0x80000000u;
   uint32_t lane_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i)
-    lane_off[i] = (uint32_t)((i * S::kRows + r) * row_bytes + (int64_t)g * D * S::kEsize + c * 16);
+    lane_off[i] = lane_ok ? (uint32_t)((i * S::kRows + r) * row_bytes + (int64_t)g * D * S::kEsize + c * 16)
+                          : kNowhere;
 
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
@@ -145,9 +158,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   Words<S::kQWords> q;
   {
     const char* qp = static_cast<const char*>(a.query) + ((int64_t)s * a.num_q_heads + h) * D * S::kQEsize +
-                     c * 16 * S::kQWords;
+                     (lane_ok ? c : 0) * 16 * S::kQWords;
 #pragma unroll
-    for (int i = 0; i < S::kQWords; ++i) q.w[i] = reinterpret_cast<const U4*>(qp)[i];
+    for (int i = 0; i < S::kQWords; ++i) {
+      const U4 v = reinterpret_cast<const U4*>(qp)[i];
+      q.w[i] = lane_ok ? v : U4{0u, 0u, 0u, 0u};
+    }
   }
 
   float m = -INFINITY, l = 0.f;
@@ -155,25 +171,26 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
 #pragma unroll
   for (int e = 0; e < S::kEpl; ++e) acc[e] = 0.f;
   bool bad = false;
-  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+  const int ntiles = (t1 - t0 + TT - 1) / TT;
 
   U4 kb[kStages][NL], vb[kStages][NL];
   // The loads stay unconditional, so the wait counters of the two register sets never merge across a branch:
-  // each 8-row half of the tile has a descriptor that covers only its rows below the partition end, and rows
-  // past it (a tile index past the end: all of them) read as zero without touching memory. The halves lie in
-  // one block unless blocks hold 8 slots; a wave-wide load of at most 8 rows never straddles them. Shapes with
-  // 16 rows per load (E4M3 at head_dim 64) take the whole tile through the first descriptor: the host refuses
-  // 8-slot blocks for them.
-  constexpr bool kHalves = S::kRows <= kTile / 2;
+  // a 16-token tile has a descriptor per 8-row half that covers only its rows below the partition end, and
+  // rows past it (a tile index past the end: all of them) read as zero without touching memory. The halves lie
+  // in one block unless blocks hold 8 slots; a wave-wide load of at most 8 rows never straddles them. Shapes
+  // with 16 rows per load (E4M3 at head_dim 64) take the whole tile through the first descriptor: the host
+  // refuses 8-slot blocks for them. Tiles of at most 8 tokens always lie in one block.
+  constexpr bool kHalves = TT == kTile && S::kRows <= kTile / 2;
   const int last8 = (t1 - 1) & ~(kTile / 2 - 1);  // start of the last live 8-row group
   auto issue = [&](U4* kq, U4* vq, int tile) {
-    const int t = t0 + min(tile, ntiles - 1) * kTile;
+    const int t = t0 + min(tile, ntiles - 1) * TT;
     const int64_t base0 = tile_slot_bytes(table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
-    const int64_t base1 = a.bs_log2 == 3
+    const int64_t base1 = !kHalves ? base0
+                          : a.bs_log2 == 3
                               ? tile_slot_bytes(table, min(t + kTile / 2, last8), a.bs_log2, a.num_blocks,
                                                 row_bytes, bad)
                               : base0 + (kTile / 2) * row_bytes;
-    const int rows = tile < ntiles ? min(kTile, t1 - t) : 0;
+    const int rows = tile < ntiles ? min(TT, t1 - t) : 0;
     const uint32_t live0 = (uint32_t)(kHalves ? min(rows, kTile / 2) : rows) * (uint32_t)row_bytes;
     const uint32_t live1 = (uint32_t)max(rows - kTile / 2, 0) * (uint32_t)row_bytes;
     const __amdgpu_buffer_rsrc_t kr0 = make_rsrc(kbase + base0, live0), kr1 = make_rsrc(kbase + base1, live1);
@@ -181,7 +198,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
     const uint32_t half_off = (uint32_t)((kTile / 2) * row_bytes);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      if (i * S::kRows < kTile / 2) {
+      if (!kHalves || i * S::kRows < kTile / 2) {
         kq[i] = load16<kPolStream>(kr0, lane_off[i]);
         vq[i] = load16<kPolStream>(vr0, lane_off[i]);
       } else {
@@ -191,8 +208,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
     }
   };
   auto consume = [&](const U4* kq, const U4* vq, int tile) {
-    const int t = t0 + tile * kTile;
-    const bool full = t + kTile <= t1;
+    const int t = t0 + tile * TT;
+    const bool full = t + TT <= t1;
     float sc[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -250,7 +267,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
     m = M;
   }
 
-  if (r == 0) {
+  if (r == 0 && lane_ok) {
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const float poison = __uint_as_float(0x7fc00000u);
     float res[S::kEpl];
@@ -294,14 +311,17 @@ constexpr int kSpec = 16;  // partitions whose outputs are loaded up front
 
 template <int D>
 __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
-  constexpr int kDpl = D / kWave;  // dims per lane
+  constexpr int kDpl = (D + kWave - 1) / kWave;  // dims per lane
+  constexpr int kActive = D / kDpl;              // lanes holding dims (all of them when 64 divides D)
+  static_assert(D % kDpl == 0, "whole dims per lane");
   const int lane = threadIdx.x;
+  const bool lane_ok = lane < kActive;  // the other lanes read lane 0's dims and store nothing
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int pm = a.max_partitions;
   const int64_t row0 = ((int64_t)s * a.num_q_heads + h) * pm;
   const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
-  const float* __restrict__ o = a.ws_o + row0 * D + lane * kDpl;
+  const float* __restrict__ o = a.ws_o + row0 * D + (lane_ok ? lane : 0) * kDpl;
 
   // indexes clamped to the row's last slot keep every speculative load inside the workspace without a branch
   const float2 v0 = ml[min(lane, pm - 1)];
@@ -358,7 +378,7 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
     }
   }
   const float inv = 1.0f / wave_sum(wsum);
-  if (!merge) return;
+  if (!merge || !lane_ok) return;
   float* dst = a.out + ((int64_t)s * a.num_q_heads + h) * D + lane * kDpl;
 #pragma unroll
   for (int e = 0; e < kDpl; ++e) dst[e] = acc[e] * inv;
@@ -366,27 +386,44 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
 
 }  // namespace
 
+template <int KV>
+hipError_t launch_kv(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: decode_valu_kernel<KV, 64><<<grid, block, 0, stream>>>(a); break;
+    case 80: decode_valu_kernel<KV, 80><<<grid, block, 0, stream>>>(a); break;
+    case 96: decode_valu_kernel<KV, 96><<<grid, block, 0, stream>>>(a); break;
+    case 112: decode_valu_kernel<KV, 112><<<grid, block, 0, stream>>>(a); break;
+    case 128: decode_valu_kernel<KV, 128><<<grid, block, 0, stream>>>(a); break;
+    case 192: decode_valu_kernel<KV, 192><<<grid, block, 0, stream>>>(a); break;
+    case 256: decode_valu_kernel<KV, 256><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.split ? a.max_partitions : 1,
                   a.num_seqs);
   const dim3 block(kWave * kWavesPerGroup);
-  if (kv_dtype == PA_BF16 && a.head_dim == 128) decode_valu_kernel<PA_BF16, 128><<<grid, block, 0, stream>>>(a);
-  else if (kv_dtype == PA_BF16 && a.head_dim == 64) decode_valu_kernel<PA_BF16, 64><<<grid, block, 0, stream>>>(a);
-  else if (kv_dtype == PA_F32 && a.head_dim == 128) decode_valu_kernel<PA_F32, 128><<<grid, block, 0, stream>>>(a);
-  else if (kv_dtype == PA_F32 && a.head_dim == 64) decode_valu_kernel<PA_F32, 64><<<grid, block, 0, stream>>>(a);
-  else if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128)
-    decode_valu_kernel<PA_FP8_E4M3, 128><<<grid, block, 0, stream>>>(a);
-  else if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64)
-    decode_valu_kernel<PA_FP8_E4M3, 64><<<grid, block, 0, stream>>>(a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (kv_dtype == PA_BF16) return launch_kv<PA_BF16>(a, grid, block, stream);
+  if (kv_dtype == PA_F32) return launch_kv<PA_F32>(a, grid, block, stream);
+  if (kv_dtype == PA_FP8_E4M3) return launch_kv<PA_FP8_E4M3>(a, grid, block, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.num_seqs);
-  if (a.head_dim == 128) lse_reduce_kernel<128><<<grid, dim3(kWave), 0, stream>>>(a);
-  else if (a.head_dim == 64) lse_reduce_kernel<64><<<grid, dim3(kWave), 0, stream>>>(a);
-  else return hipErrorInvalidValue;
+  const dim3 block(kWave);
+  switch (a.head_dim) {
+    case 64: lse_reduce_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    case 80: lse_reduce_kernel<80><<<grid, block, 0, stream>>>(a); break;
+    case 96: lse_reduce_kernel<96><<<grid, block, 0, stream>>>(a); break;
+    case 112: lse_reduce_kernel<112><<<grid, block, 0, stream>>>(a); break;
+    case 128: lse_reduce_kernel<128><<<grid, block, 0, stream>>>(a); break;
+    case 192: lse_reduce_kernel<192><<<grid, block, 0, stream>>>(a); break;
+    case 256: lse_reduce_kernel<256><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -23,7 +23,9 @@ int log2_pow2(int v) {
 }
 
 bool supported_block_size(int bs) { return bs >= 8 && bs <= 256 && log2_pow2(bs) >= 0; }
-bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_head_dim(int d) {
+  return d == 64 || d == 80 || d == 96 || d == 112 || d == 128 || d == 192 || d == 256;
+}
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -79,9 +81,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
-  // a wave-wide load covers 64 x 16 bytes of whole head rows and must stay inside one 8-slot block: E4M3 rows
-  // of 64 dims would put 16 slots in one load
-  if (block_size == 8 && head_dim * esize_of(kv_dtype) < 128) {
+  // a wave-wide load covers 64 x 16 bytes of whole head rows (padded to a power of two of 16-byte chunks) and
+  // must stay inside one 8-slot block: rows of at most 64 bytes (E4M3 at head_dim 64) would put 16 slots in it
+  if (block_size == 8 && head_dim * esize_of(kv_dtype) <= 64) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }

@@ -75,18 +75,19 @@ __device__ __forceinline__ int64_t tile_slot_bytes(const int32_t* __restrict__ t
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Sum over aligned groups of N lanes (N = 4, 8 or 16), result in every lane of the group, via DPP
+// Sum over aligned groups of N lanes (N = 4 .. 64), result in every lane of the group, via DPP
 // (quad_perm swaps, then half-row and row mirrors: each step adds the partner's partial sum).
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));  // lane ^ 1
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));  // lane ^ 2
   if constexpr (N >= 8)
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // 8-mirror
   if constexpr (N >= 16)
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));  // 16-mirror
-  if constexpr (N == 32) v += __shfl_xor(v, 16);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  if constexpr (N == 64) v += __shfl_xor(v, 32);
   return v;
 }
 

@@ -51,7 +51,8 @@ def decode_call(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(head_dim=96), PA_ERR_UNSUPPORTED),
+    (dict(head_dim=100), PA_ERR_UNSUPPORTED),
+    (dict(head_dim=48), PA_ERR_UNSUPPORTED),
     (dict(block_size=4), PA_ERR_UNSUPPORTED),
     (dict(block_size=48), PA_ERR_UNSUPPORTED),
     (dict(block_size=512, max_context_len=128), PA_ERR_UNSUPPORTED),
@@ -93,7 +94,8 @@ def scaled_call(**over):
     (dict(k_scale=0.0), PA_ERR_SHAPE),
     (dict(v_scale=float("nan")), PA_ERR_SHAPE),
     (dict(k_scale=float("inf")), PA_ERR_SHAPE),
-    (dict(head_dim=96), PA_ERR_UNSUPPORTED),
+    (dict(head_dim=100), PA_ERR_UNSUPPORTED),
+    (dict(head_dim=48), PA_ERR_UNSUPPORTED),
     (dict(head_dim=64, block_size=8, max_context_len=64), PA_ERR_UNSUPPORTED),  # 16 E4M3 rows per load
     (dict(partition_size=32), PA_ERR_WORKSPACE),
     (dict(out=None), PA_ERR_NULL),

@@ -103,6 +103,18 @@ SMALL = [
     (217, [700, 45, 513, 9], 32, 8, 128, 8, "fp8"),
     (218, [33, 64, 7, 200], 4, 4, 64, 8, "f32"),
     (219, [1100, 24, 520], 64, 8, 128, 8, "bf16"),
+    # other head dims: row groups padded to a power of two of 16-byte chunks, tiles of 4..16 tokens; grouped
+    # queries at these dims take the per-head kernel
+    (220, [5, 17, 100, 300], 8, 8, 80, 16, "bf16"),
+    (221, [33, 64, 129], 4, 2, 96, 16, "f32"),
+    (222, [90, 513, 7], 16, 4, 112, 32, "fp8"),
+    (223, [700, 45, 1], 8, 8, 192, 16, "bf16"),
+    (224, [260, 33, 1000], 8, 2, 256, 16, "bf16"),
+    (225, [100, 17, 70], 4, 4, 256, 8, "f32"),
+    (226, [300, 8, 65], 4, 4, 80, 8, "fp8"),
+    (227, [129, 64, 3], 4, 4, 192, 16, "f32"),
+    (228, [515, 31, 2], 8, 8, 96, 16, "fp8"),
+    (229, [400, 77], 8, 8, 256, 32, "fp8"),
 ]
 
 
@@ -119,9 +131,10 @@ def test_small_attention_parity(case):
         assert_attention_close(gpu, ref, dt, f"partition {part}")
 
 
-@pytest.mark.parametrize("dt,bs", [("f32", 16), ("bf16", 16), ("fp8", 16), ("bf16", 8), ("fp8", 8)])
-def test_small_cache_ops_bit_exact(dt, bs):
-    d = 128 if (dt, bs) == ("fp8", 8) else 64  # E4M3 rows of 64 dims need blocks of >= 16 slots
+@pytest.mark.parametrize("dt,bs,d", [("f32", 16, 64), ("bf16", 16, 64), ("fp8", 16, 64), ("bf16", 8, 64),
+                                     ("fp8", 8, 128), ("bf16", 16, 80), ("fp8", 16, 112), ("f32", 8, 192)])
+def test_small_cache_ops_bit_exact(dt, bs, d):
+    # (E4M3 rows of 64 dims need blocks of >= 16 slots)
     st = custom_structure("ops", 301, [65, 77, 96, 100, 130, 81], 8, 2, d, bs, dt, shared_prefix_blocks=4,
                           cow_seqs=3, pool_factor=1.5)
     t = materialize(st, DEV, include_new_token=False)
