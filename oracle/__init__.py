@@ -59,6 +59,9 @@ def _bind(lib):
                                                   ctypes.c_float, ctypes.c_float]
     lib.oracle_reshape_and_cache_e4m3.restype = ctypes.c_int
     lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_decode_multi.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                        P, P, P, ctypes.c_double, i32, i32, i32, i32, i32, i32, i64, i32, P, i64]
+    lib.oracle_decode_multi.restype = ctypes.c_int
     lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32]
     lib.oracle_reshape_and_cache.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [P, P, P, i32, i64, i64]
@@ -119,6 +122,40 @@ def decode(query, key_cache, value_cache, block_tables, context_lens, scale, *, 
                            _ptr(rw) if rw is not None else None, n)
     if rc != 0:
         raise ValueError(f"oracle_decode rejected its input (status {rc})")
+    return out
+
+
+def decode_multi(query, key_cache, value_cache, block_tables, context_lens, query_start, scale, *, rows=None,
+                 k_scale=1.0, v_scale=1.0, lib=None):
+    """fp64 attention of several new tokens per sequence (causal among them).
+
+    query [T, Hq, D] holds the rows of sequence s at query_start[s] .. query_start[s + 1] - 1, its newest
+    tokens: row j of QL sits at position L - QL + j and attends over positions 0 .. L - QL + j. Returns float64
+    [T, Hq, D]; with ``rows`` (int array [n, 2] of (query row, head)) only those rows are computed, the rest NaN.
+    """
+    lib = lib or load()
+    q = np.ascontiguousarray(query)
+    kc = np.ascontiguousarray(key_cache)
+    vc = np.ascontiguousarray(value_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, D2 = kc.shape
+    B = cl.shape[0]
+    if D2 != D or vc.shape != kc.shape or bt.shape[0] != B or qs.shape != (B + 1,):
+        raise ValueError("shape mismatch")
+    out = np.full((T, Hq, D), np.nan if rows is not None else 0.0, dtype=np.float64)
+    rw = None
+    n = 0
+    if rows is not None:
+        rw = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        n = rw.shape[0]
+    rc = lib.oracle_decode_multi(_ptr(out), _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc),
+                                 float(k_scale), float(v_scale), _ptr(bt), _ptr(cl), _ptr(qs), float(scale), bs, B,
+                                 T, Hq, Hkv, D, NB, bt.shape[1], _ptr(rw) if rw is not None else None, n)
+    if rc != 0:
+        raise ValueError(f"oracle_decode_multi rejected its input (status {rc})")
     return out
 
 

@@ -93,3 +93,30 @@ def contiguous_decode(query, k_contig, v_contig, context_lens, scale):
             w = np.exp(z - z.max())
             out[s, h] = (w @ vc[s, h // G, :L]) / w.sum()
     return out
+
+
+def decode_multi(query, key_cache, value_cache, block_tables, context_lens, query_start, scale, k_scale=1.0,
+                 v_scale=1.0):
+    """Several new tokens per sequence: row j of sequence s's QL rows attends over its first L - QL + j + 1
+    positions (none when that count is not positive), from the dense K/V rebuilt by scanning the pool."""
+    q = to_f64(np.asarray(query))
+    T, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, D))
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        if L == 0 or q1 == q0:
+            continue
+        k, v = dense_kv(key_cache, value_cache, block_tables[s], L, k_scale, v_scale)
+        for j in range(q1 - q0):
+            E = L - (q1 - q0) + j + 1
+            if E <= 0:
+                continue
+            for h in range(Hq):
+                z = (k[:E, h // G, :] @ q[q0 + j, h]) * scale
+                w = np.exp(z - z.max())
+                out[q0 + j, h] = (w @ v[:E, h // G, :]) / w.sum()
+    return out
+

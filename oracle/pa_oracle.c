@@ -117,6 +117,96 @@ int oracle_num_threads(void) {
 }
 
 /*
+ * One output row: head h of query row q_row attends over the first L logical positions of the sequence whose
+ * block-table row is s. K/V are reassembled in logical order through the block table (page 1 section 3.2,
+ * page 3 section 2.2), then out = sum_t w_t v_t / sum_t w_t with w_t = exp(z_t - max z), z_t = scale * q.k_t.
+ */
+static int attend_row(double *o, const void *query, int q_dtype, int64_t q_row, const void *key_cache,
+                      const void *value_cache, int kv_dtype, double k_scale, double v_scale,
+                      const int32_t *block_tables, int32_t s, int32_t h, int64_t L, double scale,
+                      int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t max_blocks_per_seq) {
+    const int32_t G = num_q_heads / num_kv_heads;
+    const int32_t g = h / G;
+    for (int32_t d = 0; d < head_dim; ++d) {
+        o[d] = 0.0;
+    }
+    if (L <= 0) {
+        return 0;
+    }
+    double *q = malloc(sizeof(double) * head_dim);
+    double *k = malloc(sizeof(double) * L * head_dim);
+    double *v = malloc(sizeof(double) * L * head_dim);
+    double *z = malloc(sizeof(double) * L);
+    if (!q || !k || !v || !z) {
+        free(q); free(k); free(v); free(z);
+        return -4;
+    }
+    const int64_t q_base = (q_row * num_q_heads + h) * head_dim;
+    for (int32_t d = 0; d < head_dim; ++d) {
+        q[d] = elem(query, q_base + d, q_dtype);
+    }
+    /* reassemble this head's K and V in logical order through the block table */
+    for (int64_t t = 0; t < L; ++t) {
+        const int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+        const int64_t off = t % block_size;
+        const int64_t base = ((phys * block_size + off) * num_kv_heads + g) * head_dim;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            k[t * head_dim + d] = k_scale * elem(key_cache, base + d, kv_dtype);
+            v[t * head_dim + d] = v_scale * elem(value_cache, base + d, kv_dtype);
+        }
+    }
+    double m = -INFINITY;
+    for (int64_t t = 0; t < L; ++t) {
+        double acc = 0.0;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            acc += q[d] * k[t * head_dim + d];
+        }
+        z[t] = scale * acc;
+        if (z[t] > m) {
+            m = z[t];
+        }
+    }
+    double sum = 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+        z[t] = exp(z[t] - m); /* z now holds the unnormalised weight w_t */
+        sum += z[t];
+    }
+    for (int64_t t = 0; t < L; ++t) {
+        for (int32_t d = 0; d < head_dim; ++d) {
+            o[d] += z[t] * v[t * head_dim + d];
+        }
+    }
+    for (int32_t d = 0; d < head_dim; ++d) {
+        o[d] /= sum;
+    }
+    free(q); free(k); free(v); free(z);
+    return 0;
+}
+
+static int check_tables(const int32_t *block_tables, const int32_t *context_lens, int32_t block_size,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int64_t num_blocks, int32_t max_blocks_per_seq) {
+    if (block_size <= 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0) {
+        return -1;
+    }
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int64_t L = context_lens[s];
+        if (L < 0 || (L + block_size - 1) / block_size > max_blocks_per_seq) {
+            return -2;
+        }
+        for (int64_t j = 0; j < (L + block_size - 1) / block_size; ++j) {
+            int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + j];
+            if (b < 0 || b >= num_blocks) {
+                return -3;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
  * Decode attention for the (sequence, query head) rows listed in `rows` (pairs s, h), or for every row when
  * rows == NULL. out is [num_seqs, num_q_heads, head_dim] fp64; rows not listed are left untouched.
  *
@@ -137,25 +227,12 @@ int oracle_decode(double *out, const void *query, int q_dtype, const void *key_c
                   int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, const int32_t *rows,
                   int64_t num_rows) {
-    if (block_size <= 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        num_q_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0) {
-        return -1;
+    int status = check_tables(block_tables, context_lens, block_size, num_seqs, num_q_heads, num_kv_heads,
+                              head_dim, num_blocks, max_blocks_per_seq);
+    if (status != 0) {
+        return status;
     }
-    for (int32_t s = 0; s < num_seqs; ++s) {
-        int64_t L = context_lens[s];
-        if (L < 0 || (L + block_size - 1) / block_size > max_blocks_per_seq) {
-            return -2;
-        }
-        for (int64_t j = 0; j < (L + block_size - 1) / block_size; ++j) {
-            int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + j];
-            if (b < 0 || b >= num_blocks) {
-                return -3;
-            }
-        }
-    }
-    const int32_t G = num_q_heads / num_kv_heads;
     const int64_t total = rows ? num_rows : (int64_t)num_seqs * num_q_heads;
-    int status = 0;
 
 #pragma omp parallel for schedule(dynamic)
     for (int64_t r = 0; r < total; ++r) {
@@ -168,64 +245,79 @@ int oracle_decode(double *out, const void *query, int q_dtype, const void *key_c
             h = (int32_t)(r % num_q_heads);
         }
         double *o = out + ((int64_t)s * num_q_heads + h) * head_dim;
-        const int64_t L = context_lens[s];
-        const int32_t g = h / G;
-        for (int32_t d = 0; d < head_dim; ++d) {
-            o[d] = 0.0;
-        }
-        if (L == 0) {
-            continue;
-        }
-        double *q = malloc(sizeof(double) * head_dim);
-        double *k = malloc(sizeof(double) * L * head_dim);
-        double *v = malloc(sizeof(double) * L * head_dim);
-        double *z = malloc(sizeof(double) * L);
-        if (!q || !k || !v || !z) {
-            free(q); free(k); free(v); free(z);
+        const int rc = attend_row(o, query, q_dtype, s, key_cache, value_cache, kv_dtype, k_scale, v_scale,
+                                  block_tables, s, h, context_lens[s], scale, block_size, num_q_heads,
+                                  num_kv_heads, head_dim, max_blocks_per_seq);
+        if (rc != 0) {
 #pragma omp atomic write
-            status = -4;
-            continue;
+            status = rc;
         }
-        const int64_t q_base = ((int64_t)s * num_q_heads + h) * head_dim;
-        for (int32_t d = 0; d < head_dim; ++d) {
-            q[d] = elem(query, q_base + d, q_dtype);
-        }
-        /* reassemble this head's K and V in logical order through the block table */
-        for (int64_t t = 0; t < L; ++t) {
-            const int64_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
-            const int64_t off = t % block_size;
-            const int64_t base = ((phys * block_size + off) * num_kv_heads + g) * head_dim;
-            for (int32_t d = 0; d < head_dim; ++d) {
-                k[t * head_dim + d] = k_scale * elem(key_cache, base + d, kv_dtype);
-                v[t * head_dim + d] = v_scale * elem(value_cache, base + d, kv_dtype);
-            }
-        }
-        double m = -INFINITY;
-        for (int64_t t = 0; t < L; ++t) {
-            double acc = 0.0;
-            for (int32_t d = 0; d < head_dim; ++d) {
-                acc += q[d] * k[t * head_dim + d];
-            }
-            z[t] = scale * acc;
-            if (z[t] > m) {
-                m = z[t];
-            }
-        }
-        double sum = 0.0;
-        for (int64_t t = 0; t < L; ++t) {
-            z[t] = exp(z[t] - m); /* z now holds the unnormalised weight w_t */
-            sum += z[t];
-        }
-        for (int64_t t = 0; t < L; ++t) {
-            for (int32_t d = 0; d < head_dim; ++d) {
-                o[d] += z[t] * v[t * head_dim + d];
-            }
-        }
-        for (int32_t d = 0; d < head_dim; ++d) {
-            o[d] /= sum;
-        }
-        free(q); free(k); free(v); free(z);
     }
+    return status;
+}
+
+/*
+ * Several new tokens per sequence (speculative verification, page 1 section 6; a chunk of a prompt). Sequence
+ * s owns query rows query_start[s] .. query_start[s + 1] - 1, its QL = query_start[s + 1] - query_start[s]
+ * newest tokens: token j sits at position L - QL + j of its L = context_lens[s] positions and attends over
+ * positions 0 .. L - QL + j (causal: the cache already holds all L rows, the later ones are not attended).
+ * A token with no position to attend (QL > L) gets a zero row. rows lists (query row, head) pairs, or is NULL
+ * for all; out is [num_tokens, num_q_heads, head_dim] fp64. Returns what oracle_decode returns, or -5 when
+ * query_start is not a non-decreasing run from 0 to num_tokens.
+ */
+int oracle_decode_multi(double *out, const void *query, int q_dtype, const void *key_cache,
+                        const void *value_cache, int kv_dtype, double k_scale, double v_scale,
+                        const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start,
+                        double scale, int32_t block_size, int32_t num_seqs, int32_t num_tokens,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                        int32_t max_blocks_per_seq, const int32_t *rows, int64_t num_rows) {
+    int status = check_tables(block_tables, context_lens, block_size, num_seqs, num_q_heads, num_kv_heads,
+                              head_dim, num_blocks, max_blocks_per_seq);
+    if (status != 0) {
+        return status;
+    }
+    if (num_tokens < 0 || query_start[0] != 0 || query_start[num_seqs] != num_tokens) {
+        return -5;
+    }
+    int32_t *seq_of = malloc(sizeof(int32_t) * (num_tokens > 0 ? num_tokens : 1));
+    if (!seq_of) {
+        return -4;
+    }
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        if (query_start[s + 1] < query_start[s]) {
+            free(seq_of);
+            return -5;
+        }
+        for (int32_t t = query_start[s]; t < query_start[s + 1]; ++t) {
+            seq_of[t] = s;
+        }
+    }
+    const int64_t total = rows ? num_rows : (int64_t)num_tokens * num_q_heads;
+
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < total; ++r) {
+        int32_t t, h;
+        if (rows) {
+            t = rows[2 * r];
+            h = rows[2 * r + 1];
+        } else {
+            t = (int32_t)(r / num_q_heads);
+            h = (int32_t)(r % num_q_heads);
+        }
+        const int32_t s = seq_of[t];
+        const int64_t QL = query_start[s + 1] - query_start[s];
+        const int64_t j = t - query_start[s];
+        const int64_t E = (int64_t)context_lens[s] - QL + j + 1; /* positions this token attends over */
+        double *o = out + ((int64_t)t * num_q_heads + h) * head_dim;
+        const int rc = attend_row(o, query, q_dtype, t, key_cache, value_cache, kv_dtype, k_scale, v_scale,
+                                  block_tables, s, h, E, scale, block_size, num_q_heads, num_kv_heads, head_dim,
+                                  max_blocks_per_seq);
+        if (rc != 0) {
+#pragma omp atomic write
+            status = rc;
+        }
+    }
+    free(seq_of);
     return status;
 }
 

@@ -13,5 +13,6 @@ from .decode import (  # noqa: F401
     live_slot_mask,
     materialize,
     algorithmic_bytes,
+    query_rows,
 )
 from .requests import Request, request_stream  # noqa: F401,E402

@@ -292,6 +292,27 @@ def materialize(st: DecodeStructure, device="cpu", include_new_token: bool = Tru
             "new_value": new_value}
 
 
+def query_rows(st: DecodeStructure, query_lens, device="cpu", seed: int | None = None):
+    """Query rows for several new tokens per sequence: ``query_lens[s]`` rows for sequence s, packed in sequence
+    order. Returns (query [T, Hq, D] in the query dtype, N(0, 1) then rounded; query_start int32 [B + 1] with
+    query_start[s] the first row of sequence s).
+    """
+    import torch
+
+    ql = np.asarray(query_lens, dtype=np.int64)
+    if ql.shape != (st.num_seqs,) or (ql < 0).any():
+        raise ValueError("query_lens must hold one non-negative count per sequence")
+    query_start = np.zeros(st.num_seqs + 1, dtype=np.int32)
+    query_start[1:] = np.cumsum(ql)
+    dt = torch.float32 if st.dtype == "f32" else torch.bfloat16
+    gen = torch.Generator(device=torch.device(device))
+    gen.manual_seed(int(st.seed if seed is None else seed) + 7919)
+    T = int(query_start[-1])
+    q = torch.randn((T, st.num_q_heads, st.head_dim), generator=gen, device=torch.device(device),
+                    dtype=torch.float32).to(dt)
+    return q, query_start
+
+
 def algorithmic_bytes(st: DecodeStructure) -> dict:
     """Bytes a decode call must move at minimum: every live K and V element once, the query, the fp32 output,
     the live table entries and the lengths. ``kv_unique`` counts shared prefix blocks once."""
