@@ -131,6 +131,45 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * Attention of several new tokens per sequence over the paged cache (speculative verification, which page 1
+ * section 6 lists as future work combined with paging; a chunk of a prompt). Sequence s brings the query rows
+ * query_start[s] .. query_start[s + 1] - 1, its QL newest tokens, whose K/V are already in the cache: its
+ * L = context_lens[s] positions end with them. Row j of QL sits at position L - QL + j and attends causally,
+ *     out[r][h][:] = softmax_t( scale * query[r][h][:] . K_t ) . V_t ,  t = 0 .. L - QL + j,  r = query_start[s] + j,
+ * with K_t / V_t and the scales as in paged_attention_decode_scaled. A row with no position to attend
+ * (QL > L) gives a zero row. QL = 1 for every sequence is paged_attention_decode_scaled.
+ *
+ *   out, query     [num_query_tokens][num_q_heads][head_dim] (fp32; q_dtype), rows packed by sequence
+ *   query_start    int32 [num_seqs + 1] device array: query_start[0] = 0, non-decreasing, last entry
+ *                  num_query_tokens, every difference <= max_query_len (rows beyond max_query_len are left
+ *                  unwritten; the contents are not checked on the host)
+ *   max_query_len  the largest QL (>= 1). Grouped heads x max_query_len <= 16 runs all of a sequence's rows on
+ *                  the matrix cores with one read of its K/V (bf16 or E4M3 caches at head_dim 64 or 128); other
+ *                  calls read a sequence's K/V once per row.
+ *   workspace      at least paged_attention_multi_workspace_bytes(...) bytes when that is non-zero
+ * Other arguments as in paged_attention_decode_scaled. num_seqs == 0 or num_query_tokens == 0 is a no-op;
+ * num_query_tokens > num_seqs * max_query_len is PA_ERR_SHAPE.
+ */
+int paged_attention_decode_multi(float *out, const void *query, const void *key_cache, const void *value_cache,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *query_start, float scale, float k_scale, float v_scale,
+                                 int32_t block_size, int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 int32_t q_dtype, int32_t kv_dtype, int32_t partition_size, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Partition size and workspace bytes of paged_attention_decode_multi, as the decode forms above. */
+int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t partition_size);
+size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t partition_size);
+
+/*
  * Quantising cache write into PA_FP8_E4M3 pools: like reshape_and_cache, with every element of key[n]
  * (value[n]) stored as the E4M3 code of x / k_scale (x / v_scale): an fp32 division, saturated to +-448,
  * rounded to nearest with ties to an even mantissa; NaN is stored as 0x7F.

@@ -55,6 +55,14 @@ def load_library(path: str | None = None):
     lib.paged_attention_decode_scaled.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i64, i32,
                                                   i32, i32, i32, i32, P, sz, P]
     lib.paged_attention_decode_scaled.restype = ctypes.c_int
+    lib.paged_attention_decode_multi.argtypes = [P, P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i32,
+                                                 i32, i64, i32, i32, i32, i32, i32, P, sz, P]
+    lib.paged_attention_decode_multi.restype = ctypes.c_int
+    multi_sizes = [i32] * 10
+    lib.paged_attention_multi_partition_size.argtypes = multi_sizes
+    lib.paged_attention_multi_partition_size.restype = i32
+    lib.paged_attention_multi_workspace_bytes.argtypes = multi_sizes
+    lib.paged_attention_multi_workspace_bytes.restype = sz
     lib.reshape_and_cache_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32, f32, f32, P]
     lib.reshape_and_cache_fp8.restype = ctypes.c_int
     lib.reshape_and_cache.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i32, P]
@@ -179,6 +187,66 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     else:
         st = lib.paged_attention_decode(*ptrs, float(scale), *tail)
         _check("paged_attention_decode", st)
+    return out
+
+
+def multi_workspace_bytes(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                          block_size, max_context_len, kv_dtype, partition_size=-1) -> int:
+    return int(load_library().paged_attention_multi_workspace_bytes(
+        num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        kv_dtype, partition_size))
+
+
+def multi_partition_size_for(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                             block_size, max_context_len, kv_dtype, partition_size=-1) -> int:
+    r = load_library().paged_attention_multi_partition_size(num_seqs, num_query_tokens, max_query_len, num_q_heads,
+                                                            num_kv_heads, head_dim, block_size, max_context_len,
+                                                            kv_dtype, partition_size)
+    _check("paged_attention_multi_partition_size", r if r < 0 else 0)
+    return int(r)
+
+
+def paged_attention_decode_multi(out, query, key_cache, value_cache, block_tables, context_lens, query_start,
+                                 scale: float, *, max_query_len: int, max_context_len: int | None = None,
+                                 partition_size: int = -1, workspace=None, stream=None, k_scale: float = 1.0,
+                                 v_scale: float = 1.0):
+    """Several new tokens per sequence (see the C header): rows query_start[s] .. query_start[s + 1] - 1 of
+    ``query`` [T, Hq, D] are sequence s's newest tokens and attend causally over its paged K/V.
+
+    out: fp32 [T, Hq, D]; query_start: int32 [B + 1] on the device; max_query_len: the largest rows-per-sequence
+    count (a host value, so the call needs no device sync).
+    """
+    torch = _torch()
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, query_start)
+    if out.dtype != torch.float32:
+        raise TypeError("out must be float32")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
+        _int32(t, name)
+    T, Hq, D = query.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    B = context_lens.shape[0]
+    if D2 != D or value_cache.shape != key_cache.shape or tuple(out.shape) != (T, Hq, D):
+        raise ValueError("shape mismatch between out, query and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("block_tables must be [B, MB], context_lens [B] and query_start [B + 1]")
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache must have the same dtype")
+    MB = block_tables.shape[1]
+    mcl = MB * bs if max_context_len is None else int(max_context_len)
+    qd, kd = _dtype_code(query), _dtype_code(key_cache)
+    lib = load_library()
+    need = lib.paged_attention_multi_workspace_bytes(B, T, int(max_query_len), Hq, Hkv, D, bs, mcl, kd,
+                                                     partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.paged_attention_decode_multi(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                                          value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+                                          query_start.data_ptr(), float(scale), float(k_scale), float(v_scale), bs, B,
+                                          T, int(max_query_len), Hq, Hkv, D, NB, MB, mcl, qd, kd, int(partition_size),
+                                          ws_ptr, ws_len, _stream(dev, stream))
+    _check("paged_attention_decode_multi", st)
     return out
 
 

@@ -7,6 +7,10 @@
 //   S^T[32 tokens x 16]  = K_tile[32 x D] . Q^T[D x 16]      (the G heads padded to 16 columns)
 //   O^T[D x 16]         += V_tile^T[D x 32] . P^T[32 x 16]
 //
+// The same columns serve sequences that bring several new tokens (speculative verification, a prompt chunk):
+// G heads x QL rows, each column with its own causal limit, so K/V are still read once per (sequence, KV
+// head) however many of its tokens attend. Without grouping (G = 1) the columns are the QL rows alone.
+//
 // Loads. K and V rows are read from the pool with every wave-wide load covering kRows whole 256-byte head
 // rows (full cache lines, non-temporal: each row is read once per call); both go through a per-wave LDS slice
 // (rows padded by 16 bytes). Loading K straight into the MFMA operand layout instead (16 rows x 64 bytes per
@@ -96,8 +100,22 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   if (blockIdx.y > 0 && u0 >= L) return;
   const int u1 = min(L, u0 + span);
   const int G = a.group;
-  const int n = lane & 15;  // MFMA column: query head within the group (valid when n < G)
+  const int n = lane & 15;  // MFMA column
   const int j = lane >> 4;  // 0..3
+  // Column n = qi * G + hh is head g * G + hh of the sequence's query row qi: in decode the sequence has one
+  // row (qi = 0, n < G). With several new tokens per sequence, row qi of its QL rows attends causally over the
+  // first L - QL + qi + 1 positions, and the columns hold G heads of up to 16 / G rows.
+  int q0 = s, ql = 1;
+  if (a.query_start) {
+    q0 = a.query_start[s];
+    ql = min(max(a.query_start[s + 1] - q0, 0), a.max_query_len);
+  }
+  const int qi = n / G;
+  const int hh = n - qi * G;
+  const int qrow = q0 + qi;  // the column's query row
+  const bool head_ok = qi < ql && qrow < a.num_tokens;
+  const int lim = head_ok ? min(u1, L - ql + qi + 1) : u0;  // the column attends over positions < lim
+  const int ufull = min(u1, L - ql + 1);                     // every column attends over positions < ufull
   const int rr = lane / kRowLanes;  // loads: row within a wave-wide load
   const int rc = lane % kRowLanes;  //        16-byte chunk within the row
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
@@ -105,14 +123,14 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
   char* const kslice = lds + w * 2 * kSlice;
   char* const vslice = kslice + kSlice;
 
-  // Q^T (B operand of S^T = K Q^T): lane (n, j) holds q[g*G + n][32c + 8j .. 32c + 8j + 7]; padding heads are 0.
-  const bool head_ok = n < G;
-  const char* qrow = static_cast<const char*>(a.query) +
-                     ((int64_t)s * a.num_q_heads + (int64_t)g * G + (head_ok ? n : 0)) * D * 2;
+  // Q^T (B operand of S^T = K Q^T): lane (n, j) holds dims 32c + 8j .. 32c + 8j + 7 of its column's query
+  // row; padding columns are 0 (and read row 0, head 0, which exists whenever anything is launched).
+  const char* qptr = static_cast<const char*>(a.query) +
+                     (head_ok ? ((int64_t)qrow * a.num_q_heads + (int64_t)g * G + hh) * D * 2 : 0);
   U4 qb[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const U4 v = *reinterpret_cast<const U4*>(qrow + c * 64 + j * 16);
+    const U4 v = *reinterpret_cast<const U4*>(qptr + c * 64 + j * 16);
     qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
   }
 
@@ -206,17 +224,17 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
     float lt = lp + __shfl_xor(lp, 16);
     lt += __shfl_xor(lt, 32);
     if (!head_ok) return;
-    const int h = g * G + n;
+    const int h = g * G + hh;
     const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     float* dst;
     if (!a.split || L <= a.partition) {
-      dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
+      dst = a.out + ((int64_t)qrow * a.num_q_heads + h) * D;
     } else {
-      const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + p;
-      dst = a.ws_o + row * D;
+      const int64_t wrow = ((int64_t)qrow * a.num_q_heads + h) * a.max_partitions + p;
+      dst = a.ws_o + wrow * D;
       if (j == 0) {
-        a.ws_ml[2 * row] = bad ? poison : mp;
-        a.ws_ml[2 * row + 1] = lt;
+        a.ws_ml[2 * wrow] = bad ? poison : mp;
+        a.ws_ml[2 * wrow + 1] = lt;
       }
     }
 #pragma unroll
@@ -230,7 +248,7 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 
   auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
     const int t = u0 + tile * kTileTok;
-    const bool full = t + kTileTok <= u1;
+    const bool full = t + kTileTok <= ufull;  // no column masks a position of this tile
     // stage K and V (rows past the partition end were loaded as zeros); the previous tile's reads come first
     wave_lds_sync();
 #pragma unroll
@@ -263,7 +281,7 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = sc[h2][i] * a.scale_log2;
-        if (!full && t + h2 * kTile + 4 * j + i >= u1) x = -INFINITY;
+        if (!full && t + h2 * kTile + 4 * j + i >= lim) x = -INFINITY;
         sv[h2 * 4 + i] = x;
         mt = fmaxf(mt, x);
       }
@@ -323,9 +341,10 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 
 }  // namespace
 
-bool gqa_mfma_supported(int kv_dtype, int head_dim, int group) {
-  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && (head_dim == 128 || head_dim == 64) && group >= 2 &&
-         group <= 16;
+bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len) {
+  const int64_t columns = (int64_t)group * max_query_len;
+  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && (head_dim == 128 || head_dim == 64) &&
+         columns >= 2 && columns <= 16;
 }
 
 template <int KV, int D, int W>

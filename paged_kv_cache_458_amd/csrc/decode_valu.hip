@@ -130,13 +130,16 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int lane = threadIdx.x & (kWave - 1);
   const int h = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   const int part = blockIdx.y;
-  const int s = blockIdx.z;
+  const int row = blockIdx.z;  // query row: the sequence itself unless sequences bring several new tokens
   if (h >= a.num_q_heads) return;
+  const int s = seq_of_row(a, row);
 
+  // partitions cover the sequence's L positions; this row attends over the first E of them (E = L in decode)
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   const int t0 = part * a.partition;
   if (part > 0 && t0 >= L) return;  // this sequence has fewer partitions
-  const int t1 = min(L, t0 + a.partition);
+  const int E = row_extent(a, s, row, L);
+  const int t1 = max(t0, min(min(L, t0 + a.partition), E));
   const int g = h / a.group;
   const int r = lane / S::kRowLanes;  // row group
   const int c = lane % S::kRowLanes;  // 16-byte chunk of the head's row
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   Words<S::kQWords> q;
   {
-    const char* qp = static_cast<const char*>(a.query) + ((int64_t)s * a.num_q_heads + h) * D * S::kQEsize +
+    const char* qp = static_cast<const char*>(a.query) + ((int64_t)row * a.num_q_heads + h) * D * S::kQEsize +
                      (lane_ok ? c : 0) * 16 * S::kQWords;
 #pragma unroll
     for (int i = 0; i < S::kQWords; ++i) {
@@ -275,13 +278,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
     for (int e = 0; e < S::kEpl; ++e) res[e] = bad ? poison : acc[e] * inv;
     float* dst;
     if (!a.split || L <= a.partition) {
-      dst = a.out + ((int64_t)s * a.num_q_heads + h) * D + c * S::kEpl;
+      dst = a.out + ((int64_t)row * a.num_q_heads + h) * D + c * S::kEpl;
     } else {
-      const int64_t row = ((int64_t)s * a.num_q_heads + h) * a.max_partitions + part;
-      dst = a.ws_o + row * D + c * S::kEpl;
+      const int64_t wrow = ((int64_t)row * a.num_q_heads + h) * a.max_partitions + part;
+      dst = a.ws_o + wrow * D + c * S::kEpl;
       if (c == 0) {
-        a.ws_ml[2 * row] = bad ? poison : m;
-        a.ws_ml[2 * row + 1] = l;
+        a.ws_ml[2 * wrow] = bad ? poison : m;
+        a.ws_ml[2 * wrow + 1] = l;
       }
     }
 #pragma unroll
@@ -317,9 +320,10 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x;
   const bool lane_ok = lane < kActive;  // the other lanes read lane 0's dims and store nothing
   const int h = blockIdx.x;
-  const int s = blockIdx.y;
+  const int row = blockIdx.y;  // query row
+  const int s = seq_of_row(a, row);
   const int pm = a.max_partitions;
-  const int64_t row0 = ((int64_t)s * a.num_q_heads + h) * pm;
+  const int64_t row0 = ((int64_t)row * a.num_q_heads + h) * pm;
   const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
   const float* __restrict__ o = a.ws_o + row0 * D + (lane_ok ? lane : 0) * kDpl;
 
@@ -340,6 +344,8 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   float M = lane < np ? v0.x : -INFINITY;
   for (int p = lane + kWave; p < np; p += kWave) M = fmaxf(M, ml[p].x);
   M = wave_max(M);
+  // a row that attends over nothing (a new token with no earlier position) has only empty partials
+  const float Mr = M == -INFINITY ? 0.f : M;
   float acc[kDpl];
 #pragma unroll
   for (int e = 0; e < kDpl; ++e) acc[e] = 0.f;
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
     float w = 0.f;
     if (p0 + lane < np) {
       const float2 v = p0 == 0 ? v0 : ml[p0 + lane];
-      w = v.y * fast_exp2(v.x - M);
+      w = v.y * fast_exp2(v.x - Mr);
     }
     wsum += w;
     const int n = min(kWave, np - p0);
@@ -377,9 +383,10 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
       }
     }
   }
-  const float inv = 1.0f / wave_sum(wsum);
+  const float wtot = wave_sum(wsum);
+  const float inv = wtot > 0.f ? 1.0f / wtot : 0.f;
   if (!merge || !lane_ok) return;
-  float* dst = a.out + ((int64_t)s * a.num_q_heads + h) * D + lane * kDpl;
+  float* dst = a.out + ((int64_t)row * a.num_q_heads + h) * D + lane * kDpl;
 #pragma unroll
   for (int e = 0; e < kDpl; ++e) dst[e] = acc[e] * inv;
 }
@@ -403,7 +410,7 @@ hipError_t launch_kv(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t str
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.split ? a.max_partitions : 1,
-                  a.num_seqs);
+                  a.num_tokens);
   const dim3 block(kWave * kWavesPerGroup);
   if (kv_dtype == PA_BF16) return launch_kv<PA_BF16>(a, grid, block, stream);
   if (kv_dtype == PA_F32) return launch_kv<PA_F32>(a, grid, block, stream);
@@ -412,7 +419,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t str
 }
 
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_q_heads, a.num_seqs);
+  const dim3 grid(a.num_q_heads, a.num_tokens);
   const dim3 block(kWave);
   switch (a.head_dim) {
     case 64: lse_reduce_kernel<64><<<grid, block, 0, stream>>>(a); break;

@@ -36,6 +36,7 @@ struct Plan {
   int32_t max_partitions = 1;  // partitions of the longest context
   int32_t parts_per_wave = 1;  // consecutive partitions one wave covers
   bool split = false;
+  bool mfma = false;           // the matrix-core kernel runs (else the per-head one)
   size_t ws_bytes = 0;
   size_t ws_ml_offset = 0;
 };
@@ -46,11 +47,11 @@ struct Plan {
 // load is balanced. Measured on MI355X: 512 tokens for the single-head kernel, halved while its grid would
 // hold fewer than 4096 waves (two per wave slot), and 1024 for the grouped-query kernel, halved while its grid
 // would hold fewer than 2048 waves (one per slot: its waves run longest when they all start together).
-int32_t pick_partition(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
-                       bool gqa) {
+// `rows` counts the waves per partition: (sequence, KV head) pairs for the grouped-query kernel, (query row,
+// query head) pairs for the single-head one.
+int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa) {
   int32_t part = gqa ? 1024 : 512;
   const int64_t min_waves = gqa ? 2048 : 4096;
-  const int64_t rows = (int64_t)num_seqs * (gqa ? num_kv_heads : num_q_heads);
   while (part > 64 && rows * ((max_context_len + part - 1) / part) < min_waves) part /= 2;
   return max_context_len <= part ? 0 : part;
 }
@@ -62,11 +63,14 @@ int32_t gqa_parts_per_wave(int32_t partition) {
   return partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
 }
 
-Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-               int32_t max_context_len, int32_t kv_dtype, int32_t partition_size) {
+// num_tokens query rows (num_seqs in decode), at most max_query_len per sequence (1 in decode).
+Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+               int32_t partition_size) {
   Plan p;
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_context_len < 0 || num_q_heads % num_kv_heads != 0) {
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 1 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
+      (int64_t)num_tokens > (int64_t)num_seqs * max_query_len) {
     p.status = PA_ERR_SHAPE;
     return p;
   }
@@ -77,7 +81,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
   // a 16-row tile is addressed through one buffer descriptor, whose size field is a signed 32-bit count
   const int64_t tile_bytes = (int64_t)kTileTokens * num_kv_heads * head_dim * esize_of(kv_dtype);
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size) || num_seqs > kMaxGridYZ ||
-      tile_bytes > INT32_MAX) {
+      num_tokens > kMaxGridYZ || tile_bytes > INT32_MAX) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
@@ -91,10 +95,10 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
     p.status = PA_ERR_SHAPE;
     return p;
   }
-  const bool gqa = num_q_heads > num_kv_heads && pa::gqa_mfma_supported(kv_dtype, head_dim,
-                                                                       num_q_heads / num_kv_heads);
-  int32_t part = partition_size == -1 ? pick_partition(num_seqs, num_q_heads, num_kv_heads, max_context_len, gqa)
-                                      : partition_size;
+  const bool gqa = pa::gqa_mfma_supported(kv_dtype, head_dim, num_q_heads / num_kv_heads, max_query_len);
+  p.mfma = gqa;
+  const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads : (int64_t)num_tokens * num_q_heads;
+  int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
   if (part == 0 || part >= whole) {
     p.partition = (int32_t)(whole > INT32_MAX ? INT32_MAX : whole);
@@ -111,9 +115,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
   p.max_partitions = (int32_t)pm;
   p.parts_per_wave = gqa ? gqa_parts_per_wave(part) : 1;
   p.split = true;
-  const size_t o_bytes = pa::ws_o_elems(num_seqs, num_q_heads, pm, head_dim) * sizeof(float);
+  const size_t o_bytes = pa::ws_o_elems(num_tokens, num_q_heads, pm, head_dim) * sizeof(float);
   p.ws_ml_offset = round_up(o_bytes, 256);
-  p.ws_bytes = p.ws_ml_offset + pa::ws_ml_elems(num_seqs, num_q_heads, pm) * sizeof(float);
+  p.ws_bytes = p.ws_ml_offset + pa::ws_ml_elems(num_tokens, num_q_heads, pm) * sizeof(float);
   return p;
 }
 
@@ -140,8 +144,8 @@ const char* pa_strerror(int status) {
 int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t kv_dtype, int32_t partition_size) {
-  const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
-                           partition_size);
+  const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, kv_dtype, partition_size);
   if (p.status != PA_OK) return p.status;
   return p.split ? p.partition : 0;
 }
@@ -149,8 +153,27 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t kv_dtype, int32_t partition_size) {
-  const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
-                           partition_size);
+  const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, kv_dtype, partition_size);
+  return p.status == PA_OK ? p.ws_bytes : 0;
+}
+
+int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t partition_size) {
+  const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                           block_size, max_context_len, kv_dtype, partition_size);
+  if (p.status != PA_OK) return p.status;
+  return p.split ? p.partition : 0;
+}
+
+size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t partition_size) {
+  const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                           block_size, max_context_len, kv_dtype, partition_size);
   return p.status == PA_OK ? p.ws_bytes : 0;
 }
 
@@ -167,15 +190,19 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
                                        workspace, workspace_bytes, stream);
 }
 
-int paged_attention_decode_scaled(float* out, const void* query, const void* key_cache, const void* value_cache,
-                                  const int32_t* block_tables, const int32_t* context_lens, float scale,
-                                  float k_scale, float v_scale, int32_t block_size, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
-                                  int32_t kv_dtype, int32_t partition_size, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                              kv_dtype, partition_size);
+}  // extern "C"
+
+namespace {
+
+// Shared by the decode and multi-token entry points: query_start == nullptr means one query row per sequence.
+int attention(float* out, const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start, float scale,
+              float k_scale, float v_scale, int32_t block_size, int32_t num_seqs, int32_t num_tokens,
+              int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+              int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  const Plan plan = make_plan(num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                              block_size, max_context_len, kv_dtype, partition_size);
   if (plan.status != PA_OK) return plan.status;
   const bool pair_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) || (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
@@ -184,10 +211,10 @@ int paged_attention_decode_scaled(float* out, const void* query, const void* key
   if (num_blocks <= 0 || num_blocks > INT32_MAX || max_blocks_per_seq <= 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return PA_ERR_SHAPE;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
-      !aligned4(block_tables) || !aligned4(context_lens))
+      !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start))
     return PA_ERR_ALIGN;
   if (plan.split) {
     if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE;
@@ -201,6 +228,7 @@ int paged_attention_decode_scaled(float* out, const void* query, const void* key
   a.value_cache = value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.query_start = query_start;
   a.ws_o = plan.split ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = plan.split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
   a.scale_log2 = scale * k_scale * 1.4426950408889634f;
@@ -218,16 +246,46 @@ int paged_attention_decode_scaled(float* out, const void* query, const void* key
   a.max_partitions = plan.max_partitions;
   a.parts_per_wave = plan.parts_per_wave;
   a.split = plan.split ? 1 : 0;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (a.group > 1 && pa::gqa_mfma_supported(kv_dtype, head_dim, a.group))
-    err = pa::launch_decode_gqa_mfma(a, kv_dtype, st);
-  else
-    err = pa::launch_decode_valu(a, kv_dtype, st);
+  const hipError_t err = plan.mfma ? pa::launch_decode_gqa_mfma(a, kv_dtype, st) : pa::launch_decode_valu(a, kv_dtype, st);
   if (err != hipSuccess) return PA_ERR_HIP;
   if (plan.split && pa::launch_lse_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode_scaled(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                  float k_scale, float v_scale, int32_t block_size, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+                                  int32_t kv_dtype, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr, scale, k_scale, v_scale,
+                   block_size, num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                   max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size, workspace,
+                   workspace_bytes, stream);
+}
+
+int paged_attention_decode_multi(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start, float scale, float k_scale, float v_scale,
+                                 int32_t block_size, int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 int32_t q_dtype, int32_t kv_dtype, int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && num_query_tokens > 0 && !query_start) return PA_ERR_NULL;
+  return attention(out, query, key_cache, value_cache, block_tables, context_lens, query_start, scale, k_scale,
+                   v_scale, block_size, num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads,
+                   head_dim, num_blocks, max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size,
+                   workspace, workspace_bytes, stream);
 }
 
 int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,

@@ -7,14 +7,15 @@
 namespace pa {
 
 struct DecodeArgs {
-  float* out;                  // [B][Hq][D]
-  const void* query;           // [B][Hq][D]
+  float* out;                  // [T][Hq][D], T query rows (T = B: one new token per sequence)
+  const void* query;           // [T][Hq][D]
   const void* key_cache;       // [NB][bs][Hkv][D]
   const void* value_cache;     // [NB][bs][Hkv][D]
   const int32_t* block_tables; // [B][MB]
   const int32_t* context_lens; // [B]
-  float* ws_o;                 // [B][Hq][PM][D]  normalised partial outputs      (split only)
-  float* ws_ml;                // [B][Hq][PM][2]  (running max in log2 units, sum) (split only)
+  const int32_t* query_start;  // [B + 1] first query row of each sequence, or null: row s is sequence s
+  float* ws_o;                 // [T][Hq][PM][D]  normalised partial outputs      (split only)
+  float* ws_ml;                // [T][Hq][PM][2]  (running max in log2 units, sum) (split only)
   float scale_log2;            // scale * k_scale * log2(e): scores live in the exp2 domain
   float v_scale;               // multiplies every output row (1 unless the cache is quantised)
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, group;
@@ -25,15 +26,40 @@ struct DecodeArgs {
   int32_t max_partitions;      // PM
   int32_t parts_per_wave;      // consecutive partitions one wave covers (GQA kernel; the others take 1)
   int32_t split;               // 0: every sequence is one partition, written straight to out
+  int32_t num_tokens;          // T
+  int32_t max_query_len;       // query rows per sequence at most (1 without query_start)
 };
 
+// The sequence that owns query row t: the last s with query_start[s] <= t (a scalar binary search; empty
+// sequences are skipped since the next start equals theirs).
+__device__ __forceinline__ int seq_of_row(const DecodeArgs& a, int t) {
+  if (!a.query_start) return t;
+  int lo = 0, hi = a.num_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.query_start[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Positions that query row t of sequence s (length L) attends over: all L for decode; for row j of the
+// sequence's QL rows, its causal prefix of L - QL + j + 1 positions (none when that is not positive).
+__device__ __forceinline__ int row_extent(const DecodeArgs& a, int s, int t, int L) {
+  if (!a.query_start) return L;
+  const int q0 = a.query_start[s];
+  const int ql = a.query_start[s + 1] - q0;
+  return max(0, min(L, L - ql + (t - q0) + 1));
+}
+
 // Workspace layout for a split launch: partial outputs first, then the (max, sum) pairs.
-inline size_t ws_o_elems(int64_t B, int64_t Hq, int64_t PM, int64_t D) { return B * Hq * PM * D; }
-inline size_t ws_ml_elems(int64_t B, int64_t Hq, int64_t PM) { return B * Hq * PM * 2; }
+inline size_t ws_o_elems(int64_t T, int64_t Hq, int64_t PM, int64_t D) { return T * Hq * PM * D; }
+inline size_t ws_ml_elems(int64_t T, int64_t Hq, int64_t PM) { return T * Hq * PM * 2; }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
-bool gqa_mfma_supported(int kv_dtype, int head_dim, int group);
+// The matrix-core kernel takes a (sequence, KV head) whose group x query rows fit its 16 columns.
+bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len);
 constexpr int kGqaTileTokens = 32;  // tokens per tile of the GQA kernel
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
 

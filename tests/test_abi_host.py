@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     assert {"paged_attention_decode", "reshape_and_cache", "copy_blocks", "paged_gather",
             "paged_attention_workspace_bytes", "paged_attention_partition_size", "pa_strerror",
             "pa_abi_version", "pa_stream_read", "pa_stream_copy", "pa_bm_create", "pa_bm_append_slots",
-            "paged_attention_decode_scaled", "reshape_and_cache_fp8"} <= set(names)
+            "paged_attention_decode_scaled", "reshape_and_cache_fp8", "paged_attention_decode_multi",
+            "paged_attention_multi_workspace_bytes", "paged_attention_multi_partition_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert lib.pa_abi_version() == pa.ABI_VERSION
@@ -102,6 +103,44 @@ def scaled_call(**over):
 ])
 def test_scaled_decode_rejects_before_launch(over, status):
     assert scaled_call(**over) == status
+
+
+def multi_call(**over):
+    args = dict(out=FAKE, query=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE, context_lens=FAKE,
+                query_start=FAKE, scale=0.1, k_scale=1.0, v_scale=1.0, block_size=16, num_seqs=4,
+                num_query_tokens=10, max_query_len=4, num_q_heads=8, num_kv_heads=2, head_dim=128, num_blocks=100,
+                max_blocks_per_seq=8, max_context_len=128, q_dtype=pa.PA_BF16, kv_dtype=pa.PA_BF16,
+                partition_size=0, workspace=None, workspace_bytes=0, stream=None)
+    args.update(over)
+    return pa.load_library().paged_attention_decode_multi(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(query_start=None), PA_ERR_NULL),
+    (dict(query_start=FAKE + 2), PA_ERR_ALIGN),
+    (dict(num_query_tokens=17), PA_ERR_SHAPE),  # more rows than num_seqs * max_query_len
+    (dict(max_query_len=0), PA_ERR_SHAPE),
+    (dict(num_query_tokens=-1), PA_ERR_SHAPE),
+    (dict(num_query_tokens=70000, num_seqs=20000), PA_ERR_UNSUPPORTED),
+    (dict(q_dtype=pa.PA_F32), PA_ERR_DTYPE),
+    (dict(partition_size=32), PA_ERR_WORKSPACE),
+])
+def test_multi_rejects_before_launch(over, status):
+    assert multi_call(**over) == status
+
+
+def test_multi_no_rows_is_a_no_op_and_plans_match_decode():
+    assert multi_call(num_query_tokens=0, out=None, query=None, query_start=None) == 0
+    # one row per sequence plans exactly like decode
+    for args in ((64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1), (64, 64, 8, 128, 256, 4096, pa.PA_BF16, 512)):
+        B, Hq, Hkv, D, bs, L, kd, part = args
+        assert pa.multi_workspace_bytes(B, B, 1, Hq, Hkv, D, bs, L, kd, part) == pa.workspace_bytes(*args)
+        assert pa.multi_partition_size_for(B, B, 1, Hq, Hkv, D, bs, L, kd, part) == pa.partition_size_for(*args)
+    # the workspace holds one partial per query row
+    B, T = 8, 24
+    w = pa.multi_workspace_bytes(B, T, 3, 8, 2, 64, 16, 4096, pa.PA_BF16, 512)
+    pm = 4096 // 512
+    assert w == (T * 8 * pm * 64 * 4 + 255) // 256 * 256 + T * 8 * pm * 2 * 4
 
 
 def test_unscaled_decode_refuses_an_fp8_cache():

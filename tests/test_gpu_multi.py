@@ -1,0 +1,122 @@
+"""GPU parity for several new tokens per sequence (speculative verification, page 1 section 6; a prompt
+chunk): paged_attention_decode_multi through the C ABI against oracle.decode_multi on the same seeded inputs.
+
+Row j of a sequence's QL new tokens attends causally over its first L - QL + j + 1 positions. Grouped heads x
+QL <= 16 runs on the matrix-core kernel (one K/V read per sequence and KV head for all its rows); the other
+shapes take the per-head kernel, one wave per (row, head). Tolerances as for decode: 1e-5 for fp32, 2e-3 +
+1e-2 |ref| for bf16 or E4M3 caches under a bf16 query.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_458_amd as pa
+from tests._host import to_host
+from workloads import build_structure, custom_structure, materialize, query_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def close(gpu, ref, dtype, what=""):
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    err = np.abs(gpu.astype(np.float64) - ref)
+    bad = err > (1e-5 if dtype == "f32" else 2e-3 + 1e-2 * np.abs(ref))
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {err.max():.3e}"
+    return float(err.max())
+
+
+def run_multi(st, t, q, qs, partition, tables=None):
+    T = q.shape[0]
+    out = torch.full((T, st.num_q_heads, st.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+    pa.paged_attention_decode_multi(out, q, t["key_cache"], t["value_cache"],
+                                    dev_i32(st.block_tables_pre if tables is None else tables),
+                                    dev_i32(st.context_lens), dev_i32(qs), st.scale,
+                                    max_query_len=int(np.diff(qs).max()), max_context_len=st.max_context_len,
+                                    partition_size=partition, k_scale=st.k_scale, v_scale=st.v_scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_multi(st, h, q_host, qs, rows=None):
+    return oracle.decode_multi(q_host, h["key_cache"], h["value_cache"], st.block_tables_pre, st.context_lens, qs,
+                               st.scale, rows=rows, k_scale=st.k_scale, v_scale=st.v_scale)
+
+
+CASES = [
+    # (seed, lens, query lens, Hq, Hkv, D, bs, dtype) -- matrix-core kernel: G * max QL <= 16
+    (501, [40, 300, 1030, 7], [4, 1, 3, 4], 16, 4, 128, 16, "bf16"),   # G 4 x QL 4 = 16 columns
+    (502, [100, 513, 64, 2], [8, 5, 2, 5], 8, 8, 128, 16, "bf16"),     # no grouping: QL rows are the columns
+    (503, [700, 45, 3, 260], [2, 2, 0, 1], 32, 4, 128, 8, "fp8"),      # G 8 x QL 2; an empty sequence; bs 8
+    # per-head kernel
+    (504, [90, 1200, 33], [8, 6, 33], 4, 2, 64, 32, "bf16"),           # QL = L for the last sequence; 2 x 33 > 16
+    (505, [65, 200, 9], [3, 7, 2], 8, 2, 96, 16, "bf16"),              # head_dim 96
+    (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
+    (507, [520, 47, 300], [4, 3, 2], 64, 8, 128, 256, "bf16"),         # G 8 x QL 4 = 32 columns
+    (508, [5, 40, 18], [9, 2, 18], 16, 4, 128, 16, "fp8"),             # QL > L: the first rows are zero
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"seed{c[0]}" for c in CASES])
+def test_multi_parity(case):
+    seed, lens, qls, hq, hkv, d, bs, dt = case
+    st = custom_structure(f"m{seed}", seed, lens, hq, hkv, d, bs, dt, pool_factor=1.3)
+    t = materialize(st, DEV)
+    q, qs = query_rows(st, qls, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    ref = oracle_multi(st, h, to_host(q), qs)
+    for part in (0, 16, 32, 64, 96, 512, -1):
+        gpu = run_multi(st, t, q, qs, part)
+        close(gpu, ref, dt, f"partition {part}")
+    if seed == 508:  # rows with no earlier position are exact zeros
+        assert (gpu[:4] == 0).all() and np.abs(gpu[4]).max() > 0
+
+
+@pytest.mark.parametrize("hq,hkv,dt", [(8, 8, "bf16"), (16, 2, "bf16"), (32, 8, "fp8"), (4, 4, "f32")])
+def test_one_row_per_sequence_is_decode(hq, hkv, dt):
+    st = custom_structure("m1", 511, [700, 33, 1500, 260, 1], hq, hkv, 128, 16, dt)
+    t = materialize(st, DEV)
+    qs = np.arange(st.num_seqs + 1, dtype=np.int32)
+    for part in (0, 64, -1):
+        a = run_multi(st, t, t["query"], qs, part)
+        out = torch.empty_like(torch.from_numpy(a)).to(DEV)
+        pa.paged_attention_decode(out, t["query"], t["key_cache"], t["value_cache"], dev_i32(st.block_tables_pre),
+                                  dev_i32(st.context_lens), st.scale, max_context_len=st.max_context_len,
+                                  partition_size=part, k_scale=st.k_scale, v_scale=st.v_scale)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(a, out.cpu().numpy())
+
+
+@pytest.mark.parametrize("name,ql", [("llama2_7b", 4), ("llama2_70b_gqa", 2)])
+def test_full_size_verification_batch(name, ql):
+    # every sequence of the workload verifies ql draft tokens: its last ql positions are the query rows
+    st = build_structure(name)
+    t = materialize(st, DEV)
+    q, qs = query_rows(st, np.full(st.num_seqs, ql), DEV)
+    gpu = run_multi(st, t, q, qs, st.partition_size)
+    h = {k: to_host(v) for k, v in t.items()}
+    rng = np.random.default_rng(512)
+    rows = np.stack([rng.integers(0, q.shape[0], 600), rng.integers(0, st.num_q_heads, 600)], 1)
+    rows = np.concatenate([rows, [[0, 0], [q.shape[0] - 1, st.num_q_heads - 1]]]).astype(np.int32)
+    ref = oracle_multi(st, h, to_host(q), qs, rows=rows)
+    err = close(gpu[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], st.dtype, name)
+    sys.__stderr__.write(f"[{name} x {ql}] max abs err {err:.3e} over {len(rows)} sampled rows\n")
+    assert np.isfinite(gpu).all()
