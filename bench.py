@@ -84,7 +84,8 @@ def _counter_means(db: str, counter: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
-def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch: str, cmd_write: str) -> str:
+def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch: str, cmd_write: str,
+                          query_len: int = 1) -> str:
     """Turn the FETCH_SIZE and WRITE_SIZE runs of this benchmark into bytes per attention call.
 
     Each counter is scaled by what it reads for the streaming copy kernel, whose traffic is known exactly
@@ -109,8 +110,9 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
         rows.append((kf, fetch[kf][1], fetch[kf][0], write[kw][0], f, w))
     from workloads import algorithmic_bytes, build_structure
 
-    alg = algorithmic_bytes(build_structure(workload))["total"]
-    lines = [f"# HBM traffic per attention call: {workload}", "",
+    alg = algorithmic_bytes(build_structure(workload), query_len)["total"]
+    label = workload if query_len == 1 else f"{workload}_q{query_len}"
+    lines = [f"# HBM traffic per attention call: {label}", "",
              "Two counter runs of the benchmark (run from the repository root on one MI355X):", "", "```",
              cmd_fetch, cmd_write, "```", "",
              f"Calibration: the streaming copy kernel moves {COPY_BYTES} B each way per dispatch; it reads "
@@ -124,7 +126,7 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
               TRAFFIC_TAG + json.dumps({"kernel_source_hash": kernel_source_hash(), "fetch_bytes_per_call": round(fb),
                                         "write_bytes_per_call": round(wb), "bytes_per_call": round(fb + wb),
                                         "algorithmic_bytes": alg}) + " -->"]
-    path = traffic_path(workload)
+    path = traffic_path(label)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -260,6 +262,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--query-len", type=int, default=1,
+                    help="new tokens per sequence (> 1: a verification batch through paged_attention_decode_multi)")
     ap.add_argument("--replicas", type=int, default=2, help="pool replicas cycled by consecutive steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle timing budget (0 = skip)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -269,7 +273,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.traffic_from:
-        print(write_traffic_summary(args.workload, *args.traffic_from, *args.traffic_cmds))
+        print(write_traffic_summary(args.workload, *args.traffic_from, *args.traffic_cmds,
+                                    query_len=args.query_len))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -282,7 +287,7 @@ def main() -> int:
     import torch
 
     import paged_kv_cache_458_amd as pa
-    from workloads import CONFIG_NAMES, algorithmic_bytes, build_structure, materialize
+    from workloads import CONFIG_NAMES, algorithmic_bytes, build_structure, materialize, query_rows
 
     if args.workload == "decode_loop":
         return run_decode_loop(args)
@@ -296,7 +301,15 @@ def main() -> int:
     part = st.partition_size if args.partition_size is None else args.partition_size
     B, Hq, Hkv, D, bs = st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size
     kv_code = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
-    launched_part = pa.partition_size_for(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+    Q = args.query_len
+    if Q < 1 or (st.context_lens < Q).any():
+        ap.error("--query-len must be >= 1 and at most every context length")
+    T = B * Q  # query rows
+    label = args.workload if Q == 1 else f"{args.workload}_q{Q}"
+    if Q == 1:
+        launched_part = pa.partition_size_for(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+    else:
+        launched_part = pa.multi_partition_size_for(B, T, Q, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
 
     t = materialize(st, dev, include_new_token=False)
     pools = [(t["key_cache"], t["value_cache"])]
@@ -309,8 +322,26 @@ def main() -> int:
 
     tables, lens, slots = i32(st.block_tables), i32(st.context_lens), i32(st.slot_mapping)
     pairs = i32(st.copy_pairs) if len(st.copy_pairs) else None
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    ws_bytes = pa.workspace_bytes(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    query, new_key, new_value = t["query"], t["new_key"], t["new_value"]
+    if Q > 1:
+        # a verification batch: each sequence's last Q positions are new; their K/V are written, then all Q
+        # rows attend (host-side slot list of those positions, prepared outside the timed region)
+        query, query_start = query_rows(st, np.full(B, Q), dev)
+        qstart = i32(query_start)
+        pos = (st.context_lens[:, None].astype(np.int64) - Q + np.arange(Q)[None, :]).reshape(-1)
+        seq = np.repeat(np.arange(B), Q)
+        if (pos // bs < st.notes.get("shared_prefix_blocks", 0)).any():
+            ap.error("--query-len reaches into the shared prefix blocks")
+        slots = i32(st.block_tables[seq, pos // bs].astype(np.int64) * bs + pos % bs)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(st.seed + 104729)
+        kdt = torch.float32 if st.dtype == "f32" else torch.bfloat16
+        new_key = torch.randn((T, Hkv, D), generator=gen, device=dev).to(kdt)
+        new_value = torch.randn((T, Hkv, D), generator=gen, device=dev).to(kdt)
+        ws_bytes = pa.multi_workspace_bytes(B, T, Q, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+    else:
+        ws_bytes = pa.workspace_bytes(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -318,12 +349,17 @@ def main() -> int:
         kc, vc = pools[i % len(pools)]
         if pairs is not None:
             pa.copy_blocks(kc, vc, pairs)
-        pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots, k_scale=st.k_scale, v_scale=st.v_scale)
+        pa.reshape_and_cache(new_key, new_value, kc, vc, slots, k_scale=st.k_scale, v_scale=st.v_scale)
         if ev is not None:
             ev[0].record(stream)
-        pa.paged_attention_decode(out, t["query"], kc, vc, tables, lens, st.scale, bs,
-                                  max_context_len=st.max_context_len, partition_size=part, workspace=ws,
-                                  k_scale=st.k_scale, v_scale=st.v_scale)
+        if Q == 1:
+            pa.paged_attention_decode(out, query, kc, vc, tables, lens, st.scale, bs,
+                                      max_context_len=st.max_context_len, partition_size=part, workspace=ws,
+                                      k_scale=st.k_scale, v_scale=st.v_scale)
+        else:
+            pa.paged_attention_decode_multi(out, query, kc, vc, tables, lens, qstart, st.scale, max_query_len=Q,
+                                            max_context_len=st.max_context_len, partition_size=part,
+                                            workspace=ws, k_scale=st.k_scale, v_scale=st.v_scale)
         if ev is not None:
             ev[1].record(stream)
 
@@ -368,15 +404,16 @@ def main() -> int:
     del big, big2
     log(f"streaming read {read_gbs:.0f} GB/s, copy {copy_gbs:.0f} GB/s (read + write)")
 
-    ab = algorithmic_bytes(st)
+    ab = algorithmic_bytes(st, Q)
     row_bytes = Hkv * D * st.esize
     # K and V: read the new row (query dtype), write it into the cache (cache dtype)
-    cache_write_bytes = 2 * int((st.slot_mapping >= 0).sum()) * Hkv * D * (st.q_esize + st.esize)
+    new_rows = int((st.slot_mapping >= 0).sum()) if Q == 1 else T
+    cache_write_bytes = 2 * new_rows * Hkv * D * (st.q_esize + st.esize)
     copy_bytes = 2 * 2 * len(st.copy_pairs) * bs * row_bytes
     step_bytes = ab["total"] + cache_write_bytes + copy_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     attn_gbs = ab["total"] / (attn_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(label)
 
     rec = {
         "metric": METRIC,
@@ -394,8 +431,9 @@ def main() -> int:
         "accumulate": "f32",
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": label,
             "num_seqs": B,
+            "query_len": Q,
             "num_q_heads": Hq,
             "num_kv_heads": Hkv,
             "head_dim": D,
@@ -409,13 +447,13 @@ def main() -> int:
             "seed": st.seed,
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "decode_queries_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_queries_per_s": round(T / (ms_step * 1e-3), 1),  # query rows (tokens), B * query_len
         "attention": {
             "us_mean": round(attn_avg_ms * 1e3, 2),
             "us_median": round(float(np.median(attn_ms)) * 1e3, 2),
             "us_min": round(float(np.min(attn_ms)) * 1e3, 2),
             "gb_per_s": round(attn_gbs, 1),
-            "queries_per_s": round(B / (attn_avg_ms * 1e-3), 1),
+            "queries_per_s": round(T / (attn_avg_ms * 1e-3), 1),
             "bytes_per_call": ab["total"],
             "kv_unique_bytes": ab["kv_unique"],
         },
@@ -424,7 +462,8 @@ def main() -> int:
         "device_stream_copy_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (partition kernel + log-sum-exp reduce when split)",
+            "kernel": ("paged_attention_decode" if Q == 1 else "paged_attention_decode_multi") +
+                      " (partition kernel + log-sum-exp reduce when split)",
             "achieved": round(attn_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -439,7 +478,7 @@ def main() -> int:
 
         kc, vc = pools[0]
         host = {}
-        for name, tt in (("query", t["query"]), ("key_cache", kc), ("value_cache", vc)):
+        for name, tt in (("query", query), ("key_cache", kc), ("value_cache", vc)):
             tt = tt.contiguous().cpu()
             if tt.dtype == torch.bfloat16:
                 host[name] = tt.view(torch.int16).numpy().view(np.uint16)
@@ -450,20 +489,25 @@ def main() -> int:
         lib = oracle.load()
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.decode(host["query"], host["key_cache"], host["value_cache"], st.block_tables, st.context_lens,
-                          st.scale, k_scale=st.k_scale, v_scale=st.v_scale, lib=lib)
+            if Q == 1:
+                oracle.decode(host["query"], host["key_cache"], host["value_cache"], st.block_tables,
+                              st.context_lens, st.scale, k_scale=st.k_scale, v_scale=st.v_scale, lib=lib)
+            else:
+                oracle.decode_multi(host["query"], host["key_cache"], host["value_cache"], st.block_tables,
+                                    st.context_lens, query_start, st.scale, k_scale=st.k_scale, v_scale=st.v_scale,
+                                    lib=lib)
             reps += 1
             el = time.perf_counter() - t0
             log(f"cpu oracle call {reps}: {el:.1f} s")
             if el >= args.cpu_seconds or reps >= 1000:
                 break
         rec["cpu_baseline"] = {
-            "value": round(B * reps / el, 2),
+            "value": round(T * reps / el, 2),
             "unit": "decode queries/s",
             "gb_per_s": round(ab["total"] * reps / el / 1e9, 3),
             "cores": oracle.num_threads(lib),
             "kind": "oracle",
-            "sample": f"the whole {args.workload} batch ({B} sequences x {Hq} heads, fp64 C oracle with OpenMP), "
+            "sample": f"the whole {label} batch ({T} query rows x {Hq} heads, fp64 C oracle with OpenMP), "
                       f"{reps} call(s) in {el:.1f} s",
         }
     print(json.dumps(rec), flush=True)

@@ -143,9 +143,9 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
  *   query_start    int32 [num_seqs + 1] device array: query_start[0] = 0, non-decreasing, last entry
  *                  num_query_tokens, every difference <= max_query_len (rows beyond max_query_len are left
  *                  unwritten; the contents are not checked on the host)
- *   max_query_len  the largest QL (>= 1). Grouped heads x max_query_len <= 16 runs all of a sequence's rows on
- *                  the matrix cores with one read of its K/V (bf16 or E4M3 caches at head_dim 64 or 128); other
- *                  calls read a sequence's K/V once per row.
+ *   max_query_len  the largest QL (>= 1). With bf16 or E4M3 caches at head_dim 64 or 128 the matrix cores take
+ *                  all of a sequence's rows, reading its K/V once per 16 (row, grouped head) columns (at most
+ *                  1024 columns); other calls read a sequence's K/V once per (row, head).
  *   workspace      at least paged_attention_multi_workspace_bytes(...) bytes when that is non-zero
  * Other arguments as in paged_attention_decode_scaled. num_seqs == 0 or num_query_tokens == 0 is a no-op;
  * num_query_tokens > num_seqs * max_query_len is PA_ERR_SHAPE.

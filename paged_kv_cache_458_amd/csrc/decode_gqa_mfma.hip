@@ -9,7 +9,8 @@
 //
 // The same columns serve sequences that bring several new tokens (speculative verification, a prompt chunk):
 // G heads x QL rows, each column with its own causal limit, so K/V are still read once per (sequence, KV
-// head) however many of its tokens attend. Without grouping (G = 1) the columns are the QL rows alone.
+// head) however many of its tokens attend. Without grouping (G = 1) the columns are the QL rows alone. More
+// than 16 columns run as column groups of 16 in waves of their own, each reading the K/V again.
 //
 // Loads. K and V rows are read from the pool with every wave-wide load covering kRows whole 256-byte head
 // rows (full cache lines, non-temporal: each row is read once per call); both go through a per-wave LDS slice
@@ -88,16 +89,35 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
-  const int g = blockIdx.x * W + w;
-  const int s = blockIdx.z;
+  // Work item (KV-head group, partition group, sequence) and column group cg (columns 16 cg .. 16 cg + 15).
+  // With one column group the grid indexes the item directly. With several, the groups of one item read the
+  // same K/V, so they are given workgroup ids 8 apart -- ids are dispatched in order and round-robin over the
+  // 8 XCDs, so those run back to back on one XCD and the later ones find the K/V in its L2.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z, cg = 0;
+  if (a.col_groups > 1) {
+    const int ncg = a.col_groups;
+    const int nkvg = gridDim.x / ncg;
+    const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t items = (int64_t)nkvg * gridDim.y * gridDim.z;
+    const int64_t base = lin / (8 * ncg) * 8;          // first item of this run of 8 x ncg workgroups
+    const int64_t width = min<int64_t>(8, items - base);  // items in the run (fewer in the last one)
+    const int64_t r = lin - base * ncg;
+    cg = (int)(r / width);
+    const int64_t u = base + r % width;
+    bx = (int)(u % nkvg);
+    by = (int)(u / nkvg % gridDim.y);
+    bz = (int)(u / ((int64_t)nkvg * gridDim.y));
+  }
+  const int g = bx * W + w;
+  const int s = bz;
   if (g >= a.num_kv_heads) return;  // no workgroup barriers below: each wave owns its LDS slice
 
   // The wave covers parts_per_wave (1 or 2) consecutive partitions, [u0, u1), in one load pipeline and leaves
   // one partial result per partition (partition boundaries fall on 32-token tiles whenever parts_per_wave is 2).
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   const int span = a.partition * a.parts_per_wave;
-  const int u0 = blockIdx.y * span;
-  if (blockIdx.y > 0 && u0 >= L) return;
+  const int u0 = by * span;
+  if (by > 0 && u0 >= L) return;
   const int u1 = min(L, u0 + span);
   const int G = a.group;
   const int n = lane & 15;  // MFMA column
@@ -110,8 +130,9 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
     q0 = a.query_start[s];
     ql = min(max(a.query_start[s + 1] - q0, 0), a.max_query_len);
   }
-  const int qi = n / G;
-  const int hh = n - qi * G;
+  const int col = cg * 16 + n;
+  const int qi = col / G;
+  const int hh = col - qi * G;
   const int qrow = q0 + qi;  // the column's query row
   const bool head_ok = qi < ql && qrow < a.num_tokens;
   const int lim = head_ok ? min(u1, L - ql + qi + 1) : u0;  // the column attends over positions < lim
@@ -344,13 +365,14 @@ __global__ __launch_bounds__(kWave * W) void decode_gqa_mfma_kernel(const Decode
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len) {
   const int64_t columns = (int64_t)group * max_query_len;
   return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && (head_dim == 128 || head_dim == 64) &&
-         columns >= 2 && columns <= 16;
+         columns >= 2 && columns <= 16 * kMaxColGroups;
 }
 
 template <int KV, int D, int W>
 hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
   const int groups = a.split ? (a.max_partitions + a.parts_per_wave - 1) / a.parts_per_wave : 1;
-  const dim3 grid((a.num_kv_heads + W - 1) / W, groups, a.num_seqs);
+  // column groups share the x dimension with the KV-head groups (the kernel unpacks them)
+  const dim3 grid((a.num_kv_heads + W - 1) / W * a.col_groups, groups, a.num_seqs);
   decode_gqa_mfma_kernel<KV, D, W><<<grid, dim3(kWave * W), 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -37,6 +37,7 @@ struct Plan {
   int32_t parts_per_wave = 1;  // consecutive partitions one wave covers
   bool split = false;
   bool mfma = false;           // the matrix-core kernel runs (else the per-head one)
+  int32_t col_groups = 1;      // its column groups of 16 per KV head
   size_t ws_bytes = 0;
   size_t ws_ml_offset = 0;
 };
@@ -97,7 +98,12 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   }
   const bool gqa = pa::gqa_mfma_supported(kv_dtype, head_dim, num_q_heads / num_kv_heads, max_query_len);
   p.mfma = gqa;
-  const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads : (int64_t)num_tokens * num_q_heads;
+  p.col_groups = gqa ? (num_q_heads / num_kv_heads * max_query_len + 15) / 16 : 1;
+  if ((int64_t)(num_kv_heads + 7) / 8 * p.col_groups > INT32_MAX) {
+    p.status = PA_ERR_UNSUPPORTED;
+    return p;
+  }
+  const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * p.col_groups : (int64_t)num_tokens * num_q_heads;
   int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
   if (part == 0 || part >= whole) {
@@ -248,6 +254,7 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   a.split = plan.split ? 1 : 0;
   a.num_tokens = num_tokens;
   a.max_query_len = max_query_len;
+  a.col_groups = plan.col_groups;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = plan.mfma ? pa::launch_decode_gqa_mfma(a, kv_dtype, st) : pa::launch_decode_valu(a, kv_dtype, st);

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int32_t split;               // 0: every sequence is one partition, written straight to out
   int32_t num_tokens;          // T
   int32_t max_query_len;       // query rows per sequence at most (1 without query_start)
+  int32_t col_groups;          // matrix-core kernel: groups of 16 (query row, head) columns per KV head
 };
 
 // The sequence that owns query row t: the last s with query_start[s] <= t (a scalar binary search; empty
@@ -58,7 +59,9 @@ inline size_t ws_ml_elems(int64_t T, int64_t Hq, int64_t PM) { return T * Hq * P
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
-// The matrix-core kernel takes a (sequence, KV head) whose group x query rows fit its 16 columns.
+// The matrix-core kernel takes (sequence, KV head) pairs whose group x query rows fill at least 2 of its 16
+// columns, in up to kMaxColGroups column groups (each reading the K/V once).
+constexpr int kMaxColGroups = 64;
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len);
 constexpr int kGqaTileTokens = 32;  // tokens per tile of the GQA kernel
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);

@@ -2,8 +2,9 @@
 chunk): paged_attention_decode_multi through the C ABI against oracle.decode_multi on the same seeded inputs.
 
 Row j of a sequence's QL new tokens attends causally over its first L - QL + j + 1 positions. Grouped heads x
-QL <= 16 runs on the matrix-core kernel (one K/V read per sequence and KV head for all its rows); the other
-shapes take the per-head kernel, one wave per (row, head). Tolerances as for decode: 1e-5 for fp32, 2e-3 +
+QL columns run on the matrix-core kernel in groups of 16 (one K/V read per group for all of a sequence's
+rows) for bf16 and E4M3 caches at head_dim 64 and 128; the other shapes take the per-head kernel, one wave
+per (row, head). Tolerances as for decode: 1e-5 for fp32, 2e-3 +
 1e-2 |ref| for bf16 or E4M3 caches under a bf16 query.
 """
 
@@ -62,16 +63,17 @@ def oracle_multi(st, h, q_host, qs, rows=None):
 
 
 CASES = [
-    # (seed, lens, query lens, Hq, Hkv, D, bs, dtype) -- matrix-core kernel: G * max QL <= 16
+    # (seed, lens, query lens, Hq, Hkv, D, bs, dtype) -- matrix-core kernel
     (501, [40, 300, 1030, 7], [4, 1, 3, 4], 16, 4, 128, 16, "bf16"),   # G 4 x QL 4 = 16 columns
     (502, [100, 513, 64, 2], [8, 5, 2, 5], 8, 8, 128, 16, "bf16"),     # no grouping: QL rows are the columns
     (503, [700, 45, 3, 260], [2, 2, 0, 1], 32, 4, 128, 8, "fp8"),      # G 8 x QL 2; an empty sequence; bs 8
+    (504, [90, 1200, 33], [8, 6, 33], 4, 2, 64, 32, "bf16"),           # QL = L; 2 x 33 = 66 columns, 5 groups
+    (507, [520, 47, 300], [4, 3, 2], 64, 8, 128, 256, "bf16"),         # G 8 x QL 4 = 32 columns, 2 groups
+    (508, [5, 40, 18], [9, 2, 18], 16, 4, 128, 16, "fp8"),             # QL > L: the first rows are zero; 72 cols
+    (509, [300, 64, 1000], [20, 17, 3], 8, 8, 64, 16, "bf16"),         # no grouping, 20 rows: 2 groups
     # per-head kernel
-    (504, [90, 1200, 33], [8, 6, 33], 4, 2, 64, 32, "bf16"),           # QL = L for the last sequence; 2 x 33 > 16
     (505, [65, 200, 9], [3, 7, 2], 8, 2, 96, 16, "bf16"),              # head_dim 96
     (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
-    (507, [520, 47, 300], [4, 3, 2], 64, 8, 128, 256, "bf16"),         # G 8 x QL 4 = 32 columns
-    (508, [5, 40, 18], [9, 2, 18], 16, 4, 128, 16, "fp8"),             # QL > L: the first rows are zero
 ]
 
 
@@ -105,7 +107,7 @@ def test_one_row_per_sequence_is_decode(hq, hkv, dt):
         np.testing.assert_array_equal(a, out.cpu().numpy())
 
 
-@pytest.mark.parametrize("name,ql", [("llama2_7b", 4), ("llama2_70b_gqa", 2)])
+@pytest.mark.parametrize("name,ql", [("llama2_7b", 4), ("llama2_70b_gqa", 2), ("llama2_70b_gqa", 4)])
 def test_full_size_verification_batch(name, ql):
     # every sequence of the workload verifies ql draft tokens: its last ql positions are the query rows
     st = build_structure(name)

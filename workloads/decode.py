@@ -313,14 +313,15 @@ def query_rows(st: DecodeStructure, query_lens, device="cpu", seed: int | None =
     return q, query_start
 
 
-def algorithmic_bytes(st: DecodeStructure) -> dict:
+def algorithmic_bytes(st: DecodeStructure, query_len: int = 1) -> dict:
     """Bytes a decode call must move at minimum: every live K and V element once, the query, the fp32 output,
-    the live table entries and the lengths. ``kv_unique`` counts shared prefix blocks once."""
+    the live table entries and the lengths. ``kv_unique`` counts shared prefix blocks once. With ``query_len``
+    new tokens per sequence the query and output rows multiply; K and V are still needed once."""
     lens = st.context_lens.astype(np.int64)
     row = st.num_kv_heads * st.head_dim * st.esize
     kv = int(lens.sum()) * row * 2
-    q = st.num_seqs * st.num_q_heads * st.head_dim * st.q_esize
-    out = st.num_seqs * st.num_q_heads * st.head_dim * 4
+    q = st.num_seqs * query_len * st.num_q_heads * st.head_dim * st.q_esize
+    out = st.num_seqs * query_len * st.num_q_heads * st.head_dim * 4
     tbl = int(st.blocks_per_seq().sum()) * 4 + 4 * st.num_seqs
     shared = st.notes.get("shared_prefix_blocks", 0)
     kv_unique = kv - max(0, st.num_seqs - 1) * shared * st.block_size * row * 2 if shared else kv
