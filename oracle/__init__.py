@@ -10,8 +10,8 @@ physical blocks of a [num_blocks, block_size, heads, head_dim] pool):
 * ``decode`` -- fp64 C (``pa_oracle.c``), forward gather through the block table, OpenMP over rows;
 * ``brute.decode`` -- numpy, builds the inverse map physical slot -> logical position by scanning the pool.
 
-``reshape_and_cache``, ``copy_blocks`` and ``gather`` apply the cache write, the block copy and the logical
-gather to host copies of the pools, byte for byte.
+``reshape_and_cache``, ``copy_blocks``, ``swap_blocks`` and ``gather`` apply the cache write, the block copy,
+the copy between two pools and the logical gather to host copies of the pools, byte for byte.
 """
 
 from __future__ import annotations
@@ -66,6 +66,8 @@ def _bind(lib):
     lib.oracle_reshape_and_cache.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [P, P, P, i32, i64, i64]
     lib.oracle_copy_blocks.restype = ctypes.c_int
+    lib.oracle_swap_blocks.argtypes = [P, P, i64, P, P, i64, P, i32, i64]
+    lib.oracle_swap_blocks.restype = ctypes.c_int
     lib.oracle_gather.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i32, i32]
     lib.oracle_gather.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -173,6 +175,23 @@ def reshape_and_cache(key_cache, value_cache, key, value, slot_mapping, *, lib=N
                                       D, bs, NB, key_cache.itemsize)
     if rc != 0:
         raise ValueError(f"oracle_reshape_and_cache rejected its input (status {rc})")
+
+
+def swap_blocks(dst_key, dst_value, src_key, src_value, pairs, *, lib=None):
+    """Copy blocks between two host pools of the same block shape: dst[pair.dst] = src[pair.src], K and V."""
+    lib = lib or load()
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    for a in (dst_key, dst_value, src_key, src_value):
+        if not a.flags.c_contiguous:
+            raise ValueError("pools must be C-contiguous")
+    if dst_key.shape[1:] != src_key.shape[1:] or dst_key.dtype != src_key.dtype or \
+            dst_value.shape != dst_key.shape or src_value.shape != src_key.shape:
+        raise ValueError("the pools must share the block shape and dtype")
+    block_bytes = dst_key[0].nbytes
+    rc = lib.oracle_swap_blocks(_ptr(dst_key), _ptr(dst_value), dst_key.shape[0], _ptr(src_key), _ptr(src_value),
+                                src_key.shape[0], _ptr(pr), pr.shape[0], block_bytes)
+    if rc != 0:
+        raise ValueError(f"oracle_swap_blocks rejected its input (status {rc})")
 
 
 def copy_blocks(key_cache, value_cache, pairs, *, lib=None):

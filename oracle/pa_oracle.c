@@ -351,6 +351,27 @@ int oracle_reshape_and_cache(void *key_cache, void *value_cache, const void *key
  * Copy-on-write of shared blocks: for each pair (src, dst), the whole dst block of both pools becomes a byte
  * copy of the src block. Pairs are applied in order. Returns 0, or -1 on an id outside the pool.
  */
+/*
+ * Block swap between two pools of the same block shape, e.g. the device pool and a host pool (page 1 section 5:
+ * swap space on the host; page 2 section 7.2: inactive blocks moved to host memory): for each (src, dst) pair,
+ * block dst of the destination pools becomes a copy of block src of the source pools, for K and for V.
+ * Returns -1 when a pair names a block outside its pool.
+ */
+int oracle_swap_blocks(void *dst_key, void *dst_value, int64_t dst_num_blocks, const void *src_key,
+                       const void *src_value, int64_t src_num_blocks, const int32_t *pairs, int32_t num_pairs,
+                       int64_t block_bytes) {
+    for (int32_t p = 0; p < num_pairs; ++p) {
+        const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+        if (src < 0 || src >= src_num_blocks || dst < 0 || dst >= dst_num_blocks) {
+            return -1;
+        }
+        memcpy((char *)dst_key + dst * block_bytes, (const char *)src_key + src * block_bytes, (size_t)block_bytes);
+        memcpy((char *)dst_value + dst * block_bytes, (const char *)src_value + src * block_bytes,
+               (size_t)block_bytes);
+    }
+    return 0;
+}
+
 int oracle_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int32_t num_pairs,
                        int64_t block_bytes, int64_t num_blocks) {
     for (int32_t p = 0; p < num_pairs; ++p) {
