@@ -50,6 +50,7 @@ extern "C" {
 #define PA_ERR_WORKSPACE (-5)   /* the split-context path needs a larger workspace */
 #define PA_ERR_HIP (-6)         /* a HIP launch or runtime call failed */
 #define PA_ERR_ALIGN (-7)       /* a pointer is not 16-byte aligned */
+#define PA_ERR_POINTER (-10)    /* swap_blocks: a pool or the pairs are not memory this device can access */
 
 /* PA_ABI_VERSION of the loaded library. */
 int pa_abi_version(void);
@@ -214,6 +215,28 @@ int reshape_and_cache(const void *key, const void *value, void *key_cache, void 
 int copy_blocks(void *key_cache, void *value_cache, const int32_t *block_pairs, int32_t num_pairs,
                 int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t kv_dtype,
                 void *stream);
+
+/*
+ * Block swap between two pools of the same block shape, typically the device pool and a pool in pinned host
+ * memory (page 1 section 5 recommends swap space on the host; page 2 section 7.2 moving inactive blocks to host
+ * memory). For every pair (src, dst) of block_pairs:
+ *     dst_key_cache[dst][:][:][:] = src_key_cache[src][:][:][:]      (likewise V)
+ * Either side may be memory of the current device or pinned host memory (hipHostMalloc, torch's pin_memory):
+ * the kernel reads and writes it directly, so a swap runs at the rate of the host link. Every pointer is looked
+ * up with hipPointerGetAttributes first; pageable host memory, managed memory or another GPU's memory gives
+ * PA_ERR_POINTER and nothing is launched.
+ *
+ *   dst_*_cache    [dst_num_blocks][block_size][num_kv_heads][head_dim] kv_dtype, written
+ *   src_*_cache    [src_num_blocks][block_size][num_kv_heads][head_dim] kv_dtype, read
+ *   block_pairs    int32 [num_pairs][2] = (src block, dst block), device-accessible; pairs naming a block
+ *                  outside its pool are skipped; destination blocks must be distinct, and the two sides must not
+ *                  overlap in memory
+ * Enqueued on stream like copy_blocks: the caller owns both pools and must not reuse a swapped-out device block
+ * for new writes, or read a swapped-in one, before the stream reaches the copy. num_pairs == 0 is a no-op.
+ */
+int swap_blocks(void *dst_key_cache, void *dst_value_cache, int64_t dst_num_blocks, const void *src_key_cache,
+                const void *src_value_cache, int64_t src_num_blocks, const int32_t *block_pairs, int32_t num_pairs,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype, void *stream);
 
 /*
  * Logical-order gather through the block table, with the same device address arithmetic that

@@ -116,7 +116,8 @@ def decode(query, key_cache, value_cache, block_tables, context_lens, scale, *, 
     rw = None
     n = 0
     if rows is not None:
-        rw = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        # distinct rows only: the C loop computes rows in parallel, each into its own output row
+        rw = np.ascontiguousarray(np.unique(np.asarray(rows, dtype=np.int32).reshape(-1, 2), axis=0))
         n = rw.shape[0]
     rc = lib.oracle_decode(_ptr(out), _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc),
                            float(k_scale), float(v_scale), _ptr(bt),
@@ -151,7 +152,8 @@ def decode_multi(query, key_cache, value_cache, block_tables, context_lens, quer
     rw = None
     n = 0
     if rows is not None:
-        rw = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        # distinct rows only: the C loop computes rows in parallel, each into its own output row
+        rw = np.ascontiguousarray(np.unique(np.asarray(rows, dtype=np.int32).reshape(-1, 2), axis=0))
         n = rw.shape[0]
     rc = lib.oracle_decode_multi(_ptr(out), _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc),
                                  float(k_scale), float(v_scale), _ptr(bt), _ptr(cl), _ptr(qs), float(scale), bs, B,

@@ -207,8 +207,8 @@ static int check_tables(const int32_t *block_tables, const int32_t *context_lens
 }
 
 /*
- * Decode attention for the (sequence, query head) rows listed in `rows` (pairs s, h), or for every row when
- * rows == NULL. out is [num_seqs, num_q_heads, head_dim] fp64; rows not listed are left untouched.
+ * Decode attention for the (sequence, query head) rows listed in `rows` (pairs s, h; distinct, since rows are
+ * computed in parallel, each into its own output row), or for every row when rows == NULL. out is [num_seqs, num_q_heads, head_dim] fp64; rows not listed are left untouched.
  *
  * Stored K and V elements are multiplied by k_scale and v_scale after decoding (1 for float32 / bf16 caches;
  * the dequantisation scales of an FP8 cache).
@@ -261,7 +261,7 @@ int oracle_decode(double *out, const void *query, int q_dtype, const void *key_c
  * s owns query rows query_start[s] .. query_start[s + 1] - 1, its QL = query_start[s + 1] - query_start[s]
  * newest tokens: token j sits at position L - QL + j of its L = context_lens[s] positions and attends over
  * positions 0 .. L - QL + j (causal: the cache already holds all L rows, the later ones are not attended).
- * A token with no position to attend (QL > L) gets a zero row. rows lists (query row, head) pairs, or is NULL
+ * A token with no position to attend (QL > L) gets a zero row. rows lists distinct (query row, head) pairs, or is NULL
  * for all; out is [num_tokens, num_q_heads, head_dim] fp64. Returns what oracle_decode returns, or -5 when
  * query_start is not a non-decreasing run from 0 to num_tokens.
  */

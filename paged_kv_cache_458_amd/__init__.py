@@ -69,6 +69,8 @@ def load_library(path: str | None = None):
     lib.reshape_and_cache.restype = ctypes.c_int
     lib.copy_blocks.argtypes = [P, P, P, i32, i32, i32, i32, i64, i32, P]
     lib.copy_blocks.restype = ctypes.c_int
+    lib.swap_blocks.argtypes = [P, P, i64, P, P, i64, P, i32, i32, i32, i32, i32, P]
+    lib.swap_blocks.restype = ctypes.c_int
     lib.paged_gather.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i64, i32, i32, i32, P]
     lib.paged_gather.restype = ctypes.c_int
     lib.pa_stream_read.argtypes, lib.pa_stream_read.restype = [P, sz, P, P], ctypes.c_int
@@ -296,6 +298,34 @@ def copy_blocks(key_cache, value_cache, block_pairs, *, stream=None):
                                     block_pairs.shape[0], bs, Hkv, D, NB, _dtype_code(key_cache),
                                     _stream(dev, stream))
     _check("copy_blocks", st)
+
+
+def swap_blocks(dst_key, dst_value, src_key, src_value, block_pairs, *, stream=None):
+    """dst_key[dst] = src_key[src] (and V) for each (src, dst) row of block_pairs, between two pools of the same
+    block shape: GPU tensors, or pinned CPU tensors (``pin_memory``) the kernel reads and writes directly."""
+    torch = _torch()
+    if block_pairs.device.type != "cuda":
+        raise ValueError("block_pairs must live on the GPU")
+    dev = block_pairs.device
+    _int32(block_pairs, "block_pairs")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2 or not block_pairs.is_contiguous():
+        raise ValueError("block_pairs must be a contiguous [P, 2] tensor")
+    for t in (dst_key, dst_value, src_key, src_value):
+        if not t.is_contiguous():
+            raise ValueError("pools must be contiguous")
+        if t.device.type == "cuda":
+            if t.device != dev:
+                raise ValueError("GPU pools must live on block_pairs' device")
+        elif not t.is_pinned():
+            raise ValueError("host pools must be pinned (pin_memory=True): the kernel reads them directly")
+    if dst_key.shape[1:] != src_key.shape[1:] or dst_value.shape != dst_key.shape or \
+            src_value.shape != src_key.shape or len({t.dtype for t in (dst_key, dst_value, src_key, src_value)}) != 1:
+        raise ValueError("the pools must share block shape and dtype")
+    _, bs, Hkv, D = src_key.shape
+    st = load_library().swap_blocks(dst_key.data_ptr(), dst_value.data_ptr(), dst_key.shape[0], src_key.data_ptr(),
+                                    src_value.data_ptr(), src_key.shape[0], block_pairs.data_ptr(),
+                                    block_pairs.shape[0], bs, Hkv, D, _dtype_code(src_key), _stream(dev, stream))
+    _check("swap_blocks", st)
 
 
 def paged_gather(out_key, out_value, key_cache, value_cache, block_tables, context_lens, *, stream=None):

@@ -102,16 +102,19 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
   }
 }
 
-// Copy-on-write (page 1 section 3.2): workgroup (pair, chunk) copies one chunk of block src to block dst in
-// both pools. Pairs naming a block outside the pool are skipped.
+// Block copies (src, dst) from one pair of pools into another: copy-on-write inside the device pool (page 1
+// section 3.2; both sides the same pools) and swaps between the device pool and a pool in pinned host memory
+// (page 1 section 5, page 2 section 7.2), which the kernel reads or writes directly over the host link.
+// Workgroup (pair, chunk) copies one chunk of block src to block dst in both the K and the V pools. Pairs naming
+// a block outside its pool are skipped. No __restrict__: copy-on-write reads and writes one allocation.
 constexpr int kCopyU4PerThread = 4;
-__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(U4* __restrict__ key_cache,
-                                                               U4* __restrict__ value_cache,
-                                                               const int32_t* __restrict__ pairs,
-                                                               int64_t block_u4, int64_t num_blocks) {
+__global__ __launch_bounds__(kThreads) void block_copy_kernel(U4* dst_key, U4* dst_value, int64_t dst_num_blocks,
+                                                              const U4* src_key, const U4* src_value,
+                                                              int64_t src_num_blocks,
+                                                              const int32_t* __restrict__ pairs, int64_t block_u4) {
   const int32_t src = pairs[2 * blockIdx.x];
   const int32_t dst = pairs[2 * blockIdx.x + 1];
-  if ((uint32_t)src >= (uint64_t)num_blocks || (uint32_t)dst >= (uint64_t)num_blocks) return;
+  if ((uint32_t)src >= (uint64_t)src_num_blocks || (uint32_t)dst >= (uint64_t)dst_num_blocks) return;
   const int64_t chunk0 = (int64_t)blockIdx.y * kThreads * kCopyU4PerThread;
   const int64_t sbase = (int64_t)src * block_u4, dbase = (int64_t)dst * block_u4;
   U4 kv[kCopyU4PerThread], vv[kCopyU4PerThread];
@@ -119,16 +122,16 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(U4* __restrict__ 
   for (int j = 0; j < kCopyU4PerThread; ++j) {
     const int64_t i = chunk0 + j * kThreads + threadIdx.x;
     if (i < block_u4) {
-      kv[j] = key_cache[sbase + i];
-      vv[j] = value_cache[sbase + i];
+      kv[j] = src_key[sbase + i];
+      vv[j] = src_value[sbase + i];
     }
   }
 #pragma unroll
   for (int j = 0; j < kCopyU4PerThread; ++j) {
     const int64_t i = chunk0 + j * kThreads + threadIdx.x;
     if (i < block_u4) {
-      key_cache[dbase + i] = kv[j];
-      value_cache[dbase + i] = vv[j];
+      dst_key[dbase + i] = kv[j];
+      dst_value[dbase + i] = vv[j];
     }
   }
 }
@@ -196,11 +199,19 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
 
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+  return launch_swap_blocks(key_cache, value_cache, num_blocks, key_cache, value_cache, num_blocks, pairs, num_pairs,
+                            block_bytes, stream);
+}
+
+hipError_t launch_swap_blocks(void* dst_key, void* dst_value, int64_t dst_num_blocks, const void* src_key,
+                              const void* src_value, int64_t src_num_blocks, const int32_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, hipStream_t stream) {
   const int64_t block_u4 = block_bytes / 16;
   const int64_t per_wg = (int64_t)kThreads * kCopyU4PerThread;
   const dim3 grid(num_pairs, (unsigned)((block_u4 + per_wg - 1) / per_wg));
-  copy_blocks_kernel<<<grid, dim3(kThreads), 0, stream>>>(static_cast<U4*>(key_cache), static_cast<U4*>(value_cache),
-                                                          pairs, block_u4, num_blocks);
+  block_copy_kernel<<<grid, dim3(kThreads), 0, stream>>>(
+      static_cast<U4*>(dst_key), static_cast<U4*>(dst_value), dst_num_blocks, static_cast<const U4*>(src_key),
+      static_cast<const U4*>(src_value), src_num_blocks, pairs, block_u4);
   return hipGetLastError();
 }
 

@@ -30,6 +30,31 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// A pointer as a kernel on the current device must use it: this device's memory as it is, pinned host memory
+// through its device-side address. Anything else -- pageable host memory HIP does not know, managed memory,
+// another GPU's memory -- is not something the kernel may touch: nullptr.
+void* device_view(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || attr.device != cur) return nullptr;
+    return const_cast<void*>(p);
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return d;
+  }
+  return nullptr;
+}
+
 struct Plan {
   int status = PA_OK;
   int32_t partition = 0;       // tokens per partition as launched
@@ -143,6 +168,7 @@ const char* pa_strerror(int status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch or runtime call failed";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case PA_ERR_POINTER: return "PA_ERR_POINTER: memory the device cannot access (pageable host memory, another GPU)";
     default: return "unknown status";
   }
 }
@@ -351,6 +377,35 @@ int copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs, 
   const int64_t per_wg = 256 * 4 * 16;
   if ((block_bytes + per_wg - 1) / per_wg > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
   return pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs, block_bytes, num_blocks,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int swap_blocks(void* dst_key_cache, void* dst_value_cache, int64_t dst_num_blocks, const void* src_key_cache,
+                const void* src_value_cache, int64_t src_num_blocks, const int32_t* block_pairs, int32_t num_pairs,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || dst_num_blocks <= 0 ||
+      src_num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (esize_of(kv_dtype) == 0) return PA_ERR_DTYPE;
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * esize_of(kv_dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_key_cache || !dst_value_cache || !src_key_cache || !src_value_cache || !block_pairs) return PA_ERR_NULL;
+  if (!aligned16(dst_key_cache) || !aligned16(dst_value_cache) || !aligned16(src_key_cache) ||
+      !aligned16(src_value_cache) || !aligned4(block_pairs))
+    return PA_ERR_ALIGN;
+  const int64_t per_wg = 256 * 4 * 16;
+  if ((block_bytes + per_wg - 1) / per_wg > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  // the kernel reads and writes the pools directly: each must be memory this device can reach
+  void* dk = device_view(dst_key_cache);
+  void* dv = device_view(dst_value_cache);
+  const void* sk = device_view(src_key_cache);
+  const void* sv = device_view(src_value_cache);
+  const int32_t* pairs = static_cast<const int32_t*>(device_view(block_pairs));
+  if (!dk || !dv || !sk || !sv || !pairs) return PA_ERR_POINTER;
+  return pa::launch_swap_blocks(dk, dv, dst_num_blocks, sk, sv, src_num_blocks, pairs, num_pairs, block_bytes,
                                 static_cast<hipStream_t>(stream)) == hipSuccess
              ? PA_OK
              : PA_ERR_HIP;

@@ -75,6 +75,9 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         float v_scale, hipStream_t stream);
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+hipError_t launch_swap_blocks(void* dst_key, void* dst_value, int64_t dst_num_blocks, const void* src_key,
+                              const void* src_value, int64_t src_num_blocks, const int32_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, hipStream_t stream);
 hipError_t launch_paged_gather(void* out_key, void* out_value, const void* key_cache, const void* value_cache,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t bs_log2, int64_t num_blocks, int32_t max_blocks_per_seq,

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_function():
             "paged_attention_workspace_bytes", "paged_attention_partition_size", "pa_strerror",
             "pa_abi_version", "pa_stream_read", "pa_stream_copy", "pa_bm_create", "pa_bm_append_slots",
             "paged_attention_decode_scaled", "reshape_and_cache_fp8", "paged_attention_decode_multi",
-            "paged_attention_multi_workspace_bytes", "paged_attention_multi_partition_size"} <= set(names)
+            "paged_attention_multi_workspace_bytes", "paged_attention_multi_partition_size",
+            "swap_blocks"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert lib.pa_abi_version() == pa.ABI_VERSION
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_names_every_status():
     for code in (0, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
-                 PA_ERR_ALIGN):
+                 PA_ERR_ALIGN, -10):
         assert pa.strerror(code) != "unknown status"
     assert pa.strerror(123) == "unknown status"
 
@@ -226,6 +227,24 @@ def test_copy_blocks_rejects(over, status):
                 head_dim=64, num_blocks=10, kv_dtype=pa.PA_BF16, stream=None)
     args.update(over)
     assert pa.load_library().copy_blocks(*args.values()) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_pairs=-1), PA_ERR_SHAPE),
+    (dict(src_num_blocks=0), PA_ERR_SHAPE),
+    (dict(kv_dtype=9), PA_ERR_DTYPE),
+    (dict(head_dim=3, num_kv_heads=1, block_size=2, kv_dtype=pa.PA_BF16), PA_ERR_UNSUPPORTED),
+    (dict(block_pairs=None), PA_ERR_NULL),
+    (dict(src_key_cache=FAKE + 8), PA_ERR_ALIGN),
+    # an address HIP does not know is refused on the host, before any launch (here: no device at all)
+    (dict(), -10),
+])
+def test_swap_blocks_rejects(over, status):
+    args = dict(dst_key_cache=FAKE, dst_value_cache=FAKE, dst_num_blocks=10, src_key_cache=FAKE,
+                src_value_cache=FAKE, src_num_blocks=20, block_pairs=FAKE, num_pairs=3, block_size=16, num_kv_heads=2,
+                head_dim=64, kv_dtype=pa.PA_BF16, stream=None)
+    args.update(over)
+    assert pa.load_library().swap_blocks(*args.values()) == status
 
 
 def test_gather_rejects():

@@ -116,8 +116,9 @@ def test_full_size_verification_batch(name, ql):
     gpu = run_multi(st, t, q, qs, st.partition_size)
     h = {k: to_host(v) for k, v in t.items()}
     rng = np.random.default_rng(512)
-    rows = np.stack([rng.integers(0, q.shape[0], 600), rng.integers(0, st.num_q_heads, 600)], 1)
-    rows = np.concatenate([rows, [[0, 0], [q.shape[0] - 1, st.num_q_heads - 1]]]).astype(np.int32)
+    flat = rng.choice(q.shape[0] * st.num_q_heads, 600, replace=False)  # distinct (row, head) pairs
+    rows = np.stack([flat // st.num_q_heads, flat % st.num_q_heads], 1)
+    rows = np.unique(np.concatenate([rows, [[0, 0], [q.shape[0] - 1, st.num_q_heads - 1]]]), axis=0).astype(np.int32)
     ref = oracle_multi(st, h, to_host(q), qs, rows=rows)
     err = close(gpu[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], st.dtype, name)
     sys.__stderr__.write(f"[{name} x {ql}] max abs err {err:.3e} over {len(rows)} sampled rows\n")

@@ -97,7 +97,7 @@ def pin_sampled_rows(lib):
     st, q, qs, h = multi_case(seed, lens, qls, hq, hkv, d, bs, dt)
     full = oracle.decode_multi(q, h["key_cache"], h["value_cache"], st.block_tables_pre, st.context_lens, qs,
                                st.scale, lib=lib)
-    rows = np.array([[0, 1], [4, 3], [7, 0]], np.int32)
+    rows = np.array([[0, 1], [4, 3], [7, 0], [4, 3], [0, 1], [4, 3]], np.int32)  # repeated rows are computed once
     part = oracle.decode_multi(q, h["key_cache"], h["value_cache"], st.block_tables_pre, st.context_lens, qs,
                                st.scale, rows=rows, lib=lib)
     for t, hh in rows:
