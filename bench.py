@@ -255,6 +255,80 @@ def run_decode_loop(args) -> int:
     return 0
 
 
+def run_swap(args) -> int:
+    """Block swap between the device pool and a pinned host pool (page 1 section 5: swap space): the 7B shape
+    (32 KV heads x 128, bf16, 16-token blocks: 256 KiB of K and V per block), 2048 random blocks out to the host
+    pool and 2048 back in per step. Reference: torch's DMA copy of the same bytes between pinned host memory
+    and the device, and the host link's nominal 64 GB/s per direction (PCIe 5.0 x16)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_458_amd as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+    nb_dev, nb_host, n, bs, hkv, d = 8192, 4096, 2048, 16, 32, 128
+    shape = (bs, hkv, d)
+    kc = torch.randn((nb_dev,) + shape, device=dev).to(torch.bfloat16)
+    vc = torch.randn((nb_dev,) + shape, device=dev).to(torch.bfloat16)
+    hk = torch.empty((nb_host,) + shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((nb_host,) + shape, dtype=torch.bfloat16).pin_memory()
+    rng = np.random.default_rng(7)
+    out_pairs = torch.from_numpy(np.stack([rng.choice(nb_dev, n, replace=False), rng.choice(nb_host, n, replace=False)],
+                                          1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([out_pairs[:, 1].cpu().numpy(), rng.choice(nb_dev, n, replace=False)],
+                                         1).astype(np.int32)).to(dev)
+    moved = 2 * n * kc[0].nbytes  # K and V, one direction
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / reps
+
+    ms_out = timed(lambda: pa.swap_blocks(hk, hv, kc, vc, out_pairs), args.steps)
+    ms_in = timed(lambda: pa.swap_blocks(kc, vc, hk, hv, in_pairs), args.steps)
+    flat_h = torch.empty(moved, dtype=torch.uint8).pin_memory()
+    flat_d = torch.empty(moved, dtype=torch.uint8, device=dev)
+    ms_dma_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), args.steps)
+    ms_dma_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), args.steps)
+    gbs = lambda ms: round(moved / (ms * 1e-3) / 1e9, 2)
+    value = 2 * moved / ((ms_out + ms_in) * 1e-3) / 1e9
+    rec = {
+        "metric": "block swap GB/s between device pool and pinned host pool",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 2,
+        "ms_per_step": round(ms_out + ms_in, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "swap", "blocks_per_direction": n, "block_bytes_kv": 2 * kc[0].nbytes,
+                   "device_pool_blocks": nb_dev, "host_pool_blocks": nb_host},
+        "swap_out_gbs": gbs(ms_out),
+        "swap_in_gbs": gbs(ms_in),
+        "dma_copy_d2h_gbs": gbs(ms_dma_d2h),
+        "dma_copy_h2d_gbs": gbs(ms_dma_h2d),
+        "roofline": {"bound": "host link", "achieved": round(value, 2), "peak": 64.0, "unit": "GB/s",
+                     "frac": round(value / 64.0, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,8 +365,10 @@ def main() -> int:
 
     if args.workload == "decode_loop":
         return run_decode_loop(args)
+    if args.workload == "swap":
+        return run_swap(args)
     if args.workload not in CONFIG_NAMES:
-        ap.error(f"--workload must be one of {CONFIG_NAMES} or decode_loop")
+        ap.error(f"--workload must be one of {CONFIG_NAMES}, decode_loop or swap")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.load_library()

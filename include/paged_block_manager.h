@@ -84,6 +84,34 @@ int32_t pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids, i
                            int32_t *lens_out, int32_t pad);
 
 /*
+ * Swap (page 1 section 5: swap space on the host; page 2 section 7.2: inactive blocks moved to host memory).
+ * The caller keeps a second pair of pools in host memory (pinned, so that swap_blocks of paged_attention.h can
+ * reach it) with num_host_blocks blocks of the device pools' shape; the manager hands out its block ids.
+ *
+ * pa_bm_set_host_pool: use host blocks [0, num_host_blocks). PA_ERR_SEQ while a sequence is swapped out.
+ *
+ * pa_bm_swap_out: move sequence seq_id out of the device pool. Each of its blocks, in logical order, is given
+ * a host block: pairs_out[i] = {device block, host block}. Apply them with swap_blocks (host pools <- device
+ * pools) before any freed device block is written again -- on one stream, enqueue the swap first. Device
+ * blocks the sequence alone used return to the free list; shared ones stay with their other users. The
+ * sequence keeps its length but is unknown to append/fork/block_tables (PA_ERR_SEQ) until swapped in;
+ * free_sequence releases its host blocks. Returns the number of pairs; PA_ERR_NOMEM when the host pool lacks
+ * blocks, PA_ERR_SHAPE when max_pairs is too small or copy-on-write pairs are still pending (take and apply
+ * them first). Nothing changes on failure.
+ *
+ * pa_bm_swap_in: bring a swapped-out sequence back into fresh device blocks: pairs_out[i] = {host block,
+ * device block}; apply them with swap_blocks (device pools <- host pools) before the sequence's next attention.
+ * Its host blocks return to the host pool. PA_ERR_NOMEM when the device pool lacks free blocks.
+ *
+ * pa_bm_swap_stats: int64 stats_out[4] = free host blocks, host blocks in use, swapped-out sequences, blocks
+ * moved so far (out and in).
+ */
+int32_t pa_bm_set_host_pool(pa_block_manager *bm, int32_t num_host_blocks);
+int32_t pa_bm_swap_out(pa_block_manager *bm, int64_t seq_id, int32_t *pairs_out, int32_t max_pairs);
+int32_t pa_bm_swap_in(pa_block_manager *bm, int64_t seq_id, int32_t *pairs_out, int32_t max_pairs);
+int32_t pa_bm_swap_stats(const pa_block_manager *bm, int64_t *stats_out);
+
+/*
  * Occupancy, as int64 stats_out[8]: free blocks, used blocks, blocks referenced by more than one sequence,
  * sequences, tokens summed over sequences, token slots in used blocks, slots holding a token (a shared slot
  * counted once), copy-on-write copies so far. Internal fragmentation = 1 - stats[6] / stats[5].

@@ -31,6 +31,10 @@ def _bind(lib):
     lib.pa_bm_free_sequence.argtypes, lib.pa_bm_free_sequence.restype = [P, i64], i32
     lib.pa_bm_block_tables.argtypes, lib.pa_bm_block_tables.restype = [P, P, i32, P, P, i32], i32
     lib.pa_bm_stats.argtypes, lib.pa_bm_stats.restype = [P, P], i32
+    lib.pa_bm_set_host_pool.argtypes, lib.pa_bm_set_host_pool.restype = [P, i32], i32
+    lib.pa_bm_swap_out.argtypes, lib.pa_bm_swap_out.restype = [P, i64, P, i32], i32
+    lib.pa_bm_swap_in.argtypes, lib.pa_bm_swap_in.restype = [P, i64, P, i32], i32
+    lib.pa_bm_swap_stats.argtypes, lib.pa_bm_swap_stats.restype = [P, P], i32
     lib._pa_bm_bound = True
     return lib
 
@@ -106,6 +110,31 @@ class BlockManager:
         self._check("pa_bm_block_tables", self._lib.pa_bm_block_tables(self._h, _ptr(ids), n, _ptr(tables),
                                                                          _ptr(lens), pad))
         return tables[:n], lens[:n]
+
+    def set_host_pool(self, num_host_blocks: int):
+        """Host blocks [0, num_host_blocks) of the caller's pinned host pools receive swapped-out sequences."""
+        self._check("pa_bm_set_host_pool", self._lib.pa_bm_set_host_pool(self._h, num_host_blocks))
+        self.num_host_blocks = num_host_blocks
+
+    def _swap(self, fn, seq_id: int) -> np.ndarray:
+        cap = self.max_blocks_per_seq
+        buf = np.empty((cap, 2), dtype=np.int32)
+        n = self._check(fn, getattr(self._lib, fn)(self._h, seq_id, _ptr(buf), cap))
+        return buf[:n].copy()
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """Move a sequence to host blocks: pairs [n, 2] = (device block, host block), in logical order."""
+        return self._swap("pa_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """Bring a swapped-out sequence back: pairs [n, 2] = (host block, device block), in logical order."""
+        return self._swap("pa_bm_swap_in", seq_id)
+
+    def swap_stats(self) -> dict:
+        out = np.zeros(4, dtype=np.int64)
+        self._check("pa_bm_swap_stats", self._lib.pa_bm_swap_stats(self._h, _ptr(out)))
+        return dict(zip(("free_host_blocks", "used_host_blocks", "swapped_sequences", "blocks_moved"),
+                        (int(x) for x in out)))
 
     def stats(self) -> dict:
         out = np.zeros(8, dtype=np.int64)

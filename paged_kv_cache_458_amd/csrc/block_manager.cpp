@@ -6,6 +6,9 @@
 // Page 2 ("vLLM-v0.11.0 ... how much memory does PagedAttention save"), section 4.2: a sequence of length L
 // holds ceil(L / block_size) blocks, and requests with the same prefix reuse the same blocks.
 //
+// Swap (page 1 section 5: swap space on the host; page 2 section 7.2: inactive blocks moved to host memory): a
+// sequence can leave the device pool for blocks of a host pool and come back later into fresh device blocks.
+//
 // Host code only: it decides where tokens go; the kernels move the bytes.
 #include <stdint.h>
 
@@ -55,6 +58,13 @@ struct pa_block_manager {
   std::vector<uint64_t> cached_key;
   std::vector<int32_t> copies;  // pending copy-on-write pairs {src, dst}
   int64_t cow_total = 0;
+  // host pool for swapped-out sequences: their block lists hold host block ids
+  int32_t num_host_blocks = 0;
+  std::vector<int32_t> host_free;  // stack, like free_list
+  std::unordered_map<int64_t, Sequence> swapped;
+  int64_t moved_total = 0;
+
+  bool known(int64_t id) const { return seqs.count(id) || swapped.count(id); }
 
   int32_t pop_free() {
     const int32_t b = free_list.back();
@@ -134,7 +144,7 @@ int32_t pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, const int32_t* 
                            int32_t* slots_out) {
   if (!bm) return PA_ERR_NULL;
   if (num_tokens < 0 || (num_tokens > 0 && !slots_out)) return num_tokens < 0 ? PA_ERR_SHAPE : PA_ERR_NULL;
-  if (bm->seqs.count(seq_id)) return PA_ERR_SEQ;
+  if (bm->known(seq_id)) return PA_ERR_SEQ;
   const int32_t bs = bm->block_size;
   const int32_t nblk = (num_tokens + bs - 1) / bs;
   if (nblk > bm->max_blocks) return PA_ERR_SHAPE;
@@ -182,7 +192,7 @@ int32_t pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id, const int32_t* 
 int32_t pa_bm_fork(pa_block_manager* bm, int64_t parent_id, int64_t child_id) {
   if (!bm) return PA_ERR_NULL;
   auto it = bm->seqs.find(parent_id);
-  if (it == bm->seqs.end() || bm->seqs.count(child_id)) return PA_ERR_SEQ;
+  if (it == bm->seqs.end() || bm->known(child_id)) return PA_ERR_SEQ;
   try {
     Sequence child = it->second;
     for (int32_t b : child.blocks) ++bm->ref[b];
@@ -263,6 +273,17 @@ int32_t pa_bm_take_copies(pa_block_manager* bm, int32_t* pairs_out, int32_t max_
 
 int32_t pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id) {
   if (!bm) return PA_ERR_NULL;
+  auto sw = bm->swapped.find(seq_id);
+  if (sw != bm->swapped.end()) {  // a swapped-out sequence gives back its host blocks
+    try {
+      bm->host_free.reserve(bm->host_free.size() + sw->second.blocks.size());
+    } catch (...) {
+      return PA_ERR_NOMEM;
+    }
+    for (int32_t b : sw->second.blocks) bm->host_free.push_back(b);
+    bm->swapped.erase(sw);
+    return PA_OK;
+  }
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_SEQ;
   // the free list grows by at most the sequence's block count; reserve first so nothing below can throw
@@ -292,6 +313,94 @@ int32_t pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, i
     std::copy(q.blocks.begin(), q.blocks.end(), row);
     lens_out[i] = (int32_t)q.len;
   }
+  return PA_OK;
+}
+
+int32_t pa_bm_set_host_pool(pa_block_manager* bm, int32_t num_host_blocks) {
+  if (!bm) return PA_ERR_NULL;
+  if (num_host_blocks < 0) return PA_ERR_SHAPE;
+  if (!bm->swapped.empty()) return PA_ERR_SEQ;  // blocks of the current host pool are in use
+  try {
+    std::vector<int32_t> fl;
+    fl.reserve(num_host_blocks);
+    for (int32_t b = num_host_blocks - 1; b >= 0; --b) fl.push_back(b);
+    bm->host_free.swap(fl);
+  } catch (...) {
+    return PA_ERR_NOMEM;
+  }
+  bm->num_host_blocks = num_host_blocks;
+  return PA_OK;
+}
+
+int32_t pa_bm_swap_out(pa_block_manager* bm, int64_t seq_id, int32_t* pairs_out, int32_t max_pairs) {
+  if (!bm) return PA_ERR_NULL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PA_ERR_SEQ;
+  if (!bm->copies.empty()) return PA_ERR_SHAPE;  // pending copy-on-write pairs must be taken and applied first
+  const int32_t n = (int32_t)it->second.blocks.size();
+  if (n > max_pairs) return PA_ERR_SHAPE;
+  if (n > 0 && !pairs_out) return PA_ERR_NULL;
+  if (n > (int32_t)bm->host_free.size()) return PA_ERR_NOMEM;
+  try {
+    bm->free_list.reserve(bm->free_list.size() + n);
+    Sequence out;
+    out.len = it->second.len;
+    out.blocks.reserve(n);
+    bm->swapped.reserve(bm->swapped.size() + 1);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t h = bm->host_free.back();
+      bm->host_free.pop_back();
+      pairs_out[2 * i] = it->second.blocks[i];
+      pairs_out[2 * i + 1] = h;
+      out.blocks.push_back(h);
+    }
+    // nothing below throws: the device blocks are released (shared ones stay with their other users)
+    for (int32_t b : it->second.blocks) bm->release(b);
+    bm->seqs.erase(it);
+    bm->swapped.emplace(seq_id, std::move(out));
+    bm->moved_total += n;
+    return n;
+  } catch (...) {
+    return PA_ERR_NOMEM;
+  }
+}
+
+int32_t pa_bm_swap_in(pa_block_manager* bm, int64_t seq_id, int32_t* pairs_out, int32_t max_pairs) {
+  if (!bm) return PA_ERR_NULL;
+  auto it = bm->swapped.find(seq_id);
+  if (it == bm->swapped.end()) return PA_ERR_SEQ;
+  const int32_t n = (int32_t)it->second.blocks.size();
+  if (n > max_pairs) return PA_ERR_SHAPE;
+  if (n > 0 && !pairs_out) return PA_ERR_NULL;
+  if (n > (int32_t)bm->free_list.size()) return PA_ERR_NOMEM;
+  try {
+    bm->host_free.reserve(bm->host_free.size() + n);
+    Sequence back;
+    back.len = it->second.len;
+    back.blocks.reserve(n);
+    bm->seqs.reserve(bm->seqs.size() + 1);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t b = bm->pop_free();
+      pairs_out[2 * i] = it->second.blocks[i];
+      pairs_out[2 * i + 1] = b;
+      back.blocks.push_back(b);
+    }
+    for (int32_t h : it->second.blocks) bm->host_free.push_back(h);
+    bm->swapped.erase(it);
+    bm->seqs.emplace(seq_id, std::move(back));
+    bm->moved_total += n;
+    return n;
+  } catch (...) {
+    return PA_ERR_NOMEM;
+  }
+}
+
+int32_t pa_bm_swap_stats(const pa_block_manager* bm, int64_t* stats_out) {
+  if (!bm || !stats_out) return PA_ERR_NULL;
+  stats_out[0] = (int64_t)bm->host_free.size();
+  stats_out[1] = bm->num_host_blocks - (int64_t)bm->host_free.size();
+  stats_out[2] = (int64_t)bm->swapped.size();
+  stats_out[3] = bm->moved_total;
   return PA_OK;
 }
 

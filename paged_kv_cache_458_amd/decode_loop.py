@@ -6,7 +6,9 @@ sample, update the KV cache, forward again): the block manager hands out the new
 copy-on-write pairs; copy_blocks applies the copies, reshape_and_cache writes the new K/V, and
 paged_attention_decode attends over each sequence's whole cache. Sequences join (with a prompt whose full
 blocks may be shared with earlier prompts), fork (sharing every block, page 1 section 3.2) and finish
-(their blocks return to the pool) between steps.
+(their blocks return to the pool) between steps. With a host pool (page 1 section 5: swap space; page 2
+section 7.2: inactive blocks to host memory) a step that runs out of blocks swaps the most recently admitted
+sequence out to pinned host memory, and swapped-out sequences come back, oldest first, once blocks are free.
 
 K/V values are synthetic. A prompt token's K/V is a fixed function of the prompt up to and including it, so
 two prompts with a common prefix would write identical rows there -- which is what makes sharing their
@@ -17,8 +19,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import PA_BF16, PA_F32, copy_blocks, paged_attention_decode, reshape_and_cache, workspace_bytes
-from .block_manager import BlockManager
+from . import (PA_BF16, PA_F32, PagedAttentionError, copy_blocks, paged_attention_decode, reshape_and_cache,
+               swap_blocks, workspace_bytes)
+from .block_manager import PA_ERR_NOMEM, BlockManager
 
 
 def _prefix_seed(seed: int, tokens: np.ndarray) -> int:
@@ -38,7 +41,8 @@ class DecodeLoop:
 
     def __init__(self, *, num_blocks: int, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  max_blocks_per_seq: int, dtype: str = "bf16", device="cuda", seed: int = 0, scale=None,
-                 partition_size: int = -1, record: bool = False, prompt_kv: str = "prefix"):
+                 partition_size: int = -1, record: bool = False, prompt_kv: str = "prefix",
+                 host_blocks: int = 0):
         import torch
 
         self.torch = torch
@@ -58,7 +62,15 @@ class DecodeLoop:
         self.gen = torch.Generator(device=self.dev)
         self.gen.manual_seed(seed)
         self.running: list[int] = []
+        self.swapped: list[int] = []  # swapped-out sequences, oldest first
         self.lengths: dict[int, int] = {}
+        # pinned host pools that swapped-out sequences live in (NaN until written, like the device pools)
+        self.host_key = self.host_value = None
+        if host_blocks:
+            self.bm.set_host_pool(host_blocks)
+            hshape = (host_blocks, block_size, num_kv_heads, head_dim)
+            self.host_key = torch.full(hshape, float("nan"), dtype=self.dt).pin_memory()
+            self.host_value = torch.full(hshape, float("nan"), dtype=self.dt).pin_memory()
         self._ws = None
         # with record=True every cache write and copy is kept on the host so that a test can rebuild the pools
         self.log: list | None = [] if record else None
@@ -133,8 +145,47 @@ class DecodeLoop:
 
     def finish(self, seq_id: int):
         self.bm.free_sequence(seq_id)
-        self.running.remove(seq_id)
+        (self.swapped if seq_id in self.swapped else self.running).remove(seq_id)
         del self.lengths[seq_id]
+
+    def swap_out(self, seq_id: int):
+        """Move a running sequence to the host pool (the copy is enqueued before anything reuses its blocks)."""
+        pairs = self.bm.swap_out(seq_id)
+        if len(pairs):
+            swap_blocks(self.host_key, self.host_value, self.key_cache, self.value_cache, self._to_device(pairs))
+        self.running.remove(seq_id)
+        self.swapped.append(seq_id)
+        if self.log is not None:
+            self.log.append(("swap_out", pairs.copy()))
+
+    def swap_in(self, seq_id: int):
+        """Bring a swapped-out sequence back into fresh device blocks."""
+        pairs = self.bm.swap_in(seq_id)
+        if len(pairs):
+            swap_blocks(self.key_cache, self.value_cache, self.host_key, self.host_value, self._to_device(pairs))
+        self.swapped.remove(seq_id)
+        self.running.append(seq_id)
+        if self.log is not None:
+            self.log.append(("swap_in", pairs.copy()))
+
+    def _schedule(self):
+        """Swap sequences back in while the free blocks also leave one per running sequence for this step's
+        tokens; then take this step's slots, swapping the most recently admitted sequence out while they do not
+        fit. Returns the slots of the running sequences, in order."""
+        bs = self.bs
+        while self.swapped:
+            sid = self.swapped[0]
+            need = -(-self.lengths[sid] // bs) + len(self.running) + 1
+            if self.bm.stats()["free_blocks"] < need:
+                break
+            self.swap_in(sid)
+        while True:
+            try:
+                return self.bm.append_slots(self.running)
+            except PagedAttentionError as e:
+                if e.status != PA_ERR_NOMEM or self.host_key is None or len(self.running) <= 1:
+                    raise
+                self.swap_out(self.running[-1])
 
     def step(self, query=None, new_kv=None):
         """One decode step for every running sequence; returns (seq_ids, out [n, Hq, D] fp32, copy pairs).
@@ -142,11 +193,13 @@ class DecodeLoop:
         query defaults to random rows; new_kv (k, v) of shape [n, Hkv, D] to random rows.
         """
         t = self.torch
+        if not self.running and not self.swapped:
+            return [], None, np.zeros((0, 2), np.int32)
+        slots = self._schedule()
         ids = list(self.running)
         n = len(ids)
-        if n == 0:
-            return ids, None, np.zeros((0, 2), np.int32)
-        slots = self.bm.append_slots(ids)
+        if n == 0:  # everything is swapped out and nothing fits back in yet
+            return [], None, np.zeros((0, 2), np.int32)
         pairs = self._apply_copies()  # copy-on-write before the new tokens land in the copies
         k, v = self._rows(n) if new_kv is None else new_kv
         self._write(k, v, slots)

@@ -232,3 +232,125 @@ def test_fragmentation_of_paged_against_contiguous_allocation():
     paged_waste = st["internal_fragmentation"]
     contiguous_waste = 1.0 - lens.sum() / (len(lens) * max_len)
     assert paged_waste < 0.02 < 0.35 < contiguous_waste
+
+
+# --------------------------------------------------------------------------------------------------------
+# swap to a host pool (page 1 section 5: swap space; page 2 section 7.2: inactive blocks moved to host memory)
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_random_operations_with_swaps_keep_every_sequence_intact(seed):
+    rng = np.random.default_rng(seed)
+    nb, bs, mb, nh = 40, 4, 24, 30
+    reserved = nb - 1
+    bm = BlockManager(nb, bs, mb, reserved_block=reserved)
+    bm.set_host_pool(nh)
+    dev = PoolModel(nb, bs)
+    host = PoolModel(nh, bs)
+    logical: dict[int, list[int]] = {}
+    swapped: dict[int, list[int]] = {}
+    system = rng.integers(0, 50, size=9)
+    next_id, next_token = 0, 10**12
+    for op in range(500):
+        r = rng.random()
+        if r < 0.2 or not (logical or swapped):
+            tokens = np.concatenate([system if rng.random() < 0.6 else [], rng.integers(0, 50, size=rng.integers(1, 9))])
+            tokens = tokens.astype(np.int32)
+            try:
+                slots = bm.add_sequence(next_id, len(tokens), tokens)
+            except pa.PagedAttentionError as e:
+                assert e.status == PA_ERR_NOMEM
+                continue
+            ident = [prefix_identity(tokens, t) for t in range(len(tokens))]
+            dev.write(slots, ident)
+            logical[next_id] = ident
+            next_id += 1
+        elif r < 0.35 and logical:  # swap a running sequence out
+            victim = int(rng.choice(list(logical)))
+            before = bm.swap_stats()
+            try:
+                pairs = bm.swap_out(victim)
+            except pa.PagedAttentionError as e:
+                assert e.status == PA_ERR_NOMEM and bm.swap_stats() == before
+                continue
+            for d, h in pairs:  # device -> host, applied before any freed device block is written
+                host.pool[h] = dev.pool[d]
+            swapped[victim] = logical.pop(victim)
+            with pytest.raises(pa.PagedAttentionError):
+                bm.block_tables([victim])
+        elif r < 0.5 and swapped:  # swap one back in
+            sid = int(rng.choice(list(swapped)))
+            try:
+                pairs = bm.swap_in(sid)
+            except pa.PagedAttentionError as e:
+                assert e.status == PA_ERR_NOMEM
+                continue
+            for h, d in pairs:
+                dev.pool[d] = host.pool[h]
+            logical[sid] = swapped.pop(sid)
+        elif r < 0.6:  # a finished sequence, running or swapped out
+            pool = list(logical) + list(swapped)
+            victim = int(rng.choice(pool))
+            bm.free_sequence(victim)
+            logical.pop(victim, None)
+            swapped.pop(victim, None)
+        elif logical:  # a decode step for the running ones
+            ids = [int(s) for s in rng.permutation(list(logical))[: rng.integers(1, len(logical) + 1)]]
+            try:
+                slots = bm.append_slots(ids)
+            except pa.PagedAttentionError as e:
+                assert e.status in (PA_ERR_NOMEM, -2)
+                continue
+            dev.copy(bm.take_copies())
+            new = []
+            for s in ids:
+                new.append(next_token)
+                logical[s].append(next_token)
+                next_token += 1
+            dev.write(slots, new)
+        check_all(bm, dev, logical, reserved)
+        sw = bm.swap_stats()
+        assert sw["swapped_sequences"] == len(swapped)
+        assert sw["free_host_blocks"] + sw["used_host_blocks"] == nh
+        assert sw["used_host_blocks"] == sum(-(-len(v) // bs) for v in swapped.values())
+    assert bm.swap_stats()["blocks_moved"] > 0
+
+
+def test_swap_contract():
+    bm = BlockManager(10, 4, 8, reserved_block=9)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.swap_out(1)  # unknown sequence
+    assert e.value.status == PA_ERR_SEQ
+    bm.add_sequence(1, 10, np.arange(10))  # blocks 0, 1, 2
+    bm.set_host_pool(2)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.swap_out(1)  # three blocks, two host blocks: nothing moves
+    assert e.value.status == PA_ERR_NOMEM and bm.stats()["used_blocks"] == 3
+    bm.set_host_pool(5)
+    bm.fork(1, 2)
+    bm.append_slots([1])  # sequence 1's shared last block needs a copy first
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.swap_out(1)
+    assert e.value.status == -2  # pending copy-on-write pairs
+    bm.take_copies()
+    pairs = bm.swap_out(1)
+    assert pairs[:, 0].tolist() == [0, 1, 3] and len(set(pairs[:, 1].tolist())) == 3
+    assert bm.stats()["used_blocks"] == 3  # 0, 1 still used by sequence 2; 3 freed; 2 is sequence 2's
+    for call in (lambda: bm.append_slots([1]), lambda: bm.fork(1, 5), lambda: bm.block_tables([1])):
+        with pytest.raises(pa.PagedAttentionError):
+            call()
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.add_sequence(1, 1, None)  # the id is still taken
+    assert e.value.status == PA_ERR_SEQ
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.set_host_pool(8)  # host blocks are in use
+    assert e.value.status == PA_ERR_SEQ
+    back = bm.swap_in(1)
+    assert back[:, 0].tolist() == pairs[:, 1].tolist()
+    tables, lens = bm.block_tables([1])
+    assert lens[0] == 11 and tables[0, :3].tolist() == back[:, 1].tolist()
+    assert bm.swap_stats() == {"free_host_blocks": 5, "used_host_blocks": 0, "swapped_sequences": 0,
+                               "blocks_moved": 6}
+    bm.swap_out(2)
+    bm.free_sequence(2)  # a swapped-out sequence gives its host blocks back
+    assert bm.swap_stats()["free_host_blocks"] == 5
