@@ -8,7 +8,7 @@
 namespace pa {
 
 constexpr int kWave = 64;
-constexpr int kTile = 16;  // tokens per tile; a tile never straddles a block because block_size >= 16
+constexpr int kTile = 16;  // tokens per tile; tiles start on multiples of 16 (with 8-slot blocks, a tile has two 8-row halves)
 
 struct alignas(16) U4 {
   uint32_t x, y, z, w;
