@@ -317,3 +317,33 @@ def test_full_workload_step(name):
         # copy-on-write leaves every output unchanged (bit for bit) against reading the shared blocks
         pre = decode(st, t, st.block_tables_pre, st.partition_size)
         np.testing.assert_array_equal(gpu, pre)
+
+
+# --------------------------------------------------------------------------------------------------------
+# maximum sizes: very long contexts (thousands of partitions, 64-bit pool offsets) and the grid's sequence limit
+
+
+@pytest.mark.parametrize("hq,hkv,dt", [(8, 8, "bf16"), (32, 8, "bf16"), (16, 4, "fp8")])
+def test_very_long_contexts(hq, hkv, dt):
+    st = custom_structure("long", 451, [131072, 70001, 5], hq, hkv, 128, 16, dt, pool_factor=1.02)
+    t = materialize(st, DEV, chunk_blocks=4096)
+    h = {k: to_host(v) for k, v in t.items()}
+    rows = np.array([[0, 0], [0, hq - 1], [1, hq // 2], [2, 1]], np.int32)
+    ref = oracle_decode(st, h, st.block_tables_pre, rows=rows)
+    for part in (-1, 4096):
+        gpu = decode(st, t, st.block_tables_pre, part)
+        assert np.isfinite(gpu).all()
+        assert_attention_close(gpu[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], dt, f"partition {part}")
+
+
+def test_grid_limit_of_sequences():
+    # 65535 sequences (the grid's z limit) of 0..3 tokens each, one head of 64 dims
+    B = 65535
+    lens = np.random.default_rng(452).integers(0, 4, size=B)
+    st = custom_structure("many", 452, lens, 1, 1, 64, 16, "bf16", pool_factor=1.0)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    gpu = decode(st, t, st.block_tables_pre, -1)
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    assert_attention_close(gpu, ref, "bf16", "65535 sequences")
+    assert (gpu[lens == 0] == 0).all()
