@@ -108,7 +108,22 @@ def pin_sampled_rows(lib):
                             qs[::-1].copy(), st.scale, lib=lib)
 
 
-PINS = [pin_against_brute, pin_against_sdpa, pin_one_token_is_decode, pin_sampled_rows]
+def pin_golden_multi(lib):
+    # hand-computed closed forms (tests/golden/hand_examples.json, kind "multi")
+    from tests.test_oracle_pins import _golden_cases, _golden_decode_inputs
+
+    n = 0
+    for c in _golden_cases():
+        if c["kind"] != "multi":
+            continue
+        q, kc, vc, bt, cl, scale = _golden_decode_inputs(c)
+        out = oracle.decode_multi(q, kc, vc, bt, cl, np.array(c["query_start"], np.int32), scale, lib=lib)
+        np.testing.assert_allclose(out, np.array(c["expected"]), rtol=0, atol=4e-15, err_msg=c["name"])
+        n += 1
+    assert n > 0
+
+
+PINS = [pin_against_brute, pin_against_sdpa, pin_one_token_is_decode, pin_sampled_rows, pin_golden_multi]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
