@@ -3,9 +3,9 @@
 
 A step is one decode step of a batch over its paged KV pool: copy-on-write block copies (the workload with a
 shared prefix), the slot-mapped write of every sequence's new K/V, then paged decode attention over the whole
-context (single pass, or split-context partitions plus the log-sum-exp reduce). Inputs are seeded synthetic
-tensors already resident in HBM; consecutive steps read different replicas of the pools so that no step can
-be served from the 256 MB last-level cache left warm by the previous one.
+context (single pass, split-context partitions or the balanced split, plus the log-sum-exp reduce). Inputs are
+seeded synthetic tensors already resident in HBM; consecutive steps read different replicas of the pools so
+that no step can be served from the 256 MB last-level cache left warm by the previous one.
 
 Prints one JSON line: whole-step achieved GB/s (algorithmic bytes / step time), decode queries/s, a roofline
 entry for the attention call (HIP events on the stream it runs on) and the CPU oracle's rate on the host cores.
@@ -517,7 +517,7 @@ def main() -> int:
             "kv_cache_dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[st.dtype],
             "context_len_mean": float(st.context_lens.mean()),
             "context_len_max": int(st.context_lens.max()),
-            "partition_size": launched_part,
+            "partition_size": "balanced" if launched_part == pa.PA_PARTITION_BALANCED else launched_part,
             "pool_blocks": st.num_blocks,
             "replicas": len(pools),
             "seed": st.seed,
@@ -539,7 +539,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_attention_decode" if Q == 1 else "paged_attention_decode_multi") +
-                      " (partition kernel + log-sum-exp reduce when split)",
+                      " (partition or balanced-split kernel + log-sum-exp reduce when split)",
             "achieved": round(attn_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -52,6 +52,9 @@ extern "C" {
 #define PA_ERR_ALIGN (-7)       /* a pointer is not 16-byte aligned */
 #define PA_ERR_POINTER (-10)    /* swap_blocks: a pool or the pairs are not memory this device can access */
 
+/* partition_size value that asks for the balanced split (see paged_attention_decode) */
+#define PA_PARTITION_BALANCED 1
+
 /* PA_ABI_VERSION of the loaded library. */
 int pa_abi_version(void);
 
@@ -61,7 +64,8 @@ const char *pa_strerror(int status);
 /*
  * Partition size (in tokens) that paged_attention_decode uses for a given `partition_size` argument:
  * 0 stays 0 (single pass), a positive value is returned unchanged, -1 is replaced by the library's choice
- * for these sizes. Returns a negative status for an invalid request.
+ * for these sizes (PA_PARTITION_BALANCED when that is the balanced split). Returns a negative status for an
+ * invalid request.
  */
 int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -70,6 +74,10 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
 /*
  * Bytes of workspace paged_attention_decode needs for these sizes (0 when the call runs single pass).
  * Arguments as in paged_attention_decode. Returns 0 as well for invalid sizes (the decode call reports them).
+ * Split into partitions of P tokens: partials [num_seqs][num_q_heads][ceil(max_context_len / P)][head_dim]
+ * fp32, then their (max, sum) pairs, each part 256-byte aligned. Balanced split: partials
+ * [num_q_heads][R][2][head_dim] fp32 and their pairs for R = 1024 / ceil(num_q_heads / 2) runs per head (at
+ * least 1), then (query rows + 1) int32 tile counts.
  */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -100,7 +108,13 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *                  caches: paged_attention_decode_scaled)
  *   partition_size 0 = one pass over each context; > 0 = split each context into partitions of this many
  *                  tokens (a multiple of 16) and merge the partial softmax states with a log-sum-exp
- *                  reduction; -1 = the library chooses (paged_attention_partition_size)
+ *                  reduction; PA_PARTITION_BALANCED = the balanced split: the K/V tiles of all sequences,
+ *                  in sequence order, are cut into equal runs, one per wave of a grid that fills the chip, so
+ *                  every wave streams the same number of bytes; a sequence cut by run boundaries is merged
+ *                  by the same log-sum-exp reduction (single-head kernel only, at most 2048 query rows and
+ *                  rows x max_context_len <= 2^30; PA_ERR_UNSUPPORTED otherwise); -1 = the library chooses
+ *                  (paged_attention_partition_size): the balanced split wherever the single-head kernel
+ *                  would otherwise split its contexts
  *   workspace      device scratch of at least paged_attention_workspace_bytes(...) bytes when that is
  *                  non-zero (may be NULL otherwise); contents need no initialisation and are clobbered
  *   stream         hipStream_t

@@ -22,6 +22,7 @@ STREAM_SINK_FLOATS = 8192
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_OK = 0
+PA_PARTITION_BALANCED = 1  # partition_size that asks for the balanced split (equal runs of tiles per wave)
 ABI_VERSION = 1
 
 _lib = None
@@ -131,7 +132,8 @@ def _int32(t, name):
 
 def partition_size_for(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
                        partition_size=-1) -> int:
-    """Partition size the decode call launches with (0 = single pass)."""
+    """Partition size the decode call launches with (0 = single pass, PA_PARTITION_BALANCED = the balanced
+    split)."""
     r = load_library().paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                                       max_context_len, kv_dtype, partition_size)
     _check("paged_attention_partition_size", r if r < 0 else 0)

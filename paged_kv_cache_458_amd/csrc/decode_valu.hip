@@ -391,6 +391,357 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   for (int e = 0; e < kDpl; ++e) dst[e] = acc[e] * inv;
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// Balanced split. The partition kernel gives each wave one partition of one row, so a batch of unequal
+// lengths leaves waves of unequal length: once the short ones finish, part of the chip idles while the
+// longest drain. Here the tiles of all query rows, taken in row order, form one list cut into `chunks` equal
+// runs of consecutive tiles, one run per (head, wave); the host sizes the grid to one wave per wave slot of
+// the chip, so every wave streams the same number of tiles from start to end. A run crosses row boundaries:
+// a row lying wholly inside one run is finished there and written to `out`; a row cut by run boundaries leaves
+// one partial (max, sum, normalised output) per run it touches, merged by balanced_reduce_kernel with the
+// rule of the partition merge. Partial slots: [head][run][2], slot 0 for the row a run starts inside, slot 1
+// for the row it ends inside. Loads keep the ring of kStages tiles of the partition kernel; a row's query
+// rides in the ring with the row's first tile of the run.
+//
+// Every workgroup first derives the rows' extents and the exclusive prefix of their tile counts in LDS
+// (rows of one sequence in several-token batches: row j of QL attends over L - QL + j + 1 positions); the
+// first workgroup also publishes the prefix for the merge.
+template <int KV, int D, bool kMulti>
+__global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_balanced_kernel(const DecodeArgs a) {
+  using S = Shape<KV, D>;
+  constexpr int NL = S::kLoads;
+  constexpr int TT = S::kTileTok;
+  constexpr int NT = kWave * kWavesPerGroup;
+  extern __shared__ int32_t lds_rows[];
+  __shared__ int32_t wave_total[kWavesPerGroup];
+  const int T = a.num_tokens;
+  int32_t* __restrict__ P = lds_rows;           // P[r]: tiles of the rows before r; P[T]: all tiles
+  int32_t* __restrict__ Ex = lds_rows + T + 1;  // positions row r attends over
+  int32_t* __restrict__ Sq = Ex + T;            // sequence of row r (several-token batches only)
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // extents and tile counts; P[r + 1] holds row r's count until the scan. Rows no sequence claims stay empty.
+  for (int r = tid; r < T; r += NT) {
+    P[r + 1] = 0;
+    Ex[r] = 0;
+    if constexpr (kMulti) Sq[r] = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < a.num_seqs; s += NT) {
+    const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+    int64_t q0 = s, ql = 1;
+    if constexpr (kMulti) {
+      q0 = a.query_start[s];
+      ql = (int64_t)a.query_start[s + 1] - q0;
+    }
+    const int64_t jb = q0 < 0 ? -q0 : 0, je = min(ql, (int64_t)T - q0);  // rows inside [0, T) only
+    for (int64_t j = jb; j < je; ++j) {
+      const int E = (int)max((int64_t)0, min((int64_t)L, L - ql + j + 1));
+      Ex[q0 + j] = E;
+      P[q0 + j + 1] = (E + TT - 1) / TT;
+      if constexpr (kMulti) Sq[q0 + j] = s;
+    }
+  }
+  __syncthreads();
+  {
+    // exclusive scan: each thread sums a run of rows, a wave scan and the waves' totals give its offset
+    const int per = (T + NT - 1) / NT;
+    const int rb = tid * per;
+    int sum = 0;
+    for (int k = 0; k < per; ++k)
+      if (rb + k < T) sum += P[rb + k + 1];
+    int inc = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(inc, off);
+      if (lane >= off) inc += v;
+    }
+    if (lane == kWave - 1) wave_total[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) inc += wave_total[w];
+    int run = inc - sum;
+    for (int k = 0; k < per; ++k)
+      if (rb + k < T) {
+        run += P[rb + k + 1];
+        P[rb + k + 1] = run;
+      }
+    if (tid == 0) P[0] = 0;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int r = tid; r <= T; r += NT) a.tile_prefix[r] = P[r];
+
+  const int h = blockIdx.x * kWavesPerGroup + wave;
+  if (h >= a.num_q_heads) return;
+  const int chunk = blockIdx.y;
+  const int total = __builtin_amdgcn_readfirstlane(P[T]);
+  const int C = (total + a.chunks - 1) / a.chunks;  // tiles per run
+  const int g0 = chunk * C;                          // this wave's run: tiles [g0, g1) of the list
+  const int g1 = min(g0 + C, total);
+  if (g0 >= g1) return;
+  const int n = g1 - g0;
+
+  const int g = h / a.group;
+  const int r = lane / S::kRowLanes;
+  const int c = lane % S::kRowLanes;
+  const bool lane_ok = c < S::kHeadLanes;
+  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
+  constexpr uint32_t kNowhere = 0x80000000u;
+  uint32_t lane_off[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    lane_off[i] = lane_ok ? (uint32_t)((i * S::kRows + r) * row_bytes + (int64_t)g * D * S::kEsize + c * 16)
+                          : kNowhere;
+  uint32_t q_off[S::kQWords];
+#pragma unroll
+  for (int i = 0; i < S::kQWords; ++i) q_off[i] = lane_ok ? (uint32_t)((c * S::kQWords + i) * 16) : kNowhere;
+  constexpr uint32_t kQBytes = D * S::kQEsize;
+  const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
+  const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
+  const char* __restrict__ qbase = static_cast<const char*>(a.query) + (int64_t)h * kQBytes;
+  const int64_t q_row_bytes = (int64_t)a.num_q_heads * kQBytes;
+
+  // the run's first row: the first r with P[r + 1] > g0
+  int lo = 0, hi = T - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(P[mid + 1]) <= g0) lo = mid + 1;
+    else hi = mid;
+  }
+  // the next row holding tiles after `row` (one exists while tiles of the run remain)
+  auto next_row = [&](int row) {
+    int x = row + 1;
+    while (__builtin_amdgcn_readfirstlane(P[x + 1]) == __builtin_amdgcn_readfirstlane(P[x])) ++x;
+    return x;
+  };
+  // What the consumer of a tile needs, packed at issue into one scalar per ring slot: live rows of the tile,
+  // whether it opens (takes the row's query) or closes its row segment, whether that segment is the whole row
+  // (written to out) or a partial and in which slot, a block id outside the pool, and the query row.
+  constexpr uint32_t kRowsMask = 31u, kFirst = 1u << 5, kLast = 1u << 6, kWhole = 1u << 7, kSlot1 = 1u << 8,
+                     kBad = 1u << 9;
+  constexpr int kRowShift = 12;
+  auto table_of = [&](int row) {
+    const int s = kMulti ? __builtin_amdgcn_readfirstlane(Sq[row]) : row;
+    return as_constant(a.block_tables) + (int64_t)s * a.max_blocks_per_seq;
+  };
+
+  // issue cursor: row, tile within the row, the row's first tile in the list and tile count, extent, table
+  int i_row = lo;
+  int i_p0 = __builtin_amdgcn_readfirstlane(P[i_row]);
+  int i_nt = __builtin_amdgcn_readfirstlane(P[i_row + 1]) - i_p0;
+  int i_ext = __builtin_amdgcn_readfirstlane(Ex[i_row]);
+  int i_tile = g0 - i_p0;
+  const ConstI32* i_table = table_of(i_row);
+
+  Words<S::kQWords> q;
+  float m = -INFINITY, l = 0.f;
+  float acc[S::kEpl];
+#pragma unroll
+  for (int e = 0; e < S::kEpl; ++e) acc[e] = 0.f;
+  bool seg_bad = false;
+
+  U4 kb[kStages][NL], vb[kStages][NL];
+  Words<S::kQWords> qb[kStages];
+  uint32_t info[kStages];
+  constexpr bool kHalves = TT == kTile && S::kRows <= kTile / 2;
+  auto issue = [&](U4* kq, U4* vq, Words<S::kQWords>& qq, uint32_t& tinfo, int jj) {
+    const bool live = jj < n;
+    const int t = i_tile * TT;
+    bool bad = false;
+    const int last8 = (i_ext - 1) & ~(kTile / 2 - 1);
+    const int64_t base0 = tile_slot_bytes(i_table, t, a.bs_log2, a.num_blocks, row_bytes, bad);
+    const int64_t base1 = !kHalves ? base0
+                          : a.bs_log2 == 3
+                              ? tile_slot_bytes(i_table, min(t + kTile / 2, last8), a.bs_log2, a.num_blocks,
+                                                row_bytes, bad)
+                              : base0 + (kTile / 2) * row_bytes;
+    const int rows = live ? min(TT, i_ext - t) : 0;
+    const uint32_t live0 = (uint32_t)(kHalves ? min(rows, kTile / 2) : rows) * (uint32_t)row_bytes;
+    const uint32_t live1 = (uint32_t)max(rows - kTile / 2, 0) * (uint32_t)row_bytes;
+    const __amdgpu_buffer_rsrc_t kr0 = make_rsrc(kbase + base0, live0), kr1 = make_rsrc(kbase + base1, live1);
+    const __amdgpu_buffer_rsrc_t vr0 = make_rsrc(vbase + base0, live0), vr1 = make_rsrc(vbase + base1, live1);
+    const uint32_t half_off = (uint32_t)((kTile / 2) * row_bytes);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (!kHalves || i * S::kRows < kTile / 2) {
+        kq[i] = load16<kPolStream>(kr0, lane_off[i]);
+        vq[i] = load16<kPolStream>(vr0, lane_off[i]);
+      } else {
+        kq[i] = load16<kPolStream>(kr1, lane_off[i] - half_off);
+        vq[i] = load16<kPolStream>(vr1, lane_off[i] - half_off);
+      }
+    }
+    // the row's query, with its first tile of the run (an empty descriptor otherwise: zeros, no access)
+    const bool first = i_tile == 0 || jj == 0;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(qbase + (int64_t)i_row * q_row_bytes, live && first ? kQBytes : 0u);
+#pragma unroll
+    for (int i = 0; i < S::kQWords; ++i) qq.w[i] = load16<0>(qr, q_off[i]);
+    tinfo = (uint32_t)rows | (first ? kFirst : 0u) | (i_tile == i_nt - 1 || jj == n - 1 ? kLast : 0u) |
+            (i_p0 >= g0 && i_p0 + i_nt <= g1 ? kWhole : 0u) | (i_p0 > g0 ? kSlot1 : 0u) | (bad ? kBad : 0u) |
+            ((uint32_t)i_row << kRowShift);
+    if (live && jj + 1 < n && ++i_tile == i_nt) {
+      i_row = next_row(i_row);
+      i_p0 = __builtin_amdgcn_readfirstlane(P[i_row]);
+      i_nt = __builtin_amdgcn_readfirstlane(P[i_row + 1]) - i_p0;
+      i_ext = __builtin_amdgcn_readfirstlane(Ex[i_row]);
+      i_table = table_of(i_row);
+      i_tile = 0;
+    }
+  };
+
+  // finish the current row segment: merge the row groups, write the row or its partial, reset the state
+  auto flush = [&](uint32_t tinfo) {
+#pragma unroll
+    for (int off = S::kRowLanes; off < kWave; off <<= 1) {
+      const float mo = __shfl_xor(m, off);
+      const float lo2 = __shfl_xor(l, off);
+      const float M = fmaxf(m, mo);
+      const float Mr = M == -INFINITY ? 0.f : M;
+      const float fa = fast_exp2(m - Mr), fb = fast_exp2(mo - Mr);
+      l = l * fa + lo2 * fb;
+#pragma unroll
+      for (int e = 0; e < S::kEpl; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], off) * fb;
+      m = M;
+    }
+    if (r == 0 && lane_ok) {
+      const float inv = l > 0.f ? a.v_scale / l : 0.f;
+      const float poison = __uint_as_float(0x7fc00000u);
+      float* dst;
+      if (tinfo & kWhole) {
+        dst = a.out + ((int64_t)(tinfo >> kRowShift) * a.num_q_heads + h) * D + c * S::kEpl;
+      } else {
+        const int64_t wrow = ((int64_t)h * a.chunks + chunk) * 2 + (tinfo & kSlot1 ? 1 : 0);
+        dst = a.ws_o + wrow * D + c * S::kEpl;
+        if (c == 0) {
+          a.ws_ml[2 * wrow] = seg_bad ? poison : m;
+          a.ws_ml[2 * wrow + 1] = l;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < S::kEpl; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            seg_bad ? make_float4(poison, poison, poison, poison)
+                    : make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    }
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < S::kEpl; ++e) acc[e] = 0.f;
+    seg_bad = false;
+  };
+
+  auto consume = [&](const U4* kq, const U4* vq, const Words<S::kQWords>& qq, uint32_t tinfo) {
+    tinfo = __builtin_amdgcn_readfirstlane(tinfo);
+    if (tinfo & kFirst) q = qq;
+    seg_bad |= (tinfo & kBad) != 0;
+    const int rows = (int)(tinfo & kRowsMask);
+    const bool full = rows == TT;
+    float sc[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      sc[i] = group_sum<S::kRowLanes>(dot_chunk<KV>(q, kq[i])) * a.scale_log2;
+      if (!full && i * S::kRows + r >= rows) sc[i] = -INFINITY;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) mt = fmaxf(mt, sc[i]);
+    const float mn = fmaxf(m, mt);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float p = fast_exp2(sc[i] - mref);
+      l += p;
+      U4 v = vq[i];
+      if (!full && i * S::kRows + r >= rows) v = U4{0u, 0u, 0u, 0u};
+      axpy_chunk<KV>(acc, p, v);
+    }
+    m = mn;
+    if (tinfo & kLast) flush(tinfo);
+  };
+
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) issue(kb[i], vb[i], qb[i], info[i], i);
+  int j = 0;
+  for (; j + kStages <= n; j += kStages) {
+#pragma unroll
+    for (int i = 0; i < kStages; ++i) {
+      const int w = (i + kStages - 1) % kStages;
+      issue(kb[w], vb[w], qb[w], info[w], j + i + kStages - 1);
+      consume(kb[i], vb[i], qb[i], info[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (j + i < n) consume(kb[i], vb[i], qb[i], info[i]);
+}
+
+// Merge of the balanced split's partials: one wave per (query row, head). A row whose tiles lie in one run was
+// written by the partition kernel; a row with no tile attends over nothing and gets a zero row here; a row
+// spanning runs c0 .. c1 has the partial of run c0 in slot 1 (slot 0 when it starts exactly at c0's first
+// tile) and those of runs c0 + 1 .. c1 in slot 0.
+template <int D>
+__global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs a) {
+  constexpr int kDpl = (D + kWave - 1) / kWave;
+  constexpr int kActive = D / kDpl;
+  const int lane = threadIdx.x;
+  const bool lane_ok = lane < kActive;
+  const int h = blockIdx.x;
+  const int row = blockIdx.y;
+  const int p0 = a.tile_prefix[row], p1 = a.tile_prefix[row + 1], total = a.tile_prefix[a.num_tokens];
+  float* dst = a.out + ((int64_t)row * a.num_q_heads + h) * D + (lane_ok ? lane : 0) * kDpl;
+  if (p1 <= p0) {
+    if (lane_ok)
+#pragma unroll
+      for (int e = 0; e < kDpl; ++e) dst[e] = 0.f;
+    return;
+  }
+  const int C = (total + a.chunks - 1) / a.chunks;
+  const int c0 = p0 / C, c1 = (p1 - 1) / C;
+  if (c0 == c1) return;
+  const int np = c1 - c0 + 1;
+  const int64_t base = ((int64_t)h * a.chunks + c0) * 2;
+  const int64_t first = base + (p0 != c0 * C ? 1 : 0);
+  const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.ws_ml);
+  const float* __restrict__ o = a.ws_o + (lane_ok ? lane : 0) * kDpl;
+  auto slot = [&](int k) { return k == 0 ? first : base + 2 * (int64_t)k; };
+
+  float M = -INFINITY;
+  for (int k = lane; k < np; k += kWave) M = fmaxf(M, ml[slot(k)].x);
+  M = wave_max(M);
+  const float Mr = M == -INFINITY ? 0.f : M;
+  float acc[kDpl];
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  for (int k0 = 0; k0 < np; k0 += kWave) {
+    float w = 0.f;
+    if (k0 + lane < np) {
+      const float2 v = ml[slot(k0 + lane)];
+      w = v.y * fast_exp2(v.x - Mr);
+    }
+    wsum += w;
+    const int cnt = min(kWave, np - k0);
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+      const float* __restrict__ op = o + slot(k0 + k) * D;
+#pragma unroll
+      for (int e = 0; e < kDpl; ++e) acc[e] = fmaf(wk, op[e], acc[e]);
+    }
+  }
+  const float wtot = wave_sum(wsum);
+  const float inv = wtot > 0.f ? 1.0f / wtot : 0.f;
+  if (!lane_ok) return;
+#pragma unroll
+  for (int e = 0; e < kDpl; ++e) dst[e] = acc[e] * inv;
+}
+
 }  // namespace
 
 template <int KV>
@@ -416,6 +767,60 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t str
   if (kv_dtype == PA_F32) return launch_kv<PA_F32>(a, grid, block, stream);
   if (kv_dtype == PA_FP8_E4M3) return launch_kv<PA_FP8_E4M3>(a, grid, block, stream);
   return hipErrorInvalidValue;
+}
+
+template <int KV, bool kMulti>
+hipError_t launch_balanced_kv(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: decode_valu_balanced_kernel<KV, 64, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 80: decode_valu_balanced_kernel<KV, 80, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 96: decode_valu_balanced_kernel<KV, 96, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 112: decode_valu_balanced_kernel<KV, 112, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 128: decode_valu_balanced_kernel<KV, 128, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 192: decode_valu_balanced_kernel<KV, 192, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 256: decode_valu_balanced_kernel<KV, 256, kMulti><<<grid, block, lds, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KV>
+hipError_t launch_balanced_dtype(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  const bool multi = a.query_start != nullptr;
+  const size_t lds = (size_t)((multi ? 3 : 2) * (int64_t)a.num_tokens + 1) * sizeof(int32_t);
+  return multi ? launch_balanced_kv<KV, true>(a, grid, block, lds, stream)
+               : launch_balanced_kv<KV, false>(a, grid, block, lds, stream);
+}
+
+int32_t balanced_chunks(int32_t num_q_heads) {
+  const int32_t groups = (num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+  return groups >= kResidentWaves / kWavesPerGroup ? 1 : kResidentWaves / kWavesPerGroup / groups;
+}
+
+hipError_t launch_decode_valu_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  if (a.num_tokens > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix) return hipErrorInvalidValue;
+  const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.chunks, 1);
+  const dim3 block(kWave * kWavesPerGroup);
+  if (kv_dtype == PA_BF16) return launch_balanced_dtype<PA_BF16>(a, grid, block, stream);
+  if (kv_dtype == PA_F32) return launch_balanced_dtype<PA_F32>(a, grid, block, stream);
+  if (kv_dtype == PA_FP8_E4M3) return launch_balanced_dtype<PA_FP8_E4M3>(a, grid, block, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, a.num_tokens);
+  const dim3 block(kWave);
+  switch (a.head_dim) {
+    case 64: balanced_reduce_kernel<64><<<grid, block, 0, stream>>>(a); break;
+    case 80: balanced_reduce_kernel<80><<<grid, block, 0, stream>>>(a); break;
+    case 96: balanced_reduce_kernel<96><<<grid, block, 0, stream>>>(a); break;
+    case 112: balanced_reduce_kernel<112><<<grid, block, 0, stream>>>(a); break;
+    case 128: balanced_reduce_kernel<128><<<grid, block, 0, stream>>>(a); break;
+    case 192: balanced_reduce_kernel<192><<<grid, block, 0, stream>>>(a); break;
+    case 256: balanced_reduce_kernel<256><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {

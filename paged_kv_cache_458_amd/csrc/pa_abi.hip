@@ -63,8 +63,11 @@ struct Plan {
   bool split = false;
   bool mfma = false;           // the matrix-core kernel runs (else the per-head one)
   int32_t col_groups = 1;      // its column groups of 16 per KV head
+  bool balanced = false;       // balanced split of the single-head kernel (equal runs of tiles per wave)
+  int32_t chunks = 0;          // its runs per query head
   size_t ws_bytes = 0;
   size_t ws_ml_offset = 0;
+  size_t ws_prefix_offset = 0; // balanced split: the rows' tile prefix
 };
 
 // Library choice of partition size. A partition is the unit of work of one wave (the GQA kernel may take
@@ -121,7 +124,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
-  if (partition_size < -1 || (partition_size > 0 && partition_size % kTileTokens != 0)) {
+  if (partition_size < -1 || (partition_size > PA_PARTITION_BALANCED && partition_size % kTileTokens != 0)) {
     p.status = PA_ERR_SHAPE;
     return p;
   }
@@ -133,8 +136,28 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     return p;
   }
   const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * p.col_groups : (int64_t)num_tokens * num_q_heads;
+  // The balanced split needs the single-head kernel, rows one workgroup's LDS holds, and tile counts that fit
+  // 32 bits. The library takes it wherever it would otherwise split the single-head kernel's contexts.
+  const bool balanced_ok = !gqa && num_tokens <= pa::kMaxBalancedRows &&
+                           (int64_t)num_tokens * (max_context_len > 0 ? max_context_len : 1) <= (int64_t)1 << 30;
+  if (partition_size == PA_PARTITION_BALANCED && !balanced_ok) {
+    p.status = PA_ERR_UNSUPPORTED;
+    return p;
+  }
   int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
+  if (partition_size == PA_PARTITION_BALANCED || (partition_size == -1 && balanced_ok && part > 0 && part < whole)) {
+    p.balanced = true;
+    p.split = true;
+    p.chunks = pa::balanced_chunks(num_q_heads);
+    p.partition = 0;
+    p.max_partitions = 1;
+    const size_t o_bytes = pa::balanced_o_elems(num_q_heads, p.chunks, head_dim) * sizeof(float);
+    p.ws_ml_offset = round_up(o_bytes, 256);
+    p.ws_prefix_offset = round_up(p.ws_ml_offset + pa::balanced_ml_elems(num_q_heads, p.chunks) * sizeof(float), 256);
+    p.ws_bytes = p.ws_prefix_offset + ((size_t)num_tokens + 1) * sizeof(int32_t);
+    return p;
+  }
   if (part == 0 || part >= whole) {
     p.partition = (int32_t)(whole > INT32_MAX ? INT32_MAX : whole);
     p.max_partitions = 1;
@@ -183,7 +206,7 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, kv_dtype, partition_size);
   if (p.status != PA_OK) return p.status;
-  return p.split ? p.partition : 0;
+  return p.balanced ? PA_PARTITION_BALANCED : p.split ? p.partition : 0;
 }
 
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -201,7 +224,7 @@ int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_context_len, kv_dtype, partition_size);
   if (p.status != PA_OK) return p.status;
-  return p.split ? p.partition : 0;
+  return p.balanced ? PA_PARTITION_BALANCED : p.split ? p.partition : 0;
 }
 
 size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
@@ -285,8 +308,15 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   a.num_tokens = num_tokens;
   a.max_query_len = max_query_len;
   a.col_groups = plan.col_groups;
+  a.chunks = plan.chunks;
+  a.tile_prefix =
+      plan.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_prefix_offset) : nullptr;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.balanced) {
+    if (pa::launch_decode_valu_balanced(a, kv_dtype, st) != hipSuccess) return PA_ERR_HIP;
+    return pa::launch_balanced_reduce(a, st) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
   const hipError_t err = plan.mfma ? pa::launch_decode_gqa_mfma(a, kv_dtype, st) : pa::launch_decode_valu(a, kv_dtype, st);
   if (err != hipSuccess) return PA_ERR_HIP;
   if (plan.split && pa::launch_lse_reduce(a, st) != hipSuccess) return PA_ERR_HIP;

@@ -65,14 +65,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Byte offset of the slot holding position t (t a multiple of kTile, so the kTile positions t .. t+15 are
 // consecutive slots of one block). A table entry outside [0, num_blocks) is replaced by block 0 -- always a
 // valid address -- and reported through `bad` so the caller can poison its result instead of faulting.
-__device__ __forceinline__ int64_t tile_slot_bytes(const int32_t* __restrict__ table_row, int t, int bs_log2,
-                                                   int64_t num_blocks, int64_t row_bytes, bool& bad) {
+template <typename TablePtr>
+__device__ __forceinline__ int64_t tile_slot_bytes(TablePtr table_row, int t, int bs_log2, int64_t num_blocks,
+                                                   int64_t row_bytes, bool& bad) {
   const int32_t phys = table_row[t >> bs_log2];
   const bool ok = (uint32_t)phys < (uint64_t)num_blocks;
   bad |= !ok;
   const int64_t block = ok ? (int64_t)phys : 0;
   return ((block << bs_log2) + (t & ((1 << bs_log2) - 1))) * row_bytes;
 }
+
+// Block tables are not written while a kernel runs. Read through the constant address space, a wave-uniform
+// load of them stays a scalar load even in a kernel that also stores inside its main loop (where the compiler
+// could not otherwise rule out that a store changes the table, and would load it per lane and wait for every
+// load in flight before using it).
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
+__device__ __forceinline__ const ConstI32* as_constant(const int32_t* p) { return (const ConstI32*)p; }
 
 // ---------------------------------------------------------------------------------------------------------
 // Sum over aligned groups of N lanes (N = 4 .. 64), result in every lane of the group, via DPP

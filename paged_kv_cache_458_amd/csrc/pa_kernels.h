@@ -29,6 +29,8 @@ struct DecodeArgs {
   int32_t num_tokens;          // T
   int32_t max_query_len;       // query rows per sequence at most (1 without query_start)
   int32_t col_groups;          // matrix-core kernel: groups of 16 (query row, head) columns per KV head
+  int32_t chunks;              // balanced split: runs of tiles per query head (0: partitions as above)
+  int32_t* tile_prefix;        // balanced split: [T + 1] tiles of the rows before each row (workspace)
 };
 
 // The sequence that owns query row t: the last s with query_start[s] <= t (a scalar binary search; empty
@@ -65,6 +67,16 @@ constexpr int kMaxColGroups = 64;
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len);
 constexpr int kGqaTileTokens = 32;  // tokens per tile of the GQA kernel
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
+// Balanced split of the single-head kernel: the tiles of all query rows, in row order, cut into `chunks`
+// equal runs per head, one wave each; the grid is sized to one wave per wave slot of the chip.
+constexpr int kMaxBalancedRows = 2048;  // query rows whose tile counts one workgroup scans in LDS
+constexpr int kResidentWaves = 2048;    // 256 CUs x 4 SIMDs x 2 waves of the single-head kernel
+int32_t balanced_chunks(int32_t num_q_heads);  // runs per query head: the grid fills kResidentWaves
+hipError_t launch_decode_valu_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
+hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream);
+// workspace of a balanced launch: partials [Hq][chunks][2][D] fp32, then (m, l) [Hq][chunks][2][2]
+inline size_t balanced_o_elems(int64_t Hq, int64_t chunks, int64_t D) { return Hq * chunks * 2 * D; }
+inline size_t balanced_ml_elems(int64_t Hq, int64_t chunks) { return Hq * chunks * 2 * 2; }
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int64_t row_bytes,

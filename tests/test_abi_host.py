@@ -189,11 +189,45 @@ def test_workspace_and_partition_plan():
     # a partition that covers the longest context is a single pass
     assert pa.workspace_bytes(4, 4, 4, 64, 16, 64, pa.PA_F32, 64) == 0
     # the library's own choice is consistent with its workspace size
-    p = pa.partition_size_for(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1)
-    assert p == 0 or p % 16 == 0
-    assert (pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) > 0) == (p > 0)
+    for args in ((64, 64, 8, 128, 256, 4096, pa.PA_BF16), (4, 4, 4, 64, 16, 64, pa.PA_F32)):
+        p = pa.partition_size_for(*args, -1)
+        assert p == 0 or p % 16 == 0
+        assert (pa.workspace_bytes(*args, -1) > 0) == (p > 0)
     assert lib.paged_attention_workspace_bytes(4, 8, 3, 128, 16, 64, 1, -1) == 0  # invalid -> 0
     assert lib.paged_attention_partition_size(4, 8, 3, 128, 16, 64, 1, -1) == PA_ERR_SHAPE
+
+
+def balanced_ws(T, Hq, D):
+    runs = max(1, 1024 // ((Hq + 1) // 2))
+    o = (Hq * runs * 2 * D * 4 + 255) // 256 * 256
+    ml = (Hq * runs * 2 * 2 * 4 + 255) // 256 * 256
+    return o + ml + (T + 1) * 4
+
+
+def test_balanced_split_plan():
+    lib = pa.load_library()
+    B = pa.PA_PARTITION_BALANCED
+    # the library takes the balanced split where the single-head kernel would split its contexts
+    assert pa.partition_size_for(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == B
+    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == balanced_ws(64, 32, 128)
+    assert pa.workspace_bytes(7, 5, 5, 80, 16, 900, pa.PA_FP8_E4M3, B) == balanced_ws(7, 5, 80)
+    assert pa.workspace_bytes(3, 4096, 4096, 64, 16, 900, pa.PA_F32, B) == balanced_ws(3, 4096, 64)  # one run
+    # several tokens per sequence (fp32: the per-head kernel): one tile count per query row
+    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == B
+    assert pa.multi_workspace_bytes(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == balanced_ws(256, 32, 128)
+    # contexts that fit one partition stay single pass; grouped heads on the matrix cores keep partitions
+    assert pa.partition_size_for(4, 4, 4, 64, 16, 64, pa.PA_F32, -1) == 0
+    assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
+    # beyond 2048 query rows, or 2^30 row-positions, the default falls back to partitions ...
+    assert pa.partition_size_for(4096, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) % 16 == 0
+    assert pa.partition_size_for(2048, 32, 32, 128, 16, 1 << 20, pa.PA_BF16, -1) % 16 == 0
+    # ... and an explicit request is refused, as it is for the matrix-core kernel
+    for args in ((2049, 32, 32, 128, 16, 2048, pa.PA_BF16), (2048, 32, 32, 128, 16, 1 << 20, pa.PA_BF16),
+                 (64, 64, 8, 128, 256, 4096, pa.PA_BF16)):
+        assert lib.paged_attention_partition_size(*args, B) == PA_ERR_UNSUPPORTED
+        assert lib.paged_attention_workspace_bytes(*args, B) == 0
+    # partition sizes between the balanced code and 16 are not multiples of 16
+    assert lib.paged_attention_partition_size(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 2) == PA_ERR_SHAPE
 
 
 @pytest.mark.parametrize("over,status", [

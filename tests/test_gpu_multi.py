@@ -74,6 +74,8 @@ CASES = [
     # per-head kernel
     (505, [65, 200, 9], [3, 7, 2], 8, 2, 96, 16, "bf16"),              # head_dim 96
     (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
+    (510, [0, 8, 700, 30], [3, 12, 5, 1], 8, 8, 80, 16, "bf16"),      # QL > L, an empty context
+    (513, [2000, 5, 64, 300, 1], [7, 0, 4, 2, 1], 16, 16, 112, 8, "fp8"),  # an empty sequence; bs 8
 ]
 
 
@@ -85,11 +87,16 @@ def test_multi_parity(case):
     q, qs = query_rows(st, qls, DEV)
     h = {k: to_host(v) for k, v in t.items()}
     ref = oracle_multi(st, h, to_host(q), qs)
-    for part in (0, 16, 32, 64, 96, 512, -1):
+    kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[dt]
+    balanced = pa.load_library().paged_attention_multi_partition_size(
+        st.num_seqs, q.shape[0], max(qls), hq, hkv, d, bs, st.max_context_len, kd, pa.PA_PARTITION_BALANCED) > 0
+    for part in (0, 16, 32, 64, 96, 512, -1) + ((pa.PA_PARTITION_BALANCED,) if balanced else ()):
         gpu = run_multi(st, t, q, qs, part)
         close(gpu, ref, dt, f"partition {part}")
-    if seed == 508:  # rows with no earlier position are exact zeros
-        assert (gpu[:4] == 0).all() and np.abs(gpu[4]).max() > 0
+        if seed == 508:  # rows with no earlier position are exact zeros
+            assert (gpu[:4] == 0).all() and np.abs(gpu[4]).max() > 0
+        if seed == 510:  # the empty context's rows and the first 4 of the 8-token sequence's 12
+            assert (gpu[:7] == 0).all() and np.abs(gpu[7]).max() > 0
 
 
 @pytest.mark.parametrize("hq,hkv,dt", [(8, 8, "bf16"), (16, 2, "bf16"), (32, 8, "fp8"), (4, 4, "f32")])

@@ -57,6 +57,14 @@ def decode(st, t, tables, partition_size, context_lens=None, max_context_len=Non
     return out.cpu().numpy()
 
 
+def balanced_ok(st) -> bool:
+    """Whether the library runs the balanced split for these sizes (the single-head kernel)."""
+    kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
+    return pa.load_library().paged_attention_partition_size(
+        st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size, st.max_context_len, kd,
+        pa.PA_PARTITION_BALANCED) == pa.PA_PARTITION_BALANCED
+
+
 def oracle_decode(st, h, tables, context_lens=None, rows=None):
     cl = st.context_lens if context_lens is None else context_lens
     return oracle.decode(h["query"], h["key_cache"], h["value_cache"], tables, cl, st.scale, rows=rows,
@@ -126,7 +134,8 @@ def test_small_attention_parity(case):
     h = {k: to_host(v) for k, v in t.items()}
     ref = oracle_decode(st, h, st.block_tables_pre)
     # 16 cuts GQA tiles across partitions; 32, 64, 96 and 512 let one GQA wave cover several partitions
-    for part in (0, 16, 32, 64, 96, 512, -1):
+    parts = (0, 16, 32, 64, 96, 512, -1) + ((pa.PA_PARTITION_BALANCED,) if balanced_ok(st) else ())
+    for part in parts:
         gpu = decode(st, t, st.block_tables_pre, part)
         assert_attention_close(gpu, ref, dt, f"partition {part}")
 
@@ -293,6 +302,47 @@ def test_empty_context_bad_entries_and_clamped_lengths():
         assert np.isnan(gpu[3]).all()
         ref = oracle_decode(st, h, st.block_tables_pre)
         assert_attention_close(gpu[[1]], ref[[1]], "bf16", f"partition {part}")
+
+
+# --------------------------------------------------------------------------------------------------------
+# the balanced split: equal runs of tiles cut rows anywhere; rows that attend over nothing get zero rows
+
+
+@pytest.mark.parametrize("lens,hq,d,dt", [
+    ([0, 0, 700, 1, 0, 3000, 45, 0, 0], 8, 128, "bf16"),   # empty rows before, between and after
+    ([5000], 2, 64, "f32"),                                # one row cut into about a thousand runs
+    ([3, 1, 2, 17, 16, 15, 33] * 9, 32, 80, "fp8"),        # many short rows per run
+    ([900, 1300, 20, 2500], 16, 256, "bf16"),              # few rows, 512-byte head rows
+])
+def test_balanced_split_parity(lens, hq, d, dt):
+    st = custom_structure("bal", 441, lens, hq, hq, d, 16, dt, pool_factor=1.2)
+    assert balanced_ok(st)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    a = decode(st, t, st.block_tables_pre, pa.PA_PARTITION_BALANCED)
+    assert_attention_close(a, ref, dt, "balanced")
+    empty = np.asarray(lens) == 0
+    assert (a[empty] == 0).all()
+    np.testing.assert_array_equal(a, decode(st, t, st.block_tables_pre, pa.PA_PARTITION_BALANCED))
+
+
+def test_balanced_split_edge_cases():
+    # a bad table entry in a row that several runs cut poisons that row only, through the merge
+    st = custom_structure("baledge", 442, [4000, 64, 2500, 0], 4, 4, 128, 16, "bf16", max_context_len=4096)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    tables = st.block_tables_pre.copy()
+    tables[2, 100] = -3
+    lens = st.context_lens.copy()
+    lens[1] = 9000  # clamped to max_context_len: positions past the sequence's own blocks are poisoned slots
+    gpu = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=lens)
+    assert np.isnan(gpu[2]).all() and np.isnan(gpu[1]).all() and (gpu[3] == 0).all()
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    assert_attention_close(gpu[[0]], ref[[0]], "bf16", "balanced")
+    # every row empty: zero rows, no tile to read
+    z = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=np.zeros(4, np.int32))
+    assert (z == 0).all()
 
 
 # --------------------------------------------------------------------------------------------------------
