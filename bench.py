@@ -89,8 +89,9 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
     """Turn the FETCH_SIZE and WRITE_SIZE runs of this benchmark into bytes per attention call.
 
     Each counter is scaled by what it reads for the streaming copy kernel, whose traffic is known exactly
-    (COPY_BYTES read and COPY_BYTES written per dispatch). The attention call is the decode kernel plus, when
-    the context is split, the log-sum-exp merge kernel: their per-dispatch means are added.
+    (COPY_BYTES read and COPY_BYTES written per dispatch). The attention call is the decode kernel (partition
+    or balanced split) plus, when the context is split, its log-sum-exp merge kernel: their per-dispatch means
+    are added.
     """
     fetch, write = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
 
@@ -101,7 +102,8 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
     copy_f, copy_w = pick(fetch, "stream_copy_kernel"), pick(write, "stream_copy_kernel")
     f_scale, w_scale = COPY_BYTES / fetch[copy_f][0], COPY_BYTES / write[copy_w][0]
     rows, fb, wb = [], 0.0, 0.0
-    for key in ("decode_valu_kernel", "decode_gqa_mfma_kernel", "lse_reduce_kernel"):
+    for key in ("decode_valu_kernel", "decode_valu_balanced_kernel", "decode_gqa_mfma_kernel", "lse_reduce_kernel",
+                "balanced_reduce_kernel"):
         kf, kw = pick(fetch, key), pick(write, key)
         if kf is None:
             continue
