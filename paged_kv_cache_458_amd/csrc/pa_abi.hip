@@ -70,14 +70,24 @@ struct Plan {
   size_t ws_prefix_offset = 0; // balanced split: the rows' tile prefix
 };
 
+// Consecutive partitions one wave of the GQA kernel covers (1 or 2): two when the caller asks for partitions
+// of 512..1023 tokens, so that a wave still streams about 1024 tokens. Needs partitions made of whole
+// 32-token tiles.
+int32_t gqa_parts_per_wave(int32_t partition) {
+  return partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
+}
+
 // Library choice of partition size. A partition is the unit of work of one wave (the GQA kernel may take
-// several): long enough that the partial writes and the merge stay a small fraction of the traffic and that
+// two): long enough that the partial writes and the merge stay a small fraction of the traffic and that
 // per-wave start-up is amortised, short enough that the grid holds a few waves per slot of the chip so the
 // load is balanced. Measured on MI355X: 512 tokens for the single-head kernel, halved while its grid would
 // hold fewer than 4096 waves (two per wave slot), and 1024 for the grouped-query kernel, halved while its grid
-// would hold fewer than 2048 waves (one per slot: its waves run longest when they all start together).
-// `rows` counts the waves per partition: (sequence, KV head) pairs for the grouped-query kernel, (query row,
-// query head) pairs for the single-head one.
+// would hold fewer than 2048 waves (one per slot: its waves run longest when they all start together). The
+// waves are counted per span a wave covers: 512-token partitions go two to a grouped-query wave, so halving
+// 1024 to 512 adds no wave and the rule goes on to 256 (measured on MI355X: 64 sequences x 8 KV heads with
+// 128..2048-token contexts, 88 -> 67 us).
+// `rows` counts the waves per span: (sequence, KV head, column group) triples for the grouped-query kernel,
+// (query row, query head) pairs for the single-head one.
 // The grouped-query kernel runs single pass when its grid already holds a wave per slot without splitting
 // (measured on MI355X: 13-15% faster for 7B-shaped verification batches, whose 2048 (sequence, head) waves
 // fill the chip; the single-head kernel's 4096-wave rule keeps its split there, 11-13% faster than without).
@@ -85,15 +95,12 @@ int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa) {
   int32_t part = gqa ? 1024 : 512;
   const int64_t min_waves = gqa ? 2048 : 4096;
   if (gqa && rows >= min_waves) return 0;
-  while (part > 64 && rows * ((max_context_len + part - 1) / part) < min_waves) part /= 2;
+  auto waves = [&](int32_t p) {
+    const int64_t span = (int64_t)p * (gqa ? gqa_parts_per_wave(p) : 1);
+    return rows * ((max_context_len + span - 1) / span);
+  };
+  while (part > 64 && waves(part) < min_waves) part /= 2;
   return max_context_len <= part ? 0 : part;
-}
-
-// Consecutive partitions one wave of the GQA kernel covers (1 or 2): two when the caller asks for partitions
-// of 512..1023 tokens, so that a wave still streams about 1024 tokens. Needs partitions made of whole
-// 32-token tiles.
-int32_t gqa_parts_per_wave(int32_t partition) {
-  return partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
 }
 
 // num_tokens query rows (num_seqs in decode), at most max_query_len per sequence (1 in decode).

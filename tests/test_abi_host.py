@@ -197,6 +197,16 @@ def test_workspace_and_partition_plan():
     assert lib.paged_attention_partition_size(4, 8, 3, 128, 16, 64, 1, -1) == PA_ERR_SHAPE
 
 
+def test_grouped_query_default_counts_waves_per_span():
+    # 512-token partitions go two to a grouped-query wave: where 1024 leaves fewer than 2048 waves, 512 would
+    # leave the same number, so the default goes on to 256
+    assert pa.partition_size_for(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
+    assert pa.partition_size_for(16, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 128
+    # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head) pairs run single pass
+    assert pa.partition_size_for(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
+    assert pa.partition_size_for(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+
+
 def balanced_ws(T, Hq, D):
     runs = max(1, 1024 // ((Hq + 1) // 2))
     o = (Hq * runs * 2 * D * 4 + 255) // 256 * 256
