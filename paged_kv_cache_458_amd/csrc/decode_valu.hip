@@ -406,8 +406,10 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
 // Every workgroup first derives the rows' extents and the exclusive prefix of their tile counts in LDS
 // (rows of one sequence in several-token batches: row j of QL attends over L - QL + j + 1 positions); the
 // first workgroup also publishes the prefix for the merge.
+// At least two waves per SIMD, which the grid's size assumes (without the bound the E4M3 kernels at head_dim 192
+// and 256 would take 256 VGPRs plus 12 AGPRs and one wave per SIMD).
 template <int KV, int D, bool kMulti>
-__global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_balanced_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balanced_kernel(const DecodeArgs a) {
   using S = Shape<KV, D>;
   constexpr int NL = S::kLoads;
   constexpr int TT = S::kTileTok;
