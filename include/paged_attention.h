@@ -76,8 +76,10 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
  * Arguments as in paged_attention_decode. Returns 0 as well for invalid sizes (the decode call reports them).
  * Split into partitions of P tokens: partials [num_seqs][num_q_heads][ceil(max_context_len / P)][head_dim]
  * fp32, then their (max, sum) pairs, each part 256-byte aligned. Balanced split: partials
- * [num_q_heads][R][2][head_dim] fp32 and their pairs for R = 1024 / ceil(num_q_heads / 2) runs per head (at
- * least 1), then (query rows + 1) int32 tile counts.
+ * [num_q_heads][R][2][head_dim] fp32 and their pairs, then (query rows + 1) int32 tile counts, for R runs: on
+ * the single-head kernel R = 1024 / ceil(num_q_heads / 2) per head, on the matrix-core kernel (grouped heads)
+ * R = 2048 / (num_kv_heads rounded up to whole workgroups of W = min(8, largest power of two <= num_kv_heads)
+ * KV heads); at least 1 either way.
  */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -111,10 +113,11 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *                  reduction; PA_PARTITION_BALANCED = the balanced split: the K/V tiles of all sequences,
  *                  in sequence order, are cut into equal runs, one per wave of a grid that fills the chip, so
  *                  every wave streams the same number of bytes; a sequence cut by run boundaries is merged
- *                  by the same log-sum-exp reduction (single-head kernel only, at most 2048 query rows and
- *                  rows x max_context_len <= 2^30; PA_ERR_UNSUPPORTED otherwise); -1 = the library chooses
- *                  (paged_attention_partition_size): the balanced split wherever the single-head kernel
- *                  would otherwise split its contexts
+ *                  by the same log-sum-exp reduction (at most 2048 query rows and rows x max_context_len <=
+ *                  2^30; grouped heads that run on the matrix cores -- bf16 or E4M3 caches at head_dim 64 or
+ *                  128 -- also need G <= 16 heads per KV head; PA_ERR_UNSUPPORTED otherwise); -1 = the
+ *                  library chooses (paged_attention_partition_size): the balanced split wherever the
+ *                  single-head kernel would otherwise split its contexts, partitions on the matrix cores
  *   workspace      device scratch of at least paged_attention_workspace_bytes(...) bytes when that is
  *                  non-zero (may be NULL otherwise); contents need no initialisation and are clobbered
  *   stream         hipStream_t
@@ -161,6 +164,8 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
  *   max_query_len  the largest QL (>= 1). With bf16 or E4M3 caches at head_dim 64 or 128 the matrix cores take
  *                  all of a sequence's rows, reading its K/V once per 16 (row, grouped head) columns (at most
  *                  1024 columns); other calls read a sequence's K/V once per (row, head).
+ *   partition_size as in paged_attention_decode, except that PA_PARTITION_BALANCED is refused
+ *                  (PA_ERR_UNSUPPORTED) for calls that run on the matrix cores
  *   workspace      at least paged_attention_multi_workspace_bytes(...) bytes when that is non-zero
  * Other arguments as in paged_attention_decode_scaled. num_seqs == 0 or num_query_tokens == 0 is a no-op;
  * num_query_tokens > num_seqs * max_query_len is PA_ERR_SHAPE.

@@ -5,7 +5,11 @@
 // two products run as small dense contractions on v_mfma_f32_16x16x32_bf16 (bf16 inputs, fp32 accumulate):
 //
 //   S^T[32 tokens x 16]  = K_tile[32 x D] . Q^T[D x 16]      (the G heads padded to 16 columns)
-//   O^T[D x 16]         += V_tile^T[D x 32] . P^T[32 x 16]
+//   O^T[D x 16]         += V_tile^T[D x 32] . (P_hi + P_lo)^T[32 x 16]
+//
+// The probabilities enter as two bf16 operands, P_hi = bf16(P) and P_lo = bf16(P - P_hi), so the second
+// product keeps about 16 significant bits of every weight (V is exact in bf16); the extra MFMAs are free in a
+// kernel bound by its loads.
 //
 // The same columns serve sequences that bring several new tokens (speculative verification, a prompt chunk):
 // G heads x QL rows, each column with its own causal limit, so K/V are still read once per (sequence, KV
@@ -19,11 +23,12 @@
 //
 // Operand layouts. K rows are the A operand of the first product: lane (n, j) = (lane % 16, lane / 16) reads
 // row n, bytes 64c + 16j of each 16-row half from LDS. The result leaves lane (n, j) with the scores of head n
-// for tokens 4j..4j+3 of both halves; those eight probabilities are exactly that lane's B operand of the
+// for tokens 4j..4j+3 of both halves; those eight probabilities are exactly that lane's B operands of the
 // second product once the contraction index k = 8j + e is mapped to token (e < 4 ? 4j + e : 16 + 4j + e - 4)
 // -- no data moves between lanes. V^T needs eight tokens of one dim per lane, the transpose of the pool's
-// layout: gfx950's transposing LDS reads give it with two 8-byte reads per 16-dim column tile. The accumulator of the second product leaves lane (n, j) with head n, the same
-// head as its softmax state, so the online-softmax rescale is a per-lane multiply.
+// layout: gfx950's transposing LDS reads give it with two 8-byte reads per 16-dim column tile. The
+// accumulator of the second product leaves lane (n, j) with head n, the same head as its softmax state, so
+// the online-softmax rescale is a per-lane multiply.
 //
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
 // loads of the block table (one per 16-token half). Scores use the exp2 domain (scale * log2 e folded in).
@@ -71,6 +76,25 @@ __device__ __forceinline__ void stage_e4m3(char* p, const U4& c) {
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// A lane's eight probabilities exp2(sv[e] - mref) as the B operands of the P.V product, each weight split into
+// a bf16 pair p = hi + lo (lo rounds the exact fp32 remainder), so the two products together carry about 16
+// significant bits of every weight. With one bf16 rounding alone (8 bits), a context of a few tokens, where
+// one or two weights dominate, moves outputs by up to a few 1e-3. `psum` adds the fp32 weights.
+__device__ __forceinline__ void prob_operands(const float* sv, float mref, U4& hi, U4& lo, float& psum) {
+  uint32_t h[4], r[4];
+  psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float x0 = fast_exp2(sv[e] - mref), x1 = fast_exp2(sv[e + 1] - mref);
+    const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+    psum += x0 + x1;
+    h[e / 2] = h0 | (h1 << 16);
+    r[e / 2] = bf16_bits(x0 - __uint_as_float(h0 << 16)) | (bf16_bits(x1 - __uint_as_float(h1 << 16)) << 16);
+  }
+  hi = U4{h[0], h[1], h[2], h[3]};
+  lo = U4{r[0], r[1], r[2], r[3]};
 }
 
 // W waves (KV heads of one sequence) per workgroup: they stream the same slots of the pool side by side. At
@@ -314,18 +338,10 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     const float mref = mn == -INFINITY ? 0.f : mn;
     const float alpha = fast_exp2(m - mref);
     m = mn;
-    // probabilities, rounded to bf16 for the MFMA; the running sum adds the rounded values
-    uint32_t pw[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint32_t lo = bf16_bits(fast_exp2(sv[e] - mref));
-      const uint32_t hi = bf16_bits(fast_exp2(sv[e + 1] - mref));
-      psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-      pw[e / 2] = lo | (hi << 16);
-    }
+    U4 pb, pl;
+    float psum;
+    prob_operands(sv, mref, pb, pl, psum);
     l = l * alpha + psum;
-    const U4 pb{pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
       // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4)
@@ -337,7 +353,8 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
       acc[1] *= alpha;
       acc[2] *= alpha;
       acc[3] *= alpha;
-      o[nt] = mfma(U4{lo.x, lo.y, hi.x, hi.y}, pb, acc);
+      const U4 vt{lo.x, lo.y, hi.x, hi.y};
+      o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
     }
     if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
   };
@@ -362,6 +379,246 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   }
 }
 
+// Balanced split (decode: one query row per sequence, the G heads of a KV head in one column group). With one
+// wave per (sequence, KV head, partition), unequal contexts leave waves of unequal length, and a grid of whole
+// workgroups of 8 KV heads leaves some CUs without one and some XCDs with more bytes than others. Here the
+// 32-token tiles of all sequences, in sequence order, form one list cut into `chunks` equal runs; workgroup
+// (x, r) takes run r for KV heads 8x .. 8x + 7, and the host sizes the grid to one wave per wave slot of the
+// chip, so every wave streams the same number of tiles and every XCD the same bytes. A wave walks its run one
+// sequence segment at a time, with the partition kernel's load pipeline inside a segment: a sequence lying
+// wholly inside the run is written to `out`; one cut by run boundaries leaves a partial in slot
+// [head][run][2] -- slot 0 for the sequence the run starts inside, slot 1 for the one it ends inside -- and
+// balanced_reduce_kernel merges them. Stores happen only between segments, after the pipeline has drained.
+//
+// Every workgroup first derives the prefix of the sequences' tile counts in LDS; the first one also
+// publishes it for the merge.
+template <int KV, int D, int W>
+__global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(const DecodeArgs a) {
+  constexpr int kEsize = KV == PA_BF16 ? 2 : 1;
+  constexpr int kChunks = D / 32;
+  constexpr int kNt = D / 16;
+  constexpr int kPitch = D * 2 + 16;
+  constexpr int kSlice = kTileTok * kPitch;
+  constexpr int kRowLanes = D * kEsize / 16;
+  constexpr int kRows = kWave / kRowLanes;
+  constexpr int kLoads = kTile / kRows;
+  constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
+  constexpr int NT = kWave * W;
+  static_assert(kLoads * kRows == kTile, "whole rows per load");
+  __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
+  __shared__ int32_t wave_total[W];
+  extern __shared__ int32_t P[];  // [num_seqs + 1]: tiles of the sequences before each one
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = a.num_seqs;
+  const ConstI32* __restrict__ lens = as_constant(a.context_lens);
+  for (int s = tid; s < T; s += NT) {
+    const int L = min(max(lens[s], 0), a.max_context_len);
+    P[s + 1] = (L + kTileTok - 1) / kTileTok;
+  }
+  __syncthreads();
+  block_exclusive_scan<NT>(P, T, wave_total);
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int r = tid; r <= T; r += NT) a.tile_prefix[r] = P[r];
+
+  const int g = blockIdx.x * W + w;
+  if (g >= a.num_kv_heads) return;  // no workgroup barriers below: each wave owns its LDS slice
+  const int chunk = blockIdx.y;
+  const int total = __builtin_amdgcn_readfirstlane(P[T]);
+  const int C = (total + a.chunks - 1) / a.chunks;  // tiles per run
+  const int g0 = chunk * C;                          // this run: tiles [g0, g1) of the list
+  const int g1 = min(g0 + C, total);
+  if (g0 >= g1) return;
+
+  const int G = a.group;
+  const int n = lane & 15;  // MFMA column: head g * G + n
+  const int j = lane >> 4;
+  const bool head_ok = n < G;
+  const int rr = lane / kRowLanes;
+  const int rc = lane % kRowLanes;
+  const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
+  const int64_t head_off = (int64_t)g * D * kEsize;
+  char* const kslice = lds + w * 2 * kSlice;
+  char* const vslice = kslice + kSlice;
+  uint32_t off[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) off[i] = (uint32_t)((rr + kRows * i) * row_bytes + head_off + rc * 16);
+  const int wofs = rr * kPitch + rc * 16 * (2 / kEsize);
+  const char* const kread = kslice + n * kPitch + j * 16;
+  const char* const rbase = vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
+  const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
+  const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
+  const float poison = __uint_as_float(0x7fc00000u);
+
+  // the run's first sequence: the first s with P[s + 1] > g0
+  int lo = 0, hi = T - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(P[mid + 1]) <= g0) lo = mid + 1;
+    else hi = mid;
+  }
+  int s = lo;
+  int pos = g0;  // list index of the segment's first tile
+  while (true) {
+    const int p0 = __builtin_amdgcn_readfirstlane(P[s]);
+    const int p1 = __builtin_amdgcn_readfirstlane(P[s + 1]);
+    const int L = min(max(lens[s], 0), a.max_context_len);
+    const int end = min(p1, g1);
+    const int u0 = (pos - p0) * kTileTok;          // the segment: positions [u0, u1) of sequence s
+    const int u1 = min(L, (end - p0) * kTileTok);
+    const int ntiles = end - pos;
+    const int last8 = (u1 - 1) & ~(kTile / 2 - 1);  // start of the last live 8-token group
+    const ConstI32* __restrict__ table = as_constant(a.block_tables) + (int64_t)s * a.max_blocks_per_seq;
+
+    const char* qptr = static_cast<const char*>(a.query) +
+                       (head_ok ? ((int64_t)s * a.num_q_heads + (int64_t)g * G + n) * D * 2 : 0);
+    U4 qb[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const U4 v = *reinterpret_cast<const U4*>(qptr + c * 64 + j * 16);
+      qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
+    }
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[kNt];
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+
+    U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
+    auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
+      const int t = u0 + min(tile, ntiles - 1) * kTileTok;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // 8-row quarter q4 of the tile, as in the partition kernel
+        const int h2 = q4 >> 1;
+        const int64_t base = (q4 & 1) == 0 || a.bs_log2 == 3
+                                 ? tile_slot_bytes(table, min(t + q4 * (kTile / 2), last8), a.bs_log2, a.num_blocks,
+                                                   row_bytes, bad)
+                                 : tile_slot_bytes(table, min(t + h2 * kTile, last8), a.bs_log2, a.num_blocks,
+                                                   row_bytes, bad) + (kTile / 2) * row_bytes;
+        const int rows = min(kQuarterRows, u1 - (u0 + tile * kTileTok + q4 * (kTile / 2)));
+        const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
+        const uint32_t qoff = (uint32_t)((q4 & 1) * (kTile / 2) * row_bytes);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          if ((kRows * i < kTile / 2) == ((q4 & 1) == 0)) {
+            kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
+            vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
+          }
+        }
+      }
+    };
+
+    auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
+      const int t = u0 + tile * kTileTok;
+      const bool full = t + kTileTok <= u1;
+      wave_lds_sync();
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          const int r = (h2 * kTile + kRows * i) * kPitch + wofs;
+          if constexpr (KV == PA_BF16) {
+            *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
+            *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
+          } else {
+            stage_e4m3(kslice + r, kb[h2][i]);
+            stage_e4m3(vslice + r, vb[h2][i]);
+          }
+        }
+      wave_lds_sync();
+      f32x4 sc[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c)
+          sc[h2] = mfma(*reinterpret_cast<const U4*>(kread + h2 * kTile * kPitch + c * 64), qb[c], sc[h2]);
+      }
+      float sv[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = sc[h2][i] * a.scale_log2;
+          if (!full && t + h2 * kTile + 4 * j + i >= u1) x = -INFINITY;
+          sv[h2 * 4 + i] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = fast_exp2(m - mref);
+      m = mn;
+      U4 pb, pl;
+      float psum;
+      prob_operands(sv, mref, pb, pl, psum);
+      l = l * alpha + psum;
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) {
+        const u32x2 vlo = lds_read_tr16(rbase + nt * 32);
+        const u32x2 vhi = lds_read_tr16(rbase + kTile * kPitch + nt * 32);
+        f32x4 acc = o[nt];
+        acc[0] *= alpha;
+        acc[1] *= alpha;
+        acc[2] *= alpha;
+        acc[3] *= alpha;
+        const U4 vt{vlo.x, vlo.y, vhi.x, vhi.y};
+        o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
+      }
+    };
+
+    issue(kA, vA, 0);
+    int tj = 0;
+    for (; tj + 2 <= ntiles; tj += 2) {
+      issue(kB, vB, tj + 1);
+      consume(kA, vA, tj);
+      issue(kA, vA, tj + 2);
+      consume(kB, vB, tj + 1);
+    }
+    if (tj < ntiles) consume(kA, vA, tj);
+
+    // the sequence's rows: whole in this run -> out; else the run's partial in slot 0 (the run starts inside
+    // the sequence) or slot 1 (it ends inside it)
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (head_ok) {
+      const int h = g * G + n;
+      const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+      float* dst;
+      if (p0 >= g0 && p1 <= g1) {
+        dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
+      } else {
+        const int64_t wrow = ((int64_t)h * a.chunks + chunk) * 2 + (p0 > g0 ? 1 : 0);
+        dst = a.ws_o + wrow * D;
+        if (j == 0) {
+          a.ws_ml[2 * wrow] = bad ? poison : m;
+          a.ws_ml[2 * wrow + 1] = lt;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNt; ++nt) {
+        const f32x4 v = o[nt];
+        *reinterpret_cast<float4*>(dst + nt * 16 + 4 * j) =
+            bad ? make_float4(poison, poison, poison, poison)
+                : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      }
+    }
+    if (end >= g1) break;
+    // the next sequence holding tiles (one exists while tiles of the run remain)
+    pos = end;
+    ++s;
+    while (__builtin_amdgcn_readfirstlane(P[s + 1]) == __builtin_amdgcn_readfirstlane(P[s])) ++s;
+  }
+}
+
 }  // namespace
 
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len) {
@@ -379,13 +636,20 @@ hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// KV heads per workgroup of either grouped-query kernel: up to 8 KV heads of a sequence; the LDS slices of 8
+// waves fit one CU (8 x 17 KB at D 128)
+int waves_per_group(int32_t num_kv_heads) {
+  return num_kv_heads >= 8 ? 8 : num_kv_heads >= 4 ? 4 : num_kv_heads >= 2 ? 2 : 1;
+}
+
 template <int KV, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  // a workgroup takes up to 8 KV heads of a sequence; the LDS slices of 8 waves fit one CU (8 x 17 KB at D 128)
-  if (a.num_kv_heads >= 8) return launch_w<KV, D, 8>(a, stream);
-  if (a.num_kv_heads >= 4) return launch_w<KV, D, 4>(a, stream);
-  if (a.num_kv_heads >= 2) return launch_w<KV, D, 2>(a, stream);
-  return launch_w<KV, D, 1>(a, stream);
+  switch (waves_per_group(a.num_kv_heads)) {
+    case 8: return launch_w<KV, D, 8>(a, stream);
+    case 4: return launch_w<KV, D, 4>(a, stream);
+    case 2: return launch_w<KV, D, 2>(a, stream);
+    default: return launch_w<KV, D, 1>(a, stream);
+  }
 }
 
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
@@ -393,6 +657,44 @@ hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t
   if (kv_dtype == PA_BF16 && a.head_dim == 64) return launch_d<PA_BF16, 64>(a, stream);
   if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128) return launch_d<PA_FP8_E4M3, 128>(a, stream);
   if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64) return launch_d<PA_FP8_E4M3, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int KV, int D, int W>
+hipError_t launch_balanced_w(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((a.num_kv_heads + W - 1) / W, a.chunks, 1);
+  const size_t lds = ((size_t)a.num_seqs + 1) * sizeof(int32_t);
+  decode_gqa_mfma_balanced_kernel<KV, D, W><<<grid, dim3(kWave * W), lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t launch_balanced_d(const DecodeArgs& a, hipStream_t stream) {
+  switch (waves_per_group(a.num_kv_heads)) {
+    case 8: return launch_balanced_w<KV, D, 8>(a, stream);
+    case 4: return launch_balanced_w<KV, D, 4>(a, stream);
+    case 2: return launch_balanced_w<KV, D, 2>(a, stream);
+    default: return launch_balanced_w<KV, D, 1>(a, stream);
+  }
+}
+
+}  // namespace
+
+int32_t gqa_balanced_chunks(int32_t num_kv_heads) {
+  const int32_t w = waves_per_group(num_kv_heads);
+  const int32_t waves = (num_kv_heads + w - 1) / w * w;  // waves of one run across the KV heads
+  return waves >= kResidentWaves ? 1 : kResidentWaves / waves;
+}
+
+hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  if (a.num_seqs > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix || a.query_start || a.col_groups != 1)
+    return hipErrorInvalidValue;
+  if (kv_dtype == PA_BF16 && a.head_dim == 128) return launch_balanced_d<PA_BF16, 128>(a, stream);
+  if (kv_dtype == PA_BF16 && a.head_dim == 64) return launch_balanced_d<PA_BF16, 64>(a, stream);
+  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128) return launch_balanced_d<PA_FP8_E4M3, 128>(a, stream);
+  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64) return launch_balanced_d<PA_FP8_E4M3, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 

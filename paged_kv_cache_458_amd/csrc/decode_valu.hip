@@ -447,31 +447,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     }
   }
   __syncthreads();
-  {
-    // exclusive scan: each thread sums a run of rows, a wave scan and the waves' totals give its offset
-    const int per = (T + NT - 1) / NT;
-    const int rb = tid * per;
-    int sum = 0;
-    for (int k = 0; k < per; ++k)
-      if (rb + k < T) sum += P[rb + k + 1];
-    int inc = sum;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int v = __shfl_up(inc, off);
-      if (lane >= off) inc += v;
-    }
-    if (lane == kWave - 1) wave_total[wave] = inc;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) inc += wave_total[w];
-    int run = inc - sum;
-    for (int k = 0; k < per; ++k)
-      if (rb + k < T) {
-        run += P[rb + k + 1];
-        P[rb + k + 1] = run;
-      }
-    if (tid == 0) P[0] = 0;
-  }
-  __syncthreads();
+  block_exclusive_scan<NT>(P, T, wave_total);
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int r = tid; r <= T; r += NT) a.tile_prefix[r] = P[r];
 

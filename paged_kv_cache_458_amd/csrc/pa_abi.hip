@@ -63,8 +63,8 @@ struct Plan {
   bool split = false;
   bool mfma = false;           // the matrix-core kernel runs (else the per-head one)
   int32_t col_groups = 1;      // its column groups of 16 per KV head
-  bool balanced = false;       // balanced split of the single-head kernel (equal runs of tiles per wave)
-  int32_t chunks = 0;          // its runs per query head
+  bool balanced = false;       // balanced split (equal runs of tiles per wave) of either kernel
+  int32_t chunks = 0;          // its runs (per query head for the single-head kernel)
   size_t ws_bytes = 0;
   size_t ws_ml_offset = 0;
   size_t ws_prefix_offset = 0; // balanced split: the rows' tile prefix
@@ -103,10 +103,11 @@ int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa) {
   return max_context_len <= part ? 0 : part;
 }
 
-// num_tokens query rows (num_seqs in decode), at most max_query_len per sequence (1 in decode).
+// num_tokens query rows (num_seqs in decode), at most max_query_len per sequence (1 in decode). `decode`: the
+// decode entry points, where row s is sequence s (no query_start).
 Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
-               int32_t partition_size) {
+               int32_t partition_size, bool decode) {
   Plan p;
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 1 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
@@ -143,20 +144,25 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     return p;
   }
   const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * p.col_groups : (int64_t)num_tokens * num_q_heads;
-  // The balanced split needs the single-head kernel, rows one workgroup's LDS holds, and tile counts that fit
-  // 32 bits. The library takes it wherever it would otherwise split the single-head kernel's contexts.
-  const bool balanced_ok = !gqa && num_tokens <= pa::kMaxBalancedRows &&
-                           (int64_t)num_tokens * (max_context_len > 0 ? max_context_len : 1) <= (int64_t)1 << 30;
+  // The balanced split needs rows one workgroup's LDS holds and tile counts that fit 32 bits; on the
+  // matrix-core kernel also one query row per sequence and one column group. The library takes it wherever it
+  // would otherwise split the single-head kernel's contexts. The matrix-core kernel keeps its partitions unless
+  // asked: measured on MI355X, 1024-token partitions beat the balanced split on bf16 caches (70B-shaped batch
+  // 137.6 against 143.6 us, shared-prefix batch 274 against 278 us); only E4M3 gained (89.4 -> 84.3 us).
+  const bool balanced_ok = num_tokens <= pa::kMaxBalancedRows &&
+                           (int64_t)num_tokens * (max_context_len > 0 ? max_context_len : 1) <= (int64_t)1 << 30 &&
+                           (!gqa || (decode && p.col_groups == 1));
   if (partition_size == PA_PARTITION_BALANCED && !balanced_ok) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
   int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
-  if (partition_size == PA_PARTITION_BALANCED || (partition_size == -1 && balanced_ok && part > 0 && part < whole)) {
+  if (partition_size == PA_PARTITION_BALANCED ||
+      (partition_size == -1 && balanced_ok && !gqa && part > 0 && part < whole)) {
     p.balanced = true;
     p.split = true;
-    p.chunks = pa::balanced_chunks(num_q_heads);
+    p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads) : pa::balanced_chunks(num_q_heads);
     p.partition = 0;
     p.max_partitions = 1;
     const size_t o_bytes = pa::balanced_o_elems(num_q_heads, p.chunks, head_dim) * sizeof(float);
@@ -211,7 +217,7 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t kv_dtype, int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, kv_dtype, partition_size);
+                           max_context_len, kv_dtype, partition_size, true);
   if (p.status != PA_OK) return p.status;
   return p.balanced ? PA_PARTITION_BALANCED : p.split ? p.partition : 0;
 }
@@ -220,7 +226,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t kv_dtype, int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, kv_dtype, partition_size);
+                           max_context_len, kv_dtype, partition_size, true);
   return p.status == PA_OK ? p.ws_bytes : 0;
 }
 
@@ -229,7 +235,7 @@ int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query
                                              int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
                                              int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                           block_size, max_context_len, kv_dtype, partition_size);
+                           block_size, max_context_len, kv_dtype, partition_size, false);
   if (p.status != PA_OK) return p.status;
   return p.balanced ? PA_PARTITION_BALANCED : p.split ? p.partition : 0;
 }
@@ -239,7 +245,7 @@ size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query
                                              int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
                                              int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                           block_size, max_context_len, kv_dtype, partition_size);
+                           block_size, max_context_len, kv_dtype, partition_size, false);
   return p.status == PA_OK ? p.ws_bytes : 0;
 }
 
@@ -268,7 +274,7 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
               int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   const Plan plan = make_plan(num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                              block_size, max_context_len, kv_dtype, partition_size);
+                              block_size, max_context_len, kv_dtype, partition_size, query_start == nullptr);
   if (plan.status != PA_OK) return plan.status;
   const bool pair_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) || (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
@@ -321,7 +327,9 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.balanced) {
-    if (pa::launch_decode_valu_balanced(a, kv_dtype, st) != hipSuccess) return PA_ERR_HIP;
+    const hipError_t e = plan.mfma ? pa::launch_decode_gqa_mfma_balanced(a, kv_dtype, st)
+                                   : pa::launch_decode_valu_balanced(a, kv_dtype, st);
+    if (e != hipSuccess) return PA_ERR_HIP;
     return pa::launch_balanced_reduce(a, st) == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   const hipError_t err = plan.mfma ? pa::launch_decode_gqa_mfma(a, kv_dtype, st) : pa::launch_decode_valu(a, kv_dtype, st);

@@ -101,6 +101,39 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Exclusive prefix sum in LDS over the counts of T items: on entry P[r + 1] holds item r's count, on exit P[r]
+// holds the sum of the counts of items 0 .. r-1 and P[T] the total. Called by all NT threads of the workgroup
+// (NT / kWave waves; `wave_total` holds one int per wave); each thread sums a run of items, a wave scan and
+// the waves' totals give its offset. Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan(int32_t* P, int T, int32_t* wave_total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int per = (T + NT - 1) / NT;
+  const int rb = tid * per;
+  int sum = 0;
+  for (int k = 0; k < per; ++k)
+    if (rb + k < T) sum += P[rb + k + 1];
+  int inc = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
+  }
+  if (lane == kWave - 1) wave_total[wave] = inc;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += wave_total[w];
+  int run = inc - sum;
+  for (int k = 0; k < per; ++k)
+    if (rb + k < T) {
+      run += P[rb + k + 1];
+      P[rb + k + 1] = run;
+    }
+  if (tid == 0) P[0] = 0;
+  __syncthreads();
+}
+
 // Orders one wave's LDS accesses when lanes exchange data through LDS: everything before it (in every lane) is
 // visible to everything after it. Without it the compiler may move a lane's read of another lane's data
 // above that lane's own earlier write, since a single lane sees no dependence between the two.

@@ -74,6 +74,11 @@ constexpr int kResidentWaves = 2048;    // 256 CUs x 4 SIMDs x 2 waves of the si
 int32_t balanced_chunks(int32_t num_q_heads);  // runs per query head: the grid fills kResidentWaves
 hipError_t launch_decode_valu_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream);
+// Balanced split of the matrix-core kernel (one query row per sequence, one column group): the 32-token tiles
+// of all sequences cut into `chunks` equal runs, one workgroup of up to 8 KV heads each; its partials take the
+// single-head balanced split's layout and launch_balanced_reduce merges them.
+int32_t gqa_balanced_chunks(int32_t num_kv_heads);  // runs: the grid fills kResidentWaves
+hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 // workspace of a balanced launch: partials [Hq][chunks][2][D] fp32, then (m, l) [Hq][chunks][2][2]
 inline size_t balanced_o_elems(int64_t Hq, int64_t chunks, int64_t D) { return Hq * chunks * 2 * D; }
 inline size_t balanced_ml_elems(int64_t Hq, int64_t chunks) { return Hq * chunks * 2 * 2; }

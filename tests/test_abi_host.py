@@ -214,6 +214,14 @@ def balanced_ws(T, Hq, D):
     return o + ml + (T + 1) * 4
 
 
+def gqa_balanced_ws(T, Hq, Hkv, D):
+    w = 8 if Hkv >= 8 else 4 if Hkv >= 4 else 2 if Hkv >= 2 else 1
+    runs = max(1, 2048 // ((Hkv + w - 1) // w * w))
+    o = (Hq * runs * 2 * D * 4 + 255) // 256 * 256
+    ml = (Hq * runs * 2 * 2 * 4 + 255) // 256 * 256
+    return o + ml + (T + 1) * 4
+
+
 def test_balanced_split_plan():
     lib = pa.load_library()
     B = pa.PA_PARTITION_BALANCED
@@ -225,17 +233,29 @@ def test_balanced_split_plan():
     # several tokens per sequence (fp32: the per-head kernel): one tile count per query row
     assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == B
     assert pa.multi_workspace_bytes(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == balanced_ws(256, 32, 128)
-    # contexts that fit one partition stay single pass; grouped heads on the matrix cores keep partitions
+    # contexts that fit one partition stay single pass; grouped heads on the matrix cores keep partitions by
+    # default ...
     assert pa.partition_size_for(4, 4, 4, 64, 16, 64, pa.PA_F32, -1) == 0
     assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
+    # ... and take the balanced split when asked: runs = 2048 waves / (KV heads rounded to whole workgroups of
+    # up to 8), partials per query head and run
+    assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == B
+    assert pa.workspace_bytes(64, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == gqa_balanced_ws(64, 64, 8, 128)
+    assert pa.workspace_bytes(5, 24, 12, 64, 32, 4096, pa.PA_FP8_E4M3, B) == gqa_balanced_ws(5, 24, 12, 64)
+    assert pa.workspace_bytes(3, 16, 1, 128, 16, 900, pa.PA_BF16, B) == gqa_balanced_ws(3, 16, 1, 128)
     # beyond 2048 query rows, or 2^30 row-positions, the default falls back to partitions ...
     assert pa.partition_size_for(4096, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) % 16 == 0
     assert pa.partition_size_for(2048, 32, 32, 128, 16, 1 << 20, pa.PA_BF16, -1) % 16 == 0
-    # ... and an explicit request is refused, as it is for the matrix-core kernel
+    # ... and an explicit request is refused, on either kernel; so is one for the matrix-core kernel with more
+    # than 16 (query row, head) columns per KV head
     for args in ((2049, 32, 32, 128, 16, 2048, pa.PA_BF16), (2048, 32, 32, 128, 16, 1 << 20, pa.PA_BF16),
-                 (64, 64, 8, 128, 256, 4096, pa.PA_BF16)):
+                 (2049, 64, 8, 128, 256, 4096, pa.PA_BF16), (64, 64, 2, 128, 16, 2048, pa.PA_BF16)):
         assert lib.paged_attention_partition_size(*args, B) == PA_ERR_UNSUPPORTED
         assert lib.paged_attention_workspace_bytes(*args, B) == 0
+    # several new tokens per sequence on the matrix cores: partitions only
+    assert lib.paged_attention_multi_partition_size(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16,
+                                                    B) == PA_ERR_UNSUPPORTED
+    assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
     # partition sizes between the balanced code and 16 are not multiples of 16
     assert lib.paged_attention_partition_size(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 2) == PA_ERR_SHAPE
 

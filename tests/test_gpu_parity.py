@@ -58,7 +58,7 @@ def decode(st, t, tables, partition_size, context_lens=None, max_context_len=Non
 
 
 def balanced_ok(st) -> bool:
-    """Whether the library runs the balanced split for these sizes (the single-head kernel)."""
+    """Whether the library runs the balanced split for these sizes (either kernel)."""
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
     return pa.load_library().paged_attention_partition_size(
         st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size, st.max_context_len, kd,
@@ -343,6 +343,58 @@ def test_balanced_split_edge_cases():
     # every row empty: zero rows, no tile to read
     z = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=np.zeros(4, np.int32))
     assert (z == 0).all()
+
+
+# the matrix-core kernel's balanced split (grouped heads at head_dim 64 / 128, bf16 or E4M3 caches): runs of
+# 32-token tiles cut sequences anywhere; the partials share the single-head split's layout and merge
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,bs,dt", [
+    ([0, 0, 700, 1, 0, 3000, 45, 0, 0], 32, 8, 128, 16, "bf16"),       # empty sequences before, between, after
+    ([20000], 16, 2, 64, 16, "bf16"),                                  # one sequence cut into 625 one-tile runs
+    ([3, 1, 2, 17, 16, 15, 33, 64, 65] * 40, 8, 4, 128, 8, "fp8"),     # many short sequences, 8-slot blocks
+    ([2050, 999, 513, 300, 4096, 1], 64, 8, 128, 256, "bf16"),         # 256-slot blocks, 8 heads per KV head
+    ([900, 1300, 20, 2500], 16, 1, 128, 128, "fp8"),                   # 16 heads on one KV head
+    ([129, 4000, 31, 777, 64], 24, 12, 64, 32, "bf16"),                # 12 KV heads: two workgroups per run
+])
+def test_gqa_balanced_split_parity(lens, hq, hkv, d, bs, dt):
+    st = custom_structure("gbal", 443, lens, hq, hkv, d, bs, dt, pool_factor=1.2)
+    assert balanced_ok(st)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    a = decode(st, t, st.block_tables_pre, pa.PA_PARTITION_BALANCED)
+    assert_attention_close(a, ref, dt, "balanced")
+    empty = np.asarray(lens) == 0
+    assert (a[empty] == 0).all()
+    np.testing.assert_array_equal(a, decode(st, t, st.block_tables_pre, pa.PA_PARTITION_BALANCED))
+    # permuting the physical blocks leaves the output bit for bit the same
+    perm = np.random.default_rng(444).permutation(st.num_blocks)
+    kp, vp = torch.empty_like(t["key_cache"]), torch.empty_like(t["value_cache"])
+    idx = torch.from_numpy(perm).to(DEV)
+    kp[idx], vp[idx] = t["key_cache"], t["value_cache"]
+    tp = dict(t, key_cache=kp, value_cache=vp)
+    np.testing.assert_array_equal(a, decode(st, tp, perm[st.block_tables_pre], pa.PA_PARTITION_BALANCED))
+
+
+def test_gqa_balanced_split_edge_cases():
+    st = custom_structure("gbaledge", 445, [4000, 64, 2500, 0, 3000], 32, 8, 128, 16, "bf16", max_context_len=4096)
+    assert balanced_ok(st)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    tables = st.block_tables_pre.copy()
+    tables[2, 100] = -3  # a bad entry in a sequence that several runs cut poisons that sequence only
+    lens = st.context_lens.copy()
+    lens[1] = 9000  # clamped to max_context_len: positions past the sequence's own blocks are poisoned slots
+    gpu = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=lens)
+    assert np.isnan(gpu[2]).all() and np.isnan(gpu[1]).all() and (gpu[3] == 0).all()
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    assert_attention_close(gpu[[0, 4]], ref[[0, 4]], "bf16", "balanced")
+    z = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=np.zeros(5, np.int32))
+    assert (z == 0).all()
+    # several new tokens per sequence keep the partition kernel: the balanced split is refused there
+    assert pa.load_library().paged_attention_multi_partition_size(
+        5, 10, 2, 32, 8, 128, 16, 4096, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == -4  # PA_ERR_UNSUPPORTED
 
 
 # --------------------------------------------------------------------------------------------------------
