@@ -74,9 +74,11 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
 /*
  * Bytes of workspace paged_attention_decode needs for these sizes (0 when the call runs single pass).
  * Arguments as in paged_attention_decode. Returns 0 as well for invalid sizes (the decode call reports them).
- * Split into partitions of P tokens: partials [num_seqs][num_q_heads][ceil(max_context_len / P)][head_dim]
- * fp32, then their (max, sum) pairs, each part 256-byte aligned. Balanced split: partials
- * [num_q_heads][R][2][head_dim] fp32 and their pairs, then (query rows + 1) int32 tile counts, for R runs: on
+ * Split into partitions of P tokens: partials [num_seqs][num_q_heads][ceil(max_context_len / S)][head_dim]
+ * fp32, then their (max, sum) pairs, each part 256-byte aligned, where S = P, or S = 2P when grouped heads run
+ * on the matrix cores with 512 <= P < 1024 (one wave covers two partitions and merges them itself).
+ * Balanced split: partials [num_q_heads][R][2][head_dim] fp32 and their pairs, then (query rows + 1) int32
+ * tile counts, for R runs: on
  * the single-head kernel R = 1024 / ceil(num_q_heads / 2) per head, on the matrix-core kernel (grouped heads)
  * R = 2048 / (num_kv_heads rounded up to whole workgroups of W = min(8, largest power of two <= num_kv_heads)
  * KV heads); at least 1 either way.

@@ -138,8 +138,10 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   const int s = bz;
   if (g >= a.num_kv_heads) return;  // no workgroup barriers below: each wave owns its LDS slice
 
-  // The wave covers parts_per_wave (1 or 2) consecutive partitions, [u0, u1), in one load pipeline and leaves
-  // one partial result per partition (partition boundaries fall on 32-token tiles whenever parts_per_wave is 2).
+  // The wave covers parts_per_wave (1 or 2) consecutive partitions, [u0, u1), in one load pipeline. Its online
+  // softmax restarts at the partition boundary; the two partitions' states are merged by the log-sum-exp rule
+  // at the end, and the wave leaves one partial result for its span (partition boundaries fall on 32-token
+  // tiles whenever parts_per_wave is 2).
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   const int span = a.partition * a.parts_per_wave;
   const int u0 = by * span;
@@ -244,10 +246,8 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
 
   // A wave covers at most two partitions. Finishing the first one mid-range only parks its state in
   // registers: any store inside the load loop would leave the compiler unable to count outstanding memory
-  // operations, and it would then drain the load pipeline on every tile. Both partials are written after
-  // the loop.
+  // operations, and it would then drain the load pipeline on every tile.
   const int cut = min(u0 + a.partition, u1);  // end of the wave's first partition
-  const int p0 = u0 / a.partition;            // its index
   float m_first = -INFINITY, l_first = 0.f;
   f32x4 o_first[kNt];
 #pragma unroll
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // Normalise one partition's G rows and write them: the output itself when the sequence has a single
-  // partition, else partial p of the split workspace.
+  // Normalise the span's G rows and write them: the output itself when the sequence fits one span, else
+  // partial p of the split workspace.
   const float poison = __uint_as_float(0x7fc00000u);
   auto write_rows = [&](int p, float mp, float lp, const f32x4* op) {
     // each lane summed the probabilities of its own token group j; the max is already shared
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     const int h = g * G + hh;
     const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     float* dst;
-    if (!a.split || L <= a.partition) {
+    if (!a.split || L <= span) {
       dst = a.out + ((int64_t)qrow * a.num_q_heads + h) * D;
     } else {
       const int64_t wrow = ((int64_t)qrow * a.num_q_heads + h) * a.max_partitions + p;
@@ -370,13 +370,20 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     }
     if (tj < ntiles) consume(kA, vA, tj);
   }
-  // an empty context writes a zero row (l = 0)
   if (cut < u1) {
-    write_rows(p0, m_first, l_first, o_first);
-    write_rows(p0 + 1, m, l, o);
-  } else {
-    write_rows(p0, m, l, o);
+    // merge the first partition's state into the second's: one partial per wave
+    const float M = fmaxf(m_first, m);
+    const float Mr = M == -INFINITY ? 0.f : M;
+    const float fa = fast_exp2(m_first - Mr), fb = fast_exp2(m - Mr);
+    l = l_first * fa + l * fb;
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[nt][e] = o_first[nt][e] * fa + o[nt][e] * fb;
+    m = M;
   }
+  // an empty context writes a zero row (l = 0)
+  write_rows(by, m, l, o);
 }
 
 // Balanced split (decode: one query row per sequence, the G heads of a KV head in one column group). With one
@@ -629,7 +636,7 @@ bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len
 
 template <int KV, int D, int W>
 hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
-  const int groups = a.split ? (a.max_partitions + a.parts_per_wave - 1) / a.parts_per_wave : 1;
+  const int groups = a.split ? a.max_partitions : 1;  // one partial slot per wave span
   // column groups share the x dimension with the KV-head groups (the kernel unpacks them)
   const dim3 grid((a.num_kv_heads + W - 1) / W * a.col_groups, groups, a.num_seqs);
   decode_gqa_mfma_kernel<KV, D, W><<<grid, dim3(kWave * W), 0, stream>>>(a);

@@ -338,8 +338,9 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   // a row with a single partition was written by the partition kernel: it is merged as one partition here
   // (no early exit, which would let the compiler sink the loads above behind the length) and not stored
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
-  const bool merge = L > a.partition;
-  const int np = merge ? (L + a.partition - 1) / a.partition : 1;
+  const int span = a.partition * a.parts_per_wave;  // positions behind one partial: a wave's span
+  const bool merge = L > span;
+  const int np = merge ? (L + span - 1) / span : 1;
 
   float M = lane < np ? v0.x : -INFINITY;
   for (int p = lane + kWave; p < np; p += kWave) M = fmaxf(M, ml[p].x);

@@ -177,14 +177,16 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     p.split = false;
     return p;
   }
-  const int64_t pm = (max_context_len + (int64_t)part - 1) / part;
+  // one partial per wave span: a grouped-query wave that covers two partitions merges their states itself
+  p.parts_per_wave = gqa ? gqa_parts_per_wave(part) : 1;
+  const int64_t span = (int64_t)part * p.parts_per_wave;
+  const int64_t pm = (max_context_len + span - 1) / span;
   if (pm > kMaxGridYZ) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
   p.partition = part;
   p.max_partitions = (int32_t)pm;
-  p.parts_per_wave = gqa ? gqa_parts_per_wave(part) : 1;
   p.split = true;
   const size_t o_bytes = pa::ws_o_elems(num_tokens, num_q_heads, pm, head_dim) * sizeof(float);
   p.ws_ml_offset = round_up(o_bytes, 256);

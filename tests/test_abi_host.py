@@ -137,10 +137,11 @@ def test_multi_no_rows_is_a_no_op_and_plans_match_decode():
         B, Hq, Hkv, D, bs, L, kd, part = args
         assert pa.multi_workspace_bytes(B, B, 1, Hq, Hkv, D, bs, L, kd, part) == pa.workspace_bytes(*args)
         assert pa.multi_partition_size_for(B, B, 1, Hq, Hkv, D, bs, L, kd, part) == pa.partition_size_for(*args)
-    # the workspace holds one partial per query row
+    # the workspace holds one partial per query row and wave span: a matrix-core wave covers two 512-token
+    # partitions and merges them itself
     B, T = 8, 24
     w = pa.multi_workspace_bytes(B, T, 3, 8, 2, 64, 16, 4096, pa.PA_BF16, 512)
-    pm = 4096 // 512
+    pm = 4096 // 1024
     assert w == (T * 8 * pm * 64 * 4 + 255) // 256 * 256 + T * 8 * pm * 2 * 4
 
 
@@ -179,9 +180,10 @@ def test_workspace_and_partition_plan():
     # single pass needs no workspace
     assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 0) == 0
     assert pa.partition_size_for(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 0) == 0
-    # an explicit split: o [B, Hq, PM, D] fp32, then (m, l) pairs, 256-byte aligned
+    # an explicit split: o [B, Hq, PM, D] fp32, then (m, l) pairs, 256-byte aligned; PM counts wave spans, and a
+    # matrix-core wave covers two 512-token partitions
     B, Hq, D, P, L = 64, 64, 128, 512, 4096
-    pm = L // P
+    pm = L // (2 * P)
     o = B * Hq * pm * D * 4
     want = (o + 255) // 256 * 256 + B * Hq * pm * 2 * 4
     assert pa.workspace_bytes(B, Hq, 8, D, 256, L, pa.PA_BF16, P) == want
