@@ -377,6 +377,20 @@ def test_gqa_balanced_split_parity(lens, hq, hkv, d, bs, dt):
     np.testing.assert_array_equal(a, decode(st, tp, perm[st.block_tables_pre], pa.PA_PARTITION_BALANCED))
 
 
+def test_gqa_balanced_split_at_its_row_limit():
+    # 2048 sequences, the most the workgroups' tile-count scan takes (the one beyond is refused)
+    lens = np.random.default_rng(446).integers(0, 300, size=2048)
+    st = custom_structure("gbalmax", 446, lens, 16, 4, 128, 16, "bf16", pool_factor=1.05)
+    assert balanced_ok(st)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    gpu = decode(st, t, st.block_tables_pre, pa.PA_PARTITION_BALANCED)
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    assert_attention_close(gpu, ref, "bf16", "2048 sequences")
+    assert (gpu[lens == 0] == 0).all()
+    np.testing.assert_allclose(gpu, decode(st, t, st.block_tables_pre, 256), rtol=1e-2, atol=2e-3)
+
+
 def test_gqa_balanced_split_edge_cases():
     st = custom_structure("gbaledge", 445, [4000, 64, 2500, 0, 3000], 32, 8, 128, 16, "bf16", max_context_len=4096)
     assert balanced_ok(st)
