@@ -145,10 +145,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   }
   const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * p.col_groups : (int64_t)num_tokens * num_q_heads;
   // The balanced split needs rows one workgroup's LDS holds and tile counts that fit 32 bits; on the
-  // matrix-core kernel also one query row per sequence and one column group. The library takes it wherever it
-  // would otherwise split the single-head kernel's contexts. The matrix-core kernel keeps its partitions unless
-  // asked: measured on MI355X, 1024-token partitions beat the balanced split on bf16 caches (70B-shaped batch
-  // 137.6 against 143.6 us, shared-prefix batch 274 against 278 us); only E4M3 gained (89.4 -> 84.3 us).
+  // matrix-core kernel also one query row per sequence and one column group.
   const bool balanced_ok = num_tokens <= pa::kMaxBalancedRows &&
                            (int64_t)num_tokens * (max_context_len > 0 ? max_context_len : 1) <= (int64_t)1 << 30 &&
                            (!gqa || (decode && p.col_groups == 1));
@@ -158,8 +155,18 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   }
   int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
-  if (partition_size == PA_PARTITION_BALANCED ||
-      (partition_size == -1 && balanced_ok && !gqa && part > 0 && part < whole)) {
+  // The library takes the balanced split wherever it would otherwise split the single-head kernel's contexts.
+  // On the matrix cores it takes it only where the partitions would launch more than one round of resident
+  // waves: measured on MI355X over grouped-query batches (bf16 and E4M3), it then gained 5-21%, while partitions
+  // that all start together won by 3-8% (70B-shaped batch, 16 sequences of 8k-16k tokens) -- their fewer
+  // concurrent read streams keep the memory system less congested. A shared prefix favours partitions
+  // slightly (278 against 274 us for 128 sequences sharing 1024 tokens), and the host cannot see sharing.
+  const bool split_default = partition_size == -1 && balanced_ok && part > 0 && part < whole;
+  const bool more_than_a_round =
+      gqa && part > 0 &&
+      rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part) - 1) /
+              ((int64_t)part * gqa_parts_per_wave(part))) > pa::kResidentWaves;
+  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round))) {
     p.balanced = true;
     p.split = true;
     p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads) : pa::balanced_chunks(num_q_heads);

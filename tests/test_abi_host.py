@@ -200,13 +200,29 @@ def test_workspace_and_partition_plan():
 
 
 def test_grouped_query_default_counts_waves_per_span():
-    # 512-token partitions go two to a grouped-query wave: where 1024 leaves fewer than 2048 waves, 512 would
-    # leave the same number, so the default goes on to 256
-    assert pa.partition_size_for(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
-    assert pa.partition_size_for(16, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 128
+    # the partition rule, seen where the balanced split does not apply (several new tokens per sequence, here
+    # with 2 rows x 4 heads = 8 columns per KV head): 512-token partitions go two to a grouped-query wave, so
+    # where 1024 leaves fewer than 2048 waves, 512 would leave the same number and the default goes on to 256
+    def multi(B, *args):
+        return pa.multi_partition_size_for(B, 2 * B, 2, *args)
+    assert multi(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
+    assert multi(16, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 128
     # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head) pairs run single pass
-    assert pa.partition_size_for(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
+    assert multi(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
+    assert multi(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+
+
+def test_grouped_query_decode_default_takes_the_balanced_split_beyond_one_round():
+    B = pa.PA_PARTITION_BALANCED
+    # partitions of 256 tokens would launch 64 x 8 x 8 = 4096 waves, two rounds: balanced
+    assert pa.partition_size_for(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == B
+    assert pa.partition_size_for(128, 32, 8, 128, 16, 4096, pa.PA_FP8_E4M3, -1) == B
+    # one round of 2048 waves (64 x 8 x 4 spans of 1024 tokens) keeps its partitions; so does single pass
+    assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
+    assert pa.partition_size_for(16, 64, 8, 128, 16, 16384, pa.PA_BF16, -1) == 1024
     assert pa.partition_size_for(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+    # more than 16 heads per KV head (two column groups): partitions
+    assert pa.partition_size_for(64, 64, 2, 128, 16, 2048, pa.PA_BF16, -1) % 16 == 0
 
 
 def balanced_ws(T, Hq, D):
@@ -235,8 +251,8 @@ def test_balanced_split_plan():
     # several tokens per sequence (fp32: the per-head kernel): one tile count per query row
     assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == B
     assert pa.multi_workspace_bytes(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == balanced_ws(256, 32, 128)
-    # contexts that fit one partition stay single pass; grouped heads on the matrix cores keep partitions by
-    # default ...
+    # contexts that fit one partition stay single pass; grouped heads on the matrix cores whose partitions fit
+    # one round of waves keep them by default ...
     assert pa.partition_size_for(4, 4, 4, 64, 16, 64, pa.PA_F32, -1) == 0
     assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
     # ... and take the balanced split when asked: runs = 2048 waves / (KV heads rounded to whole workgroups of
