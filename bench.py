@@ -102,8 +102,8 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
     copy_f, copy_w = pick(fetch, "stream_copy_kernel"), pick(write, "stream_copy_kernel")
     f_scale, w_scale = COPY_BYTES / fetch[copy_f][0], COPY_BYTES / write[copy_w][0]
     rows, fb, wb = [], 0.0, 0.0
-    for key in ("decode_valu_kernel", "decode_valu_balanced_kernel", "decode_gqa_mfma_kernel", "lse_reduce_kernel",
-                "balanced_reduce_kernel"):
+    for key in ("decode_valu_kernel", "decode_valu_balanced_kernel", "decode_gqa_mfma_kernel",
+                "decode_gqa_mfma_balanced_kernel", "lse_reduce_kernel", "balanced_reduce_kernel"):
         kf, kw = pick(fetch, key), pick(write, key)
         if kf is None:
             continue
