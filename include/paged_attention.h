@@ -78,10 +78,11 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
  * fp32, then their (max, sum) pairs, each part 256-byte aligned, where S = P, or S = 2P when grouped heads run
  * on the matrix cores with 512 <= P < 1024 (one wave covers two partitions and merges them itself).
  * Balanced split: partials [num_q_heads][R][2][head_dim] fp32 and their pairs, then (query rows + 1) int32
- * tile counts, for R runs: on
- * the single-head kernel R = 1024 / ceil(num_q_heads / 2) per head, on the matrix-core kernel (grouped heads)
+ * tile counts, for R runs. On the single-head kernel R = 1024 / ceil(ceil(num_q_heads / H) / 2) per head,
+ * where a wave takes H = 2 adjacent heads if head rows are 64 or 128 bytes (E4M3 at head_dim 64 or 128, bf16
+ * at 64) and num_q_heads == num_kv_heads, else H = 1. On the matrix-core kernel (grouped heads)
  * R = 2048 / (num_kv_heads rounded up to whole workgroups of W = min(8, largest power of two <= num_kv_heads)
- * KV heads); at least 1 either way.
+ * KV heads). R is at least 1 either way.
  */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,

@@ -25,15 +25,21 @@ namespace {
 
 constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2); }
 
-template <int KV, int D>
+// HPW heads per wave: 1, or 2 adjacent heads whose rows are exactly one row group (64- or 128-byte head rows
+// without grouping), so that every wave-wide load covers pieces of two heads' rows at once.
+template <int KV, int D, int HPW = 1>
 struct Shape {
   static constexpr int kEsize = KV == PA_F32 ? 4 : KV == PA_BF16 ? 2 : 1;
   static constexpr int kEpl = 16 / kEsize;               // elements per lane per 16-byte load
   static constexpr int kHeadLanes = D / kEpl;            // lanes holding one head's row
-  static constexpr int kRowLanes = next_pow2(kHeadLanes);  // lanes per row group (the rest of them idle)
+  static constexpr int kRowLanes = next_pow2(kHeadLanes * HPW);  // lanes per row group (the rest of them idle)
+  static_assert(HPW == 1 || (HPW == 2 && kHeadLanes * HPW == kRowLanes), "two heads fill a row group exactly");
+  static constexpr int kSumLanes = HPW == 1 ? kRowLanes : kHeadLanes;  // lanes one dot product is summed over
   static constexpr int kRows = kWave / kRowLanes;        // slots per wave-wide load
-  // tokens per tile: at most 4 loads per lane for K (and for V), at most 16 tokens
-  static constexpr int kTileTok = kRows * 4 < kTile ? kRows * 4 : kTile;
+  // tokens per tile: at most 4 loads per lane for K (and for V), 2 with two heads per wave (the same bytes in
+  // flight per wave as one head), at most 16 tokens
+  static constexpr int kMaxLoads = HPW == 1 ? 4 : 2;
+  static constexpr int kTileTok = kRows * kMaxLoads < kTile ? kRows * kMaxLoads : kTile;
   static constexpr int kLoads = kTileTok / kRows;        // loads per tile (per K and per V)
   static_assert(D % kEpl == 0 && kRowLanes <= kWave, "head_dim must fill whole 16-byte chunks");
   static constexpr int kQEsize = KV == PA_F32 ? 4 : 2;  // the query is bf16 over an E4M3 cache
@@ -409,9 +415,9 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
 // first workgroup also publishes the prefix for the merge.
 // At least two waves per SIMD, which the grid's size assumes (without the bound the E4M3 kernels at head_dim 192
 // and 256 would take 256 VGPRs plus 12 AGPRs and one wave per SIMD).
-template <int KV, int D, bool kMulti>
+template <int KV, int D, bool kMulti, int HPW>
 __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balanced_kernel(const DecodeArgs a) {
-  using S = Shape<KV, D>;
+  using S = Shape<KV, D, HPW>;
   constexpr int NL = S::kLoads;
   constexpr int TT = S::kTileTok;
   constexpr int NT = kWave * kWavesPerGroup;
@@ -452,8 +458,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int r = tid; r <= T; r += NT) a.tile_prefix[r] = P[r];
 
-  const int h = blockIdx.x * kWavesPerGroup + wave;
-  if (h >= a.num_q_heads) return;
+  const int h0 = (blockIdx.x * kWavesPerGroup + wave) * HPW;  // the wave's first head
+  if (h0 >= a.num_q_heads) return;
   const int chunk = blockIdx.y;
   const int total = __builtin_amdgcn_readfirstlane(P[T]);
   const int C = (total + a.chunks - 1) / a.chunks;  // tiles per run
@@ -462,24 +468,28 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   if (g0 >= g1) return;
   const int n = g1 - g0;
 
-  const int g = h / a.group;
   const int r = lane / S::kRowLanes;
   const int c = lane % S::kRowLanes;
-  const bool lane_ok = c < S::kHeadLanes;
+  const int hw = HPW == 1 ? 0 : c / S::kHeadLanes;  // the lane's head within the wave
+  const int cc = HPW == 1 ? c : c % S::kHeadLanes;  // its 16-byte chunk of that head's row
+  const int h = h0 + hw;
+  const bool lane_ok = HPW == 1 ? c < S::kHeadLanes : h < a.num_q_heads;
+  const int g = h / a.group;
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
   constexpr uint32_t kNowhere = 0x80000000u;
   uint32_t lane_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i)
-    lane_off[i] = lane_ok ? (uint32_t)((i * S::kRows + r) * row_bytes + (int64_t)g * D * S::kEsize + c * 16)
+    lane_off[i] = lane_ok ? (uint32_t)((i * S::kRows + r) * row_bytes + (int64_t)g * D * S::kEsize + cc * 16)
                           : kNowhere;
+  constexpr uint32_t kQBytes = D * S::kQEsize;
   uint32_t q_off[S::kQWords];
 #pragma unroll
-  for (int i = 0; i < S::kQWords; ++i) q_off[i] = lane_ok ? (uint32_t)((c * S::kQWords + i) * 16) : kNowhere;
-  constexpr uint32_t kQBytes = D * S::kQEsize;
+  for (int i = 0; i < S::kQWords; ++i)
+    q_off[i] = lane_ok ? (uint32_t)(hw * kQBytes + (cc * S::kQWords + i) * 16) : kNowhere;
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
-  const char* __restrict__ qbase = static_cast<const char*>(a.query) + (int64_t)h * kQBytes;
+  const char* __restrict__ qbase = static_cast<const char*>(a.query) + (int64_t)h0 * kQBytes;
   const int64_t q_row_bytes = (int64_t)a.num_q_heads * kQBytes;
 
   // the run's first row: the first r with P[r + 1] > g0
@@ -555,7 +565,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     // the row's query, with its first tile of the run (an empty descriptor otherwise: zeros, no access)
     const bool first = i_tile == 0 || jj == 0;
     const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc(qbase + (int64_t)i_row * q_row_bytes, live && first ? kQBytes : 0u);
+        make_rsrc(qbase + (int64_t)i_row * q_row_bytes, live && first ? kQBytes * HPW : 0u);
 #pragma unroll
     for (int i = 0; i < S::kQWords; ++i) qq.w[i] = load16<0>(qr, q_off[i]);
     tinfo = (uint32_t)rows | (first ? kFirst : 0u) | (i_tile == i_nt - 1 || jj == n - 1 ? kLast : 0u) |
@@ -590,11 +600,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
       const float poison = __uint_as_float(0x7fc00000u);
       float* dst;
       if (tinfo & kWhole) {
-        dst = a.out + ((int64_t)(tinfo >> kRowShift) * a.num_q_heads + h) * D + c * S::kEpl;
+        dst = a.out + ((int64_t)(tinfo >> kRowShift) * a.num_q_heads + h) * D + cc * S::kEpl;
       } else {
         const int64_t wrow = ((int64_t)h * a.chunks + chunk) * 2 + (tinfo & kSlot1 ? 1 : 0);
-        dst = a.ws_o + wrow * D + c * S::kEpl;
-        if (c == 0) {
+        dst = a.ws_o + wrow * D + cc * S::kEpl;
+        if (cc == 0) {
           a.ws_ml[2 * wrow] = seg_bad ? poison : m;
           a.ws_ml[2 * wrow + 1] = l;
         }
@@ -621,7 +631,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     float sc[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      sc[i] = group_sum<S::kRowLanes>(dot_chunk<KV>(q, kq[i])) * a.scale_log2;
+      sc[i] = group_sum<S::kSumLanes>(dot_chunk<KV>(q, kq[i])) * a.scale_log2;
       if (!full && i * S::kRows + r >= rows) sc[i] = -INFINITY;
     }
     float mt = sc[0];
@@ -749,40 +759,62 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t str
 }
 
 template <int KV, bool kMulti>
-hipError_t launch_balanced_kv(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+hipError_t launch_balanced_kv(const DecodeArgs& a, int hpw, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: decode_valu_balanced_kernel<KV, 64, kMulti><<<grid, block, lds, stream>>>(a); break;
-    case 80: decode_valu_balanced_kernel<KV, 80, kMulti><<<grid, block, lds, stream>>>(a); break;
-    case 96: decode_valu_balanced_kernel<KV, 96, kMulti><<<grid, block, lds, stream>>>(a); break;
-    case 112: decode_valu_balanced_kernel<KV, 112, kMulti><<<grid, block, lds, stream>>>(a); break;
-    case 128: decode_valu_balanced_kernel<KV, 128, kMulti><<<grid, block, lds, stream>>>(a); break;
-    case 192: decode_valu_balanced_kernel<KV, 192, kMulti><<<grid, block, lds, stream>>>(a); break;
-    case 256: decode_valu_balanced_kernel<KV, 256, kMulti><<<grid, block, lds, stream>>>(a); break;
+    case 64:
+      if constexpr (KV != PA_F32)
+        if (hpw == 2) {
+          decode_valu_balanced_kernel<KV, 64, kMulti, 2><<<grid, block, lds, stream>>>(a);
+          break;
+        }
+      decode_valu_balanced_kernel<KV, 64, kMulti, 1><<<grid, block, lds, stream>>>(a);
+      break;
+    case 80: decode_valu_balanced_kernel<KV, 80, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
+    case 96: decode_valu_balanced_kernel<KV, 96, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
+    case 112: decode_valu_balanced_kernel<KV, 112, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
+    case 128:
+      if constexpr (KV == PA_FP8_E4M3)
+        if (hpw == 2) {
+          decode_valu_balanced_kernel<KV, 128, kMulti, 2><<<grid, block, lds, stream>>>(a);
+          break;
+        }
+      decode_valu_balanced_kernel<KV, 128, kMulti, 1><<<grid, block, lds, stream>>>(a);
+      break;
+    case 192: decode_valu_balanced_kernel<KV, 192, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
+    case 256: decode_valu_balanced_kernel<KV, 256, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int KV>
-hipError_t launch_balanced_dtype(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+hipError_t launch_balanced_dtype(const DecodeArgs& a, int hpw, dim3 grid, dim3 block, hipStream_t stream) {
   const bool multi = a.query_start != nullptr;
   const size_t lds = (size_t)((multi ? 3 : 2) * (int64_t)a.num_tokens + 1) * sizeof(int32_t);
-  return multi ? launch_balanced_kv<KV, true>(a, grid, block, lds, stream)
-               : launch_balanced_kv<KV, false>(a, grid, block, lds, stream);
+  return multi ? launch_balanced_kv<KV, true>(a, hpw, grid, block, lds, stream)
+               : launch_balanced_kv<KV, false>(a, hpw, grid, block, lds, stream);
 }
 
-int32_t balanced_chunks(int32_t num_q_heads) {
-  const int32_t groups = (num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+int valu_heads_per_wave(int kv_dtype, int head_dim, int group) {
+  const int row_bytes = head_dim * (kv_dtype == PA_F32 ? 4 : kv_dtype == PA_BF16 ? 2 : 1);
+  return group == 1 && (row_bytes == 64 || row_bytes == 128) ? 2 : 1;
+}
+
+int32_t balanced_chunks(int32_t num_q_heads, int32_t heads_per_wave) {
+  const int32_t waves = (num_q_heads + heads_per_wave - 1) / heads_per_wave;
+  const int32_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
   return groups >= kResidentWaves / kWavesPerGroup ? 1 : kResidentWaves / kWavesPerGroup / groups;
 }
 
 hipError_t launch_decode_valu_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   if (a.num_tokens > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix) return hipErrorInvalidValue;
-  const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.chunks, 1);
+  const int hpw = valu_heads_per_wave(kv_dtype, a.head_dim, a.group);
+  const int waves = (a.num_q_heads + hpw - 1) / hpw;
+  const dim3 grid((waves + kWavesPerGroup - 1) / kWavesPerGroup, a.chunks, 1);
   const dim3 block(kWave * kWavesPerGroup);
-  if (kv_dtype == PA_BF16) return launch_balanced_dtype<PA_BF16>(a, grid, block, stream);
-  if (kv_dtype == PA_F32) return launch_balanced_dtype<PA_F32>(a, grid, block, stream);
-  if (kv_dtype == PA_FP8_E4M3) return launch_balanced_dtype<PA_FP8_E4M3>(a, grid, block, stream);
+  if (kv_dtype == PA_BF16) return launch_balanced_dtype<PA_BF16>(a, hpw, grid, block, stream);
+  if (kv_dtype == PA_F32) return launch_balanced_dtype<PA_F32>(a, hpw, grid, block, stream);
+  if (kv_dtype == PA_FP8_E4M3) return launch_balanced_dtype<PA_FP8_E4M3>(a, hpw, grid, block, stream);
   return hipErrorInvalidValue;
 }
 

@@ -169,7 +169,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round))) {
     p.balanced = true;
     p.split = true;
-    p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads) : pa::balanced_chunks(num_q_heads);
+    p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads)
+                   : pa::balanced_chunks(num_q_heads,
+                                         pa::valu_heads_per_wave(kv_dtype, head_dim, num_q_heads / num_kv_heads));
     p.partition = 0;
     p.max_partitions = 1;
     const size_t o_bytes = pa::balanced_o_elems(num_q_heads, p.chunks, head_dim) * sizeof(float);

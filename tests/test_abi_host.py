@@ -225,8 +225,8 @@ def test_grouped_query_decode_default_takes_the_balanced_split_beyond_one_round(
     assert pa.partition_size_for(64, 64, 2, 128, 16, 2048, pa.PA_BF16, -1) % 16 == 0
 
 
-def balanced_ws(T, Hq, D):
-    runs = max(1, 1024 // ((Hq + 1) // 2))
+def balanced_ws(T, Hq, D, hpw=1):
+    runs = max(1, 1024 // (((Hq + hpw - 1) // hpw + 1) // 2))
     o = (Hq * runs * 2 * D * 4 + 255) // 256 * 256
     ml = (Hq * runs * 2 * 2 * 4 + 255) // 256 * 256
     return o + ml + (T + 1) * 4
@@ -248,6 +248,11 @@ def test_balanced_split_plan():
     assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == balanced_ws(64, 32, 128)
     assert pa.workspace_bytes(7, 5, 5, 80, 16, 900, pa.PA_FP8_E4M3, B) == balanced_ws(7, 5, 80)
     assert pa.workspace_bytes(3, 4096, 4096, 64, 16, 900, pa.PA_F32, B) == balanced_ws(3, 4096, 64)  # one run
+    # two heads per wave where head rows are 64 or 128 bytes and every query head has its own KV head: half
+    # the waves per run, twice the runs
+    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_FP8_E4M3, B) == balanced_ws(64, 32, 128, 2)
+    assert pa.workspace_bytes(9, 5, 5, 64, 16, 900, pa.PA_BF16, B) == balanced_ws(9, 5, 64, 2)
+    assert pa.workspace_bytes(9, 8, 4, 64, 16, 900, pa.PA_F32, B) == balanced_ws(9, 8, 64)
     # several tokens per sequence (fp32: the per-head kernel): one tile count per query row
     assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == B
     assert pa.multi_workspace_bytes(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == balanced_ws(256, 32, 128)

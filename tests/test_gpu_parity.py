@@ -123,6 +123,9 @@ SMALL = [
     (227, [129, 64, 3], 4, 4, 192, 16, "f32"),
     (228, [515, 31, 2], 8, 8, 96, 16, "fp8"),
     (229, [400, 77], 8, 8, 256, 32, "fp8"),
+    # two heads per wave in the balanced split (64- and 128-byte head rows), 8-slot blocks
+    (230, [90, 33, 257, 16, 1], 8, 8, 128, 8, "fp8"),
+    (231, [300, 8, 65, 1000], 4, 4, 64, 8, "bf16"),
 ]
 
 
@@ -313,6 +316,11 @@ def test_empty_context_bad_entries_and_clamped_lengths():
     ([5000], 2, 64, "f32"),                                # one row cut into about a thousand runs
     ([3, 1, 2, 17, 16, 15, 33] * 9, 32, 80, "fp8"),        # many short rows per run
     ([900, 1300, 20, 2500], 16, 256, "bf16"),              # few rows, 512-byte head rows
+    # two adjacent heads per wave where head rows are 64 or 128 bytes
+    ([0, 0, 700, 1, 0, 3000, 45, 0, 0], 8, 128, "fp8"),    # empty rows, E4M3 128-byte rows
+    ([3, 1, 2, 17, 16, 15, 33] * 9, 5, 128, "fp8"),        # odd head count: the last wave holds one head
+    ([900, 1300, 20, 2500], 6, 64, "bf16"),                # bf16 128-byte rows
+    ([5000], 2, 64, "fp8"),                                # E4M3 64-byte rows, one row cut into many runs
 ])
 def test_balanced_split_parity(lens, hq, d, dt):
     st = custom_structure("bal", 441, lens, hq, hq, d, 16, dt, pool_factor=1.2)
