@@ -97,20 +97,135 @@ __device__ __forceinline__ void prob_operands(const float* sv, float mref, U4& h
   lo = U4{r[0], r[1], r[2], r[3]};
 }
 
+// Geometry of the K/V tiles of both grouped-query kernels (bf16 or E4M3 cache, head_dim D).
+template <int KV, int D>
+struct GqaShape {
+  static constexpr int kEsize = KV == PA_BF16 ? 2 : 1;  // bytes per cached element
+  static constexpr int kChunks = D / 32;                // 32-dim k-chunks of the QK product
+  static constexpr int kNt = D / 16;                    // 16-dim column tiles of the PV product
+  static constexpr int kPitch = D * 2 + 16;             // LDS bytes per K or V row (bf16 in LDS for both caches)
+  static constexpr int kSlice = kTileTok * kPitch;      // one 32-row tile of K or of V
+  static constexpr int kRowLanes = D * kEsize / 16;     // lanes covering one head row with 16-byte loads
+  static constexpr int kRows = kWave / kRowLanes;       // rows per wave-wide load
+  static constexpr int kLoads = kTile / kRows;          // loads per 16-row half, for K and for V
+  // a load of at most 8 rows stays inside one 8-row quarter; 16-row loads (E4M3 at head_dim 64) take a whole
+  // half through the even quarter's descriptor (the host refuses 8-slot blocks for them)
+  static constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
+  static_assert(kLoads * kRows == kTile, "whole rows per load");
+};
+
+// Loads of one 32-token tile into a register set. `t` is the tile's first position, clamped to the last live
+// tile (table entries are read at live positions only); `t_live` is the unclamped one. Each 8-row quarter goes
+// through a descriptor covering only its rows below `u1`: the rest read as zero without touching memory.
+// Quarters of one 16-row half share a block unless blocks hold 8 slots. `last8` is the start of the last live
+// 8-row group.
+template <int KV, int D, int NL, typename TablePtr>
+__device__ __forceinline__ void gqa_issue(U4 (*kb)[NL], U4 (*vb)[NL], TablePtr table, int t, int t_live, int u1,
+                                          int last8, const DecodeArgs& a, int64_t row_bytes, const char* kbase,
+                                          const char* vbase, const uint32_t* off, bool& bad) {
+  using S = GqaShape<KV, D>;
+  static_assert(NL == S::kLoads, "register sets of the tile's shape");
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int h2 = q4 >> 1;
+    const int64_t base = (q4 & 1) == 0 || a.bs_log2 == 3
+                             ? tile_slot_bytes(table, min(t + q4 * (kTile / 2), last8), a.bs_log2, a.num_blocks,
+                                               row_bytes, bad)
+                             : tile_slot_bytes(table, min(t + h2 * kTile, last8), a.bs_log2, a.num_blocks, row_bytes,
+                                               bad) + (kTile / 2) * row_bytes;
+    const int rows = min(S::kQuarterRows, u1 - (t_live + q4 * (kTile / 2)));
+    const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
+    const uint32_t qoff = (uint32_t)((q4 & 1) * (kTile / 2) * row_bytes);
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      if ((S::kRows * i < kTile / 2) == ((q4 & 1) == 0)) {
+        kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
+        vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
+      }
+    }
+  }
+}
+
+// One tile through the matrix cores: stage K and V into the wave's LDS slices (E4M3 widened to bf16; rows
+// past the range end were loaded as zeros), S^T = K Q^T, the online-softmax update of (m, l) in the exp2
+// domain with positions >= `lim` masked unless the whole tile is `full`, then O^T += V^T (P_hi + P_lo)^T.
+template <int KV, int D, int NL>
+__device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* kslice, char* vslice, int wofs,
+                                            const char* kread, const char* rbase, const U4* qb, float scale_log2,
+                                            int t, bool full, int lim, int j, float& m, float& l, f32x4* o) {
+  using S = GqaShape<KV, D>;
+  static_assert(NL == S::kLoads, "register sets of the tile's shape");
+  // the previous tile's reads come first
+  wave_lds_sync();
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int r = (h2 * kTile + S::kRows * i) * S::kPitch + wofs;
+      if constexpr (KV == PA_BF16) {
+        *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
+        *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
+      } else {
+        stage_e4m3(kslice + r, kb[h2][i]);
+        stage_e4m3(vslice + r, vb[h2][i]);
+      }
+    }
+  wave_lds_sync();
+  f32x4 sc[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < S::kChunks; ++c)
+      sc[h2] = mfma(*reinterpret_cast<const U4*>(kread + h2 * kTile * S::kPitch + c * 64), qb[c], sc[h2]);
+  }
+  float sv[8];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = sc[h2][i] * scale_log2;
+      if (!full && t + h2 * kTile + 4 * j + i >= lim) x = -INFINITY;
+      sv[h2 * 4 + i] = x;
+      mt = fmaxf(mt, x);
+    }
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float mn = fmaxf(m, mt);
+  const float mref = mn == -INFINITY ? 0.f : mn;
+  const float alpha = fast_exp2(m - mref);
+  m = mn;
+  U4 pb, pl;
+  float psum;
+  prob_operands(sv, mref, pb, pl, psum);
+  l = l * alpha + psum;
+#pragma unroll
+  for (int nt = 0; nt < S::kNt; ++nt) {
+    // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4)
+    // two transposed reads give this lane dim 16nt + n of tokens 4j..4j+3 and 16+4j..16+4j+3
+    const u32x2 lo = lds_read_tr16(rbase + nt * 32);
+    const u32x2 hi = lds_read_tr16(rbase + kTile * S::kPitch + nt * 32);
+    f32x4 acc = o[nt];
+    acc[0] *= alpha;
+    acc[1] *= alpha;
+    acc[2] *= alpha;
+    acc[3] *= alpha;
+    const U4 vt{lo.x, lo.y, hi.x, hi.y};
+    o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
+  }
+}
+
 // W waves (KV heads of one sequence) per workgroup: they stream the same slots of the pool side by side. At
 // least two waves per SIMD: with smaller workgroups the compiler would otherwise spend the register budget of
 // one (measured on MI355X with 4, 2 and 1 KV heads: 3-8% slower).
 template <int KV, int D, int W>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const DecodeArgs a) {
-  constexpr int kEsize = KV == PA_BF16 ? 2 : 1;  // bytes per cached element
-  constexpr int kChunks = D / 32;          // 32-dim k-chunks of the QK product
-  constexpr int kNt = D / 16;              // 16-dim column tiles of the PV product
-  constexpr int kPitch = D * 2 + 16;       // LDS bytes per K or V row (bf16 in LDS for both caches)
-  constexpr int kSlice = kTileTok * kPitch;  // one 32-row tile of K or of V
-  constexpr int kRowLanes = D * kEsize / 16; // lanes covering one head row with 16-byte loads
-  constexpr int kRows = kWave / kRowLanes; // rows per wave-wide load
-  constexpr int kLoads = kTile / kRows;    // loads per 16-row half, for K and for V
-  static_assert(kLoads * kRows == kTile, "whole rows per load");
+  using S = GqaShape<KV, D>;
+  constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
+  constexpr int kRowLanes = S::kRowLanes, kRows = S::kRows, kLoads = S::kLoads;
   __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -200,37 +315,10 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   bool bad = false;
   const int ntiles = (u1 - u0 + kTileTok - 1) / kTileTok;
   const int last8 = ntiles > 0 ? ((u1 - 1) & ~(kTile / 2 - 1)) : u0;  // start of the last live 8-token group
-  // a load of at most 8 rows stays inside one 8-row quarter; 16-row loads (E4M3 at head_dim 64) take a whole
-  // half through the even quarter's descriptor (the host refuses 8-slot blocks for them)
-  constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
-
   U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
   auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-    const int t = u0 + min(tile, ntiles - 1) * kTileTok;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      // 8-row quarter q4 of the tile (rows 8 q4 .. 8 q4 + 7): the table is read at a live position, and the
-      // quarter's rows past the range end read as zero without touching memory. Quarters of one 16-row half
-      // share a block unless blocks hold 8 slots.
-      const int h2 = q4 >> 1;
-      const int64_t base = (q4 & 1) == 0 || a.bs_log2 == 3
-                               ? tile_slot_bytes(table, min(t + q4 * (kTile / 2), last8), a.bs_log2, a.num_blocks,
-                                                 row_bytes, bad)
-                               : tile_slot_bytes(table, min(t + h2 * kTile, last8), a.bs_log2, a.num_blocks,
-                                                 row_bytes, bad) + (kTile / 2) * row_bytes;
-      const int rows = min(kQuarterRows, u1 - (u0 + tile * kTileTok + q4 * (kTile / 2)));
-      const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
-      const uint32_t qoff = (uint32_t)((q4 & 1) * (kTile / 2) * row_bytes);
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        if ((kRows * i < kTile / 2) == ((q4 & 1) == 0)) {
-          kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
-          vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
-        }
-      }
-    }
+    gqa_issue<KV, D>(kb, vb, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1, last8, a,
+                     row_bytes, kbase, vbase, off, bad);
   };
 
   // LDS: row r of the tile at slice + r * kPitch, K and V each in their own slice. This lane writes rows
@@ -295,67 +383,9 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
 
   auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
     const int t = u0 + tile * kTileTok;
-    const bool full = t + kTileTok <= ufull;  // no column masks a position of this tile
-    // stage K and V (rows past the partition end were loaded as zeros); the previous tile's reads come first
-    wave_lds_sync();
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        const int r = (h2 * kTile + kRows * i) * kPitch + wofs;
-        if constexpr (KV == PA_BF16) {
-          *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
-          *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
-        } else {
-          stage_e4m3(kslice + r, kb[h2][i]);
-          stage_e4m3(vslice + r, vb[h2][i]);
-        }
-      }
-    wave_lds_sync();
-    // scores
-    f32x4 sc[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-        sc[h2] = mfma(*reinterpret_cast<const U4*>(kread + h2 * kTile * kPitch + c * 64), qb[c], sc[h2]);
-    }
-    float sv[8];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = sc[h2][i] * a.scale_log2;
-        if (!full && t + h2 * kTile + 4 * j + i >= lim) x = -INFINITY;
-        sv[h2 * 4 + i] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    m = mn;
-    U4 pb, pl;
-    float psum;
-    prob_operands(sv, mref, pb, pl, psum);
-    l = l * alpha + psum;
-#pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) {
-      // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4)
-      // two transposed reads give this lane dim 16nt + n of tokens 4j..4j+3 and 16+4j..16+4j+3
-      const u32x2 lo = lds_read_tr16(rbase + nt * 32);
-      const u32x2 hi = lds_read_tr16(rbase + kTile * kPitch + nt * 32);
-      f32x4 acc = o[nt];
-      acc[0] *= alpha;
-      acc[1] *= alpha;
-      acc[2] *= alpha;
-      acc[3] *= alpha;
-      const U4 vt{lo.x, lo.y, hi.x, hi.y};
-      o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
-    }
+    // no column masks a position of a tile below ufull
+    gqa_consume<KV, D>(kb, vb, kslice, vslice, wofs, kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull, lim,
+                       j, m, l, o);
     if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
   };
 
@@ -401,17 +431,10 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
 // publishes it for the merge.
 template <int KV, int D, int W>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(const DecodeArgs a) {
-  constexpr int kEsize = KV == PA_BF16 ? 2 : 1;
-  constexpr int kChunks = D / 32;
-  constexpr int kNt = D / 16;
-  constexpr int kPitch = D * 2 + 16;
-  constexpr int kSlice = kTileTok * kPitch;
-  constexpr int kRowLanes = D * kEsize / 16;
-  constexpr int kRows = kWave / kRowLanes;
-  constexpr int kLoads = kTile / kRows;
-  constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
+  using S = GqaShape<KV, D>;
+  constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
+  constexpr int kRowLanes = S::kRowLanes, kRows = S::kRows, kLoads = S::kLoads;
   constexpr int NT = kWave * W;
-  static_assert(kLoads * kRows == kTile, "whole rows per load");
   __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
   __shared__ int32_t wave_total[W];
   extern __shared__ int32_t P[];  // [num_seqs + 1]: tiles of the sequences before each one
@@ -496,90 +519,14 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
 
     U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
     auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-      const int t = u0 + min(tile, ntiles - 1) * kTileTok;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // 8-row quarter q4 of the tile, as in the partition kernel
-        const int h2 = q4 >> 1;
-        const int64_t base = (q4 & 1) == 0 || a.bs_log2 == 3
-                                 ? tile_slot_bytes(table, min(t + q4 * (kTile / 2), last8), a.bs_log2, a.num_blocks,
-                                                   row_bytes, bad)
-                                 : tile_slot_bytes(table, min(t + h2 * kTile, last8), a.bs_log2, a.num_blocks,
-                                                   row_bytes, bad) + (kTile / 2) * row_bytes;
-        const int rows = min(kQuarterRows, u1 - (u0 + tile * kTileTok + q4 * (kTile / 2)));
-        const uint32_t live = rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u;
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live);
-        const uint32_t qoff = (uint32_t)((q4 & 1) * (kTile / 2) * row_bytes);
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-          if ((kRows * i < kTile / 2) == ((q4 & 1) == 0)) {
-            kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
-            vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
-          }
-        }
-      }
+      gqa_issue<KV, D>(kb, vb, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1, last8, a,
+                       row_bytes, kbase, vbase, off, bad);
     };
 
     auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
       const int t = u0 + tile * kTileTok;
-      const bool full = t + kTileTok <= u1;
-      wave_lds_sync();
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-          const int r = (h2 * kTile + kRows * i) * kPitch + wofs;
-          if constexpr (KV == PA_BF16) {
-            *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
-            *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
-          } else {
-            stage_e4m3(kslice + r, kb[h2][i]);
-            stage_e4m3(vslice + r, vb[h2][i]);
-          }
-        }
-      wave_lds_sync();
-      f32x4 sc[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c)
-          sc[h2] = mfma(*reinterpret_cast<const U4*>(kread + h2 * kTile * kPitch + c * 64), qb[c], sc[h2]);
-      }
-      float sv[8];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = sc[h2][i] * a.scale_log2;
-          if (!full && t + h2 * kTile + 4 * j + i >= u1) x = -INFINITY;
-          sv[h2 * 4 + i] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m - mref);
-      m = mn;
-      U4 pb, pl;
-      float psum;
-      prob_operands(sv, mref, pb, pl, psum);
-      l = l * alpha + psum;
-#pragma unroll
-      for (int nt = 0; nt < kNt; ++nt) {
-        const u32x2 vlo = lds_read_tr16(rbase + nt * 32);
-        const u32x2 vhi = lds_read_tr16(rbase + kTile * kPitch + nt * 32);
-        f32x4 acc = o[nt];
-        acc[0] *= alpha;
-        acc[1] *= alpha;
-        acc[2] *= alpha;
-        acc[3] *= alpha;
-        const U4 vt{vlo.x, vlo.y, vhi.x, vhi.y};
-        o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
-      }
+      gqa_consume<KV, D>(kb, vb, kslice, vslice, wofs, kread, rbase, qb, a.scale_log2, t, t + kTileTok <= u1, u1,
+                         j, m, l, o);
     };
 
     issue(kA, vA, 0);
