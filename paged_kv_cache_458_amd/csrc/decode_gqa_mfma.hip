@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
 // wave per (sequence, KV head, partition), unequal contexts leave waves of unequal length, and a grid of whole
 // workgroups of 8 KV heads leaves some CUs without one and some XCDs with more bytes than others. Here the
 // 32-token tiles of all sequences, in sequence order, form one list cut into `chunks` equal runs; workgroup
-// (x, r) takes run r for KV heads 8x .. 8x + 7, and the host sizes the grid to one wave per wave slot of the
+// (x, r) takes run r for KV heads Wx .. Wx + W - 1, and the host sizes the grid to one wave per wave slot of the
 // chip, so every wave streams the same number of tiles and every XCD the same bytes. A wave walks its run one
 // sequence segment at a time, with the partition kernel's load pipeline inside a segment: a sequence lying
 // wholly inside the run is written to `out`; one cut by run boundaries leaves a partial in slot

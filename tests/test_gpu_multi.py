@@ -76,6 +76,9 @@ CASES = [
     (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
     (510, [0, 8, 700, 30], [3, 12, 5, 1], 8, 8, 80, 16, "bf16"),      # QL > L, an empty context
     (513, [2000, 5, 64, 300, 1], [7, 0, 4, 2, 1], 16, 16, 112, 8, "fp8"),  # an empty sequence; bs 8
+    # at most one row per sequence without grouping: the per-head kernel, two heads per wave in its balanced split
+    (514, [300, 1, 900, 0, 45, 2048], [1, 1, 1, 0, 1, 1], 6, 6, 64, 16, "fp8"),
+    (515, [77, 1500, 16, 640], [1, 0, 1, 1], 5, 5, 128, 16, "fp8"),   # odd head count
 ]
 
 
@@ -99,9 +102,10 @@ def test_multi_parity(case):
             assert (gpu[:7] == 0).all() and np.abs(gpu[7]).max() > 0
 
 
-@pytest.mark.parametrize("hq,hkv,dt", [(8, 8, "bf16"), (16, 2, "bf16"), (32, 8, "fp8"), (4, 4, "f32")])
-def test_one_row_per_sequence_is_decode(hq, hkv, dt):
-    st = custom_structure("m1", 511, [700, 33, 1500, 260, 1], hq, hkv, 128, 16, dt)
+@pytest.mark.parametrize("hq,hkv,dt,d", [(8, 8, "bf16", 128), (16, 2, "bf16", 128), (32, 8, "fp8", 128),
+                                         (4, 4, "f32", 128), (8, 8, "fp8", 128), (6, 6, "bf16", 64)])
+def test_one_row_per_sequence_is_decode(hq, hkv, dt, d):
+    st = custom_structure("m1", 511, [700, 33, 1500, 260, 1], hq, hkv, d, 16, dt)
     t = materialize(st, DEV)
     qs = np.arange(st.num_seqs + 1, dtype=np.int32)
     for part in (0, 64, -1):
