@@ -11,6 +11,7 @@ Prints one JSON line: whole-step achieved GB/s (algorithmic bytes / step time), 
 entry for the attention call (HIP events on the stream it runs on) and the CPU oracle's rate on the host cores.
 
     python bench.py [--workload llama2_7b] [--steps 100] [--warmup 10]
+    python bench.py --workload configs    (one line per synthetic decode workload, each in a fresh process)
     python bench.py --workload decode_loop --steps 100 --warmup 50   (continuous batching, block manager)
 """
 
@@ -359,6 +360,22 @@ def main() -> int:
                   "same kernels on its own share of sequences or KV heads); use --gpus 1", flush=True)
         return 2
 
+    if args.workload == "configs":
+        # every synthetic decode workload, one JSON line each, each run in a process of its own (this one never
+        # touches the GPU)
+        import subprocess
+
+        from workloads import CONFIG_NAMES
+
+        rc = 0
+        for name in CONFIG_NAMES:
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(args.steps),
+                   "--warmup", str(args.warmup), "--replicas", str(args.replicas), "--cpu-seconds",
+                   str(args.cpu_seconds)]
+            log(f"configs: {name}")
+            rc = rc or subprocess.run(cmd).returncode
+        return rc
+
     import numpy as np
     import torch
 
@@ -370,7 +387,7 @@ def main() -> int:
     if args.workload == "swap":
         return run_swap(args)
     if args.workload not in CONFIG_NAMES:
-        ap.error(f"--workload must be one of {CONFIG_NAMES}, decode_loop or swap")
+        ap.error(f"--workload must be one of {CONFIG_NAMES}, configs, decode_loop or swap")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.load_library()
