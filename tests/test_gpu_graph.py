@@ -35,31 +35,33 @@ def i32(a: np.ndarray) -> torch.Tensor:
 
 
 CASES = [
-    # (Hq, Hkv, partition_size, what runs)
-    (8, 8, -1, "single-head balanced split + merge"),
-    (8, 8, 0, "single-head single pass"),
-    (32, 8, 512, "matrix-core partitions, two per wave, + log-sum-exp merge"),
-    (32, 8, pa.PA_PARTITION_BALANCED, "matrix-core balanced split + merge"),
+    # (Hq, Hkv, partition_size, cache dtype, what runs)
+    (8, 8, -1, "bf16", "single-head balanced split + merge"),
+    (8, 8, 0, "bf16", "single-head single pass"),
+    (32, 8, 512, "bf16", "matrix-core partitions, two per wave, + log-sum-exp merge"),
+    (32, 8, pa.PA_PARTITION_BALANCED, "bf16", "matrix-core balanced split + merge"),
+    (8, 8, -1, "fp8", "E4M3: quantising cache write, balanced split with two heads per wave + merge"),
 ]
 
 
-@pytest.mark.parametrize("hq,hkv,part,what", CASES, ids=[c[3] for c in CASES])
-def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, what):
-    st = custom_structure("graph", 461, [700, 1500, 33, 2048, 1, 900], hq, hkv, 128, 16, "bf16")
+@pytest.mark.parametrize("hq,hkv,part,dt,what", CASES, ids=[c[4] for c in CASES])
+def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, dt, what):
+    st = custom_structure("graph", 461, [700, 1500, 33, 2048, 1, 900], hq, hkv, 128, 16, dt)
     t = materialize(st, DEV, include_new_token=False)
     kc, vc = t["key_cache"], t["value_cache"]
     kc0, vc0 = kc.clone(), vc.clone()
     tables, lens, slots = i32(st.block_tables_pre), i32(st.context_lens), i32(st.slot_mapping)
-    need = pa.workspace_bytes(st.num_seqs, hq, hkv, st.head_dim, st.block_size, st.max_context_len, pa.PA_BF16,
-                              part)
+    kd = pa.PA_FP8_E4M3 if dt == "fp8" else pa.PA_BF16
+    need = pa.workspace_bytes(st.num_seqs, hq, hkv, st.head_dim, st.block_size, st.max_context_len, kd, part)
     assert (need > 0) == (part != 0)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
     out = torch.empty((st.num_seqs, hq, st.head_dim), dtype=torch.float32, device=DEV)
 
     def step():
-        pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots)
+        pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots, k_scale=st.k_scale, v_scale=st.v_scale)
         pa.paged_attention_decode(out, t["query"], kc, vc, tables, lens, st.scale, st.block_size,
-                                  max_context_len=st.max_context_len, partition_size=part, workspace=ws)
+                                  max_context_len=st.max_context_len, partition_size=part, workspace=ws,
+                                  k_scale=st.k_scale, v_scale=st.v_scale)
 
     step()
     torch.cuda.synchronize()
@@ -81,5 +83,5 @@ def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, what):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), want_out.view(torch.int32)), f"{what}: replay {rep} output"
-        assert torch.equal(kc.view(torch.int16), want_k.view(torch.int16)), f"{what}: replay {rep} key pool"
-        assert torch.equal(vc.view(torch.int16), want_v.view(torch.int16)), f"{what}: replay {rep} value pool"
+        assert torch.equal(kc.view(torch.uint8), want_k.view(torch.uint8)), f"{what}: replay {rep} key pool"
+        assert torch.equal(vc.view(torch.uint8), want_v.view(torch.uint8)), f"{what}: replay {rep} value pool"
