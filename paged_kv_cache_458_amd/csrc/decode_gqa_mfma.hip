@@ -33,9 +33,12 @@
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
 // loads of the block table (one per 16-token half). Scores use the exp2 domain (scale * log2 e folded in).
 //
-// An FP8 (OCP E4M3) cache is read at one byte per element and widened to bf16 while being staged into LDS
-// (every E4M3 value is exactly a bf16 value); from the LDS slices on, both caches take the same path. The
-// cache's scales enter as k_scale folded into the score scale and v_scale into the final normalisation.
+// An FP8 (OCP E4M3) cache is read at one byte per element and staged into LDS as it is; its operands are
+// widened to bf16 after the LDS reads (every E4M3 value is exactly a bf16 value): K through 8-byte reads, V^T
+// through gfx950's 8-bit transposing read, one per 16-dim column tile. Staging the widened values instead
+// (32 bytes per lane and load) stepped the lanes of each LDS write 32 bytes apart, with bank conflicts on every
+// write. The cache's scales enter as k_scale folded into the score scale and v_scale into the final
+// normalisation.
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "../../include/paged_attention.h"
@@ -63,15 +66,23 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// 16 E4M3 codes -> 16 bf16 values (32 bytes) at p
-__device__ __forceinline__ void stage_e4m3(char* p, const U4& c) {
-  U4 lo, hi;
-  e4m3x4_to_bf16x4(c.x, lo.x, lo.y);
-  e4m3x4_to_bf16x4(c.y, lo.z, lo.w);
-  e4m3x4_to_bf16x4(c.z, hi.x, hi.y);
-  e4m3x4_to_bf16x4(c.w, hi.z, hi.w);
-  reinterpret_cast<U4*>(p)[0] = lo;
-  reinterpret_cast<U4*>(p)[1] = hi;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte transposing LDS read of 8-bit elements (gfx950 ds_read_b64_tr_b8). Within each 16-lane group, lane l
+// receives element l % 8 of the 8-byte rows addressed by lanes (l % 16) / 8 + 2e, e = 0..7, in order of e
+// (checked on the device with an in-bounds probe).
+__device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 8 E4M3 codes (first in the lowest byte) -> 8 bf16 values, exactly
+__device__ __forceinline__ U4 widen8(const u32x2& c) {
+  U4 r;
+  e4m3x4_to_bf16x4(c.x, r.x, r.y);
+  e4m3x4_to_bf16x4(c.y, r.z, r.w);
+  return r;
 }
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -103,7 +114,9 @@ struct GqaShape {
   static constexpr int kEsize = KV == PA_BF16 ? 2 : 1;  // bytes per cached element
   static constexpr int kChunks = D / 32;                // 32-dim k-chunks of the QK product
   static constexpr int kNt = D / 16;                    // 16-dim column tiles of the PV product
-  static constexpr int kPitch = D * 2 + 16;             // LDS bytes per K or V row (bf16 in LDS for both caches)
+  // E4M3 codes are staged as they are and widened to bf16 after the LDS reads
+  static constexpr bool kRaw = KV != PA_BF16;
+  static constexpr int kPitch = D * (kRaw ? 1 : 2) + 16;  // LDS bytes per K or V row, padded by 16
   static constexpr int kSlice = kTileTok * kPitch;      // one 32-row tile of K or of V
   static constexpr int kRowLanes = D * kEsize / 16;     // lanes covering one head row with 16-byte loads
   static constexpr int kRows = kWave / kRowLanes;       // rows per wave-wide load
@@ -112,6 +125,26 @@ struct GqaShape {
   // half through the even quarter's descriptor (the host refuses 8-slot blocks for them)
   static constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
   static_assert(kLoads * kRows == kTile, "whole rows per load");
+
+  // Where lane (n, j) = (lane % 16, lane / 16) reads its operands in a tile's LDS slices. K, the A operand of
+  // S^T = K Q^T: row n, elements 32c + 8j .. 32c + 8j + 7 (plus c * 64 bytes of bf16 or c * 32 of codes).
+  static __device__ __forceinline__ const char* k_read(const char* kslice, int n, int j) {
+    return kslice + n * kPitch + j * (kRaw ? 8 : 16);
+  }
+  // V^T, the A operand of O^T += V^T P^T, for contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j +
+  // e - 4). bf16: two 16-bit transposing reads per 16-dim column tile; within each 16-lane group, lane l
+  // receives element l % 4 of the 8-byte rows addressed by lanes (l % 16) / 4 + 4e, e = 0..3, so lane
+  // (q, r) = (n / 4, n % 4) addresses token row 4j + q at dims 16nt + 4r .. + 3 and ends up with its own dim
+  // 16nt + n of the four token rows. E4M3: one 8-bit transposing read; lane n addresses token e = n / 2 at dims
+  // 16nt + 8 (n % 2) .. + 7 and receives dim 16nt + n of the eight tokens in order.
+  static __device__ __forceinline__ const char* v_read(const char* vslice, int n, int j) {
+    if constexpr (kRaw) {
+      const int e = n >> 1;
+      return vslice + (e < 4 ? 4 * j + e : kTile + 4 * j + e - 4) * kPitch + 8 * (n & 1);
+    } else {
+      return vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
+    }
+  }
 };
 
 // Loads of one 32-token tile into a register set. `t` is the tile's first position, clamped to the last live
@@ -164,13 +197,8 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int r = (h2 * kTile + S::kRows * i) * S::kPitch + wofs;
-      if constexpr (KV == PA_BF16) {
-        *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
-        *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
-      } else {
-        stage_e4m3(kslice + r, kb[h2][i]);
-        stage_e4m3(vslice + r, vb[h2][i]);
-      }
+      *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
+      *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
     }
   wave_lds_sync();
   f32x4 sc[2];
@@ -179,7 +207,9 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
     sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < S::kChunks; ++c)
-      sc[h2] = mfma(*reinterpret_cast<const U4*>(kread + h2 * kTile * S::kPitch + c * 64), qb[c], sc[h2]);
+      sc[h2] = mfma(S::kRaw ? widen8(*reinterpret_cast<const u32x2*>(kread + h2 * kTile * S::kPitch + c * 32))
+                            : *reinterpret_cast<const U4*>(kread + h2 * kTile * S::kPitch + c * 64),
+                    qb[c], sc[h2]);
   }
   float sv[8];
   float mt = -INFINITY;
@@ -204,16 +234,21 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
   l = l * alpha + psum;
 #pragma unroll
   for (int nt = 0; nt < S::kNt; ++nt) {
-    // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4)
-    // two transposed reads give this lane dim 16nt + n of tokens 4j..4j+3 and 16+4j..16+4j+3
-    const u32x2 lo = lds_read_tr16(rbase + nt * 32);
-    const u32x2 hi = lds_read_tr16(rbase + kTile * S::kPitch + nt * 32);
+    // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4);
+    // this lane gets dim 16nt + n of tokens 4j..4j+3 and 16+4j..16+4j+3
+    U4 vt;
+    if constexpr (S::kRaw) {
+      vt = widen8(lds_read_tr8(rbase + nt * 16));
+    } else {
+      const u32x2 lo = lds_read_tr16(rbase + nt * 32);
+      const u32x2 hi = lds_read_tr16(rbase + kTile * S::kPitch + nt * 32);
+      vt = U4{lo.x, lo.y, hi.x, hi.y};
+    }
     f32x4 acc = o[nt];
     acc[0] *= alpha;
     acc[1] *= alpha;
     acc[2] *= alpha;
     acc[3] *= alpha;
-    const U4 vt{lo.x, lo.y, hi.x, hi.y};
     o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
   }
 }
@@ -321,16 +356,12 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
                      row_bytes, kbase, vbase, off, bad);
   };
 
-  // LDS: row r of the tile at slice + r * kPitch, K and V each in their own slice. This lane writes rows
-  // rr + kRows*i (+16 for the second half) at bf16 column rc * 16 / kEsize of both slices.
-  const int wofs = rr * kPitch + rc * 16 * (2 / kEsize);
-  // K is read back in the A-operand layout of S^T = K Q^T: lane (n, j) takes row n, bytes 64c + 16j.
-  const char* const kread = kslice + n * kPitch + j * 16;
-  // Transposed reads (ds_read_b64_tr_b16): within each 16-lane group, lane l receives element l % 4 of the
-  // 8-byte rows addressed by lanes (l % 16) / 4 + 4e, e = 0..3. So lane (q, r) = ((l%16)/4, l%4) of group j
-  // addresses token row 4j + q at dims 16nt + 4r .. 16nt + 4r + 3, and every lane ends up with its own dim
-  // 16nt + n of the group's four token rows.
-  const char* const rbase = vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
+  // LDS: row r of the tile at slice + r * kPitch, K and V each in their own slice (bf16, or E4M3 codes as
+  // loaded). This lane writes its 16 loaded bytes of rows rr + kRows*i (+16 for the second half) at byte
+  // rc * 16 of both slices; it reads its MFMA operands back as S::k_read and S::v_read describe.
+  const int wofs = rr * kPitch + rc * 16;
+  const char* const kread = S::k_read(kslice, n, j);
+  const char* const rbase = S::v_read(vslice, n, j);
 
   // A wave covers at most two partitions. Finishing the first one mid-range only parks its state in
   // registers: any store inside the load loop would leave the compiler unable to count outstanding memory
@@ -475,9 +506,9 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   uint32_t off[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) off[i] = (uint32_t)((rr + kRows * i) * row_bytes + head_off + rc * 16);
-  const int wofs = rr * kPitch + rc * 16 * (2 / kEsize);
-  const char* const kread = kslice + n * kPitch + j * 16;
-  const char* const rbase = vslice + (4 * j + (n >> 2)) * kPitch + 8 * (n & 3);
+  const int wofs = rr * kPitch + rc * 16;
+  const char* const kread = S::k_read(kslice, n, j);
+  const char* const rbase = S::v_read(vslice, n, j);
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
   const float poison = __uint_as_float(0x7fc00000u);
