@@ -232,6 +232,17 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
   float psum;
   prob_operands(sv, mref, pb, pl, psum);
   l = l * alpha + psum;
+  // Once the running maxima settle, alpha = exp2(0) is exactly 1 in every lane and the rescale would change
+  // nothing: it is skipped for the whole wave then.
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int nt = 0; nt < S::kNt; ++nt) {
+      o[nt][0] *= alpha;
+      o[nt][1] *= alpha;
+      o[nt][2] *= alpha;
+      o[nt][3] *= alpha;
+    }
+  }
 #pragma unroll
   for (int nt = 0; nt < S::kNt; ++nt) {
     // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4);
@@ -244,12 +255,7 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
       const u32x2 hi = lds_read_tr16(rbase + kTile * S::kPitch + nt * 32);
       vt = U4{lo.x, lo.y, hi.x, hi.y};
     }
-    f32x4 acc = o[nt];
-    acc[0] *= alpha;
-    acc[1] *= alpha;
-    acc[2] *= alpha;
-    acc[3] *= alpha;
-    o[nt] = mfma(vt, pl, mfma(vt, pb, acc));
+    o[nt] = mfma(vt, pl, mfma(vt, pb, o[nt]));
   }
 }
 
