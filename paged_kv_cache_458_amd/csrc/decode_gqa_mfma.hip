@@ -16,22 +16,22 @@
 // head) however many of its tokens attend. Without grouping (G = 1) the columns are the QL rows alone. More
 // than 16 columns run as column groups of 16 in waves of their own, each reading the K/V again.
 //
-// Loads. K and V rows are read from the pool with every wave-wide load covering kRows whole 256-byte head
-// rows (full cache lines, non-temporal: each row is read once per call); both go through a per-wave LDS slice
-// (rows padded by 16 bytes). Loading K straight into the MFMA operand layout instead (16 rows x 64 bytes per
+// Loads. K and V rows are read from the pool with every wave-wide load covering kRows whole head rows (256
+// bytes of bf16 at D = 128: full cache lines, non-temporal, each row is read once per call); both go through a
+// per-wave LDS slice (rows padded by 16 bytes). Loading K straight into the MFMA operand layout instead (16 rows x 64 bytes per
 // load, each line split across two loads) costs about 12% of bandwidth with non-temporal loads.
 //
 // Operand layouts. K rows are the A operand of the first product: lane (n, j) = (lane % 16, lane / 16) reads
-// row n, bytes 64c + 16j of each 16-row half from LDS. The result leaves lane (n, j) with the scores of head n
+// row n, elements 32c + 8j .. 32c + 8j + 7 of each 16-row half from LDS. The result leaves lane (n, j) with the scores of head n
 // for tokens 4j..4j+3 of both halves; those eight probabilities are exactly that lane's B operands of the
 // second product once the contraction index k = 8j + e is mapped to token (e < 4 ? 4j + e : 16 + 4j + e - 4)
 // -- no data moves between lanes. V^T needs eight tokens of one dim per lane, the transpose of the pool's
 // layout: gfx950's transposing LDS reads give it with two 8-byte reads per 16-dim column tile. The
 // accumulator of the second product leaves lane (n, j) with head n, the same head as its softmax state, so
-// the online-softmax rescale is a per-lane multiply.
+// the online-softmax rescale is a per-lane multiply, skipped for the whole wave once no maximum moves.
 //
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
-// loads of the block table (one per 16-token half). Scores use the exp2 domain (scale * log2 e folded in).
+// loads of the block table (one per 16-token half, one per 8-token quarter with 8-slot blocks). Scores use the exp2 domain (scale * log2 e folded in).
 //
 // An FP8 (OCP E4M3) cache is read at one byte per element and staged into LDS as it is; its operands are
 // widened to bf16 after the LDS reads (every E4M3 value is exactly a bf16 value): K through 8-byte reads, V^T
