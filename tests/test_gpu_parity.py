@@ -335,9 +335,10 @@ def test_balanced_split_parity(lens, hq, d, dt):
     np.testing.assert_array_equal(a, decode(st, t, st.block_tables_pre, pa.PA_PARTITION_BALANCED))
 
 
-def test_balanced_split_edge_cases():
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])  # fp8: two heads per wave
+def test_balanced_split_edge_cases(dt):
     # a bad table entry in a row that several runs cut poisons that row only, through the merge
-    st = custom_structure("baledge", 442, [4000, 64, 2500, 0], 4, 4, 128, 16, "bf16", max_context_len=4096)
+    st = custom_structure("baledge", 442, [4000, 64, 2500, 0], 4, 4, 128, 16, dt, max_context_len=4096)
     t = materialize(st, DEV)
     h = {k: to_host(v) for k, v in t.items()}
     tables = st.block_tables_pre.copy()
@@ -347,7 +348,7 @@ def test_balanced_split_edge_cases():
     gpu = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=lens)
     assert np.isnan(gpu[2]).all() and np.isnan(gpu[1]).all() and (gpu[3] == 0).all()
     ref = oracle_decode(st, h, st.block_tables_pre)
-    assert_attention_close(gpu[[0]], ref[[0]], "bf16", "balanced")
+    assert_attention_close(gpu[[0]], ref[[0]], dt, "balanced")
     # every row empty: zero rows, no tile to read
     z = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=np.zeros(4, np.int32))
     assert (z == 0).all()
