@@ -28,7 +28,10 @@
 // -- no data moves between lanes. V^T needs eight tokens of one dim per lane, the transpose of the pool's
 // layout: gfx950's transposing LDS reads give it with two 8-byte reads per 16-dim column tile. The
 // accumulator of the second product leaves lane (n, j) with head n, the same head as its softmax state, so
-// the online-softmax rescale is a per-lane multiply, skipped for the whole wave once no maximum moves.
+// the online-softmax rescale is a per-lane multiply, skipped for the whole wave once no maximum moves. A
+// head's tile maximum spans the wave's four 16-lane rows and is taken with gfx950's row swaps, in registers;
+// positions past the range are masked only in a tile that holds some; weights become bf16 pairs through
+// packed conversions.
 //
 // K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
 // loads of the block table (one per 16-token half, one per 8-token quarter with 8-slot blocks). Scores use the exp2 domain (scale * log2 e folded in).
@@ -77,6 +80,16 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Maximum over lanes n, n + 16, n + 32 and n + 48, in registers (no LDS round trip). gfx950's row swaps with
+// both operands holding x: the 16-lane swap returns (rows 0, 0, 2, 2) and (rows 1, 1, 3, 3) of x, the 32-lane
+// swap (low half twice) and (high half twice) (checked on the device with an in-bounds probe).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // 8 E4M3 codes (first in the lowest byte) -> 8 bf16 values, exactly
 __device__ __forceinline__ U4 widen8(const u32x2& c) {
   U4 r;
@@ -85,8 +98,12 @@ __device__ __forceinline__ U4 widen8(const u32x2& c) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest even) in one word, the first in the low half: one packed conversion.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // A lane's eight probabilities exp2(sv[e] - mref) as the B operands of the P.V product, each weight split into
@@ -99,10 +116,10 @@ __device__ __forceinline__ void prob_operands(const float* sv, float mref, U4& h
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     const float x0 = fast_exp2(sv[e] - mref), x1 = fast_exp2(sv[e + 1] - mref);
-    const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+    const uint32_t hw = bf16x2_bits(x0, x1);
     psum += x0 + x1;
-    h[e / 2] = h0 | (h1 << 16);
-    r[e / 2] = bf16_bits(x0 - __uint_as_float(h0 << 16)) | (bf16_bits(x1 - __uint_as_float(h1 << 16)) << 16);
+    h[e / 2] = hw;
+    r[e / 2] = bf16x2_bits(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
   }
   hi = U4{h[0], h[1], h[2], h[3]};
   lo = U4{r[0], r[1], r[2], r[3]};
@@ -212,18 +229,23 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
                     qb[c], sc[h2]);
   }
   float sv[8];
-  float mt = -INFINITY;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = sc[h2][i] * scale_log2;
-      if (!full && t + h2 * kTile + 4 * j + i >= lim) x = -INFINITY;
-      sv[h2 * 4 + i] = x;
-      mt = fmaxf(mt, x);
-    }
-  mt = fmaxf(mt, __shfl_xor(mt, 16));
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+    for (int i = 0; i < 4; ++i) sv[h2 * 4 + i] = sc[h2][i] * scale_log2;
+  if (!full) {
+    // this lane's score (h2, i) is position t + h2 * kTile + 4j + i: masked from offset `rel` on
+    const int rel = lim - t - 4 * j;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (h2 * kTile + i >= rel) sv[h2 * 4 + i] = -INFINITY;
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+  mt = max_over_rows(mt);
   const float mn = fmaxf(m, mt);
   const float mref = mn == -INFINITY ? 0.f : mn;
   const float alpha = fast_exp2(m - mref);
