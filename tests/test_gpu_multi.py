@@ -71,6 +71,7 @@ CASES = [
     (507, [520, 47, 300], [4, 3, 2], 64, 8, 128, 256, "bf16"),         # G 8 x QL 4 = 32 columns, 2 groups
     (508, [5, 40, 18], [9, 2, 18], 16, 4, 128, 16, "fp8"),             # QL > L: the first rows are zero; 72 cols
     (509, [300, 64, 1000], [20, 17, 3], 8, 8, 64, 16, "bf16"),         # no grouping, 20 rows: 2 groups
+    (516, [300, 47, 1100, 2], [3, 2, 4, 2], 16, 4, 64, 16, "fp8"),     # E4M3 at head_dim 64: 16-row loads
     # per-head kernel
     (505, [65, 200, 9], [3, 7, 2], 8, 2, 96, 16, "bf16"),              # head_dim 96
     (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
