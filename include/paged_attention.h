@@ -169,9 +169,14 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
  *   max_query_len  the largest QL (>= 1). With bf16 or E4M3 caches at head_dim 64 or 128 the matrix cores take
  *                  all of a sequence's rows, reading its K/V once per 16 (row, grouped head) columns (at most
  *                  1024 columns); other calls read a sequence's K/V once per (row, head).
- *   partition_size as in paged_attention_decode, except that PA_PARTITION_BALANCED is refused
- *                  (PA_ERR_UNSUPPORTED) for calls that run on the matrix cores
- *   workspace      at least paged_attention_multi_workspace_bytes(...) bytes when that is non-zero
+ *   partition_size as in paged_attention_decode. On the matrix cores PA_PARTITION_BALANCED needs the grouped
+ *                  heads x max_query_len columns to fit one group of 16 and at most 2048 sequences
+ *                  (PA_ERR_UNSUPPORTED otherwise); its tile list holds sequences, each read once for all its
+ *                  rows. The library's choice (-1) there is the balanced split also where a single pass would
+ *                  fill a round of 2048 waves of unequal length (several rows per sequence only).
+ *   workspace      at least paged_attention_multi_workspace_bytes(...) bytes when that is non-zero; for the
+ *                  balanced split on the matrix cores, as paged_attention_workspace_bytes describes with
+ *                  partials [num_q_heads][R][2][max_query_len][head_dim] and (num_seqs + 1) tile counts
  * Other arguments as in paged_attention_decode_scaled. num_seqs == 0 or num_query_tokens == 0 is a no-op;
  * num_query_tokens > num_seqs * max_query_len is PA_ERR_SHAPE.
  */

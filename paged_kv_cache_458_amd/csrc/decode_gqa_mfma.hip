@@ -475,16 +475,17 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   write_rows(by, m, l, o);
 }
 
-// Balanced split (decode: one query row per sequence, the G heads of a KV head in one column group). With one
-// wave per (sequence, KV head, partition), unequal contexts leave waves of unequal length, and a grid of whole
+// Balanced split (one column group: the G heads of a KV head times at most 16 / G query rows per sequence). With
+// one wave per (sequence, KV head, partition), unequal contexts leave waves of unequal length, and a grid of whole
 // workgroups of 8 KV heads leaves some CUs without one and some XCDs with more bytes than others. Here the
 // 32-token tiles of all sequences, in sequence order, form one list cut into `chunks` equal runs; workgroup
 // (x, r) takes run r for KV heads Wx .. Wx + W - 1, and the host sizes the grid to one wave per wave slot of the
 // chip, so every wave streams the same number of tiles and every XCD the same bytes. A wave walks its run one
 // sequence segment at a time, with the partition kernel's load pipeline inside a segment: a sequence lying
-// wholly inside the run is written to `out`; one cut by run boundaries leaves a partial in slot
-// [head][run][2] -- slot 0 for the sequence the run starts inside, slot 1 for the one it ends inside -- and
-// balanced_reduce_kernel merges them. Stores happen only between segments, after the pipeline has drained.
+// wholly inside the run is written to `out`; one cut by run boundaries leaves, for each of its query rows qi, a
+// partial in slot [head][run][2][qi] -- side 0 for the sequence the run starts inside, side 1 for the one it
+// ends inside -- and balanced_reduce_kernel merges them. A sequence without query rows contributes no tiles.
+// Stores happen only between segments, after the pipeline has drained.
 //
 // Every workgroup first derives the prefix of the sequences' tile counts in LDS; the first one also
 // publishes it for the merge.
@@ -505,7 +506,8 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   const ConstI32* __restrict__ lens = as_constant(a.context_lens);
   for (int s = tid; s < T; s += NT) {
     const int L = min(max(lens[s], 0), a.max_context_len);
-    P[s + 1] = (L + kTileTok - 1) / kTileTok;
+    const int ql = a.query_start ? min(max(a.query_start[s + 1] - a.query_start[s], 0), a.max_query_len) : 1;
+    P[s + 1] = ql > 0 ? (L + kTileTok - 1) / kTileTok : 0;
   }
   __syncthreads();
   block_exclusive_scan<NT>(P, T, wave_total);
@@ -522,9 +524,10 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   if (g0 >= g1) return;
 
   const int G = a.group;
-  const int n = lane & 15;  // MFMA column: head g * G + n
+  const int n = lane & 15;  // MFMA column n = qi * G + hh: head g * G + hh of the sequence's query row qi
   const int j = lane >> 4;
-  const bool head_ok = n < G;
+  const int qi = n / G;
+  const int hh = n - qi * G;
   const int rr = lane / kRowLanes;
   const int rc = lane % kRowLanes;
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
@@ -560,9 +563,20 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
     const int ntiles = end - pos;
     const int last8 = (u1 - 1) & ~(kTile / 2 - 1);  // start of the last live 8-token group
     const ConstI32* __restrict__ table = as_constant(a.block_tables) + (int64_t)s * a.max_blocks_per_seq;
+    // the sequence's query rows (one in decode); row qi attends causally over its first L - ql + qi + 1
+    // positions, and every column over those below ufull
+    int q0 = s, ql = 1;
+    if (a.query_start) {
+      q0 = __builtin_amdgcn_readfirstlane(a.query_start[s]);
+      ql = min(max(__builtin_amdgcn_readfirstlane(a.query_start[s + 1]) - q0, 0), a.max_query_len);
+    }
+    const int qrow = q0 + qi;
+    const bool head_ok = qi < ql && qrow < a.num_tokens;
+    const int lim = head_ok ? min(u1, L - ql + qi + 1) : u0;
+    const int ufull = min(u1, L - ql + 1);
 
     const char* qptr = static_cast<const char*>(a.query) +
-                       (head_ok ? ((int64_t)s * a.num_q_heads + (int64_t)g * G + n) * D * 2 : 0);
+                       (head_ok ? ((int64_t)qrow * a.num_q_heads + (int64_t)g * G + hh) * D * 2 : 0);
     U4 qb[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
@@ -584,8 +598,8 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
 
     auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
       const int t = u0 + tile * kTileTok;
-      gqa_consume<KV, D>(kb, vb, kslice, vslice, wofs, kread, rbase, qb, a.scale_log2, t, t + kTileTok <= u1, u1,
-                         j, m, l, o);
+      gqa_consume<KV, D>(kb, vb, kslice, vslice, wofs, kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull,
+                         lim, j, m, l, o);
     };
 
     issue(kA, vA, 0);
@@ -598,18 +612,18 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
     }
     if (tj < ntiles) consume(kA, vA, tj);
 
-    // the sequence's rows: whole in this run -> out; else the run's partial in slot 0 (the run starts inside
-    // the sequence) or slot 1 (it ends inside it)
+    // the sequence's rows: whole in this run -> out; else the run's partial for row qi in slot 0 (the run
+    // starts inside the sequence) or slot 1 (it ends inside it)
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     if (head_ok) {
-      const int h = g * G + n;
+      const int h = g * G + hh;
       const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
       float* dst;
       if (p0 >= g0 && p1 <= g1) {
-        dst = a.out + ((int64_t)s * a.num_q_heads + h) * D;
+        dst = a.out + ((int64_t)qrow * a.num_q_heads + h) * D;
       } else {
-        const int64_t wrow = ((int64_t)h * a.chunks + chunk) * 2 + (p0 > g0 ? 1 : 0);
+        const int64_t wrow = (((int64_t)h * a.chunks + chunk) * 2 + (p0 > g0 ? 1 : 0)) * a.max_query_len + qi;
         dst = a.ws_o + wrow * D;
         if (j == 0) {
           a.ws_ml[2 * wrow] = bad ? poison : m;
@@ -702,7 +716,8 @@ int32_t gqa_balanced_chunks(int32_t num_kv_heads) {
 }
 
 hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
-  if (a.num_seqs > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix || a.query_start || a.col_groups != 1)
+  if (a.num_seqs > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix || a.col_groups != 1 ||
+      a.group * a.max_query_len > 16 || !a.seq_prefix)
     return hipErrorInvalidValue;
   if (kv_dtype == PA_BF16 && a.head_dim == 128) return launch_balanced_d<PA_BF16, 128>(a, stream);
   if (kv_dtype == PA_BF16 && a.head_dim == 64) return launch_balanced_d<PA_BF16, 64>(a, stream);

@@ -671,10 +671,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     if (j + i < n) consume(kb[i], vb[i], qb[i], info[i]);
 }
 
-// Merge of the balanced split's partials: one wave per (query row, head). A row whose tiles lie in one run was
-// written by the partition kernel; a row with no tile attends over nothing and gets a zero row here; a row
-// spanning runs c0 .. c1 has the partial of run c0 in slot 1 (slot 0 when it starts exactly at c0's first
-// tile) and those of runs c0 + 1 .. c1 in slot 0.
+// Merge of the balanced split's partials: one wave per (query row, head). The tile list holds query rows, or
+// sequences on the matrix-core kernel (seq_prefix), whose partials then carry the row's index qi within its
+// sequence. A row whose list item lies in one run was written by the decode kernel; an item with no tile
+// attends over nothing and its rows get a zero row here; an item spanning runs c0 .. c1 has the partial of run
+// c0 on side 1 (side 0 when it starts exactly at c0's first tile) and those of runs c0 + 1 .. c1 on side 0.
 template <int D>
 __global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs a) {
   constexpr int kDpl = (D + kWave - 1) / kWave;
@@ -683,7 +684,15 @@ __global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs
   const bool lane_ok = lane < kActive;
   const int h = blockIdx.x;
   const int row = blockIdx.y;
-  const int p0 = a.tile_prefix[row], p1 = a.tile_prefix[row + 1], total = a.tile_prefix[a.num_tokens];
+  int item = row, qi = 0, ql = 1, items = a.num_tokens;
+  if (a.seq_prefix) {
+    item = seq_of_row(a, row);
+    qi = a.query_start ? row - a.query_start[item] : 0;
+    ql = a.max_query_len;
+    items = a.num_seqs;
+    if (qi >= ql) return;  // past the rows a sequence may bring: not computed, as in the partition kernel
+  }
+  const int p0 = a.tile_prefix[item], p1 = a.tile_prefix[item + 1], total = a.tile_prefix[items];
   float* dst = a.out + ((int64_t)row * a.num_q_heads + h) * D + (lane_ok ? lane : 0) * kDpl;
   if (p1 <= p0) {
     if (lane_ok)
@@ -699,7 +708,7 @@ __global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs
   const int64_t first = base + (p0 != c0 * C ? 1 : 0);
   const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.ws_ml);
   const float* __restrict__ o = a.ws_o + (lane_ok ? lane : 0) * kDpl;
-  auto slot = [&](int k) { return k == 0 ? first : base + 2 * (int64_t)k; };
+  auto slot = [&](int k) { return (k == 0 ? first : base + 2 * (int64_t)k) * ql + qi; };
 
   float M = -INFINITY;
   for (int k = lane; k < np; k += kWave) M = fmaxf(M, ml[slot(k)].x);

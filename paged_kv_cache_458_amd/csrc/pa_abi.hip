@@ -103,11 +103,10 @@ int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa) {
   return max_context_len <= part ? 0 : part;
 }
 
-// num_tokens query rows (num_seqs in decode), at most max_query_len per sequence (1 in decode). `decode`: the
-// decode entry points, where row s is sequence s (no query_start).
+// num_tokens query rows (num_seqs in decode), at most max_query_len per sequence (1 in decode).
 Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
-               int32_t partition_size, bool decode) {
+               int32_t partition_size) {
   Plan p;
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 1 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
@@ -144,11 +143,12 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     return p;
   }
   const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * p.col_groups : (int64_t)num_tokens * num_q_heads;
-  // The balanced split needs rows one workgroup's LDS holds and tile counts that fit 32 bits; on the
-  // matrix-core kernel also one query row per sequence and one column group.
-  const bool balanced_ok = num_tokens <= pa::kMaxBalancedRows &&
-                           (int64_t)num_tokens * (max_context_len > 0 ? max_context_len : 1) <= (int64_t)1 << 30 &&
-                           (!gqa || (decode && p.col_groups == 1));
+  // The balanced split needs rows (sequences, on the matrix-core kernel) one workgroup's LDS holds and tile
+  // counts that fit 32 bits; on the matrix-core kernel also one column group.
+  const int64_t listed = gqa ? num_seqs : num_tokens;  // items of the tile list
+  const bool balanced_ok = num_tokens <= pa::kMaxBalancedRows && listed <= pa::kMaxBalancedRows &&
+                           listed * (max_context_len > 0 ? max_context_len : 1) <= (int64_t)1 << 30 &&
+                           (!gqa || p.col_groups == 1);
   if (partition_size == PA_PARTITION_BALANCED && !balanced_ok) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
@@ -166,7 +166,12 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
       gqa && part > 0 &&
       rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part) - 1) /
               ((int64_t)part * gqa_parts_per_wave(part))) > pa::kResidentWaves;
-  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round))) {
+  // Several new tokens per sequence on the matrix cores: a single pass that fills a round of resident waves
+  // leaves them unequal (each reads its sequence's whole context); equal runs gained 1-8% there (7B-shaped
+  // batches of 2, 4 and 8 rows per sequence, bf16 and E4M3).
+  const bool uneven_pass = gqa && max_query_len > 1 && partition_size == -1 && balanced_ok &&
+                           (part == 0 || part >= whole) && rows >= pa::kResidentWaves;
+  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round)) || uneven_pass) {
     p.balanced = true;
     p.split = true;
     p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads)
@@ -174,10 +179,12 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
                                          pa::valu_heads_per_wave(kv_dtype, head_dim, num_q_heads / num_kv_heads));
     p.partition = 0;
     p.max_partitions = 1;
-    const size_t o_bytes = pa::balanced_o_elems(num_q_heads, p.chunks, head_dim) * sizeof(float);
+    const int64_t ql = gqa ? max_query_len : 1;  // partial slots per (head, run, side)
+    const size_t o_bytes = pa::balanced_o_elems(num_q_heads, p.chunks, head_dim, ql) * sizeof(float);
     p.ws_ml_offset = round_up(o_bytes, 256);
-    p.ws_prefix_offset = round_up(p.ws_ml_offset + pa::balanced_ml_elems(num_q_heads, p.chunks) * sizeof(float), 256);
-    p.ws_bytes = p.ws_prefix_offset + ((size_t)num_tokens + 1) * sizeof(int32_t);
+    p.ws_prefix_offset =
+        round_up(p.ws_ml_offset + pa::balanced_ml_elems(num_q_heads, p.chunks, ql) * sizeof(float), 256);
+    p.ws_bytes = p.ws_prefix_offset + ((size_t)listed + 1) * sizeof(int32_t);
     return p;
   }
   if (part == 0 || part >= whole) {
@@ -228,7 +235,7 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t kv_dtype, int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, kv_dtype, partition_size, true);
+                           max_context_len, kv_dtype, partition_size);
   if (p.status != PA_OK) return p.status;
   return p.balanced ? PA_PARTITION_BALANCED : p.split ? p.partition : 0;
 }
@@ -237,7 +244,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
                                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                        int32_t kv_dtype, int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, kv_dtype, partition_size, true);
+                           max_context_len, kv_dtype, partition_size);
   return p.status == PA_OK ? p.ws_bytes : 0;
 }
 
@@ -246,7 +253,7 @@ int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query
                                              int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
                                              int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                           block_size, max_context_len, kv_dtype, partition_size, false);
+                           block_size, max_context_len, kv_dtype, partition_size);
   if (p.status != PA_OK) return p.status;
   return p.balanced ? PA_PARTITION_BALANCED : p.split ? p.partition : 0;
 }
@@ -256,7 +263,7 @@ size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query
                                              int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
                                              int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                           block_size, max_context_len, kv_dtype, partition_size, false);
+                           block_size, max_context_len, kv_dtype, partition_size);
   return p.status == PA_OK ? p.ws_bytes : 0;
 }
 
@@ -285,7 +292,7 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
               int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   const Plan plan = make_plan(num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                              block_size, max_context_len, kv_dtype, partition_size, query_start == nullptr);
+                              block_size, max_context_len, kv_dtype, partition_size);
   if (plan.status != PA_OK) return plan.status;
   const bool pair_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) || (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
@@ -335,6 +342,7 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   a.chunks = plan.chunks;
   a.tile_prefix =
       plan.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_prefix_offset) : nullptr;
+  a.seq_prefix = plan.balanced && plan.mfma ? 1 : 0;  // the matrix-core tile list is one of sequences
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.balanced) {

@@ -30,7 +30,8 @@ struct DecodeArgs {
   int32_t max_query_len;       // query rows per sequence at most (1 without query_start)
   int32_t col_groups;          // matrix-core kernel: groups of 16 (query row, head) columns per KV head
   int32_t chunks;              // balanced split: runs of tiles per query head (0: partitions as above)
-  int32_t* tile_prefix;        // balanced split: [T + 1] tiles of the rows before each row (workspace)
+  int32_t* tile_prefix;        // balanced split: tiles of the rows before each row, [T + 1] (workspace) ...
+  int32_t seq_prefix;          // ... or, when 1 (matrix-core kernel), of the sequences before each, [B + 1]
 };
 
 // The sequence that owns query row t: the last s with query_start[s] <= t (a scalar binary search; empty
@@ -77,14 +78,16 @@ int valu_heads_per_wave(int kv_dtype, int head_dim, int group);
 int32_t balanced_chunks(int32_t num_q_heads, int32_t heads_per_wave);  // runs per head: the grid fills kResidentWaves
 hipError_t launch_decode_valu_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
 hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream);
-// Balanced split of the matrix-core kernel (one query row per sequence, one column group): the 32-token tiles
-// of all sequences cut into `chunks` equal runs, one workgroup of up to 8 KV heads each; its partials take the
-// single-head balanced split's layout and launch_balanced_reduce merges them.
+// Balanced split of the matrix-core kernel (one column group): the 32-token tiles of all sequences cut into
+// `chunks` equal runs, one workgroup of up to 8 KV heads each; its partials take the single-head balanced
+// split's layout with a further index, the query row within its sequence (max_query_len of them), and
+// launch_balanced_reduce merges them.
 int32_t gqa_balanced_chunks(int32_t num_kv_heads);  // runs: the grid fills kResidentWaves
 hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream);
-// workspace of a balanced launch: partials [Hq][chunks][2][D] fp32, then (m, l) [Hq][chunks][2][2]
-inline size_t balanced_o_elems(int64_t Hq, int64_t chunks, int64_t D) { return Hq * chunks * 2 * D; }
-inline size_t balanced_ml_elems(int64_t Hq, int64_t chunks) { return Hq * chunks * 2 * 2; }
+// workspace of a balanced launch: partials [Hq][chunks][2][QL][D] fp32, then (m, l) [Hq][chunks][2][QL][2];
+// QL = 1 but on the matrix-core kernel, where it is the most query rows of a sequence
+inline size_t balanced_o_elems(int64_t Hq, int64_t chunks, int64_t D, int64_t QL = 1) { return Hq * chunks * 2 * QL * D; }
+inline size_t balanced_ml_elems(int64_t Hq, int64_t chunks, int64_t QL = 1) { return Hq * chunks * 2 * QL * 2; }
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int64_t row_bytes,

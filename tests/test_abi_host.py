@@ -200,16 +200,32 @@ def test_workspace_and_partition_plan():
 
 
 def test_grouped_query_default_counts_waves_per_span():
-    # the partition rule, seen where the balanced split does not apply (several new tokens per sequence, here
-    # with 2 rows x 4 heads = 8 columns per KV head): 512-token partitions go two to a grouped-query wave, so
-    # where 1024 leaves fewer than 2048 waves, 512 would leave the same number and the default goes on to 256
+    # the partition rule, seen where the balanced split does not apply (8 new tokens per sequence x 4 heads = 32
+    # columns per KV head: two column groups, so 16 waves per sequence): 512-token partitions go two to a
+    # grouped-query wave, so where 1024 leaves fewer than 2048 waves, 512 would leave the same number and the
+    # default goes on to 256
     def multi(B, *args):
-        return pa.multi_partition_size_for(B, 2 * B, 2, *args)
-    assert multi(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
-    assert multi(16, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 128
-    # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head) pairs run single pass
-    assert multi(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
-    assert multi(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+        return pa.multi_partition_size_for(B, 8 * B, 8, *args)
+    assert multi(32, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
+    assert multi(8, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 128
+    # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head, group) waves run single pass
+    assert multi(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
+    assert multi(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+    assert pa.load_library().paged_attention_multi_partition_size(
+        32, 256, 8, 32, 8, 128, 16, 2048, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == PA_ERR_UNSUPPORTED
+
+
+def test_several_tokens_per_sequence_take_the_balanced_split_where_measured():
+    B = pa.PA_PARTITION_BALANCED
+    # one column group: beyond one round of partitions, as in decode
+    assert pa.multi_partition_size_for(64, 128, 2, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == B
+    # 64 sequences x 32 heads x 4 rows (MHA): a single pass of 2048 unequal waves -> balanced
+    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == B
+    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_FP8_E4M3, -1) == B
+    # 70B shape, 2 rows: one round of partitions keeps them (partitions measured faster there)
+    assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
+    # decode keeps its single pass where it fills a round
+    assert pa.partition_size_for(256, 32, 8, 128, 16, 1024, pa.PA_BF16, -1) == 0
 
 
 def test_grouped_query_decode_default_takes_the_balanced_split_beyond_one_round():
@@ -232,12 +248,13 @@ def balanced_ws(T, Hq, D, hpw=1):
     return o + ml + (T + 1) * 4
 
 
-def gqa_balanced_ws(T, Hq, Hkv, D):
+def gqa_balanced_ws(B, Hq, Hkv, D, ql=1):
+    # B sequences (the tile list's items), ql partial slots per (head, run, side): the most rows of a sequence
     w = 8 if Hkv >= 8 else 4 if Hkv >= 4 else 2 if Hkv >= 2 else 1
     runs = max(1, 2048 // ((Hkv + w - 1) // w * w))
-    o = (Hq * runs * 2 * D * 4 + 255) // 256 * 256
-    ml = (Hq * runs * 2 * 2 * 4 + 255) // 256 * 256
-    return o + ml + (T + 1) * 4
+    o = (Hq * runs * 2 * ql * D * 4 + 255) // 256 * 256
+    ml = (Hq * runs * 2 * ql * 2 * 4 + 255) // 256 * 256
+    return o + ml + (B + 1) * 4
 
 
 def test_balanced_split_plan():
@@ -275,8 +292,12 @@ def test_balanced_split_plan():
                  (2049, 64, 8, 128, 256, 4096, pa.PA_BF16), (64, 64, 2, 128, 16, 2048, pa.PA_BF16)):
         assert lib.paged_attention_partition_size(*args, B) == PA_ERR_UNSUPPORTED
         assert lib.paged_attention_workspace_bytes(*args, B) == 0
-    # several new tokens per sequence on the matrix cores: partitions only
-    assert lib.paged_attention_multi_partition_size(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16,
+    # several new tokens per sequence on the matrix cores: one column group takes it, with partial slots for
+    # every row of a sequence; more columns are refused
+    assert lib.paged_attention_multi_partition_size(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == B
+    assert lib.paged_attention_multi_workspace_bytes(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == \
+        gqa_balanced_ws(64, 64, 8, 128, ql=2)
+    assert lib.paged_attention_multi_partition_size(64, 192, 3, 64, 8, 128, 256, 4096, pa.PA_BF16,
                                                     B) == PA_ERR_UNSUPPORTED
     assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
     # partition sizes between the balanced code and 16 are not multiples of 16

@@ -415,9 +415,13 @@ def test_gqa_balanced_split_edge_cases():
     assert_attention_close(gpu[[0, 4]], ref[[0, 4]], "bf16", "balanced")
     z = decode(st, t, tables, pa.PA_PARTITION_BALANCED, context_lens=np.zeros(5, np.int32))
     assert (z == 0).all()
-    # several new tokens per sequence keep the partition kernel: the balanced split is refused there
-    assert pa.load_library().paged_attention_multi_partition_size(
-        5, 10, 2, 32, 8, 128, 16, 4096, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == -4  # PA_ERR_UNSUPPORTED
+    # several new tokens per sequence take it while grouped heads x rows fill one column group of 16, and are
+    # refused beyond that
+    lib = pa.load_library()
+    assert lib.paged_attention_multi_partition_size(
+        5, 20, 4, 32, 8, 128, 16, 4096, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == pa.PA_PARTITION_BALANCED
+    assert lib.paged_attention_multi_partition_size(
+        5, 40, 8, 32, 8, 128, 16, 4096, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == -4  # PA_ERR_UNSUPPORTED
 
 
 # --------------------------------------------------------------------------------------------------------
