@@ -684,12 +684,14 @@ __global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs
   const bool lane_ok = lane < kActive;
   const int h = blockIdx.x;
   const int row = blockIdx.y;
-  int item = row, qi = 0, ql = 1, items = a.num_tokens;
-  if (a.seq_prefix) {
+  // sizes taken as values (a select between two fields of the argument block went through scratch memory)
+  const bool by_seq = a.seq_prefix != 0;
+  const int items = __builtin_amdgcn_readfirstlane(by_seq ? a.num_seqs : a.num_tokens);
+  const int ql = by_seq ? __builtin_amdgcn_readfirstlane(a.max_query_len) : 1;
+  int item = row, qi = 0;
+  if (by_seq) {
     item = seq_of_row(a, row);
     qi = a.query_start ? row - a.query_start[item] : 0;
-    ql = a.max_query_len;
-    items = a.num_seqs;
     if (qi >= ql) return;  // past the rows a sequence may bring: not computed, as in the partition kernel
   }
   const int p0 = a.tile_prefix[item], p1 = a.tile_prefix[item + 1], total = a.tile_prefix[items];
