@@ -34,9 +34,30 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library; always rebuilds."""
+    """Compile every source to an object (in parallel, under _build/), then link one shared library; always
+    rebuilds."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(obj_dir, os.path.basename(s) + ".o") for s in srcs]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(so):
+        src, obj = so
+        cmd = [HIPCC, *compile_flags, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return subprocess.run(cmd).returncode
+
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(jobs) as ex:
+        codes = list(ex.map(compile_one, zip(srcs, objs)))
+    if any(codes):
+        raise RuntimeError(f"hipcc failed for {[s for s, c in zip(srcs, codes) if c]}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
