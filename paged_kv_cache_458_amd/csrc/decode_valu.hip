@@ -145,6 +145,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   const int t0 = part * a.partition;
   if (part > 0 && t0 >= L) return;  // this sequence has fewer partitions
   const int E = row_extent(a, s, row, L);
+  if (E < 0) return;  // not one of the sequence's query rows: left unwritten
   const int t1 = max(t0, min(min(L, t0 + a.partition), E));
   const int g = h / a.group;
   const int r = lane / S::kRowLanes;  // row group
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   // (no early exit, which would let the compiler sink the loads above behind the length) and not stored
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   const int span = a.partition * a.parts_per_wave;  // positions behind one partial: a wave's span
-  const bool merge = L > span;
+  // a row that is not one of its sequence's query rows was not computed and is not written
+  const bool merge = L > span && (!a.query_start || row - a.query_start[s] < rows_of_seq(a, s));
   const int np = merge ? (L + span - 1) / span : 1;
 
   float M = lane < np ? v0.x : -INFINITY;
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     int64_t q0 = s, ql = 1;
     if constexpr (kMulti) {
       q0 = a.query_start[s];
-      ql = (int64_t)a.query_start[s + 1] - q0;
+      ql = rows_of_seq(a, s);
     }
     const int64_t jb = q0 < 0 ? -q0 : 0, je = min(ql, (int64_t)T - q0);  // rows inside [0, T) only
     for (int64_t j = jb; j < je; ++j) {
@@ -689,10 +691,14 @@ __global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs
   const int items = __builtin_amdgcn_readfirstlane(by_seq ? a.num_seqs : a.num_tokens);
   const int ql = by_seq ? __builtin_amdgcn_readfirstlane(a.max_query_len) : 1;
   int item = row, qi = 0;
-  if (by_seq) {
-    item = seq_of_row(a, row);
-    qi = a.query_start ? row - a.query_start[item] : 0;
-    if (qi >= ql) return;  // past the rows a sequence may bring: not computed, as in the partition kernel
+  if (a.query_start) {
+    const int s = seq_of_row(a, row);
+    const int q0 = a.query_start[s];
+    if (row - q0 >= rows_of_seq(a, s)) return;  // not one of the sequence's query rows: left unwritten
+    if (by_seq) {
+      item = s;
+      qi = row - q0;
+    }
   }
   const int p0 = a.tile_prefix[item], p1 = a.tile_prefix[item + 1], total = a.tile_prefix[items];
   float* dst = a.out + ((int64_t)row * a.num_q_heads + h) * D + (lane_ok ? lane : 0) * kDpl;

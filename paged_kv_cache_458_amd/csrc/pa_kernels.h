@@ -47,13 +47,22 @@ __device__ __forceinline__ int seq_of_row(const DecodeArgs& a, int t) {
   return lo;
 }
 
+// Query rows of sequence s as every kernel takes them: query_start[s + 1] - query_start[s], clamped to
+// [0, max_query_len] (a larger difference breaks the caller's contract; its rows past max_query_len are left
+// unwritten by every kernel alike).
+__device__ __forceinline__ int rows_of_seq(const DecodeArgs& a, int s) {
+  return min(max(a.query_start[s + 1] - a.query_start[s], 0), a.max_query_len);
+}
+
 // Positions that query row t of sequence s (length L) attends over: all L for decode; for row j of the
-// sequence's QL rows, its causal prefix of L - QL + j + 1 positions (none when that is not positive).
+// sequence's QL rows (rows_of_seq), its causal prefix of L - QL + j + 1 positions (none when that is not
+// positive); -1 for a row that is not among the sequence's QL rows, which no kernel computes or writes.
 __device__ __forceinline__ int row_extent(const DecodeArgs& a, int s, int t, int L) {
   if (!a.query_start) return L;
-  const int q0 = a.query_start[s];
-  const int ql = a.query_start[s + 1] - q0;
-  return max(0, min(L, L - ql + (t - q0) + 1));
+  const int ql = rows_of_seq(a, s);
+  const int j = t - a.query_start[s];
+  if (j >= ql) return -1;
+  return max(0, min(L, L - ql + j + 1));
 }
 
 // Workspace layout for a split launch: partial outputs first, then the (max, sum) pairs.

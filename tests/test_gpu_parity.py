@@ -457,12 +457,11 @@ def test_very_long_contexts(hq, hkv, dt):
     st = custom_structure("long", 451, [131072, 70001, 5], hq, hkv, 128, 16, dt, pool_factor=1.02)
     t = materialize(st, DEV, chunk_blocks=4096)
     h = {k: to_host(v) for k, v in t.items()}
-    rows = np.array([[0, 0], [0, hq - 1], [1, hq // 2], [2, 1]], np.int32)
-    ref = oracle_decode(st, h, st.block_tables_pre, rows=rows)
+    ref = oracle_decode(st, h, st.block_tables_pre)  # every (sequence, head) row
     for part in (-1, 4096):
         gpu = decode(st, t, st.block_tables_pre, part)
-        assert np.isfinite(gpu).all()
-        assert_attention_close(gpu[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], dt, f"partition {part}")
+        err = assert_attention_close(gpu, ref, dt, f"partition {part}")
+        sys.__stderr__.write(f"[long {hq}/{hkv} {dt} partition {part}] max abs err {err:.3e}\n")
 
 
 def test_grid_limit_of_sequences():
