@@ -8,9 +8,11 @@ seeded synthetic tensors already resident in HBM; consecutive steps read differe
 that no step can be served from the 256 MB last-level cache left warm by the previous one.
 
 Prints one JSON line: whole-step achieved GB/s (algorithmic bytes / step time), decode queries/s, a roofline
-entry for the attention call (HIP events on the stream it runs on) and the CPU oracle's rate on the host cores.
+entry for the attention call (HIP events on the stream it runs on; the bytes HBM must deliver, a block shared by
+several sequences counted once) and the CPU oracle's rate on the host cores. The default (headline) run also
+measures every other synthetic workload, each in a fresh child process, and reports them under "configs".
 
-    python bench.py [--workload llama2_7b] [--steps 100] [--warmup 10]
+    python bench.py [--workload llama2_7b] [--steps 100] [--warmup 10] [--no-configs]
     python bench.py --workload configs    (one line per synthetic decode workload, each in a fresh process)
     python bench.py --workload decode_loop --steps 100 --warmup 50   (continuous batching, block manager)
 """
@@ -136,6 +138,24 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
     return path
 
 
+def unique_slots(tables, lens, bs: int) -> int:
+    """Distinct pool slots that one decode call reads: a physical block referenced by several sequences counts
+    once, with the most rows any of them uses in it."""
+    import numpy as np
+
+    lens = np.asarray(lens, dtype=np.int64)
+    nblk = (lens + bs - 1) // bs
+    seq = np.repeat(np.arange(len(lens)), nblk)
+    j = np.arange(int(nblk.sum())) - np.repeat(np.cumsum(nblk) - nblk, nblk)  # logical block within its sequence
+    ids = np.asarray(tables)[seq, j].astype(np.int64)
+    rows = np.minimum(bs, lens[seq] - j * bs)
+    most = {}
+    for b, r in zip(ids.tolist(), rows.tolist()):
+        if r > most.get(b, 0):
+            most[b] = r
+    return int(sum(most.values()))
+
+
 def run_decode_loop(args) -> int:
     """Continuous-batching decode over a request stream: the block manager places every token, the kernels
     move and read them. Llama-2-7B-shaped attention (32 heads x 128, bf16, 16-token blocks), up to 256
@@ -212,11 +232,14 @@ def run_decode_loop(args) -> int:
         step()
         stats.append(loop.stats())
     row = hkv * d * 2
-    attn_s, attn_bytes, stepped = 0.0, 0, 0
-    for (e0, e1), lens in events:
+    attn_s, attn_bytes, unique_bytes, stepped = 0.0, 0, 0, 0
+    for (e0, e1), lens, tables in events:
         attn_s += e0.elapsed_time(e1) * 1e-3
-        nb = int(((lens.astype(np.int64) + bs - 1) // bs).sum())
-        attn_bytes += int(lens.astype(np.int64).sum()) * row * 2 + len(lens) * hq * d * (2 + 4) + nb * 4 + 4 * len(lens)
+        lens = lens.astype(np.int64)
+        nb = int(((lens + bs - 1) // bs).sum())
+        other = len(lens) * hq * d * (2 + 4) + nb * 4 + 4 * len(lens)
+        attn_bytes += int(lens.sum()) * row * 2 + other
+        unique_bytes += unique_slots(tables, lens, bs) * row * 2 + other
         stepped += len(lens)
     frag = float(np.mean([s["internal_fragmentation"] for s in stats]))
     contiguous_slots = float(np.mean([s["sequences"] for s in stats])) * max_len
@@ -239,6 +262,7 @@ def run_decode_loop(args) -> int:
         "decode_queries_per_s": round(stepped / wall, 1),
         "attention": {"us_mean": round(attn_s / len(events) * 1e6, 2),
                       "gb_per_s": round(attn_bytes / attn_s / 1e9, 1),
+                      "gb_per_s_unique": round(unique_bytes / attn_s / 1e9, 1),
                       "share_of_step": round(attn_s / wall, 3)},
         "decode_loop": {
             "admitted": admitted, "finished": finished, "deferred_for_memory": deferred,
@@ -249,9 +273,11 @@ def run_decode_loop(args) -> int:
             "shared_blocks_mean": round(float(np.mean([s["shared_blocks"] for s in stats])), 1),
             "cow_copies": stats[-1]["cow_copies"],
         },
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode within the loop", "achieved":
-                     round(attn_bytes / attn_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(attn_bytes / attn_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+        # unique bytes: blocks shared by several sequences (prompt prefixes, forks) count once per call
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode within the loop",
+                     "achieved": round(unique_bytes / attn_s / 1e9, 1),
+                     "achieved_logical": round(attn_bytes / attn_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(unique_bytes / attn_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
@@ -332,17 +358,70 @@ def run_swap(args) -> int:
     return 0
 
 
+HEADLINE = "llama2_7b"
+
+
+def config_summary(rec: dict) -> dict:
+    """The per-workload figures the headline line carries for each synthetic workload."""
+    att, roof = rec["attention"], rec["roofline"]
+    traffic = roof.get("traffic")
+    out = {
+        "attention_us": {"mean": att["us_mean"], "median": att["us_median"], "min": att["us_min"]},
+        "gb_per_s": att["gb_per_s"],
+        "gb_per_s_unique": att["gb_per_s_unique"],
+        "frac": roof["frac"],
+        "traffic_over_unique": round(traffic / att["unique_bytes_per_call"], 4) if traffic else None,
+        "traffic_over_logical": round(traffic / att["bytes_per_call"], 4) if traffic else None,
+        "decode_queries_per_s": att["queries_per_s"],
+        "step_ms": rec["ms_per_step"],
+        "bytes_per_call": att["bytes_per_call"],
+        "unique_bytes_per_call": att["unique_bytes_per_call"],
+        "kv_cache_dtype": rec["config"]["kv_cache_dtype"],
+        "partition_size": rec["config"]["partition_size"],
+        "cpu_baseline": rec["cpu_baseline"],
+    }
+    return out
+
+
+def run_config_children(args) -> dict:
+    """Every synthetic workload but the headline, each measured by this script in a fresh process of its own (run
+    before this process touches the GPU), summarised per workload."""
+    import subprocess
+
+    from workloads import CONFIG_NAMES
+
+    res = {}
+    for name in CONFIG_NAMES:
+        if name == HEADLINE:
+            continue
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--replicas", str(args.replicas), "--cpu-seconds",
+               str(args.config_cpu_seconds), "--no-configs"]
+        log(f"configs: {name}")
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            raise RuntimeError(f"bench.py --workload {name} failed (exit {r.returncode}); no further GPU runs")
+        res[name] = config_summary(json.loads(lines[-1]))
+        log(f"configs: {name}: attention {res[name]['attention_us']['mean']} us, frac {res[name]['frac']}")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--partition-size", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--query-len", type=int, default=1,
                     help="new tokens per sequence (> 1: a verification batch through paged_attention_decode_multi)")
     ap.add_argument("--replicas", type=int, default=2, help="pool replicas cycled by consecutive steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle timing budget (0 = skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="headline run only: skip measuring the other synthetic workloads in child processes")
+    ap.add_argument("--config-cpu-seconds", type=float, default=2.0,
+                    help="CPU oracle budget of each other workload's child run")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) of this benchmark "
                          "into profiles/traffic_<workload>.md and exit")
@@ -375,6 +454,12 @@ def main() -> int:
             log(f"configs: {name}")
             rc = rc or subprocess.run(cmd).returncode
         return rc
+
+    # the headline run also reports every other synthetic workload, each measured in a fresh child process
+    # before this one touches the GPU
+    configs = None
+    if args.workload == HEADLINE and args.query_len == 1 and not args.no_configs:
+        configs = run_config_children(args)
 
     import numpy as np
     import torch
@@ -508,6 +593,9 @@ def main() -> int:
     step_bytes = ab["total"] + cache_write_bytes + copy_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     attn_gbs = ab["total"] / (attn_avg_ms * 1e-3) / 1e9
+    # bytes HBM must deliver: a block that several sequences share (a common prefix) counts once per call
+    unique_bytes = ab["kv_unique"] + ab["query"] + ab["out"] + ab["tables"]
+    attn_gbs_unique = unique_bytes / (attn_avg_ms * 1e-3) / 1e9
     traffic = load_traffic(label)
 
     rec = {
@@ -548,8 +636,10 @@ def main() -> int:
             "us_median": round(float(np.median(attn_ms)) * 1e3, 2),
             "us_min": round(float(np.min(attn_ms)) * 1e3, 2),
             "gb_per_s": round(attn_gbs, 1),
+            "gb_per_s_unique": round(attn_gbs_unique, 1),
             "queries_per_s": round(T / (attn_avg_ms * 1e-3), 1),
             "bytes_per_call": ab["total"],
+            "unique_bytes_per_call": unique_bytes,
             "kv_unique_bytes": ab["kv_unique"],
         },
         "step_bytes": step_bytes,
@@ -559,10 +649,12 @@ def main() -> int:
             "bound": "hbm",
             "kernel": ("paged_attention_decode" if Q == 1 else "paged_attention_decode_multi") +
                       " (partition or balanced-split kernel + log-sum-exp reduce when split)",
-            "achieved": round(attn_gbs, 1),
+            # unique bytes (shared blocks once); the logical count of the metric's byte formula beside it
+            "achieved": round(attn_gbs_unique, 1),
+            "achieved_logical": round(attn_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+            "frac": round(attn_gbs_unique / PEAK_HBM_GBS, 4),
             "traffic": traffic,
         },
         "cpu_baseline": None,
@@ -582,7 +674,7 @@ def main() -> int:
             else:
                 host[name] = tt.numpy()
         lib = oracle.load()
-        reps, t0 = 0, time.perf_counter()
+        reps, t0, last = 0, time.perf_counter(), 0.0
         while True:
             if Q == 1:
                 oracle.decode(host["query"], host["key_cache"], host["value_cache"], st.block_tables,
@@ -593,18 +685,25 @@ def main() -> int:
                                     lib=lib)
             reps += 1
             el = time.perf_counter() - t0
-            log(f"cpu oracle call {reps}: {el:.1f} s")
+            if el - last >= 5.0:
+                log(f"cpu oracle: {reps} calls in {el:.1f} s")
+                last = el
             if el >= args.cpu_seconds or reps >= 1000:
                 break
+        log(f"cpu oracle: {reps} calls in {el:.1f} s")
         rec["cpu_baseline"] = {
             "value": round(T * reps / el, 2),
             "unit": "decode queries/s",
             "gb_per_s": round(ab["total"] * reps / el / 1e9, 3),
             "cores": oracle.num_threads(lib),
+            "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"the whole {label} batch ({T} query rows x {Hq} heads, fp64 C oracle with OpenMP), "
                       f"{reps} call(s) in {el:.1f} s",
         }
+    if configs is not None:
+        rec["configs"] = {HEADLINE: config_summary(rec), **configs}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -225,7 +225,7 @@ class DecodeLoop:
                                workspace=self._ws if need else None)
         if ev is not None:
             ev[1].record(t.cuda.current_stream(self.dev))
-            self.attention_events.append((ev, lens.copy()))
+            self.attention_events.append((ev, lens.copy(), tables.copy()))
         self.last_query = query
         return ids, out, pairs
 
