@@ -51,6 +51,10 @@ extern "C" {
 #define PA_ERR_HIP (-6)         /* a HIP launch or runtime call failed */
 #define PA_ERR_ALIGN (-7)       /* a pointer is not 16-byte aligned */
 #define PA_ERR_POINTER (-10)    /* swap_blocks: a pool or the pairs are not memory this device can access */
+#define PA_ERR_SCRATCH (-11)    /* paged_attention_decode_noalloc: more scratch than PA_STATIC_SCRATCH_BYTES */
+
+/* bytes of the static device scratch of paged_attention_decode_noalloc (one copy per GPU, 32 MiB) */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* partition_size value that asks for the balanced split (see paged_attention_decode) */
 #define PA_PARTITION_BALANCED 1
@@ -152,6 +156,26 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
                                   int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
                                   int32_t kv_dtype, int32_t partition_size, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_scaled for callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, plan, kernels and
+ * results as paged_attention_decode_scaled (bit for bit), without the workspace arguments: the split-context
+ * partials go to a static device buffer of PA_STATIC_SCRATCH_BYTES inside the library, one per GPU, allocated
+ * when the library's device code is loaded and held until the process ends. The call allocates nothing.
+ *
+ * The buffer's device address is looked up once per GPU, on the first call with that GPU current. Calls whose
+ * plan needs more than PA_STATIC_SCRATCH_BYTES (paged_attention_workspace_bytes for the same sizes) return
+ * PA_ERR_SCRATCH and launch nothing. Every call on one GPU shares that GPU's buffer: two calls that may run at
+ * the same time on one GPU (on different streams without ordering between them) race, and must be ordered by
+ * the caller. No call needs the buffer cleared: each writes the partials it reads.
+ */
+int paged_attention_decode_noalloc(float *out, const void *query, const void *key_cache, const void *value_cache,
+                                   const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                   float k_scale, float v_scale, int32_t block_size, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+                                   int32_t kv_dtype, int32_t partition_size, void *stream);
 
 /*
  * Attention of several new tokens per sequence over the paged cache (speculative verification, which page 1

@@ -23,6 +23,8 @@ STREAM_SINK_FLOATS = 8192
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_OK = 0
 PA_PARTITION_BALANCED = 1  # partition_size that asks for the balanced split (equal runs of tiles per wave)
+PA_ERR_SCRATCH = -11
+PA_STATIC_SCRATCH_BYTES = 32 << 20  # the static device scratch of paged_attention_decode_noalloc
 ABI_VERSION = 1
 
 _lib = None
@@ -56,6 +58,9 @@ def load_library(path: str | None = None):
     lib.paged_attention_decode_scaled.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i64, i32,
                                                   i32, i32, i32, i32, P, sz, P]
     lib.paged_attention_decode_scaled.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i64,
+                                                   i32, i32, i32, i32, i32, P]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.paged_attention_decode_multi.argtypes = [P, P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i32,
                                                  i32, i64, i32, i32, i32, i32, i32, P, sz, P]
     lib.paged_attention_decode_multi.restype = ctypes.c_int
@@ -191,6 +196,36 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     else:
         st = lib.paged_attention_decode(*ptrs, float(scale), *tail)
         _check("paged_attention_decode", st)
+    return out
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                                   *, max_context_len: int | None = None, partition_size: int = -1, stream=None,
+                                   k_scale: float = 1.0, v_scale: float = 1.0):
+    """paged_attention_decode without a workspace: the library keeps the split-context partials in a static
+    device buffer of PA_STATIC_SCRATCH_BYTES per GPU and allocates nothing (for callers that may not allocate).
+    Calls that overlap on one GPU race on that buffer. Arguments as in paged_attention_decode."""
+    torch = _torch()
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+    if out.dtype != torch.float32:
+        raise TypeError("out must be float32")
+    _int32(block_tables, "block_tables")
+    _int32(context_lens, "context_lens")
+    B, Hq, D = query.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    if D2 != D or value_cache.shape != key_cache.shape or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("shape mismatch between out, query and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache must have the same dtype")
+    MB = block_tables.shape[1]
+    mcl = MB * bs if max_context_len is None else int(max_context_len)
+    st = load_library().paged_attention_decode_noalloc(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), float(k_scale), float(v_scale), bs, B, Hq, Hkv, D, NB, MB, mcl,
+        _dtype_code(query), _dtype_code(key_cache), int(partition_size), _stream(dev, stream))
+    _check("paged_attention_decode_noalloc", st)
     return out
 
 

@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/paged_attention.h"
 #include "pa_kernels.h"
 
@@ -210,6 +212,35 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   return p;
 }
 
+// Scratch of paged_attention_decode_noalloc: the split-context partials of a call that may not allocate. One copy
+// per GPU the library runs on, held until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: the device address of each GPU's copy comes from hipGetSymbolAddress with that GPU
+// current, and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[PA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch copy, looked up once per device (nullptr on failure).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  return g_scratch_addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +258,9 @@ const char* pa_strerror(int status) {
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP launch or runtime call failed";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case PA_ERR_POINTER: return "PA_ERR_POINTER: memory the device cannot access (pageable host memory, another GPU)";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the call needs more split-context scratch than the library's static buffer "
+             "(PA_STATIC_SCRATCH_BYTES) holds; pass a workspace to paged_attention_decode_scaled instead";
     default: return "unknown status";
   }
 }
@@ -285,15 +319,18 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
 namespace {
 
 // Shared by the decode and multi-token entry points: query_start == nullptr means one query row per sequence.
+// With static_scratch the split-context partials go to this GPU's static scratch instead of `workspace`.
 int attention(float* out, const void* query, const void* key_cache, const void* value_cache,
               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start, float scale,
               float k_scale, float v_scale, int32_t block_size, int32_t num_seqs, int32_t num_tokens,
               int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
-              int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+              int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
+              bool static_scratch = false) {
   const Plan plan = make_plan(num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
                               block_size, max_context_len, kv_dtype, partition_size);
   if (plan.status != PA_OK) return plan.status;
+  if (static_scratch && plan.ws_bytes > PA_STATIC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
   const bool pair_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) || (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
   if (!pair_ok) return PA_ERR_DTYPE;
@@ -307,6 +344,11 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
       !aligned4(block_tables) || !aligned4(context_lens) || !aligned4(query_start))
     return PA_ERR_ALIGN;
   if (plan.split) {
+    if (static_scratch) {  // every argument is valid: the call will launch
+      workspace = scratch_of_current_device();
+      if (!workspace) return PA_ERR_HIP;
+      workspace_bytes = PA_STATIC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_ALIGN;
   }
@@ -372,6 +414,18 @@ int paged_attention_decode_scaled(float* out, const void* query, const void* key
                    block_size, num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks,
                    max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size, workspace,
                    workspace_bytes, stream);
+}
+
+int paged_attention_decode_noalloc(float* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                   float k_scale, float v_scale, int32_t block_size, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+                                   int32_t kv_dtype, int32_t partition_size, void* stream) {
+  return attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr, scale, k_scale, v_scale,
+                   block_size, num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                   max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size, nullptr, 0, stream,
+                   /*static_scratch=*/true);
 }
 
 int paged_attention_decode_multi(float* out, const void* query, const void* key_cache, const void* value_cache,

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
             "pa_abi_version", "pa_stream_read", "pa_stream_copy", "pa_bm_create", "pa_bm_append_slots",
             "paged_attention_decode_scaled", "reshape_and_cache_fp8", "paged_attention_decode_multi",
             "paged_attention_multi_workspace_bytes", "paged_attention_multi_partition_size",
-            "swap_blocks"} <= set(names)
+            "swap_blocks", "paged_attention_decode_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert lib.pa_abi_version() == pa.ABI_VERSION
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_names_every_status():
     for code in (0, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
-                 PA_ERR_ALIGN, -10):
+                 PA_ERR_ALIGN, -10, pa.PA_ERR_SCRATCH):
         assert pa.strerror(code) != "unknown status"
     assert pa.strerror(123) == "unknown status"
 
@@ -381,3 +381,41 @@ def test_stream_diagnostics_reject():
     assert lib.pa_stream_read(FAKE + 8, 1024, FAKE, None) == PA_ERR_ALIGN
     assert lib.pa_stream_copy(FAKE, FAKE, 0, None) == PA_ERR_SHAPE
     assert lib.pa_stream_copy(FAKE + 4, FAKE, 1024, None) == PA_ERR_ALIGN
+
+
+def noalloc_call(**over):
+    args = dict(out=FAKE, query=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE, context_lens=FAKE,
+                scale=0.1, k_scale=1.0, v_scale=1.0, block_size=16, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, num_blocks=100, max_blocks_per_seq=8, max_context_len=128, q_dtype=pa.PA_BF16,
+                kv_dtype=pa.PA_BF16, partition_size=32, stream=None)
+    args.update(over)
+    return pa.load_library().paged_attention_decode_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=100), PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=4), PA_ERR_SHAPE),
+    (dict(q_dtype=pa.PA_F32), PA_ERR_DTYPE),
+    (dict(v_scale=0.0), PA_ERR_SHAPE),
+    (dict(max_context_len=129), PA_ERR_SHAPE),
+    (dict(partition_size=24), PA_ERR_SHAPE),
+    (dict(out=None), PA_ERR_NULL),
+    (dict(query=FAKE + 8), PA_ERR_ALIGN),
+    # 256 sequences x 32 heads x 256 partitions of 16 tokens x 128 dims of fp32 partials: 1 GiB > 32 MiB
+    (dict(num_seqs=256, num_q_heads=32, num_kv_heads=32, max_blocks_per_seq=256, max_context_len=4096,
+          partition_size=16), pa.PA_ERR_SCRATCH),
+])
+def test_noalloc_decode_rejects_before_launch(over, status):
+    # every rejection comes before the static scratch is looked up (no device is touched here)
+    assert noalloc_call(**over) == status
+
+
+def test_noalloc_scratch_limit_matches_the_workspace_rule():
+    lib = pa.load_library()
+    # the largest plan that fits: the workspace size function gives the same bytes the no-alloc call needs
+    need = lib.paged_attention_workspace_bytes(256, 32, 32, 128, 16, 4096, pa.PA_BF16, 16)
+    assert need > pa.PA_STATIC_SCRATCH_BYTES
+    fits = lib.paged_attention_workspace_bytes(64, 64, 8, 128, 256, 4096, pa.PA_BF16, 512)
+    assert 0 < fits <= pa.PA_STATIC_SCRATCH_BYTES
+    assert "PA_STATIC_SCRATCH_BYTES" in pa.strerror(pa.PA_ERR_SCRATCH)
+    assert noalloc_call(num_seqs=0) == 0  # nothing to do: no-op
