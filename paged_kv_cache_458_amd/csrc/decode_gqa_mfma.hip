@@ -33,8 +33,8 @@
 // positions past the range are masked only in a tile that holds some; weights become bf16 pairs through
 // packed conversions.
 //
-// K/V of tile j+1 are loaded into a second register set while tile j is consumed; block ids come from scalar
-// loads of the block table (one per 16-token half, one per 8-token quarter with 8-slot blocks). Scores use the exp2 domain (scale * log2 e folded in).
+// A tile's loads land in one register set and are staged into LDS; the next tile's loads are then issued into the
+// same registers while the staged tile goes through the products. Block ids come from scalar loads of the block table (one per 16-token half, one per 8-token quarter with 8-slot blocks). Scores use the exp2 domain (scale * log2 e folded in).
 //
 // An FP8 (OCP E4M3) cache is read at one byte per element and staged into LDS as it is; its operands are
 // widened to bf16 after the LDS reads (every E4M3 value is exactly a bf16 value): K through 8-byte reads, V^T
@@ -198,13 +198,12 @@ __device__ __forceinline__ void gqa_issue(U4 (*kb)[NL], U4 (*vb)[NL], TablePtr t
   }
 }
 
-// One tile through the matrix cores: stage K and V into the wave's LDS slices (E4M3 widened to bf16; rows
-// past the range end were loaded as zeros), S^T = K Q^T, the online-softmax update of (m, l) in the exp2
-// domain with positions >= `lim` masked unless the whole tile is `full`, then O^T += V^T (P_hi + P_lo)^T.
+// Stage one tile's K and V from the load registers into the wave's LDS slices (rows past the range end were
+// loaded as zeros); this is where the wave waits for the tile's loads. Afterwards the registers are free for the
+// next tile's loads.
 template <int KV, int D, int NL>
-__device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* kslice, char* vslice, int wofs,
-                                            const char* kread, const char* rbase, const U4* qb, float scale_log2,
-                                            int t, bool full, int lim, int j, float& m, float& l, f32x4* o) {
+__device__ __forceinline__ void gqa_stage(const U4 (*kb)[NL], const U4 (*vb)[NL], char* kslice, char* vslice,
+                                          int wofs) {
   using S = GqaShape<KV, D>;
   static_assert(NL == S::kLoads, "register sets of the tile's shape");
   // the previous tile's reads come first
@@ -218,6 +217,15 @@ __device__ __forceinline__ void gqa_consume(U4 (*kb)[NL], U4 (*vb)[NL], char* ks
       *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
     }
   wave_lds_sync();
+}
+
+// One staged tile through the matrix cores (E4M3 widened to bf16 after the LDS reads): S^T = K Q^T, the
+// online-softmax update of (m, l) in the exp2 domain with positions >= `lim` masked unless the whole tile is
+// `full`, then O^T += V^T (P_hi + P_lo)^T.
+template <int KV, int D>
+__device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase, const U4* qb, float scale_log2,
+                                            int t, bool full, int lim, int j, float& m, float& l, f32x4* o) {
+  using S = GqaShape<KV, D>;
   f32x4 sc[2];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
@@ -378,9 +386,13 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   bool bad = false;
   const int ntiles = (u1 - u0 + kTileTok - 1) / kTileTok;
   const int last8 = ntiles > 0 ? ((u1 - 1) & ~(kTile / 2 - 1)) : u0;  // start of the last live 8-token group
-  U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
-  auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-    gqa_issue<KV, D>(kb, vb, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1, last8, a,
+  // One register set: a tile's loads land in it, are staged into LDS, and the next tile's loads are issued into
+  // it before the staged tile's products are computed -- about one tile of loads in flight per wave at all times.
+  // (Two register sets, two tiles in flight, were measured slower: more concurrent reads congest the memory
+  // system rather than feed it.)
+  U4 kR[2][kLoads], vR[2][kLoads];
+  auto issue = [&](int tile) {
+    gqa_issue<KV, D>(kR, vR, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1, last8, a,
                      row_bytes, kbase, vbase, off, bad);
   };
 
@@ -440,24 +452,16 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     }
   };
 
-  auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-    const int t = u0 + tile * kTileTok;
-    // no column masks a position of a tile below ufull
-    gqa_consume<KV, D>(kb, vb, kslice, vslice, wofs, kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull, lim,
-                       j, m, l, o);
-    if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
-  };
-
   if (ntiles > 0) {
-    issue(kA, vA, 0);
-    int tj = 0;
-    for (; tj + 2 <= ntiles; tj += 2) {
-      issue(kB, vB, tj + 1);
-      consume(kA, vA, tj);
-      issue(kA, vA, tj + 2);
-      consume(kB, vB, tj + 1);
+    issue(0);
+    for (int tj = 0; tj < ntiles; ++tj) {
+      gqa_stage<KV, D>(kR, vR, kslice, vslice, wofs);
+      issue(tj + 1);  // past the last tile every row is beyond the range: nothing is read
+      const int t = u0 + tj * kTileTok;
+      // no column masks a position of a tile below ufull
+      gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull, lim, j, m, l, o);
+      if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
     }
-    if (tj < ntiles) consume(kA, vA, tj);
   }
   if (cut < u1) {
     // merge the first partition's state into the second's: one partial per wave
@@ -480,12 +484,13 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
 // workgroups of 8 KV heads leaves some CUs without one and some XCDs with more bytes than others. Here the
 // 32-token tiles of all sequences, in sequence order, form one list cut into `chunks` equal runs; workgroup
 // (x, r) takes run r for KV heads Wx .. Wx + W - 1, and the host sizes the grid to one wave per wave slot of the
-// chip, so every wave streams the same number of tiles and every XCD the same bytes. A wave walks its run one
-// sequence segment at a time, with the partition kernel's load pipeline inside a segment: a sequence lying
-// wholly inside the run is written to `out`; one cut by run boundaries leaves, for each of its query rows qi, a
-// partial in slot [head][run][2][qi] -- side 0 for the sequence the run starts inside, side 1 for the one it
-// ends inside -- and balanced_reduce_kernel merges them. A sequence without query rows contributes no tiles.
-// Stores happen only between segments, after the pipeline has drained.
+// chip, so every wave streams the same number of tiles and every XCD the same bytes. A run crosses sequence
+// boundaries: the load pipeline runs straight through them (the first tile of the next sequence is in flight while
+// the last one of the current sequence goes through the products, and its query rows come in with it), so a wave
+// never drains its loads between sequences. When a sequence's last tile of the run is done, its rows are written:
+// a sequence lying wholly inside the run goes to `out`; one cut by run boundaries leaves, for each of its query
+// rows qi, a partial in slot [head][run][2][qi] -- side 0 for the sequence the run starts inside, side 1 for the
+// one it ends inside -- and balanced_reduce_kernel merges them. A sequence without query rows contributes no tiles.
 //
 // Every workgroup first derives the prefix of the sequences' tile counts in LDS; the first one also
 // publishes it for the merge.
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   const ConstI32* __restrict__ lens = as_constant(a.context_lens);
   for (int s = tid; s < T; s += NT) {
     const int L = min(max(lens[s], 0), a.max_context_len);
-    const int ql = a.query_start ? min(max(a.query_start[s + 1] - a.query_start[s], 0), a.max_query_len) : 1;
+    const int ql = a.query_start ? rows_of_seq(a, s) : 1;
     P[s + 1] = ql > 0 ? (L + kTileTok - 1) / kTileTok : 0;
   }
   __syncthreads();
@@ -551,79 +556,113 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
     if (__builtin_amdgcn_readfirstlane(P[mid + 1]) <= g0) lo = mid + 1;
     else hi = mid;
   }
-  int s = lo;
-  int pos = g0;  // list index of the segment's first tile
-  while (true) {
-    const int p0 = __builtin_amdgcn_readfirstlane(P[s]);
-    const int p1 = __builtin_amdgcn_readfirstlane(P[s + 1]);
-    const int L = min(max(lens[s], 0), a.max_context_len);
-    const int end = min(p1, g1);
-    const int u0 = (pos - p0) * kTileTok;          // the segment: positions [u0, u1) of sequence s
-    const int u1 = min(L, (end - p0) * kTileTok);
-    const int ntiles = end - pos;
-    const int last8 = (u1 - 1) & ~(kTile / 2 - 1);  // start of the last live 8-token group
-    const ConstI32* __restrict__ table = as_constant(a.block_tables) + (int64_t)s * a.max_blocks_per_seq;
-    // the sequence's query rows (one in decode); row qi attends causally over its first L - ql + qi + 1
-    // positions, and every column over those below ufull
+
+  // A sequence segment of the run: the sequence's tiles in [g0, g1), positions [u0, u1).
+  struct Seg {
+    int s, p0, p1, L, u1, last8;
+    const ConstI32* table;
+  };
+  auto segment = [&](int s) {
+    Seg q;
+    q.s = s;
+    q.p0 = __builtin_amdgcn_readfirstlane(P[s]);
+    q.p1 = __builtin_amdgcn_readfirstlane(P[s + 1]);
+    q.L = min(max(lens[s], 0), a.max_context_len);
+    q.u1 = min(q.L, (min(q.p1, g1) - q.p0) * kTileTok);
+    q.last8 = (q.u1 - 1) & ~(kTile / 2 - 1);  // start of the last live 8-token group
+    q.table = as_constant(a.block_tables) + (int64_t)s * a.max_blocks_per_seq;
+    return q;
+  };
+  // the next sequence holding tiles after s (one exists while tiles of the run remain)
+  auto next_seq = [&](int s) {
+    ++s;
+    while (__builtin_amdgcn_readfirstlane(P[s + 1]) == __builtin_amdgcn_readfirstlane(P[s])) ++s;
+    return s;
+  };
+  // the query operand of sequence s's columns (Q^T, B operand of S^T = K Q^T): lane (n, j) holds dims 32c + 8j ..
+  // 32c + 8j + 7 of its column's query row; columns past the sequence's rows are 0 (and read row 0, head 0)
+  auto load_query = [&](int s, U4* qv) {
     int q0 = s, ql = 1;
     if (a.query_start) {
       q0 = __builtin_amdgcn_readfirstlane(a.query_start[s]);
-      ql = min(max(__builtin_amdgcn_readfirstlane(a.query_start[s + 1]) - q0, 0), a.max_query_len);
+      ql = rows_of_seq(a, s);
     }
-    const int qrow = q0 + qi;
-    const bool head_ok = qi < ql && qrow < a.num_tokens;
-    const int lim = head_ok ? min(u1, L - ql + qi + 1) : u0;
-    const int ufull = min(u1, L - ql + 1);
-
+    const bool ok = qi < ql && q0 + qi < a.num_tokens;
     const char* qptr = static_cast<const char*>(a.query) +
-                       (head_ok ? ((int64_t)qrow * a.num_q_heads + (int64_t)g * G + hh) * D * 2 : 0);
-    U4 qb[kChunks];
+                       (ok ? ((int64_t)(q0 + qi) * a.num_q_heads + (int64_t)g * G + hh) * D * 2 : 0);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const U4 v = *reinterpret_cast<const U4*>(qptr + c * 64 + j * 16);
-      qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
+      qv[c] = ok ? v : U4{0u, 0u, 0u, 0u};
     }
+  };
 
-    float m = -INFINITY, l = 0.f;
-    f32x4 o[kNt];
+  // issue cursor: the segment of the next tile to load; compute cursor: the segment of the staged tile
+  Seg is = segment(lo);
+  Seg cs = is;
+  U4 qb[kChunks], qn[kChunks];
+  load_query(cs.s, qb);
+  U4 kR[2][kLoads], vR[2][kLoads];
+  bool bad_staged = false, bad_issued = false;
+  auto issue = [&](int gi) {  // tile gi of the list, inside the issue segment
+    const int t = (gi - is.p0) * kTileTok;
+    gqa_issue<KV, D>(kR, vR, is.table, t, t, is.u1, is.last8, a, row_bytes, kbase, vbase, off, bad_issued);
+  };
+
+  // per-segment state of the compute cursor
+  int q0, ql, qrow, lim0, ufull;
+  bool head_ok;
+  auto begin_segment = [&]() {
+    q0 = cs.s;
+    ql = 1;
+    if (a.query_start) {
+      q0 = __builtin_amdgcn_readfirstlane(a.query_start[cs.s]);
+      ql = rows_of_seq(a, cs.s);
+    }
+    qrow = q0 + qi;
+    head_ok = qi < ql && qrow < a.num_tokens;
+    // row qi attends causally over its first L - ql + qi + 1 positions, every column over those below ufull
+    lim0 = head_ok ? min(cs.u1, cs.L - ql + qi + 1) : 0;
+    ufull = min(cs.u1, cs.L - ql + 1);
+  };
+  begin_segment();
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[kNt];
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
+  for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
 
-    U4 kA[2][kLoads], vA[2][kLoads], kB[2][kLoads], vB[2][kLoads];
-    auto issue = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-      gqa_issue<KV, D>(kb, vb, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1, last8, a,
-                       row_bytes, kbase, vbase, off, bad);
-    };
-
-    auto consume = [&](U4 (*kb)[kLoads], U4 (*vb)[kLoads], int tile) {
-      const int t = u0 + tile * kTileTok;
-      gqa_consume<KV, D>(kb, vb, kslice, vslice, wofs, kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull,
-                         lim, j, m, l, o);
-    };
-
-    issue(kA, vA, 0);
-    int tj = 0;
-    for (; tj + 2 <= ntiles; tj += 2) {
-      issue(kB, vB, tj + 1);
-      consume(kA, vA, tj);
-      issue(kA, vA, tj + 2);
-      consume(kB, vB, tj + 1);
+  issue(g0);
+  for (int gi = g0; gi < g1; ++gi) {
+    gqa_stage<KV, D>(kR, vR, kslice, vslice, wofs);
+    bad_staged = bad_issued;
+    bad_issued = false;
+    if (gi + 1 < g1) {
+      if (gi + 1 >= is.p1) {  // the next tile opens the next sequence: its query rows come in with it
+        is = segment(next_seq(is.s));
+        load_query(is.s, qn);
+      }
+      issue(gi + 1);
     }
-    if (tj < ntiles) consume(kA, vA, tj);
+    const int cu0 = (max(g0, cs.p0) - cs.p0) * kTileTok;  // the segment's first position
+    const int t = (gi - cs.p0) * kTileTok;
+    const int lim = head_ok ? lim0 : cu0;
+    gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull, lim, j, m, l, o);
+    bad |= bad_staged;
+    if (gi + 1 < min(cs.p1, g1)) continue;
 
-    // the sequence's rows: whole in this run -> out; else the run's partial for row qi in slot 0 (the run
-    // starts inside the sequence) or slot 1 (it ends inside it)
+    // the segment's last tile: its rows, whole in this run -> out; else the run's partial for row qi in slot 0
+    // (the run starts inside the sequence) or slot 1 (it ends inside it)
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     if (head_ok) {
       const int h = g * G + hh;
       const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
       float* dst;
-      if (p0 >= g0 && p1 <= g1) {
+      if (cs.p0 >= g0 && cs.p1 <= g1) {
         dst = a.out + ((int64_t)qrow * a.num_q_heads + h) * D;
       } else {
-        const int64_t wrow = (((int64_t)h * a.chunks + chunk) * 2 + (p0 > g0 ? 1 : 0)) * a.max_query_len + qi;
+        const int64_t wrow = (((int64_t)h * a.chunks + chunk) * 2 + (cs.p0 > g0 ? 1 : 0)) * a.max_query_len + qi;
         dst = a.ws_o + wrow * D;
         if (j == 0) {
           a.ws_ml[2 * wrow] = bad ? poison : m;
@@ -638,11 +677,17 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
                 : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
       }
     }
-    if (end >= g1) break;
-    // the next sequence holding tiles (one exists while tiles of the run remain)
-    pos = end;
-    ++s;
-    while (__builtin_amdgcn_readfirstlane(P[s + 1]) == __builtin_amdgcn_readfirstlane(P[s])) ++s;
+    if (gi + 1 >= g1) break;
+    // the next segment: the one the issue cursor opened
+    cs = is;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) qb[c] = qn[c];
+    begin_segment();
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bad = false;
   }
 }
 
