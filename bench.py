@@ -465,14 +465,14 @@ def main() -> int:
     import torch
 
     import paged_kv_cache_458_amd as pa
-    from workloads import CONFIG_NAMES, algorithmic_bytes, build_structure, materialize, query_rows
+    from workloads import CONFIG_NAMES, EXTRA_NAMES, algorithmic_bytes, build_structure, materialize, query_rows
 
     if args.workload == "decode_loop":
         return run_decode_loop(args)
     if args.workload == "swap":
         return run_swap(args)
-    if args.workload not in CONFIG_NAMES:
-        ap.error(f"--workload must be one of {CONFIG_NAMES}, configs, decode_loop or swap")
+    if args.workload not in CONFIG_NAMES + EXTRA_NAMES:
+        ap.error(f"--workload must be one of {CONFIG_NAMES + EXTRA_NAMES}, configs, decode_loop or swap")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.load_library()

@@ -80,7 +80,8 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
  * Arguments as in paged_attention_decode. Returns 0 as well for invalid sizes (the decode call reports them).
  * Split into partitions of P tokens: partials [num_seqs][num_q_heads][ceil(max_context_len / S)][head_dim]
  * fp32, then their (max, sum) pairs, each part 256-byte aligned, where S = P, or S = 2P when grouped heads run
- * on the matrix cores with 512 <= P < 1024 (one wave covers two partitions and merges them itself).
+ * on the matrix cores at head_dim <= 128 with 512 <= P < 1024 (one wave covers two partitions and merges them
+ * itself).
  * Balanced split: partials [num_q_heads][R][2][head_dim] fp32 and their pairs, then (query rows + 1) int32
  * tile counts, for R runs. On the single-head kernel R = 1024 / ceil(ceil(num_q_heads / H) / 2) per head,
  * where a wave takes H = 2 adjacent heads if head rows are 64 or 128 bytes (E4M3 at head_dim 64 or 128, bf16
@@ -109,8 +110,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *   scale          multiplies q . k before the softmax (1/sqrt(head_dim) in the usual models)
  *   block_size     tokens per block: 8, 16, 32, 64, 128 or 256 (page 1 section 5 suggests 8 for short
  *                  sequences; 8 needs head rows of at least 128 bytes, so not E4M3 at head_dim 64)
- *   head_dim       64, 80, 96, 112, 128, 192 or 256 (grouped heads run on the matrix cores at 64 and 128
- *                  with bf16 or E4M3 caches, on the vector ALUs otherwise)
+ *   head_dim       64, 80, 96, 112, 128, 192 or 256 (grouped heads with bf16 or E4M3 caches run on the matrix
+ *                  cores at every head dim; one query head per KV head and fp32 caches on the vector ALUs)
  *   num_q_heads    a multiple of num_kv_heads
  *   max_context_len  upper bound of context_lens, <= max_blocks_per_seq * block_size
  *   (q_dtype, kv_dtype)  (PA_F32, PA_F32) or (PA_BF16, PA_BF16); accumulation is fp32 either way (FP8
@@ -121,12 +122,12 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *                  in sequence order, are cut into equal runs, one per wave of a grid that fills the chip, so
  *                  every wave streams the same number of bytes; a sequence cut by run boundaries is merged
  *                  by the same log-sum-exp reduction (at most 2048 query rows and rows x max_context_len <=
- *                  2^30; grouped heads that run on the matrix cores -- bf16 or E4M3 caches at head_dim 64 or
- *                  128 -- also need G <= 16 heads per KV head; PA_ERR_UNSUPPORTED otherwise); -1 = the
- *                  library chooses (paged_attention_partition_size): the balanced split wherever the
- *                  single-head kernel would otherwise split its contexts, and on the matrix cores wherever
- *                  its partitions would launch more than one round of 2048 resident waves; partitions
- *                  otherwise
+ *                  2^30; grouped heads that run on the matrix cores -- bf16 or E4M3 caches -- also need
+ *                  G <= 16 heads per KV head; PA_ERR_UNSUPPORTED otherwise); -1 = the library chooses
+ *                  (paged_attention_partition_size): the balanced split wherever the single-head kernel would
+ *                  otherwise split its contexts, and on the matrix cores wherever its partitions would launch
+ *                  more than one round of 2048 resident waves or give a wave fewer than 1024 tokens;
+ *                  partitions otherwise
  *   workspace      device scratch of at least paged_attention_workspace_bytes(...) bytes when that is
  *                  non-zero (may be NULL otherwise); contents need no initialisation and are clobbered
  *   stream         hipStream_t
@@ -190,9 +191,10 @@ int paged_attention_decode_noalloc(float *out, const void *query, const void *ke
  *   query_start    int32 [num_seqs + 1] device array: query_start[0] = 0, non-decreasing, last entry
  *                  num_query_tokens, every difference <= max_query_len (rows beyond max_query_len are left
  *                  unwritten; the contents are not checked on the host)
- *   max_query_len  the largest QL (>= 1). With bf16 or E4M3 caches at head_dim 64 or 128 the matrix cores take
- *                  all of a sequence's rows, reading its K/V once per 16 (row, grouped head) columns (at most
- *                  1024 columns); other calls read a sequence's K/V once per (row, head).
+ *   max_query_len  the largest QL (>= 1). With bf16 or E4M3 caches the matrix cores take all of a sequence's
+ *                  rows whenever grouped heads x QL give at least 2 columns, reading its K/V once per 16
+ *                  (row, grouped head) columns (at most 1024 columns); other calls read a sequence's K/V once
+ *                  per (row, head).
  *   partition_size as in paged_attention_decode. On the matrix cores PA_PARTITION_BALANCED needs the grouped
  *                  heads x max_query_len columns to fit one group of 16 and at most 2048 sequences
  *                  (PA_ERR_UNSUPPORTED otherwise); its tile list holds sequences, each read once for all its

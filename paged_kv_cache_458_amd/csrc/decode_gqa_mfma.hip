@@ -125,19 +125,33 @@ __device__ __forceinline__ void prob_operands(const float* sv, float mref, U4& h
   lo = U4{r[0], r[1], r[2], r[3]};
 }
 
-// Geometry of the K/V tiles of both grouped-query kernels (bf16 or E4M3 cache, head_dim D).
+constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+
+// Geometry of the K/V tiles of both grouped-query kernels (bf16 or E4M3 cache, head_dim D: 64, 80, 96, 112, 128,
+// 192 or 256).
 template <int KV, int D>
 struct GqaShape {
   static constexpr int kEsize = KV == PA_BF16 ? 2 : 1;  // bytes per cached element
-  static constexpr int kChunks = D / 32;                // 32-dim k-chunks of the QK product
+  static constexpr int kDP = (D + 31) / 32 * 32;        // dims of the QK product, zero-padded to 32-dim k-chunks
+  static constexpr int kChunks = kDP / 32;              // 32-dim k-chunks of the QK product
   static constexpr int kNt = D / 16;                    // 16-dim column tiles of the PV product
   // E4M3 codes are staged as they are and widened to bf16 after the LDS reads
   static constexpr bool kRaw = KV != PA_BF16;
-  static constexpr int kPitch = D * (kRaw ? 1 : 2) + 16;  // LDS bytes per K or V row, padded by 16
-  static constexpr int kSlice = kTileTok * kPitch;      // one 32-row tile of K or of V
-  static constexpr int kRowLanes = D * kEsize / 16;     // lanes covering one head row with 16-byte loads
-  static constexpr int kRows = kWave / kRowLanes;       // rows per wave-wide load
-  static constexpr int kLoads = kTile / kRows;          // loads per 16-row half, for K and for V
+  static constexpr int kPitch = kDP * (kRaw ? 1 : 2) + 16;  // LDS bytes per K or V row, padded by 16
+  static constexpr int kSlice = kTileTok * kPitch;          // one 32-row tile of K or of V
+  static constexpr int kHeadLanes = D * kEsize / 16;        // 16-byte pieces of one head row
+  // lanes per head row with 16-byte loads, a power of two; the lanes past the row's pieces load nothing, and those
+  // inside the padded dims store the zeros they read there
+  static constexpr int kRowLanes = pow2_ceil(kHeadLanes);
+  static constexpr int kStageLanes = kDP * (kRaw ? 1 : 2) / 16;  // lanes whose 16 bytes lie in the staged row
+  static constexpr int kRows = kWave / kRowLanes;               // rows per wave-wide load
+  static constexpr int kLoads = kTile / kRows;                  // loads per 16-row half, for K and for V
+  // bf16 head rows over 256 bytes: K and V take turns through one register set and one LDS slice (two slices of
+  // 32 rows of such rows would not fit 8 waves in a CU's LDS, nor two register sets in the register file)
+  static constexpr bool kPhased = !kRaw && D > 128;
+  static constexpr int kSlices = kPhased ? 1 : 2;
+  // a wave may cover two consecutive partitions only at head_dim <= 128 (registers for the parked state)
+  static constexpr bool kTwoParts = D <= 128;
   // a load of at most 8 rows stays inside one 8-row quarter; 16-row loads (E4M3 at head_dim 64) take a whole
   // half through the even quarter's descriptor (the host refuses 8-slot blocks for them)
   static constexpr int kQuarterRows = kRows <= kTile / 2 ? kTile / 2 : kTile;
@@ -164,12 +178,12 @@ struct GqaShape {
   }
 };
 
-// Loads of one 32-token tile into a register set. `t` is the tile's first position, clamped to the last live
+// Loads of one 32-token tile's K (LK) and/or V (LV) into register sets. `t` is the tile's first position, clamped to the last live
 // tile (table entries are read at live positions only); `t_live` is the unclamped one. Each 8-row quarter goes
 // through a descriptor covering only its rows below `u1`: the rest read as zero without touching memory.
 // Quarters of one 16-row half share a block unless blocks hold 8 slots. `last8` is the start of the last live
 // 8-row group.
-template <int KV, int D, int NL, typename TablePtr>
+template <int KV, int D, bool LK, bool LV, int NL, typename TablePtr>
 __device__ __forceinline__ void gqa_issue(U4 (*kb)[NL], U4 (*vb)[NL], TablePtr table, int t, int t_live, int u1,
                                           int last8, const DecodeArgs& a, int64_t row_bytes, const char* kbase,
                                           const char* vbase, const uint32_t* off, bool& bad) {
@@ -191,40 +205,35 @@ __device__ __forceinline__ void gqa_issue(U4 (*kb)[NL], U4 (*vb)[NL], TablePtr t
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       if ((S::kRows * i < kTile / 2) == ((q4 & 1) == 0)) {
-        kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
-        vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
+        if constexpr (LK) kb[h2][i] = load16<kPolStream>(kr, off[i] - qoff);
+        if constexpr (LV) vb[h2][i] = load16<kPolStream>(vr, off[i] - qoff);
       }
     }
   }
 }
 
-// Stage one tile's K and V from the load registers into the wave's LDS slices (rows past the range end were
-// loaded as zeros); this is where the wave waits for the tile's loads. Afterwards the registers are free for the
-// next tile's loads.
+// Stage one tile of K or V from the load registers into an LDS slice (rows past the range end were loaded as
+// zeros); this is where the wave waits for those loads. Lanes past the padded row store nothing. The caller
+// orders it against the slice's reads (wave_lds_sync before and after).
 template <int KV, int D, int NL>
-__device__ __forceinline__ void gqa_stage(const U4 (*kb)[NL], const U4 (*vb)[NL], char* kslice, char* vslice,
-                                          int wofs) {
+__device__ __forceinline__ void gqa_stage(const U4 (*rb)[NL], char* slice, int wofs, bool stage_lane) {
   using S = GqaShape<KV, D>;
   static_assert(NL == S::kLoads, "register sets of the tile's shape");
-  // the previous tile's reads come first
-  wave_lds_sync();
+  if (S::kStageLanes == S::kRowLanes || stage_lane) {
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int i = 0; i < S::kLoads; ++i) {
-      const int r = (h2 * kTile + S::kRows * i) * S::kPitch + wofs;
-      *reinterpret_cast<U4*>(kslice + r) = kb[h2][i];
-      *reinterpret_cast<U4*>(vslice + r) = vb[h2][i];
-    }
-  wave_lds_sync();
+      for (int i = 0; i < S::kLoads; ++i)
+        *reinterpret_cast<U4*>(slice + (h2 * kTile + S::kRows * i) * S::kPitch + wofs) = rb[h2][i];
+  }
 }
 
-// One staged tile through the matrix cores (E4M3 widened to bf16 after the LDS reads): S^T = K Q^T, the
-// online-softmax update of (m, l) in the exp2 domain with positions >= `lim` masked unless the whole tile is
-// `full`, then O^T += V^T (P_hi + P_lo)^T.
+// The scores of one staged K tile through the matrix cores (E4M3 widened to bf16 after the LDS reads):
+// S^T = K Q^T, then the online-softmax update of (m, l) in the exp2 domain with positions >= `lim` masked unless
+// the whole tile is `full`, the rescale of the accumulator, and the tile's weights as the bf16 pair (pb, pl).
 template <int KV, int D>
-__device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase, const U4* qb, float scale_log2,
-                                            int t, bool full, int lim, int j, float& m, float& l, f32x4* o) {
+__device__ __forceinline__ void gqa_scores(const char* kread, const U4* qb, float scale_log2, int t, bool full,
+                                           int lim, int j, float& m, float& l, f32x4* o, U4& pb, U4& pl) {
   using S = GqaShape<KV, D>;
   f32x4 sc[2];
 #pragma unroll
@@ -258,7 +267,6 @@ __device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase
   const float mref = mn == -INFINITY ? 0.f : mn;
   const float alpha = fast_exp2(m - mref);
   m = mn;
-  U4 pb, pl;
   float psum;
   prob_operands(sv, mref, pb, pl, psum);
   l = l * alpha + psum;
@@ -273,6 +281,12 @@ __device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase
       o[nt][3] *= alpha;
     }
   }
+}
+
+// O^T += V^T (P_hi + P_lo)^T over one staged V tile.
+template <int KV, int D>
+__device__ __forceinline__ void gqa_pv(const char* rbase, const U4& pb, const U4& pl, f32x4* o) {
+  using S = GqaShape<KV, D>;
 #pragma unroll
   for (int nt = 0; nt < S::kNt; ++nt) {
     // A operand: V^T rows = dims 16nt + n, contraction index k = 8j + e -> token (e < 4 ? 4j + e : 16 + 4j + e - 4);
@@ -289,6 +303,42 @@ __device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase
   }
 }
 
+// Both products of one tile staged whole (K and V in their own slices).
+template <int KV, int D>
+__device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase, const U4* qb, float scale_log2,
+                                            int t, bool full, int lim, int j, float& m, float& l, f32x4* o) {
+  U4 pb, pl;
+  gqa_scores<KV, D>(kread, qb, scale_log2, t, full, lim, j, m, l, o, pb, pl);
+  gqa_pv<KV, D>(rbase, pb, pl, o);
+}
+
+// Q^T, the B operand of S^T = K Q^T, for a column whose query row starts at element `qe` of the bf16 query:
+// lane (n, j) holds dims 32c + 8j .. 32c + 8j + 7; dims past D (the zero padding of the last k-chunk) and columns
+// that hold no query row (`ok` false) are 0. Every load stays inside the column's row (or row 0, head 0).
+template <int D>
+__device__ __forceinline__ void load_query_operand(const void* query, bool ok, int64_t qe, int j, U4* qb) {
+  constexpr int kChunks = (D + 31) / 32;
+  const char* qptr = static_cast<const char*>(query) + (ok ? qe * 2 : 0);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const bool in = 32 * c + 8 * j < D;
+    const U4 v = *reinterpret_cast<const U4*>(qptr + (in ? c * 64 + j * 16 : 0));
+    qb[c] = ok && in ? v : U4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Per-lane byte offsets of a wave-wide load inside a 16-row half tile: lane (rr, rc) takes the 16-byte piece rc
+// of row rr + kRows i. Lanes past the head row's pieces load at an offset above every descriptor's size (at most
+// 8 rows, under 2^30 bytes), so they read zeros without touching memory.
+template <int KV, int D>
+__device__ __forceinline__ void gqa_offsets(int rr, int rc, int64_t row_bytes, int64_t head_off, uint32_t* off) {
+  using S = GqaShape<KV, D>;
+  constexpr uint32_t kNowhere = 0x80000000u;
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i)
+    off[i] = rc < S::kHeadLanes ? (uint32_t)((rr + S::kRows * i) * row_bytes + head_off + rc * 16) : kNowhere;
+}
+
 // W waves (KV heads of one sequence) per workgroup: they stream the same slots of the pool side by side. At
 // least two waves per SIMD: with smaller workgroups the compiler would otherwise spend the register budget of
 // one (measured on MI355X with 4, 2 and 1 KV heads: 3-8% slower).
@@ -296,8 +346,8 @@ template <int KV, int D, int W>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const DecodeArgs a) {
   using S = GqaShape<KV, D>;
   constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
-  constexpr int kRowLanes = S::kRowLanes, kRows = S::kRows, kLoads = S::kLoads;
-  __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
+  constexpr int kRowLanes = S::kRowLanes, kLoads = S::kLoads;
+  __shared__ __attribute__((aligned(16))) char lds[W * S::kSlices * kSlice];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
@@ -355,25 +405,18 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   const int rc = lane % kRowLanes;  //        16-byte chunk within the row
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
   const int64_t head_off = (int64_t)g * D * kEsize;
-  char* const kslice = lds + w * 2 * kSlice;
-  char* const vslice = kslice + kSlice;
+  char* const kslice = lds + w * S::kSlices * kSlice;
+  char* const vslice = S::kPhased ? kslice : kslice + kSlice;  // phased: V takes K's slice after the scores
 
-  // Q^T (B operand of S^T = K Q^T): lane (n, j) holds dims 32c + 8j .. 32c + 8j + 7 of its column's query
-  // row; padding columns are 0 (and read row 0, head 0, which exists whenever anything is launched).
-  const char* qptr = static_cast<const char*>(a.query) +
-                     (head_ok ? ((int64_t)qrow * a.num_q_heads + (int64_t)g * G + hh) * D * 2 : 0);
+  // Q^T (B operand of S^T = K Q^T): lane (n, j) holds dims 32c + 8j .. 32c + 8j + 7 of its column's query row
   U4 qb[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const U4 v = *reinterpret_cast<const U4*>(qptr + c * 64 + j * 16);
-    qb[c] = head_ok ? v : U4{0u, 0u, 0u, 0u};
-  }
+  load_query_operand<D>(a.query, head_ok, ((int64_t)qrow * a.num_q_heads + (int64_t)g * G + hh) * D, j, qb);
 
   // per-lane byte offsets inside a 16-row half tile: each wave-wide load covers kRows whole head rows (full
   // cache lines: 256 bytes of bf16 or 128 of E4M3 at D = 128), for K as for V
   uint32_t off[kLoads];
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) off[i] = (uint32_t)((rr + kRows * i) * row_bytes + head_off + rc * 16);
+  gqa_offsets<KV, D>(rr, rc, row_bytes, head_off, off);
+  const bool stage_lane = rc < S::kStageLanes;
 
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
@@ -389,11 +432,16 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // One register set: a tile's loads land in it, are staged into LDS, and the next tile's loads are issued into
   // it before the staged tile's products are computed -- about one tile of loads in flight per wave at all times.
   // (Two register sets, two tiles in flight, were measured slower: more concurrent reads congest the memory
-  // system rather than feed it.)
-  U4 kR[2][kLoads], vR[2][kLoads];
-  auto issue = [&](int tile) {
-    gqa_issue<KV, D>(kR, vR, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1, last8, a,
-                     row_bytes, kbase, vbase, off, bad);
+  // system rather than feed it.) Phased shapes hold K or V of a tile at a time.
+  U4 kR[2][kLoads], vR[2][S::kPhased ? 1 : kLoads];
+  auto issue_kv = [&](int tile) {
+    gqa_issue<KV, D, true, !S::kPhased>(kR, (U4(*)[kLoads])vR, table, u0 + min(tile, ntiles - 1) * kTileTok,
+                                        u0 + tile * kTileTok, u1, last8, a, row_bytes, kbase, vbase, off, bad);
+  };
+  auto issue_v = [&](int tile) {  // phased: V of a tile into the register set K has left
+    bool unused = false;  // the same table entries as the tile's K loads
+    gqa_issue<KV, D, false, true>(kR, kR, table, u0 + min(tile, ntiles - 1) * kTileTok, u0 + tile * kTileTok, u1,
+                                  last8, a, row_bytes, kbase, vbase, off, unused);
   };
 
   // LDS: row r of the tile at slice + r * kPitch, K and V each in their own slice (bf16, or E4M3 codes as
@@ -406,16 +454,18 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // A wave covers at most two partitions. Finishing the first one mid-range only parks its state in
   // registers: any store inside the load loop would leave the compiler unable to count outstanding memory
   // operations, and it would then drain the load pipeline on every tile.
-  const int cut = min(u0 + a.partition, u1);  // end of the wave's first partition
+  const int cut = min(u0 + a.partition, u1);  // end of the wave's first partition (u1 unless S::kTwoParts)
   float m_first = -INFINITY, l_first = 0.f;
-  f32x4 o_first[kNt];
+  constexpr int kNtFirst = S::kTwoParts ? kNt : 1;
+  f32x4 o_first[kNtFirst];
 #pragma unroll
-  for (int nt = 0; nt < kNt; ++nt) o_first[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < kNtFirst; ++nt) o_first[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto park_first = [&]() {
+    if constexpr (!S::kTwoParts) return;
     m_first = m;
     l_first = l;
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) o_first[nt] = o[nt];
+    for (int nt = 0; nt < kNtFirst; ++nt) o_first[nt] = o[nt];
     m = -INFINITY;
     l = 0.f;
 #pragma unroll
@@ -453,24 +503,39 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   };
 
   if (ntiles > 0) {
-    issue(0);
+    issue_kv(0);
     for (int tj = 0; tj < ntiles; ++tj) {
-      gqa_stage<KV, D>(kR, vR, kslice, vslice, wofs);
-      issue(tj + 1);  // past the last tile every row is beyond the range: nothing is read
       const int t = u0 + tj * kTileTok;
-      // no column masks a position of a tile below ufull
-      gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull, lim, j, m, l, o);
+      const bool full = t + kTileTok <= ufull;  // no column masks a position of a tile below ufull
+      wave_lds_sync();  // the previous tile's reads come first
+      gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
+      if constexpr (S::kPhased) {
+        wave_lds_sync();
+        issue_v(tj);
+        U4 pb, pl;
+        gqa_scores<KV, D>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
+        wave_lds_sync();
+        gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
+        wave_lds_sync();
+        issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
+        gqa_pv<KV, D>(rbase, pb, pl, o);
+      } else {
+        gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
+        wave_lds_sync();
+        issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
+        gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
+      }
       if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
     }
   }
-  if (cut < u1) {
+  if (S::kTwoParts && cut < u1) {
     // merge the first partition's state into the second's: one partial per wave
     const float M = fmaxf(m_first, m);
     const float Mr = M == -INFINITY ? 0.f : M;
     const float fa = fast_exp2(m_first - Mr), fb = fast_exp2(m - Mr);
     l = l_first * fa + l * fb;
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt)
+    for (int nt = 0; nt < kNtFirst; ++nt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[nt][e] = o_first[nt][e] * fa + o[nt][e] * fb;
     m = M;
@@ -498,9 +563,9 @@ template <int KV, int D, int W>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(const DecodeArgs a) {
   using S = GqaShape<KV, D>;
   constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
-  constexpr int kRowLanes = S::kRowLanes, kRows = S::kRows, kLoads = S::kLoads;
+  constexpr int kRowLanes = S::kRowLanes, kLoads = S::kLoads;
   constexpr int NT = kWave * W;
-  __shared__ __attribute__((aligned(16))) char lds[W * 2 * kSlice];
+  __shared__ __attribute__((aligned(16))) char lds[W * S::kSlices * kSlice];
   __shared__ int32_t wave_total[W];
   extern __shared__ int32_t P[];  // [num_seqs + 1]: tiles of the sequences before each one
 
@@ -537,11 +602,11 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   const int rc = lane % kRowLanes;
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
   const int64_t head_off = (int64_t)g * D * kEsize;
-  char* const kslice = lds + w * 2 * kSlice;
-  char* const vslice = kslice + kSlice;
+  char* const kslice = lds + w * S::kSlices * kSlice;
+  char* const vslice = S::kPhased ? kslice : kslice + kSlice;  // phased: V takes K's slice after the scores
   uint32_t off[kLoads];
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) off[i] = (uint32_t)((rr + kRows * i) * row_bytes + head_off + rc * 16);
+  gqa_offsets<KV, D>(rr, rc, row_bytes, head_off, off);
+  const bool stage_lane = rc < S::kStageLanes;
   const int wofs = rr * kPitch + rc * 16;
   const char* const kread = S::k_read(kslice, n, j);
   const char* const rbase = S::v_read(vslice, n, j);
@@ -588,13 +653,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
       ql = rows_of_seq(a, s);
     }
     const bool ok = qi < ql && q0 + qi < a.num_tokens;
-    const char* qptr = static_cast<const char*>(a.query) +
-                       (ok ? ((int64_t)(q0 + qi) * a.num_q_heads + (int64_t)g * G + hh) * D * 2 : 0);
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const U4 v = *reinterpret_cast<const U4*>(qptr + c * 64 + j * 16);
-      qv[c] = ok ? v : U4{0u, 0u, 0u, 0u};
-    }
+    load_query_operand<D>(a.query, ok, ((int64_t)(q0 + qi) * a.num_q_heads + (int64_t)g * G + hh) * D, j, qv);
   };
 
   // issue cursor: the segment of the next tile to load; compute cursor: the segment of the staged tile
@@ -602,11 +661,19 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   Seg cs = is;
   U4 qb[kChunks], qn[kChunks];
   load_query(cs.s, qb);
-  U4 kR[2][kLoads], vR[2][kLoads];
+  // one register set (phased shapes: K or V of a tile at a time), as in the partition kernel
+  U4 kR[2][kLoads], vR[2][S::kPhased ? 1 : kLoads];
   bool bad_staged = false, bad_issued = false;
-  auto issue = [&](int gi) {  // tile gi of the list, inside the issue segment
+  auto issue_kv = [&](int gi) {  // tile gi of the list, inside the issue segment
     const int t = (gi - is.p0) * kTileTok;
-    gqa_issue<KV, D>(kR, vR, is.table, t, t, is.u1, is.last8, a, row_bytes, kbase, vbase, off, bad_issued);
+    gqa_issue<KV, D, true, !S::kPhased>(kR, (U4(*)[kLoads])vR, is.table, t, t, is.u1, is.last8, a, row_bytes,
+                                        kbase, vbase, off, bad_issued);
+  };
+  auto issue_v = [&](int gi) {  // phased: V of tile gi (still in the issue segment) into the set K has left
+    const int t = (gi - is.p0) * kTileTok;
+    bool unused = false;  // the same table entries as the tile's K loads
+    gqa_issue<KV, D, false, true>(kR, kR, is.table, t, t, is.u1, is.last8, a, row_bytes, kbase, vbase, off,
+                                  unused);
   };
 
   // per-segment state of the compute cursor
@@ -632,22 +699,42 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
-  issue(g0);
-  for (int gi = g0; gi < g1; ++gi) {
-    gqa_stage<KV, D>(kR, vR, kslice, vslice, wofs);
-    bad_staged = bad_issued;
-    bad_issued = false;
+  auto issue_next = [&](int gi) {  // the tile after gi, if the run holds one
     if (gi + 1 < g1) {
       if (gi + 1 >= is.p1) {  // the next tile opens the next sequence: its query rows come in with it
         is = segment(next_seq(is.s));
         load_query(is.s, qn);
       }
-      issue(gi + 1);
+      issue_kv(gi + 1);
     }
+  };
+
+  issue_kv(g0);
+  for (int gi = g0; gi < g1; ++gi) {
     const int cu0 = (max(g0, cs.p0) - cs.p0) * kTileTok;  // the segment's first position
     const int t = (gi - cs.p0) * kTileTok;
     const int lim = head_ok ? lim0 : cu0;
-    gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, t + kTileTok <= ufull, lim, j, m, l, o);
+    const bool full = t + kTileTok <= ufull;
+    wave_lds_sync();  // the previous tile's reads come first
+    gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
+    bad_staged = bad_issued;
+    bad_issued = false;
+    if constexpr (S::kPhased) {
+      wave_lds_sync();
+      issue_v(gi);
+      U4 pb, pl;
+      gqa_scores<KV, D>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
+      wave_lds_sync();
+      gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
+      wave_lds_sync();
+      issue_next(gi);
+      gqa_pv<KV, D>(rbase, pb, pl, o);
+    } else {
+      gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
+      wave_lds_sync();
+      issue_next(gi);
+      gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
+    }
     bad |= bad_staged;
     if (gi + 1 < min(cs.p1, g1)) continue;
 
@@ -695,12 +782,15 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
 
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len) {
   const int64_t columns = (int64_t)group * max_query_len;
-  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && (head_dim == 128 || head_dim == 64) &&
+  const bool dim_ok = head_dim == 64 || head_dim == 80 || head_dim == 96 || head_dim == 112 || head_dim == 128 ||
+                      head_dim == 192 || head_dim == 256;
+  return (kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) && dim_ok &&
          columns >= 2 && columns <= 16 * kMaxColGroups;
 }
 
 template <int KV, int D, int W>
 hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
+  if (a.parts_per_wave > (GqaShape<KV, D>::kTwoParts ? 2 : 1)) return hipErrorInvalidValue;
   const int groups = a.split ? a.max_partitions : 1;  // one partial slot per wave span
   // column groups share the x dimension with the KV-head groups (the kernel unpacks them)
   const dim3 grid((a.num_kv_heads + W - 1) / W * a.col_groups, groups, a.num_seqs);
@@ -724,11 +814,29 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+struct Launch {
+  template <int KV, int D>
+  static hipError_t run(const DecodeArgs& a, hipStream_t stream) { return launch_d<KV, D>(a, stream); }
+};
+
+// the head dims the grouped-query kernels serve
+template <int KV, typename L>
+hipError_t dispatch_dim(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return L::template run<KV, 64>(a, stream);
+    case 80: return L::template run<KV, 80>(a, stream);
+    case 96: return L::template run<KV, 96>(a, stream);
+    case 112: return L::template run<KV, 112>(a, stream);
+    case 128: return L::template run<KV, 128>(a, stream);
+    case 192: return L::template run<KV, 192>(a, stream);
+    case 256: return L::template run<KV, 256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
-  if (kv_dtype == PA_BF16 && a.head_dim == 128) return launch_d<PA_BF16, 128>(a, stream);
-  if (kv_dtype == PA_BF16 && a.head_dim == 64) return launch_d<PA_BF16, 64>(a, stream);
-  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128) return launch_d<PA_FP8_E4M3, 128>(a, stream);
-  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64) return launch_d<PA_FP8_E4M3, 64>(a, stream);
+  if (kv_dtype == PA_BF16) return dispatch_dim<PA_BF16, Launch>(a, stream);
+  if (kv_dtype == PA_FP8_E4M3) return dispatch_dim<PA_FP8_E4M3, Launch>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -752,6 +860,11 @@ hipError_t launch_balanced_d(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+struct LaunchBalanced {
+  template <int KV, int D>
+  static hipError_t run(const DecodeArgs& a, hipStream_t stream) { return launch_balanced_d<KV, D>(a, stream); }
+};
+
 }  // namespace
 
 int32_t gqa_balanced_chunks(int32_t num_kv_heads) {
@@ -764,10 +877,8 @@ hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hi
   if (a.num_seqs > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix || a.col_groups != 1 ||
       a.group * a.max_query_len > 16 || !a.seq_prefix)
     return hipErrorInvalidValue;
-  if (kv_dtype == PA_BF16 && a.head_dim == 128) return launch_balanced_d<PA_BF16, 128>(a, stream);
-  if (kv_dtype == PA_BF16 && a.head_dim == 64) return launch_balanced_d<PA_BF16, 64>(a, stream);
-  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 128) return launch_balanced_d<PA_FP8_E4M3, 128>(a, stream);
-  if (kv_dtype == PA_FP8_E4M3 && a.head_dim == 64) return launch_balanced_d<PA_FP8_E4M3, 64>(a, stream);
+  if (kv_dtype == PA_BF16) return dispatch_dim<PA_BF16, LaunchBalanced>(a, stream);
+  if (kv_dtype == PA_FP8_E4M3) return dispatch_dim<PA_FP8_E4M3, LaunchBalanced>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -74,9 +74,9 @@ struct Plan {
 
 // Consecutive partitions one wave of the GQA kernel covers (1 or 2): two when the caller asks for partitions
 // of 512..1023 tokens, so that a wave still streams about 1024 tokens. Needs partitions made of whole
-// 32-token tiles.
-int32_t gqa_parts_per_wave(int32_t partition) {
-  return partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
+// 32-token tiles, and head_dim <= 128 (the registers that park the first partition's state).
+int32_t gqa_parts_per_wave(int32_t partition, int32_t head_dim) {
+  return head_dim <= 128 && partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
 }
 
 // Library choice of partition size. A partition is the unit of work of one wave (the GQA kernel may take
@@ -93,12 +93,12 @@ int32_t gqa_parts_per_wave(int32_t partition) {
 // The grouped-query kernel runs single pass when its grid already holds a wave per slot without splitting
 // (measured on MI355X: 13-15% faster for 7B-shaped verification batches, whose 2048 (sequence, head) waves
 // fill the chip; the single-head kernel's 4096-wave rule keeps its split there, 11-13% faster than without).
-int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa) {
+int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa, int32_t head_dim) {
   int32_t part = gqa ? 1024 : 512;
   const int64_t min_waves = gqa ? 2048 : 4096;
   if (gqa && rows >= min_waves) return 0;
   auto waves = [&](int32_t p) {
-    const int64_t span = (int64_t)p * (gqa ? gqa_parts_per_wave(p) : 1);
+    const int64_t span = (int64_t)p * (gqa ? gqa_parts_per_wave(p, head_dim) : 1);
     return rows * ((max_context_len + span - 1) / span);
   };
   while (part > 64 && waves(part) < min_waves) part /= 2;
@@ -155,7 +155,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
-  int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa) : partition_size;
+  int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa, head_dim) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
   // The library takes the balanced split wherever it would otherwise split the single-head kernel's contexts.
   // On the matrix cores it takes it only where the partitions would launch more than one round of resident
@@ -166,14 +166,19 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   const bool split_default = partition_size == -1 && balanced_ok && part > 0 && part < whole;
   const bool more_than_a_round =
       gqa && part > 0 &&
-      rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part) - 1) /
-              ((int64_t)part * gqa_parts_per_wave(part))) > pa::kResidentWaves;
+      rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part, head_dim) - 1) /
+              ((int64_t)part * gqa_parts_per_wave(part, head_dim))) > pa::kResidentWaves;
+  // Spans under 1024 tokens leave the partitions' last, partial spans a larger share of the grid: measured on
+  // MI355X, 64 sequences of 1k-4k tokens with 32 query heads on 4 KV heads of 256 dims (512-token spans, one
+  // round) took 143.4 us in partitions against 121.9 us in the balanced split (E4M3 80.8 against 72.5).
+  const bool short_spans = gqa && part > 0 && (int64_t)part * gqa_parts_per_wave(part, head_dim) < 1024;
   // Several new tokens per sequence on the matrix cores: a single pass that fills a round of resident waves
   // leaves them unequal (each reads its sequence's whole context); equal runs gained 1-8% there (7B-shaped
   // batches of 2, 4 and 8 rows per sequence, bf16 and E4M3).
   const bool uneven_pass = gqa && max_query_len > 1 && partition_size == -1 && balanced_ok &&
                            (part == 0 || part >= whole) && rows >= pa::kResidentWaves;
-  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round)) || uneven_pass) {
+  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round || short_spans)) ||
+      uneven_pass) {
     p.balanced = true;
     p.split = true;
     p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads)
@@ -196,7 +201,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     return p;
   }
   // one partial per wave span: a grouped-query wave that covers two partitions merges their states itself
-  p.parts_per_wave = gqa ? gqa_parts_per_wave(part) : 1;
+  p.parts_per_wave = gqa ? gqa_parts_per_wave(part, head_dim) : 1;
   const int64_t span = (int64_t)part * p.parts_per_wave;
   const int64_t pm = (max_context_len + span - 1) / span;
   if (pm > kMaxGridYZ) {

@@ -419,3 +419,21 @@ def test_noalloc_scratch_limit_matches_the_workspace_rule():
     assert 0 < fits <= pa.PA_STATIC_SCRATCH_BYTES
     assert "PA_STATIC_SCRATCH_BYTES" in pa.strerror(pa.PA_ERR_SCRATCH)
     assert noalloc_call(num_seqs=0) == 0  # nothing to do: no-op
+
+
+def test_grouped_query_default_prefers_the_balanced_split_for_short_spans():
+    lib = pa.load_library()
+    # 64 sequences of up to 4096 tokens, 32 query heads on 4 KV heads of 256 dims: 512-token spans (one wave
+    # per partition at head_dim > 128) fill one round, but spans under 1024 tokens take the balanced split
+    assert lib.paged_attention_partition_size(64, 32, 4, 256, 16, 4096, pa.PA_BF16, -1) == pa.PA_PARTITION_BALANCED
+    # the 70B shape keeps its partitions: 1024-token spans, one round of 2048 waves
+    assert lib.paged_attention_partition_size(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
+    # grouped heads at every served head dim plan on the matrix cores (workspace of the balanced split with
+    # one partial slot per query head and run, not per query row)
+    for d in (64, 80, 96, 112, 128, 192, 256):
+        for kd in (pa.PA_BF16, pa.PA_FP8_E4M3):
+            assert lib.paged_attention_partition_size(4, 16, 2, d, 16, 4096, kd, pa.PA_PARTITION_BALANCED) == 1
+    # at head_dim > 128 a grouped-query wave covers one partition: 512-token partitions need a partial each
+    ws_128 = lib.paged_attention_workspace_bytes(8, 16, 2, 128, 16, 4096, pa.PA_BF16, 512)
+    ws_256 = lib.paged_attention_workspace_bytes(8, 16, 2, 256, 16, 4096, pa.PA_BF16, 512)
+    assert ws_256 > 2 * ws_128 * 1.9

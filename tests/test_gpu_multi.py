@@ -3,8 +3,8 @@ chunk): paged_attention_decode_multi through the C ABI against oracle.decode_mul
 
 Row j of a sequence's QL new tokens attends causally over its first L - QL + j + 1 positions. Grouped heads x
 QL columns run on the matrix-core kernel in groups of 16 (one K/V read per group for all of a sequence's
-rows) for bf16 and E4M3 caches at head_dim 64 and 128; the other shapes take the per-head kernel, one wave
-per (row, head). Tolerances as for decode: 1e-5 for fp32, 2e-3 +
+rows) for bf16 and E4M3 caches at every head dim; fp32 caches and single columns (one row of one head per KV
+head) take the per-head kernel, one wave per (row, head). Tolerances as for decode: 1e-5 for fp32, 2e-3 +
 1e-2 |ref| for bf16 or E4M3 caches under a bf16 query.
 """
 
@@ -72,8 +72,12 @@ CASES = [
     (508, [5, 40, 18], [9, 2, 18], 16, 4, 128, 16, "fp8"),             # QL > L: the first rows are zero; 72 cols
     (509, [300, 64, 1000], [20, 17, 3], 8, 8, 64, 16, "bf16"),         # no grouping, 20 rows: 2 groups
     (516, [300, 47, 1100, 2], [3, 2, 4, 2], 16, 4, 64, 16, "fp8"),     # E4M3 at head_dim 64: 16-row loads
+    (518, [300, 47, 1100, 5], [3, 2, 4, 5], 16, 4, 192, 16, "bf16"),   # K and V take turns; 16 columns
+    (519, [520, 33, 900], [5, 2, 7], 8, 4, 256, 32, "fp8"),            # 14 columns, padded-free 256 dims
+    (520, [700, 45, 90], [4, 3, 4], 64, 8, 80, 16, "bf16"),            # 32 columns in 2 groups at 80 dims
+    (521, [64, 400, 3], [6, 4, 3], 6, 6, 112, 8, "bf16"),              # no grouping, 112 dims, 8-slot blocks
+    (505, [65, 200, 9], [3, 7, 2], 8, 2, 96, 16, "bf16"),              # head_dim 96, 28 columns
     # per-head kernel
-    (505, [65, 200, 9], [3, 7, 2], 8, 2, 96, 16, "bf16"),              # head_dim 96
     (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
     (510, [0, 8, 700, 30], [3, 12, 5, 1], 8, 8, 80, 16, "bf16"),      # QL > L, an empty context
     (513, [2000, 5, 64, 300, 1], [7, 0, 4, 2, 1], 16, 16, 112, 8, "fp8"),  # an empty sequence; bs 8

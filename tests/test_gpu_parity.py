@@ -126,6 +126,21 @@ SMALL = [
     # two heads per wave in the balanced split (64- and 128-byte head rows), 8-slot blocks
     (230, [90, 33, 257, 16, 1], 8, 8, 128, 8, "fp8"),
     (231, [300, 8, 65, 1000], 4, 4, 64, 8, "bf16"),
+    # grouped heads on the matrix cores at every head dim: rows padded to whole 16-byte pieces per power of two of
+    # lanes, the score contraction zero-padded to 32-dim chunks (80, 112), K and V taking turns through one
+    # register set and LDS slice for bf16 rows over 256 bytes (192, 256)
+    (232, [700, 45, 1, 300], 32, 8, 80, 16, "bf16"),
+    (233, [513, 90, 1030], 16, 4, 96, 16, "bf16"),
+    (234, [260, 33, 1000, 7], 16, 2, 112, 32, "bf16"),
+    (235, [700, 1200, 45, 1], 32, 4, 192, 16, "bf16"),
+    (236, [2050, 999, 513, 300], 16, 2, 256, 256, "bf16"),
+    (237, [90, 33, 257, 16, 1], 8, 2, 256, 8, "bf16"),
+    (238, [700, 45, 1, 300], 32, 8, 80, 16, "fp8"),
+    (239, [513, 90, 1030], 16, 4, 96, 8, "fp8"),
+    (240, [260, 33, 1000, 7], 16, 2, 192, 32, "fp8"),
+    (241, [2050, 999, 513, 300], 16, 2, 256, 256, "fp8"),
+    (242, [129, 64, 3, 517], 24, 3, 112, 16, "fp8"),
+    (243, [1500, 2, 64], 12, 6, 80, 64, "bf16"),
 ]
 
 
@@ -365,6 +380,9 @@ def test_balanced_split_edge_cases(dt):
     ([2050, 999, 513, 300, 4096, 1], 64, 8, 128, 256, "bf16"),         # 256-slot blocks, 8 heads per KV head
     ([900, 1300, 20, 2500], 16, 1, 128, 128, "fp8"),                   # 16 heads on one KV head
     ([129, 4000, 31, 777, 64], 24, 12, 64, 32, "bf16"),                # 12 KV heads: two workgroups per run
+    ([0, 2300, 1, 700, 45, 0], 32, 4, 256, 16, "bf16"),                # K and V take turns through one slice
+    ([3, 1, 2, 17, 16, 15, 33, 64, 65] * 20, 16, 4, 192, 8, "fp8"),    # padded row lanes, many short sequences
+    ([900, 1300, 20, 2500], 16, 2, 80, 32, "bf16"),                    # zero-padded score contraction
 ])
 def test_gqa_balanced_split_parity(lens, hq, hkv, d, bs, dt):
     st = custom_structure("gbal", 443, lens, hq, hkv, d, bs, dt, pool_factor=1.2)
@@ -446,6 +464,20 @@ def test_full_workload_step(name):
         # copy-on-write leaves every output unchanged (bit for bit) against reading the shared blocks
         pre = decode(st, t, st.block_tables_pre, st.partition_size)
         np.testing.assert_array_equal(gpu, pre)
+
+
+@pytest.mark.parametrize("name", ["gqa_d256", "gqa_d256_fp8"])
+def test_full_size_head_dim_256(name):
+    # 64 sequences of 1k-4k tokens, 8 query heads per KV head of 256 dims, on the matrix cores, every output
+    # element against the oracle, for the library's plan and explicit partitions
+    st = build_structure(name)
+    t = materialize(st, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    ref = oracle_decode(st, h, st.block_tables_pre)
+    for part in (-1, 512, pa.PA_PARTITION_BALANCED):
+        gpu = decode(st, t, st.block_tables_pre, part)
+        err = assert_attention_close(gpu, ref, st.dtype, f"{name} partition {part}")
+        sys.__stderr__.write(f"[{name} partition {part}] max abs err {err:.3e}\n")
 
 
 # --------------------------------------------------------------------------------------------------------

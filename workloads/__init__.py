@@ -7,6 +7,7 @@ and the HIP library can both consume it without sharing any of the method's code
 
 from .decode import (  # noqa: F401
     CONFIG_NAMES,
+    EXTRA_NAMES,
     DecodeStructure,
     build_structure,
     custom_structure,

@@ -29,6 +29,8 @@ import numpy as np
 
 CONFIG_NAMES = ("tiny_fp32", "llama2_7b", "mixed_len", "mistral_gqa_prefix", "llama2_70b_gqa", "llama2_7b_fp8",
                 "llama2_70b_gqa_fp8")
+# further batches beside the configurations: grouped heads at head_dim 256 (8 query heads per KV head)
+EXTRA_NAMES = ("gqa_d256", "gqa_d256_fp8")
 
 _ESIZE = {"f32": 4, "bf16": 2, "fp8": 1}
 FP8_KV_SCALE = 1.0 / 64
@@ -190,9 +192,10 @@ def custom_structure(
 def build_structure(name: str, seed: int | None = None) -> DecodeStructure:
     """The synthetic decode workloads at their full sizes (seeds 1..7 by default). A name ending in "_fp8" is
     the structure of the workload without the suffix (same seed, same lengths and tables) over E4M3 caches."""
-    if name not in CONFIG_NAMES:
-        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_NAMES}")
-    idx = CONFIG_NAMES.index(name)
+    names = CONFIG_NAMES + EXTRA_NAMES
+    if name not in names:
+        raise KeyError(f"unknown workload {name!r}; known: {names}")
+    idx = names.index(name)
     if name.endswith("_fp8"):
         base = build_structure(name[: -len("_fp8")], seed)
         return dataclasses.replace(base, name=name, seed=idx + 1 if seed is None else seed, dtype="fp8",
@@ -219,6 +222,11 @@ def build_structure(name: str, seed: int | None = None) -> DecodeStructure:
         lens = np.full(128, 4096)
         return custom_structure(name, seed, lens, 32, 8, 128, 16, "bf16", pool_factor=1.1,
                                 shared_prefix_blocks=64, cow_seqs=32, max_context_len=4096, rng=rng)
+    if name == "gqa_d256":
+        # 64 sequences of 1024..4096 tokens, 32 query heads on 4 KV heads of 256 dims, 16-token blocks
+        lens = rng.integers(1024, 4096, size=64, endpoint=True)
+        return custom_structure(name, seed, lens, 32, 4, 256, 16, "bf16", pool_factor=1.1, max_context_len=4096,
+                                rng=rng)
     # llama2_70b_gqa
     lens = rng.integers(2048, 4096, size=64, endpoint=True)
     return custom_structure(name, seed, lens, 64, 8, 128, 256, "bf16", pool_factor=1.1,
