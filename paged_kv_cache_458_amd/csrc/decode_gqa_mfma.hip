@@ -228,64 +228,73 @@ __device__ __forceinline__ void gqa_stage(const U4 (*rb)[NL], char* slice, int w
   }
 }
 
-// The scores of one staged K tile through the matrix cores (E4M3 widened to bf16 after the LDS reads):
-// S^T = K Q^T, then the online-softmax update of (m, l) in the exp2 domain with positions >= `lim` masked unless
-// the whole tile is `full`, the rescale of the accumulator, and the tile's weights as the bf16 pair (pb, pl).
-template <int KV, int D>
-__device__ __forceinline__ void gqa_scores(const char* kread, const U4* qb, float scale_log2, int t, bool full,
-                                           int lim, int j, float& m, float& l, f32x4* o, U4& pb, U4& pl) {
+// The scores of one staged K tile through the matrix cores (E4M3 widened to bf16 after the LDS reads), for NCG
+// groups of 16 columns that share each K operand read: S^T = K Q^T, then each group's online-softmax update of
+// (m, l) in the exp2 domain with positions >= `lim` masked unless the whole tile is `full`, the rescale of its
+// accumulator, and its tile weights as the bf16 pair (pb, pl).
+template <int KV, int D, int NCG>
+__device__ __forceinline__ void gqa_scores(const char* kread, const U4 (*qb)[GqaShape<KV, D>::kChunks],
+                                           float scale_log2, int t, bool full, const int* lim, int j, float* m,
+                                           float* l, f32x4 (*o)[GqaShape<KV, D>::kNt], U4* pb, U4* pl) {
   using S = GqaShape<KV, D>;
-  f32x4 sc[2];
+  f32x4 sc[NCG][2];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
-    sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < S::kChunks; ++c)
-      sc[h2] = mfma(S::kRaw ? widen8(*reinterpret_cast<const u32x2*>(kread + h2 * kTile * S::kPitch + c * 32))
-                            : *reinterpret_cast<const U4*>(kread + h2 * kTile * S::kPitch + c * 64),
-                    qb[c], sc[h2]);
+    for (int k = 0; k < NCG; ++k) sc[k][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < S::kChunks; ++c) {
+      const U4 kop = S::kRaw ? widen8(*reinterpret_cast<const u32x2*>(kread + h2 * kTile * S::kPitch + c * 32))
+                             : *reinterpret_cast<const U4*>(kread + h2 * kTile * S::kPitch + c * 64);
+#pragma unroll
+      for (int k = 0; k < NCG; ++k) sc[k][h2] = mfma(kop, qb[k][c], sc[k][h2]);
+    }
   }
-  float sv[8];
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[h2 * 4 + i] = sc[h2][i] * scale_log2;
-  if (!full) {
-    // this lane's score (h2, i) is position t + h2 * kTile + 4j + i: masked from offset `rel` on
-    const int rel = lim - t - 4 * j;
+  for (int k = 0; k < NCG; ++k) {
+    float sv[8];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (h2 * kTile + i >= rel) sv[h2 * 4 + i] = -INFINITY;
-  }
-  float mt = -INFINITY;
+      for (int i = 0; i < 4; ++i) sv[h2 * 4 + i] = sc[k][h2][i] * scale_log2;
+    if (!full) {
+      // this lane's score (h2, i) is position t + h2 * kTile + 4j + i: masked from offset `rel` on
+      const int rel = lim[k] - t - 4 * j;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-  mt = max_over_rows(mt);
-  const float mn = fmaxf(m, mt);
-  const float mref = mn == -INFINITY ? 0.f : mn;
-  const float alpha = fast_exp2(m - mref);
-  m = mn;
-  float psum;
-  prob_operands(sv, mref, pb, pl, psum);
-  l = l * alpha + psum;
-  // Once the running maxima settle, alpha = exp2(0) is exactly 1 in every lane and the rescale would change
-  // nothing: it is skipped for the whole wave then.
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int nt = 0; nt < S::kNt; ++nt) {
-      o[nt][0] *= alpha;
-      o[nt][1] *= alpha;
-      o[nt][2] *= alpha;
-      o[nt][3] *= alpha;
+        for (int i = 0; i < 4; ++i)
+          if (h2 * kTile + i >= rel) sv[h2 * 4 + i] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+    mt = max_over_rows(mt);
+    const float mn = fmaxf(m[k], mt);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m[k] - mref);
+    m[k] = mn;
+    float psum;
+    prob_operands(sv, mref, pb[k], pl[k], psum);
+    l[k] = l[k] * alpha + psum;
+    // Once the running maxima settle, alpha = exp2(0) is exactly 1 in every lane and the rescale would change
+    // nothing: it is skipped for the whole wave then.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < S::kNt; ++nt) {
+        o[k][nt][0] *= alpha;
+        o[k][nt][1] *= alpha;
+        o[k][nt][2] *= alpha;
+        o[k][nt][3] *= alpha;
+      }
     }
   }
 }
 
-// O^T += V^T (P_hi + P_lo)^T over one staged V tile.
-template <int KV, int D>
-__device__ __forceinline__ void gqa_pv(const char* rbase, const U4& pb, const U4& pl, f32x4* o) {
+// O^T += V^T (P_hi + P_lo)^T over one staged V tile, for NCG groups of columns sharing each V^T operand read.
+template <int KV, int D, int NCG>
+__device__ __forceinline__ void gqa_pv(const char* rbase, const U4* pb, const U4* pl,
+                                       f32x4 (*o)[GqaShape<KV, D>::kNt]) {
   using S = GqaShape<KV, D>;
 #pragma unroll
   for (int nt = 0; nt < S::kNt; ++nt) {
@@ -299,17 +308,20 @@ __device__ __forceinline__ void gqa_pv(const char* rbase, const U4& pb, const U4
       const u32x2 hi = lds_read_tr16(rbase + kTile * S::kPitch + nt * 32);
       vt = U4{lo.x, lo.y, hi.x, hi.y};
     }
-    o[nt] = mfma(vt, pl, mfma(vt, pb, o[nt]));
+#pragma unroll
+    for (int k = 0; k < NCG; ++k) o[k][nt] = mfma(vt, pl[k], mfma(vt, pb[k], o[k][nt]));
   }
 }
 
 // Both products of one tile staged whole (K and V in their own slices).
-template <int KV, int D>
-__device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase, const U4* qb, float scale_log2,
-                                            int t, bool full, int lim, int j, float& m, float& l, f32x4* o) {
-  U4 pb, pl;
-  gqa_scores<KV, D>(kread, qb, scale_log2, t, full, lim, j, m, l, o, pb, pl);
-  gqa_pv<KV, D>(rbase, pb, pl, o);
+template <int KV, int D, int NCG>
+__device__ __forceinline__ void gqa_compute(const char* kread, const char* rbase,
+                                            const U4 (*qb)[GqaShape<KV, D>::kChunks], float scale_log2, int t,
+                                            bool full, const int* lim, int j, float* m, float* l,
+                                            f32x4 (*o)[GqaShape<KV, D>::kNt]) {
+  U4 pb[NCG], pl[NCG];
+  gqa_scores<KV, D, NCG>(kread, qb, scale_log2, t, full, lim, j, m, l, o, pb, pl);
+  gqa_pv<KV, D, NCG>(rbase, pb, pl, o);
 }
 
 // Q^T, the B operand of S^T = K Q^T, for a column whose query row starts at element `qe` of the bf16 query:
@@ -341,29 +353,33 @@ __device__ __forceinline__ void gqa_offsets(int rr, int rc, int64_t row_bytes, i
 
 // W waves (KV heads of one sequence) per workgroup: they stream the same slots of the pool side by side. At
 // least two waves per SIMD: with smaller workgroups the compiler would otherwise spend the register budget of
-// one (measured on MI355X with 4, 2 and 1 KV heads: 3-8% slower).
-template <int KV, int D, int W>
+// one (measured on MI355X with 4, 2 and 1 KV heads: 3-8% slower). A wave serves NCG consecutive groups of 16
+// columns (1, or 2 at head_dim <= 128 where the registers hold two accumulators): they share every K/V load and
+// every LDS operand read.
+template <int KV, int D, int W, int NCG>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const DecodeArgs a) {
   using S = GqaShape<KV, D>;
   constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
   constexpr int kRowLanes = S::kRowLanes, kLoads = S::kLoads;
+  // a wave may cover two partitions (parking the first one's state) only with one column group
+  constexpr bool kPark = S::kTwoParts && NCG == 1;
   __shared__ __attribute__((aligned(16))) char lds[W * S::kSlices * kSlice];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
-  // Work item (KV-head group, partition group, sequence) and column group cg (columns 16 cg .. 16 cg + 15).
-  // With one column group the grid indexes the item directly. With several, the groups of one item read the
-  // same K/V, so they are given workgroup ids 8 apart -- ids are dispatched in order and round-robin over the
-  // 8 XCDs, so those run back to back on one XCD and the later ones find the K/V in its L2.
+  // Work item (KV-head group, partition group, sequence) and the wave's column-group slot cg (columns
+  // 16 NCG cg .. 16 NCG (cg + 1) - 1). With one slot the grid indexes the item directly. With several, the slots
+  // of one item read the same K/V, so they are given workgroup ids 8 apart -- ids are dispatched in order and
+  // round-robin over the 8 XCDs, so those run back to back on one XCD and the later ones find the K/V in its L2.
+  const int nslots = (a.col_groups + NCG - 1) / NCG;
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z, cg = 0;
-  if (a.col_groups > 1) {
-    const int ncg = a.col_groups;
-    const int nkvg = gridDim.x / ncg;
+  if (nslots > 1) {
+    const int nkvg = gridDim.x / nslots;
     const int64_t lin = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
     const int64_t items = (int64_t)nkvg * gridDim.y * gridDim.z;
-    const int64_t base = lin / (8 * ncg) * 8;          // first item of this run of 8 x ncg workgroups
+    const int64_t base = lin / (8 * nslots) * 8;         // first item of this run of 8 x nslots workgroups
     const int64_t width = min<int64_t>(8, items - base);  // items in the run (fewer in the last one)
-    const int64_t r = lin - base * ncg;
+    const int64_t r = lin - base * nslots;
     cg = (int)(r / width);
     const int64_t u = base + r % width;
     bx = (int)(u % nkvg);
@@ -386,21 +402,26 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   const int G = a.group;
   const int n = lane & 15;  // MFMA column
   const int j = lane >> 4;  // 0..3
-  // Column n = qi * G + hh is head g * G + hh of the sequence's query row qi: in decode the sequence has one
-  // row (qi = 0, n < G). With several new tokens per sequence, row qi of its QL rows attends causally over the
-  // first L - QL + qi + 1 positions, and the columns hold G heads of up to 16 / G rows.
+  // Column c = qi * G + hh is head g * G + hh of the sequence's query row qi: in decode the sequence has one
+  // row (qi = 0, c < G). With several new tokens per sequence, row qi of its QL rows attends causally over the
+  // first L - QL + qi + 1 positions, and the columns hold G heads of the rows in groups of 16.
   int q0 = s, ql = 1;
   if (a.query_start) {
     q0 = a.query_start[s];
-    ql = min(max(a.query_start[s + 1] - q0, 0), a.max_query_len);
+    ql = rows_of_seq(a, s);
   }
-  const int col = cg * 16 + n;
-  const int qi = col / G;
-  const int hh = col - qi * G;
-  const int qrow = q0 + qi;  // the column's query row
-  const bool head_ok = qi < ql && qrow < a.num_tokens;
-  const int lim = head_ok ? min(u1, L - ql + qi + 1) : u0;  // the column attends over positions < lim
-  const int ufull = min(u1, L - ql + 1);                     // every column attends over positions < ufull
+  int qrow[NCG], hh[NCG], lim[NCG];
+  bool head_ok[NCG];
+#pragma unroll
+  for (int k = 0; k < NCG; ++k) {
+    const int col = (cg * NCG + k) * 16 + n;
+    const int qi = col / G;
+    hh[k] = col - qi * G;
+    qrow[k] = q0 + qi;  // the column's query row
+    head_ok[k] = qi < ql && qrow[k] < a.num_tokens;
+    lim[k] = head_ok[k] ? min(u1, L - ql + qi + 1) : u0;  // the column attends over positions < lim
+  }
+  const int ufull = min(u1, L - ql + 1);  // every column attends over positions < ufull
   const int rr = lane / kRowLanes;  // loads: row within a wave-wide load
   const int rc = lane % kRowLanes;  //        16-byte chunk within the row
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * kEsize;
@@ -409,8 +430,11 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   char* const vslice = S::kPhased ? kslice : kslice + kSlice;  // phased: V takes K's slice after the scores
 
   // Q^T (B operand of S^T = K Q^T): lane (n, j) holds dims 32c + 8j .. 32c + 8j + 7 of its column's query row
-  U4 qb[kChunks];
-  load_query_operand<D>(a.query, head_ok, ((int64_t)qrow * a.num_q_heads + (int64_t)g * G + hh) * D, j, qb);
+  U4 qb[NCG][kChunks];
+#pragma unroll
+  for (int k = 0; k < NCG; ++k)
+    load_query_operand<D>(a.query, head_ok[k], ((int64_t)qrow[k] * a.num_q_heads + (int64_t)g * G + hh[k]) * D, j,
+                          qb[k]);
 
   // per-lane byte offsets inside a 16-row half tile: each wave-wide load covers kRows whole head rows (full
   // cache lines: 256 bytes of bf16 or 128 of E4M3 at D = 128), for K as for V
@@ -422,10 +446,15 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
   const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[kNt];
+  float m[NCG], l[NCG];
+  f32x4 o[NCG][kNt];
 #pragma unroll
-  for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NCG; ++k) {
+    m[k] = -INFINITY;
+    l[k] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < kNt; ++nt) o[k][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   bool bad = false;
   const int ntiles = (u1 - u0 + kTileTok - 1) / kTileTok;
   const int last8 = ntiles > 0 ? ((u1 - 1) & ~(kTile / 2 - 1)) : u0;  // start of the last live 8-token group
@@ -454,39 +483,39 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // A wave covers at most two partitions. Finishing the first one mid-range only parks its state in
   // registers: any store inside the load loop would leave the compiler unable to count outstanding memory
   // operations, and it would then drain the load pipeline on every tile.
-  const int cut = min(u0 + a.partition, u1);  // end of the wave's first partition (u1 unless S::kTwoParts)
+  const int cut = min(u0 + a.partition, u1);  // end of the wave's first partition (u1 unless kPark)
   float m_first = -INFINITY, l_first = 0.f;
-  constexpr int kNtFirst = S::kTwoParts ? kNt : 1;
+  constexpr int kNtFirst = kPark ? kNt : 1;
   f32x4 o_first[kNtFirst];
 #pragma unroll
   for (int nt = 0; nt < kNtFirst; ++nt) o_first[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto park_first = [&]() {
-    if constexpr (!S::kTwoParts) return;
-    m_first = m;
-    l_first = l;
+    if constexpr (!kPark) return;
+    m_first = m[0];
+    l_first = l[0];
 #pragma unroll
-    for (int nt = 0; nt < kNtFirst; ++nt) o_first[nt] = o[nt];
-    m = -INFINITY;
-    l = 0.f;
+    for (int nt = 0; nt < kNtFirst; ++nt) o_first[nt] = o[0][nt];
+    m[0] = -INFINITY;
+    l[0] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kNt; ++nt) o[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // Normalise the span's G rows and write them: the output itself when the sequence fits one span, else
-  // partial p of the split workspace.
+  // Normalise the span's rows of column group k and write them: the output itself when the sequence fits one
+  // span, else partial p of the split workspace.
   const float poison = __uint_as_float(0x7fc00000u);
-  auto write_rows = [&](int p, float mp, float lp, const f32x4* op) {
+  auto write_rows = [&](int k, int p, float mp, float lp, const f32x4* op) {
     // each lane summed the probabilities of its own token group j; the max is already shared
     float lt = lp + __shfl_xor(lp, 16);
     lt += __shfl_xor(lt, 32);
-    if (!head_ok) return;
-    const int h = g * G + hh;
+    if (!head_ok[k]) return;
+    const int h = g * G + hh[k];
     const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
     float* dst;
     if (!a.split || L <= span) {
-      dst = a.out + ((int64_t)qrow * a.num_q_heads + h) * D;
+      dst = a.out + ((int64_t)qrow[k] * a.num_q_heads + h) * D;
     } else {
-      const int64_t wrow = ((int64_t)qrow * a.num_q_heads + h) * a.max_partitions + p;
+      const int64_t wrow = ((int64_t)qrow[k] * a.num_q_heads + h) * a.max_partitions + p;
       dst = a.ws_o + wrow * D;
       if (j == 0) {
         a.ws_ml[2 * wrow] = bad ? poison : mp;
@@ -512,36 +541,37 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
       if constexpr (S::kPhased) {
         wave_lds_sync();
         issue_v(tj);
-        U4 pb, pl;
-        gqa_scores<KV, D>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
+        U4 pb[NCG], pl[NCG];
+        gqa_scores<KV, D, NCG>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
         wave_lds_sync();
         gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
         wave_lds_sync();
         issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
-        gqa_pv<KV, D>(rbase, pb, pl, o);
+        gqa_pv<KV, D, NCG>(rbase, pb, pl, o);
       } else {
         gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
         wave_lds_sync();
         issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
-        gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
+        gqa_compute<KV, D, NCG>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
       }
       if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
     }
   }
-  if (S::kTwoParts && cut < u1) {
+  if (kPark && cut < u1) {
     // merge the first partition's state into the second's: one partial per wave
-    const float M = fmaxf(m_first, m);
+    const float M = fmaxf(m_first, m[0]);
     const float Mr = M == -INFINITY ? 0.f : M;
-    const float fa = fast_exp2(m_first - Mr), fb = fast_exp2(m - Mr);
-    l = l_first * fa + l * fb;
+    const float fa = fast_exp2(m_first - Mr), fb = fast_exp2(m[0] - Mr);
+    l[0] = l_first * fa + l[0] * fb;
 #pragma unroll
     for (int nt = 0; nt < kNtFirst; ++nt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[nt][e] = o_first[nt][e] * fa + o[nt][e] * fb;
-    m = M;
+      for (int e = 0; e < 4; ++e) o[0][nt][e] = o_first[nt][e] * fa + o[0][nt][e] * fb;
+    m[0] = M;
   }
   // an empty context writes a zero row (l = 0)
-  write_rows(by, m, l, o);
+#pragma unroll
+  for (int k = 0; k < NCG; ++k) write_rows(k, by, m[k], l[k], o[k]);
 }
 
 // Balanced split (one column group: the G heads of a KV head times at most 16 / G query rows per sequence). With
@@ -723,17 +753,19 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
       wave_lds_sync();
       issue_v(gi);
       U4 pb, pl;
-      gqa_scores<KV, D>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
+      gqa_scores<KV, D, 1>(kread, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
+                           (f32x4(*)[kNt])o, &pb, &pl);
       wave_lds_sync();
       gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
       wave_lds_sync();
       issue_next(gi);
-      gqa_pv<KV, D>(rbase, pb, pl, o);
+      gqa_pv<KV, D, 1>(rbase, &pb, &pl, (f32x4(*)[kNt])o);
     } else {
       gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
       wave_lds_sync();
       issue_next(gi);
-      gqa_compute<KV, D>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
+      gqa_compute<KV, D, 1>(kread, rbase, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
+                            (f32x4(*)[kNt])o);
     }
     bad |= bad_staged;
     if (gi + 1 < min(cs.p1, g1)) continue;
@@ -788,14 +820,23 @@ bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len
          columns >= 2 && columns <= 16 * kMaxColGroups;
 }
 
+template <int KV, int D, int W, int NCG>
+hipError_t launch_wc(const DecodeArgs& a, hipStream_t stream) {
+  if (a.parts_per_wave > (GqaShape<KV, D>::kTwoParts && NCG == 1 ? 2 : 1)) return hipErrorInvalidValue;
+  const int groups = a.split ? a.max_partitions : 1;  // one partial slot per wave span
+  // the waves' column-group slots share the x dimension with the KV-head groups (the kernel unpacks them)
+  const int nslots = (a.col_groups + NCG - 1) / NCG;
+  const dim3 grid((a.num_kv_heads + W - 1) / W * nslots, groups, a.num_seqs);
+  decode_gqa_mfma_kernel<KV, D, W, NCG><<<grid, dim3(kWave * W), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int KV, int D, int W>
 hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
-  if (a.parts_per_wave > (GqaShape<KV, D>::kTwoParts ? 2 : 1)) return hipErrorInvalidValue;
-  const int groups = a.split ? a.max_partitions : 1;  // one partial slot per wave span
-  // column groups share the x dimension with the KV-head groups (the kernel unpacks them)
-  const dim3 grid((a.num_kv_heads + W - 1) / W * a.col_groups, groups, a.num_seqs);
-  decode_gqa_mfma_kernel<KV, D, W><<<grid, dim3(kWave * W), 0, stream>>>(a);
-  return hipGetLastError();
+  if constexpr (D <= 128)
+    if (a.cg_per_wave == 2) return launch_wc<KV, D, W, 2>(a, stream);
+  if (a.cg_per_wave != 1) return hipErrorInvalidValue;
+  return launch_wc<KV, D, W, 1>(a, stream);
 }
 
 // KV heads per workgroup of either grouped-query kernel: up to 8 KV heads of a sequence; the LDS slices of 8

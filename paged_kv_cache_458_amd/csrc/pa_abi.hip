@@ -65,6 +65,7 @@ struct Plan {
   bool split = false;
   bool mfma = false;           // the matrix-core kernel runs (else the per-head one)
   int32_t col_groups = 1;      // its column groups of 16 per KV head
+  int32_t cg_per_wave = 1;     // column groups one wave of its partition kernel serves
   bool balanced = false;       // balanced split (equal runs of tiles per wave) of either kernel
   int32_t chunks = 0;          // its runs (per query head for the single-head kernel)
   size_t ws_bytes = 0;
@@ -74,9 +75,13 @@ struct Plan {
 
 // Consecutive partitions one wave of the GQA kernel covers (1 or 2): two when the caller asks for partitions
 // of 512..1023 tokens, so that a wave still streams about 1024 tokens. Needs partitions made of whole
-// 32-token tiles, and head_dim <= 128 (the registers that park the first partition's state).
-int32_t gqa_parts_per_wave(int32_t partition, int32_t head_dim) {
-  return head_dim <= 128 && partition >= 512 && partition < 1024 && partition % pa::kGqaTileTokens == 0 ? 2 : 1;
+// 32-token tiles, head_dim <= 128 and one column group per wave (the registers that park the first
+// partition's state).
+int32_t gqa_parts_per_wave(int32_t partition, int32_t head_dim, int32_t cg_per_wave) {
+  return head_dim <= 128 && cg_per_wave == 1 && partition >= 512 && partition < 1024 &&
+                 partition % pa::kGqaTileTokens == 0
+             ? 2
+             : 1;
 }
 
 // Library choice of partition size. A partition is the unit of work of one wave (the GQA kernel may take
@@ -93,12 +98,12 @@ int32_t gqa_parts_per_wave(int32_t partition, int32_t head_dim) {
 // The grouped-query kernel runs single pass when its grid already holds a wave per slot without splitting
 // (measured on MI355X: 13-15% faster for 7B-shaped verification batches, whose 2048 (sequence, head) waves
 // fill the chip; the single-head kernel's 4096-wave rule keeps its split there, 11-13% faster than without).
-int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa, int32_t head_dim) {
+int32_t pick_partition(int64_t rows, int32_t max_context_len, bool gqa, int32_t head_dim, int32_t cg_per_wave) {
   int32_t part = gqa ? 1024 : 512;
   const int64_t min_waves = gqa ? 2048 : 4096;
   if (gqa && rows >= min_waves) return 0;
   auto waves = [&](int32_t p) {
-    const int64_t span = (int64_t)p * (gqa ? gqa_parts_per_wave(p, head_dim) : 1);
+    const int64_t span = (int64_t)p * (gqa ? gqa_parts_per_wave(p, head_dim, cg_per_wave) : 1);
     return rows * ((max_context_len + span - 1) / span);
   };
   while (part > 64 && waves(part) < min_waves) part /= 2;
@@ -140,11 +145,13 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   const bool gqa = pa::gqa_mfma_supported(kv_dtype, head_dim, num_q_heads / num_kv_heads, max_query_len);
   p.mfma = gqa;
   p.col_groups = gqa ? (num_q_heads / num_kv_heads * max_query_len + 15) / 16 : 1;
+  p.cg_per_wave = gqa ? pa::gqa_cg_per_wave(p.col_groups, head_dim) : 1;
+  const int32_t slots = (p.col_groups + p.cg_per_wave - 1) / p.cg_per_wave;  // waves per (sequence, KV head)
   if ((int64_t)(num_kv_heads + 7) / 8 * p.col_groups > INT32_MAX) {
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
-  const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * p.col_groups : (int64_t)num_tokens * num_q_heads;
+  const int64_t rows = gqa ? (int64_t)num_seqs * num_kv_heads * slots : (int64_t)num_tokens * num_q_heads;
   // The balanced split needs rows (sequences, on the matrix-core kernel) one workgroup's LDS holds and tile
   // counts that fit 32 bits; on the matrix-core kernel also one column group.
   const int64_t listed = gqa ? num_seqs : num_tokens;  // items of the tile list
@@ -155,7 +162,8 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     p.status = PA_ERR_UNSUPPORTED;
     return p;
   }
-  int32_t part = partition_size == -1 ? pick_partition(rows, max_context_len, gqa, head_dim) : partition_size;
+  int32_t part =
+      partition_size == -1 ? pick_partition(rows, max_context_len, gqa, head_dim, p.cg_per_wave) : partition_size;
   const int64_t whole = round_up((size_t)(max_context_len > 0 ? max_context_len : 1), kTileTokens);
   // The library takes the balanced split wherever it would otherwise split the single-head kernel's contexts.
   // On the matrix cores it takes it only where the partitions would launch more than one round of resident
@@ -166,12 +174,13 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   const bool split_default = partition_size == -1 && balanced_ok && part > 0 && part < whole;
   const bool more_than_a_round =
       gqa && part > 0 &&
-      rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part, head_dim) - 1) /
-              ((int64_t)part * gqa_parts_per_wave(part, head_dim))) > pa::kResidentWaves;
+      rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part, head_dim, p.cg_per_wave) - 1) /
+              ((int64_t)part * gqa_parts_per_wave(part, head_dim, p.cg_per_wave))) > pa::kResidentWaves;
   // Spans under 1024 tokens leave the partitions' last, partial spans a larger share of the grid: measured on
   // MI355X, 64 sequences of 1k-4k tokens with 32 query heads on 4 KV heads of 256 dims (512-token spans, one
   // round) took 143.4 us in partitions against 121.9 us in the balanced split (E4M3 80.8 against 72.5).
-  const bool short_spans = gqa && part > 0 && (int64_t)part * gqa_parts_per_wave(part, head_dim) < 1024;
+  const bool short_spans =
+      gqa && part > 0 && (int64_t)part * gqa_parts_per_wave(part, head_dim, p.cg_per_wave) < 1024;
   // Several new tokens per sequence on the matrix cores: a single pass that fills a round of resident waves
   // leaves them unequal (each reads its sequence's whole context); equal runs gained 1-8% there (7B-shaped
   // batches of 2, 4 and 8 rows per sequence, bf16 and E4M3).
@@ -201,7 +210,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
     return p;
   }
   // one partial per wave span: a grouped-query wave that covers two partitions merges their states itself
-  p.parts_per_wave = gqa ? gqa_parts_per_wave(part, head_dim) : 1;
+  p.parts_per_wave = gqa ? gqa_parts_per_wave(part, head_dim, p.cg_per_wave) : 1;
   const int64_t span = (int64_t)part * p.parts_per_wave;
   const int64_t pm = (max_context_len + span - 1) / span;
   if (pm > kMaxGridYZ) {
@@ -386,6 +395,7 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   a.num_tokens = num_tokens;
   a.max_query_len = max_query_len;
   a.col_groups = plan.col_groups;
+  a.cg_per_wave = plan.cg_per_wave;
   a.chunks = plan.chunks;
   a.tile_prefix =
       plan.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_prefix_offset) : nullptr;

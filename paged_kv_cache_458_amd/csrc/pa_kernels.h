@@ -29,6 +29,8 @@ struct DecodeArgs {
   int32_t num_tokens;          // T
   int32_t max_query_len;       // query rows per sequence at most (1 without query_start)
   int32_t col_groups;          // matrix-core kernel: groups of 16 (query row, head) columns per KV head
+  int32_t cg_per_wave;         // matrix-core partition kernel: column groups one wave serves (1, or 2 when
+                               // head_dim <= 128)
   int32_t chunks;              // balanced split: runs of tiles per query head (0: partitions as above)
   int32_t* tile_prefix;        // balanced split: tiles of the rows before each row, [T + 1] (workspace) ...
   int32_t seq_prefix;          // ... or, when 1 (matrix-core kernel), of the sequences before each, [B + 1]
@@ -75,6 +77,9 @@ hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t
 // columns, in up to kMaxColGroups column groups (each reading the K/V once).
 constexpr int kMaxColGroups = 64;
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len);
+// Column groups one wave of the matrix-core partition kernel serves: 2 (two accumulators, every K/V load and LDS
+// operand read shared) where there are several and head_dim <= 128, else 1.
+inline int gqa_cg_per_wave(int col_groups, int head_dim) { return col_groups >= 2 && head_dim <= 128 ? 2 : 1; }
 constexpr int kGqaTileTokens = 32;  // tokens per tile of the GQA kernel
 hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream);
 // Balanced split of the single-head kernel: the tiles of all query rows, in row order, cut into `chunks`

@@ -201,16 +201,19 @@ def test_workspace_and_partition_plan():
 
 def test_grouped_query_default_counts_waves_per_span():
     # the partition rule, seen where the balanced split does not apply (8 new tokens per sequence x 4 heads = 32
-    # columns per KV head: two column groups, so 16 waves per sequence): 512-token partitions go two to a
-    # grouped-query wave, so where 1024 leaves fewer than 2048 waves, 512 would leave the same number and the
-    # default goes on to 256
+    # columns per KV head: two column groups, which one wave serves, so 8 waves per sequence, and partitions one
+    # to a wave since that wave holds two accumulators): 1024 halves while the grid holds fewer than 2048 waves
     def multi(B, *args):
         return pa.multi_partition_size_for(B, 8 * B, 8, *args)
     assert multi(32, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
-    assert multi(8, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 128
-    # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head, group) waves run single pass
-    assert multi(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
-    assert multi(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+    assert multi(8, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 64
+    assert multi(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 512
+    # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head, wave) triples run single
+    # pass
+    assert multi(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
+    assert multi(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+    # at head_dim 256 a wave serves one column group: 16 waves per sequence
+    assert multi(8, 32, 8, 256, 16, 2048, pa.PA_BF16, -1) == 128
     assert pa.load_library().paged_attention_multi_partition_size(
         32, 256, 8, 32, 8, 128, 16, 2048, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == PA_ERR_UNSUPPORTED
 
