@@ -36,17 +36,27 @@ struct DecodeArgs {
   int32_t seq_prefix;          // ... or, when 1 (matrix-core kernel), of the sequences before each, [B + 1]
 };
 
-// The sequence that owns query row t: the last s with query_start[s] <= t (a scalar binary search; empty
-// sequences are skipped since the next start equals theirs).
+// The sequence that owns query row t: the last s with query_start[s] <= t (empty sequences are skipped since the
+// next start equals theirs). Called by a whole wave with one t: the entries <= t form a prefix of the
+// non-decreasing query_start, so each lane compares one entry of a window and a ballot counts the prefix. A
+// window of up to 64 entries takes one round of loads; a longer one is first narrowed by sampling it at a
+// stride (64 sequences: one round of loads where a binary search takes six dependent ones; 4096: two).
 __device__ __forceinline__ int seq_of_row(const DecodeArgs& a, int t) {
   if (!a.query_start) return t;
-  int lo = 0, hi = a.num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.query_start[mid] <= t) lo = mid;
-    else hi = mid;
+  const int lane = __lane_id();
+  int lo = 0, n = a.num_seqs;  // the owner lies in [lo, lo + n)
+  while (n > 64) {
+    const int stride = (n + 63) / 64;
+    const int idx = lo + lane * stride;
+    const bool le = lane * stride < n && a.query_start[idx] <= t;
+    // at least 1 (query_start[lo] <= t); kept so even for contents that break the contract
+    const int k = max(__builtin_popcountll(__builtin_amdgcn_ballot_w64(le)), 1);
+    lo += (k - 1) * stride;
+    n = min(stride, n - (k - 1) * stride);
   }
-  return lo;
+  const bool le = lane < n && a.query_start[lo + lane] <= t;
+  const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+  return lo + max(k, 1) - 1;
 }
 
 // Query rows of sequence s as every kernel takes them: query_start[s + 1] - query_start[s], clamped to

@@ -172,3 +172,19 @@ def test_rows_past_max_query_len_are_clamped_alike(hq, hkv, d, dt):
         gpu = out.cpu().numpy()
         close(gpu[keep], ref, dt, f"partition {part}")
         assert np.isnan(gpu[[4, 5]]).all(), f"partition {part}: rows past max_query_len were written"
+
+
+@pytest.mark.parametrize("dt,hq,hkv", [("f32", 2, 2), ("bf16", 8, 2)])
+def test_row_lookup_over_many_sequences(dt, hq, hkv):
+    # 5000 sequences bring 0..3 rows each: every merge and per-head wave finds its row's sequence by narrowing
+    # query_start in windows of 64 entries (three rounds here), including past empty sequences
+    rng = np.random.default_rng(522)
+    lens = rng.integers(1, 40, size=5000)
+    qls = np.minimum(rng.integers(0, 4, size=5000), lens)
+    st = custom_structure("many", 522, lens, hq, hkv, 64, 16, dt, pool_factor=1.05)
+    t = materialize(st, DEV)
+    q, qs = query_rows(st, qls, DEV)
+    h = {k: to_host(v) for k, v in t.items()}
+    ref = oracle_multi(st, h, to_host(q), qs)
+    for part in (0, 16, -1):
+        close(run_multi(st, t, q, qs, part), ref, dt, f"partition {part}")
