@@ -126,8 +126,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *                  G <= 16 heads per KV head; PA_ERR_UNSUPPORTED otherwise); -1 = the library chooses
  *                  (paged_attention_partition_size): the balanced split wherever the single-head kernel would
  *                  otherwise split its contexts, and on the matrix cores wherever its partitions would launch
- *                  more than one round of 2048 resident waves or give a wave fewer than 1024 tokens;
- *                  partitions otherwise
+ *                  more than one round of 2048 resident waves; partitions otherwise
  *   workspace      device scratch of at least paged_attention_workspace_bytes(...) bytes when that is
  *                  non-zero (may be NULL otherwise); contents need no initialisation and are clobbered
  *   stream         hipStream_t

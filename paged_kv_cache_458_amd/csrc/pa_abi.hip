@@ -176,18 +176,12 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
       gqa && part > 0 &&
       rows * ((max_context_len + (int64_t)part * gqa_parts_per_wave(part, head_dim, p.cg_per_wave) - 1) /
               ((int64_t)part * gqa_parts_per_wave(part, head_dim, p.cg_per_wave))) > pa::kResidentWaves;
-  // Spans under 1024 tokens leave the partitions' last, partial spans a larger share of the grid: measured on
-  // MI355X, 64 sequences of 1k-4k tokens with 32 query heads on 4 KV heads of 256 dims (512-token spans, one
-  // round) took 143.4 us in partitions against 121.9 us in the balanced split (E4M3 80.8 against 72.5).
-  const bool short_spans =
-      gqa && part > 0 && (int64_t)part * gqa_parts_per_wave(part, head_dim, p.cg_per_wave) < 1024;
   // Several new tokens per sequence on the matrix cores: a single pass that fills a round of resident waves
   // leaves them unequal (each reads its sequence's whole context); equal runs gained 1-8% there (7B-shaped
   // batches of 2, 4 and 8 rows per sequence, bf16 and E4M3).
   const bool uneven_pass = gqa && max_query_len > 1 && partition_size == -1 && balanced_ok &&
                            (part == 0 || part >= whole) && rows >= pa::kResidentWaves;
-  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round || short_spans)) ||
-      uneven_pass) {
+  if (partition_size == PA_PARTITION_BALANCED || (split_default && (!gqa || more_than_a_round)) || uneven_pass) {
     p.balanced = true;
     p.split = true;
     p.chunks = gqa ? pa::gqa_balanced_chunks(num_kv_heads)

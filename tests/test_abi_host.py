@@ -424,12 +424,12 @@ def test_noalloc_scratch_limit_matches_the_workspace_rule():
     assert noalloc_call(num_seqs=0) == 0  # nothing to do: no-op
 
 
-def test_grouped_query_default_prefers_the_balanced_split_for_short_spans():
+def test_grouped_query_default_partitions_within_one_round():
     lib = pa.load_library()
-    # 64 sequences of up to 4096 tokens, 32 query heads on 4 KV heads of 256 dims: 512-token spans (one wave
-    # per partition at head_dim > 128) fill one round, but spans under 1024 tokens take the balanced split
-    assert lib.paged_attention_partition_size(64, 32, 4, 256, 16, 4096, pa.PA_BF16, -1) == pa.PA_PARTITION_BALANCED
-    # the 70B shape keeps its partitions: 1024-token spans, one round of 2048 waves
+    # 64 sequences of up to 4096 tokens, 32 query heads on 4 KV heads of 256 dims: 512-token partitions (one per
+    # wave at head_dim > 128) fill one round of workgroups, which the kernel spreads over the XCDs by sequence
+    assert lib.paged_attention_partition_size(64, 32, 4, 256, 16, 4096, pa.PA_BF16, -1) == 512
+    # the 70B shape: 1024-token spans, one round of 2048 waves
     assert lib.paged_attention_partition_size(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
     # grouped heads at every served head dim plan on the matrix cores (workspace of the balanced split with
     # one partial slot per query head and run, not per query row)
