@@ -85,7 +85,7 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
  * Balanced split: partials [num_q_heads][R][2][head_dim] fp32 and their pairs, then (query rows + 1) int32
  * tile counts, for R runs. On the single-head kernel R = 1024 / ceil(ceil(num_q_heads / H) / 2) per head,
  * where a wave takes H = 2 adjacent heads if head rows are 64 or 128 bytes (E4M3 at head_dim 64 or 128, bf16
- * at 64) and num_q_heads == num_kv_heads, else H = 1. On the matrix-core kernel (grouped heads)
+ * at 64) or bf16 rows of 256 bytes (head_dim 128), and num_q_heads == num_kv_heads, else H = 1. On the matrix-core kernel (grouped heads)
  * R = 2048 / (num_kv_heads rounded up to whole workgroups of W = min(8, largest power of two <= num_kv_heads)
  * KV heads). R is at least 1 either way.
  */

@@ -37,8 +37,8 @@ struct Shape {
   static constexpr int kSumLanes = HPW == 1 ? kRowLanes : kHeadLanes;  // lanes one dot product is summed over
   static constexpr int kRows = kWave / kRowLanes;        // slots per wave-wide load
   // tokens per tile: at most 4 loads per lane for K (and for V), 2 with two heads per wave (the same bytes in
-  // flight per wave as one head), at most 16 tokens
-  static constexpr int kMaxLoads = HPW == 1 ? 4 : 2;
+  // flight per wave as one head; 4 where two heads' rows take 512 bytes, two rows per load), at most 16 tokens
+  static constexpr int kMaxLoads = HPW == 1 || kRows == 2 ? 4 : 2;
   static constexpr int kTileTok = kRows * kMaxLoads < kTile ? kRows * kMaxLoads : kTile;
   static constexpr int kLoads = kTileTok / kRows;        // loads per tile (per K and per V)
   static_assert(D % kEpl == 0 && kRowLanes <= kWave, "head_dim must fill whole 16-byte chunks");
@@ -794,7 +794,7 @@ hipError_t launch_balanced_kv(const DecodeArgs& a, int hpw, dim3 grid, dim3 bloc
     case 96: decode_valu_balanced_kernel<KV, 96, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
     case 112: decode_valu_balanced_kernel<KV, 112, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
     case 128:
-      if constexpr (KV == PA_FP8_E4M3)
+      if constexpr (KV != PA_F32)
         if (hpw == 2) {
           decode_valu_balanced_kernel<KV, 128, kMulti, 2><<<grid, block, lds, stream>>>(a);
           break;
@@ -818,7 +818,7 @@ hipError_t launch_balanced_dtype(const DecodeArgs& a, int hpw, dim3 grid, dim3 b
 
 int valu_heads_per_wave(int kv_dtype, int head_dim, int group) {
   const int row_bytes = head_dim * (kv_dtype == PA_F32 ? 4 : kv_dtype == PA_BF16 ? 2 : 1);
-  return group == 1 && (row_bytes == 64 || row_bytes == 128) ? 2 : 1;
+  return group == 1 && (row_bytes == 64 || row_bytes == 128 || (row_bytes == 256 && kv_dtype == PA_BF16)) ? 2 : 1;
 }
 
 int32_t balanced_chunks(int32_t num_q_heads, int32_t heads_per_wave) {

@@ -265,11 +265,12 @@ def test_balanced_split_plan():
     B = pa.PA_PARTITION_BALANCED
     # the library takes the balanced split where the single-head kernel would split its contexts
     assert pa.partition_size_for(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == B
-    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == balanced_ws(64, 32, 128)
+    # (bf16 rows of 256 bytes: two heads per wave, half the waves per run, twice the runs)
+    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == balanced_ws(64, 32, 128, 2)
     assert pa.workspace_bytes(7, 5, 5, 80, 16, 900, pa.PA_FP8_E4M3, B) == balanced_ws(7, 5, 80)
     assert pa.workspace_bytes(3, 4096, 4096, 64, 16, 900, pa.PA_F32, B) == balanced_ws(3, 4096, 64)  # one run
-    # two heads per wave where head rows are 64 or 128 bytes and every query head has its own KV head: half
-    # the waves per run, twice the runs
+    # two heads per wave where head rows are 64 or 128 bytes (or 256 bytes of bf16) and every query head has its
+    # own KV head: half the waves per run, twice the runs
     assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_FP8_E4M3, B) == balanced_ws(64, 32, 128, 2)
     assert pa.workspace_bytes(9, 5, 5, 64, 16, 900, pa.PA_BF16, B) == balanced_ws(9, 5, 64, 2)
     assert pa.workspace_bytes(9, 8, 4, 64, 16, 900, pa.PA_F32, B) == balanced_ws(9, 8, 64)

@@ -336,6 +336,8 @@ def test_empty_context_bad_entries_and_clamped_lengths():
     ([3, 1, 2, 17, 16, 15, 33] * 9, 5, 128, "fp8"),        # odd head count: the last wave holds one head
     ([900, 1300, 20, 2500], 6, 64, "bf16"),                # bf16 128-byte rows
     ([5000], 2, 64, "fp8"),                                # E4M3 64-byte rows, one row cut into many runs
+    ([3, 1, 2, 17, 16, 15, 33] * 9, 5, 128, "bf16"),       # bf16 256-byte rows, odd head count: 8-token tiles
+    ([4000, 1, 0, 900], 4, 128, "bf16"),                   # a row cut into many runs, 512-byte pieces
 ])
 def test_balanced_split_parity(lens, hq, d, dt):
     st = custom_structure("bal", 441, lens, hq, hq, d, 16, dt, pool_factor=1.2)
