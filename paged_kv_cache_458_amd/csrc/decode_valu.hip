@@ -321,9 +321,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kSpec = 16;  // partitions whose outputs are loaded up front
-
-template <int D>
+// kSpec is the smallest of 4, 8 and 16 that covers the longest row's partitions (16 past that): with the clamped
+// indexes a larger kSpec would only repeat the last slot's loads, which for short grids of many rows (several
+// new tokens per sequence, a few partitions each) was the bulk of the merge's time.
+template <int D, int kSpec>
 __global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
   constexpr int kDpl = (D + kWave - 1) / kWave;  // dims per lane
   constexpr int kActive = D / kDpl;              // lanes holding dims (all of them when 64 divides D)
@@ -855,20 +856,27 @@ hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
+template <int kSpec>
+hipError_t launch_lse_reduce_spec(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.num_tokens);
   const dim3 block(kWave);
   switch (a.head_dim) {
-    case 64: lse_reduce_kernel<64><<<grid, block, 0, stream>>>(a); break;
-    case 80: lse_reduce_kernel<80><<<grid, block, 0, stream>>>(a); break;
-    case 96: lse_reduce_kernel<96><<<grid, block, 0, stream>>>(a); break;
-    case 112: lse_reduce_kernel<112><<<grid, block, 0, stream>>>(a); break;
-    case 128: lse_reduce_kernel<128><<<grid, block, 0, stream>>>(a); break;
-    case 192: lse_reduce_kernel<192><<<grid, block, 0, stream>>>(a); break;
-    case 256: lse_reduce_kernel<256><<<grid, block, 0, stream>>>(a); break;
+    case 64: lse_reduce_kernel<64, kSpec><<<grid, block, 0, stream>>>(a); break;
+    case 80: lse_reduce_kernel<80, kSpec><<<grid, block, 0, stream>>>(a); break;
+    case 96: lse_reduce_kernel<96, kSpec><<<grid, block, 0, stream>>>(a); break;
+    case 112: lse_reduce_kernel<112, kSpec><<<grid, block, 0, stream>>>(a); break;
+    case 128: lse_reduce_kernel<128, kSpec><<<grid, block, 0, stream>>>(a); break;
+    case 192: lse_reduce_kernel<192, kSpec><<<grid, block, 0, stream>>>(a); break;
+    case 256: lse_reduce_kernel<256, kSpec><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_lse_reduce(const DecodeArgs& a, hipStream_t stream) {
+  if (a.max_partitions <= 4) return launch_lse_reduce_spec<4>(a, stream);
+  if (a.max_partitions <= 8) return launch_lse_reduce_spec<8>(a, stream);
+  return launch_lse_reduce_spec<16>(a, stream);
 }
 
 }  // namespace pa
