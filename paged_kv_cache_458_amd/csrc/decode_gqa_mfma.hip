@@ -547,31 +547,38 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     }
   };
 
+  auto tile_step = [&](int tj) {
+    const int t = u0 + tj * kTileTok;
+    const bool full = t + kTileTok <= ufull;  // no column masks a position of a tile below ufull
+    wave_lds_sync();  // the previous tile's reads come first
+    gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
+    if constexpr (S::kPhased) {
+      wave_lds_sync();
+      issue_v(tj);
+      U4 pb[NCG], pl[NCG];
+      gqa_scores<KV, D, NCG>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
+      wave_lds_sync();
+      gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
+      wave_lds_sync();
+      issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
+      gqa_pv<KV, D, NCG>(rbase, pb, pl, o);
+    } else {
+      gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
+      wave_lds_sync();
+      issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
+      gqa_compute<KV, D, NCG>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
+    }
+  };
   if (ntiles > 0) {
     issue_kv(0);
-    for (int tj = 0; tj < ntiles; ++tj) {
-      const int t = u0 + tj * kTileTok;
-      const bool full = t + kTileTok <= ufull;  // no column masks a position of a tile below ufull
-      wave_lds_sync();  // the previous tile's reads come first
-      gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
-      if constexpr (S::kPhased) {
-        wave_lds_sync();
-        issue_v(tj);
-        U4 pb[NCG], pl[NCG];
-        gqa_scores<KV, D, NCG>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
-        wave_lds_sync();
-        gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
-        wave_lds_sync();
-        issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
-        gqa_pv<KV, D, NCG>(rbase, pb, pl, o);
-      } else {
-        gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
-        wave_lds_sync();
-        issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
-        gqa_compute<KV, D, NCG>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
-      }
-      if (t + kTileTok == cut && cut < u1) park_first();  // the tile ends the first of two partitions
-    }
+    // The tiles of the first partition, the park, then the rest: two loops around one pipeline. (A park taken
+    // conditionally inside a single loop made the compiler copy every accumulator and parked register on each
+    // tile, about 100 moves per tile.)
+    const int ncut = kPark && cut < u1 ? (cut - u0) / kTileTok : ntiles;
+    int tj = 0;
+    for (; tj < ncut; ++tj) tile_step(tj);
+    if (kPark && cut < u1) park_first();  // the tile before ends the first of two partitions
+    for (; tj < ntiles; ++tj) tile_step(tj);
   }
   if (kPark && cut < u1) {
     // merge the first partition's state into the second's: one partial per wave
