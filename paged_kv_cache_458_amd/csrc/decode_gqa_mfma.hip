@@ -763,38 +763,43 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   };
 
   issue_kv(g0);
-  for (int gi = g0; gi < g1; ++gi) {
-    const int cu0 = (max(g0, cs.p0) - cs.p0) * kTileTok;  // the segment's first position
-    const int t = (gi - cs.p0) * kTileTok;
-    const int lim = head_ok ? lim0 : cu0;
-    const bool full = t + kTileTok <= ufull;
-    wave_lds_sync();  // the previous tile's reads come first
-    gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
-    bad_staged = bad_issued;
-    bad_issued = false;
-    if constexpr (S::kPhased) {
-      wave_lds_sync();
-      issue_v(gi);
-      U4 pb, pl;
-      gqa_scores<KV, D, 1>(kread, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
-                           (f32x4(*)[kNt])o, &pb, &pl);
-      wave_lds_sync();
-      gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
-      wave_lds_sync();
-      issue_next(gi);
-      gqa_pv<KV, D, 1>(rbase, &pb, &pl, (f32x4(*)[kNt])o);
-    } else {
-      gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
-      wave_lds_sync();
-      issue_next(gi);
-      gqa_compute<KV, D, 1>(kread, rbase, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
-                            (f32x4(*)[kNt])o);
+  // Segments in an outer loop, their tiles in an inner one. (Closing a segment conditionally inside one tile loop
+  // made the compiler copy every accumulator on each tile, as in the partition kernel.)
+  int gi = g0;
+  while (true) {
+    const int gend = min(cs.p1, g1);  // the segment's tiles in this run end here
+    for (; gi < gend; ++gi) {
+      const int cu0 = (max(g0, cs.p0) - cs.p0) * kTileTok;  // the segment's first position
+      const int t = (gi - cs.p0) * kTileTok;
+      const int lim = head_ok ? lim0 : cu0;
+      const bool full = t + kTileTok <= ufull;
+      wave_lds_sync();  // the previous tile's reads come first
+      gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
+      bad_staged = bad_issued;
+      bad_issued = false;
+      if constexpr (S::kPhased) {
+        wave_lds_sync();
+        issue_v(gi);
+        U4 pb, pl;
+        gqa_scores<KV, D, 1>(kread, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
+                             (f32x4(*)[kNt])o, &pb, &pl);
+        wave_lds_sync();
+        gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
+        wave_lds_sync();
+        issue_next(gi);
+        gqa_pv<KV, D, 1>(rbase, &pb, &pl, (f32x4(*)[kNt])o);
+      } else {
+        gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
+        wave_lds_sync();
+        issue_next(gi);
+        gqa_compute<KV, D, 1>(kread, rbase, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
+                              (f32x4(*)[kNt])o);
+      }
+      bad |= bad_staged;
     }
-    bad |= bad_staged;
-    if (gi + 1 < min(cs.p1, g1)) continue;
 
-    // the segment's last tile: its rows, whole in this run -> out; else the run's partial for row qi in slot 0
-    // (the run starts inside the sequence) or slot 1 (it ends inside it)
+    // the segment's last tile is done: its rows, whole in this run -> out; else the run's partial for row qi in
+    // slot 0 (the run starts inside the sequence) or slot 1 (it ends inside it)
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     if (head_ok) {
@@ -819,7 +824,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
                 : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
       }
     }
-    if (gi + 1 >= g1) break;
+    if (gi >= g1) break;
     // the next segment: the one the issue cursor opened
     cs = is;
 #pragma unroll
