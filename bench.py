@@ -450,7 +450,7 @@ def main() -> int:
         for name in CONFIG_NAMES:
             cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(args.steps),
                    "--warmup", str(args.warmup), "--replicas", str(args.replicas), "--cpu-seconds",
-                   str(args.cpu_seconds)]
+                   str(args.cpu_seconds), "--no-configs"]
             log(f"configs: {name}")
             rc = rc or subprocess.run(cmd).returncode
         return rc

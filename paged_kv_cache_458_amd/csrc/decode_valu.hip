@@ -306,7 +306,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
 
 // Merge of split-context partials: with partition p giving running max m_p (log2 units), sum l_p and
 // normalised output o_p, out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - max_p m_p). One wave per
-// (sequence, head): lane p owns partition p's weight, and every lane accumulates its own head_dim / 64 dims.
+// (query row, head), four heads' waves to a workgroup (both merge kernels: a quarter of the workgroups to launch,
+// 7B-shaped balanced merge 4.9 -> 4.3 us): lane p owns partition p's weight, and every lane accumulates its own
+// head_dim / 64 dims.
 // The kernel is latency-bound, so the (max, sum) pairs and the first kSpec partitions' outputs are loaded
 // before the context length is known (slots past the row's partition count hold stale values and are never
 // combined: the loops below stop at the count).
@@ -325,13 +327,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 // indexes a larger kSpec would only repeat the last slot's loads, which for short grids of many rows (several
 // new tokens per sequence, a few partitions each) was the bulk of the merge's time.
 template <int D, int kSpec>
-__global__ __launch_bounds__(kWave) void lse_reduce_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kWave * 4) void lse_reduce_kernel(const DecodeArgs a) {
   constexpr int kDpl = (D + kWave - 1) / kWave;  // dims per lane
   constexpr int kActive = D / kDpl;              // lanes holding dims (all of them when 64 divides D)
   static_assert(D % kDpl == 0, "whole dims per lane");
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const bool lane_ok = lane < kActive;  // the other lanes read lane 0's dims and store nothing
-  const int h = blockIdx.x;
+  const int h = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (h >= a.num_q_heads) return;
   const int row = blockIdx.y;  // query row
   const int s = seq_of_row(a, row);
   const int pm = a.max_partitions;
@@ -684,12 +687,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
 // attends over nothing and its rows get a zero row here; an item spanning runs c0 .. c1 has the partial of run
 // c0 on side 1 (side 0 when it starts exactly at c0's first tile) and those of runs c0 + 1 .. c1 on side 0.
 template <int D>
-__global__ __launch_bounds__(kWave) void balanced_reduce_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kWave * 4) void balanced_reduce_kernel(const DecodeArgs a) {
   constexpr int kDpl = (D + kWave - 1) / kWave;
   constexpr int kActive = D / kDpl;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const bool lane_ok = lane < kActive;
-  const int h = blockIdx.x;
+  const int h = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (h >= a.num_q_heads) return;
   const int row = blockIdx.y;
   // sizes taken as values (a select between two fields of the argument block went through scratch memory)
   const bool by_seq = a.seq_prefix != 0;
@@ -841,8 +845,8 @@ hipError_t launch_decode_valu_balanced(const DecodeArgs& a, int kv_dtype, hipStr
 }
 
 hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_q_heads, a.num_tokens);
-  const dim3 block(kWave);
+  const dim3 grid((a.num_q_heads + 3) / 4, a.num_tokens);
+  const dim3 block(kWave * 4);
   switch (a.head_dim) {
     case 64: balanced_reduce_kernel<64><<<grid, block, 0, stream>>>(a); break;
     case 80: balanced_reduce_kernel<80><<<grid, block, 0, stream>>>(a); break;
@@ -858,8 +862,8 @@ hipError_t launch_balanced_reduce(const DecodeArgs& a, hipStream_t stream) {
 
 template <int kSpec>
 hipError_t launch_lse_reduce_spec(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_q_heads, a.num_tokens);
-  const dim3 block(kWave);
+  const dim3 grid((a.num_q_heads + 3) / 4, a.num_tokens);
+  const dim3 block(kWave * 4);
   switch (a.head_dim) {
     case 64: lse_reduce_kernel<64, kSpec><<<grid, block, 0, stream>>>(a); break;
     case 80: lse_reduce_kernel<80, kSpec><<<grid, block, 0, stream>>>(a); break;
