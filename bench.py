@@ -487,9 +487,9 @@ def main() -> int:
     T = B * Q  # query rows
     label = args.workload if Q == 1 else f"{args.workload}_q{Q}"
     if Q == 1:
-        launched_part = pa.partition_size_for(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+        launched_part = pa.partition_size_for(B, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
     else:
-        launched_part = pa.multi_partition_size_for(B, T, Q, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+        launched_part = pa.multi_partition_size_for(B, T, Q, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
 
     t = materialize(st, dev, include_new_token=False)
     pools = [(t["key_cache"], t["value_cache"])]
@@ -519,9 +519,9 @@ def main() -> int:
         kdt = torch.float32 if st.dtype == "f32" else torch.bfloat16
         new_key = torch.randn((T, Hkv, D), generator=gen, device=dev).to(kdt)
         new_value = torch.randn((T, Hkv, D), generator=gen, device=dev).to(kdt)
-        ws_bytes = pa.multi_workspace_bytes(B, T, Q, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+        ws_bytes = pa.multi_workspace_bytes(B, T, Q, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
     else:
-        ws_bytes = pa.workspace_bytes(B, Hq, Hkv, D, bs, st.max_context_len, kv_code, part)
+        ws_bytes = pa.workspace_bytes(B, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 

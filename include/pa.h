@@ -1,5 +1,5 @@
 /*
- * paged_attention.h -- C ABI of libpagedattn.so, the MI355X (gfx950) paged decode attention library.
+ * pa.h -- C ABI of libpagedattn.so, the MI355X (gfx950) paged decode attention library.
  *
  * The paged KV cache (vLLM PagedAttention, page 1 "LLM inference framework evaluation ...", section 3.2):
  * keys and values live in two global block pools, each laid out as
@@ -24,8 +24,8 @@
  *    max_context_len, and out-of-range slots or copy pairs are skipped.
  *  - Pointers must be 16-byte aligned (PA_ERR_ALIGN otherwise).
  */
-#ifndef PAGED_ATTENTION_H
-#define PAGED_ATTENTION_H
+#ifndef PA_H
+#define PA_H
 
 #include <stddef.h>
 #include <stdint.h>
@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 /* dtype codes */
 #define PA_F32 0
@@ -66,18 +66,20 @@ int pa_abi_version(void);
 const char *pa_strerror(int status);
 
 /*
- * Partition size (in tokens) that paged_attention_decode uses for a given `partition_size` argument:
+ * Partition size (in tokens) that paged_attention_decode uses for a given `partition_size` argument (arguments
+ * in the order of paged_attention_workspace_bytes: max_context_len, then block_size):
  * 0 stays 0 (single pass), a positive value is returned unchanged, -1 is replaced by the library's choice
  * for these sizes (PA_PARTITION_BALANCED when that is the balanced split). Returns a negative status for an
  * invalid request.
  */
 int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t head_dim, int32_t max_context_len, int32_t block_size,
                                        int32_t kv_dtype, int32_t partition_size);
 
 /*
  * Bytes of workspace paged_attention_decode needs for these sizes (0 when the call runs single pass).
- * Arguments as in paged_attention_decode. Returns 0 as well for invalid sizes (the decode call reports them).
+ * Arguments mean what they mean in paged_attention_decode; note the order here: max_context_len, then
+ * block_size. Returns 0 as well for invalid sizes (the decode call reports them).
  * Split into partitions of P tokens: partials [num_seqs][num_q_heads][ceil(max_context_len / S)][head_dim]
  * fp32, then their (max, sum) pairs, each part 256-byte aligned, where S = P, or S = 2P when grouped heads run
  * on the matrix cores at head_dim <= 128 with 512 <= P < 1024 (one wave covers two partitions and merges them
@@ -90,7 +92,7 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
  * KV heads). R is at least 1 either way.
  */
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t head_dim, int32_t max_context_len, int32_t block_size,
                                        int32_t kv_dtype, int32_t partition_size);
 
 /*
@@ -217,11 +219,11 @@ int paged_attention_decode_multi(float *out, const void *query, const void *key_
 /* Partition size and workspace bytes of paged_attention_decode_multi, as the decode forms above. */
 int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t max_context_len, int32_t block_size, int32_t kv_dtype,
                                              int32_t partition_size);
 size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t max_context_len, int32_t block_size, int32_t kv_dtype,
                                              int32_t partition_size);
 
 /*
@@ -311,4 +313,4 @@ int paged_gather(void *out_key, void *out_value, const void *key_cache, const vo
 }
 #endif
 
-#endif /* PAGED_ATTENTION_H */
+#endif /* PA_H */

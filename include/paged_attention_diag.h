@@ -5,7 +5,7 @@
  * attention kernels are compared with), and so that hardware counters (bytes fetched from / written to HBM)
  * can be calibrated on kernels whose traffic is known exactly.
  *
- * Conventions as in paged_attention.h: device pointers, 16-byte aligned, `stream` is a hipStream_t, work is
+ * Conventions as in pa.h: device pointers, 16-byte aligned, `stream` is a hipStream_t, work is
  * enqueued and the call returns without synchronising; negative PA_ERR_* status on invalid arguments.
  */
 #ifndef PAGED_ATTENTION_DIAG_H

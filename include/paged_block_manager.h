@@ -14,12 +14,12 @@
  *
  * The manager never touches device memory: it hands out slots (slot = block * block_size + offset, the
  * slot_mapping of reshape_and_cache), copy pairs and block tables, and the caller moves the bytes with the
- * kernels of paged_attention.h. Within one decode step the caller must apply the copy pairs
+ * kernels of pa.h. Within one decode step the caller must apply the copy pairs
  * (copy_blocks) before writing the step's new tokens (reshape_and_cache).
  *
  * Conventions: host pointers only; the handle is not thread-safe (one caller at a time); every call either
  * succeeds completely or returns a negative status and changes nothing (short of the host itself running out
- * of memory, reported as PA_ERR_NOMEM). Status codes are those of paged_attention.h plus PA_ERR_NOMEM and
+ * of memory, reported as PA_ERR_NOMEM). Status codes are those of pa.h plus PA_ERR_NOMEM and
  * PA_ERR_SEQ below.
  */
 #ifndef PAGED_BLOCK_MANAGER_H
@@ -85,7 +85,7 @@ int32_t pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids, i
 
 /*
  * Swap (page 1 section 5: swap space on the host; page 2 section 7.2: inactive blocks moved to host memory).
- * The caller keeps a second pair of pools in host memory (pinned, so that swap_blocks of paged_attention.h can
+ * The caller keeps a second pair of pools in host memory (pinned, so that swap_blocks of pa.h can
  * reach it) with num_host_blocks blocks of the device pools' shape; the manager hands out its block ids.
  *
  * pa_bm_set_host_pool: use host blocks [0, num_host_blocks). PA_ERR_SEQ while a sequence is swapped out.

@@ -1,6 +1,6 @@
 """MI355X (gfx950) paged decode attention.
 
-A thin Python binding over ``libpagedattn.so`` (the C ABI in ``include/paged_attention.h``). It only checks and
+A thin Python binding over ``libpagedattn.so`` (the C ABI in ``include/pa.h``). It only checks and
 marshals arguments -- every step of the decode path runs in the library's HIP kernels. There is no fallback:
 if the library is missing or fails to load, every call raises.
 
@@ -15,7 +15,7 @@ import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libpagedattn.so")
-HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention.h")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "pa.h")
 DIAG_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_attention_diag.h")
 BM_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "paged_block_manager.h")
 STREAM_SINK_FLOATS = 8192
@@ -25,7 +25,7 @@ PA_OK = 0
 PA_PARTITION_BALANCED = 1  # partition_size that asks for the balanced split (equal runs of tiles per wave)
 PA_ERR_SCRATCH = -11
 PA_STATIC_SCRATCH_BYTES = 32 << 20  # the static device scratch of paged_attention_decode_noalloc
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 
@@ -135,20 +135,20 @@ def _int32(t, name):
         raise TypeError(f"{name} must be int32")
 
 
-def partition_size_for(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
+def partition_size_for(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, kv_dtype,
                        partition_size=-1) -> int:
     """Partition size the decode call launches with (0 = single pass, PA_PARTITION_BALANCED = the balanced
     split)."""
-    r = load_library().paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                                      max_context_len, kv_dtype, partition_size)
+    r = load_library().paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                      max_context_len, block_size, kv_dtype, partition_size)
     _check("paged_attention_partition_size", r if r < 0 else 0)
     return int(r)
 
 
-def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kv_dtype,
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, kv_dtype,
                     partition_size=-1) -> int:
     return int(load_library().paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                              block_size, max_context_len, kv_dtype, partition_size))
+                                                              max_context_len, block_size, kv_dtype, partition_size))
 
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
@@ -180,7 +180,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     mcl = MB * bs if max_context_len is None else int(max_context_len)
     qd, kd = _dtype_code(query), _dtype_code(key_cache)
     lib = load_library()
-    need = lib.paged_attention_workspace_bytes(B, Hq, Hkv, D, bs, mcl, kd, partition_size)
+    need = lib.paged_attention_workspace_bytes(B, Hq, Hkv, D, mcl, bs, kd, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -230,16 +230,16 @@ def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tab
 
 
 def multi_workspace_bytes(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                          block_size, max_context_len, kv_dtype, partition_size=-1) -> int:
+                          max_context_len, block_size, kv_dtype, partition_size=-1) -> int:
     return int(load_library().paged_attention_multi_workspace_bytes(
-        num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size,
         kv_dtype, partition_size))
 
 
 def multi_partition_size_for(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
-                             block_size, max_context_len, kv_dtype, partition_size=-1) -> int:
+                             max_context_len, block_size, kv_dtype, partition_size=-1) -> int:
     r = load_library().paged_attention_multi_partition_size(num_seqs, num_query_tokens, max_query_len, num_q_heads,
-                                                            num_kv_heads, head_dim, block_size, max_context_len,
+                                                            num_kv_heads, head_dim, max_context_len, block_size,
                                                             kv_dtype, partition_size)
     _check("paged_attention_multi_partition_size", r if r < 0 else 0)
     return int(r)
@@ -274,7 +274,7 @@ def paged_attention_decode_multi(out, query, key_cache, value_cache, block_table
     mcl = MB * bs if max_context_len is None else int(max_context_len)
     qd, kd = _dtype_code(query), _dtype_code(key_cache)
     lib = load_library()
-    need = lib.paged_attention_multi_workspace_bytes(B, T, int(max_query_len), Hq, Hkv, D, bs, mcl, kd,
+    need = lib.paged_attention_multi_workspace_bytes(B, T, int(max_query_len), Hq, Hkv, D, mcl, bs, kd,
                                                      partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -18,7 +18,7 @@
 #include <unordered_set>
 #include <vector>
 
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 #include "../../include/paged_block_manager.h"
 
 namespace {

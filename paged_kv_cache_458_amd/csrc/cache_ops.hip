@@ -2,7 +2,7 @@
 // block copy, and the logical-order gather used to check block-table indexing byte for byte.
 #include "pa_device.h"
 #include "pa_kernels.h"
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 
 namespace pa {
 namespace {

@@ -44,7 +44,7 @@
 // normalisation.
 #include "pa_device.h"
 #include "pa_kernels.h"
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 
 namespace pa {
 namespace {

@@ -18,7 +18,7 @@
 // tile comes from a scalar load of the table, so address generation stays on the scalar unit.
 #include "pa_device.h"
 #include "pa_kernels.h"
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 
 namespace pa {
 namespace {

@@ -1,7 +1,7 @@
 // Streaming read and copy kernels used to measure the achievable HBM rate and to calibrate byte counters.
 #include <stdint.h>
 
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 #include "../../include/paged_attention_diag.h"
 #include "pa_device.h"
 

@@ -6,7 +6,7 @@
 
 #include <mutex>
 
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 #include "pa_kernels.h"
 
 namespace {
@@ -274,7 +274,7 @@ const char* pa_strerror(int status) {
 }
 
 int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t head_dim, int32_t max_context_len, int32_t block_size,
                                        int32_t kv_dtype, int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, kv_dtype, partition_size);
@@ -283,7 +283,7 @@ int32_t paged_attention_partition_size(int32_t num_seqs, int32_t num_q_heads, in
 }
 
 size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                       int32_t head_dim, int32_t max_context_len, int32_t block_size,
                                        int32_t kv_dtype, int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, kv_dtype, partition_size);
@@ -292,7 +292,7 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 
 int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t max_context_len, int32_t block_size, int32_t kv_dtype,
                                              int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_context_len, kv_dtype, partition_size);
@@ -302,7 +302,7 @@ int32_t paged_attention_multi_partition_size(int32_t num_seqs, int32_t num_query
 
 size_t paged_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_query_tokens, int32_t max_query_len,
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                             int32_t block_size, int32_t max_context_len, int32_t kv_dtype,
+                                             int32_t max_context_len, int32_t block_size, int32_t kv_dtype,
                                              int32_t partition_size) {
   const Plan p = make_plan(num_seqs, num_query_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_context_len, kv_dtype, partition_size);

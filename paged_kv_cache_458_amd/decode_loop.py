@@ -210,7 +210,7 @@ class DecodeLoop:
                             dtype=t.float32).to(self.dt)
         tables, lens = self.bm.block_tables(ids)
         mcl = int(lens.max())
-        need = workspace_bytes(n, self.hq, self.hkv, self.d, self.bs, mcl, self.kv_code, self.partition_size)
+        need = workspace_bytes(n, self.hq, self.hkv, self.d, mcl, self.bs, self.kv_code, self.partition_size)
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = t.empty(need, dtype=t.uint8, device=self.dev)
         out = t.empty((n, self.hq, self.d), dtype=t.float32, device=self.dev)

@@ -11,7 +11,7 @@
 #include <map>
 #include <vector>
 
-#include "../../include/paged_attention.h"
+#include "../../include/pa.h"
 #include "../../include/paged_block_manager.h"
 
 namespace {

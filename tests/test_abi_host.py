@@ -133,14 +133,14 @@ def test_multi_rejects_before_launch(over, status):
 def test_multi_no_rows_is_a_no_op_and_plans_match_decode():
     assert multi_call(num_query_tokens=0, out=None, query=None, query_start=None) == 0
     # one row per sequence plans exactly like decode
-    for args in ((64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1), (64, 64, 8, 128, 256, 4096, pa.PA_BF16, 512)):
-        B, Hq, Hkv, D, bs, L, kd, part = args
-        assert pa.multi_workspace_bytes(B, B, 1, Hq, Hkv, D, bs, L, kd, part) == pa.workspace_bytes(*args)
-        assert pa.multi_partition_size_for(B, B, 1, Hq, Hkv, D, bs, L, kd, part) == pa.partition_size_for(*args)
+    for args in ((64, 32, 32, 128, 2048, 16, pa.PA_BF16, -1), (64, 64, 8, 128, 4096, 256, pa.PA_BF16, 512)):
+        B, Hq, Hkv, D, L, bs, kd, part = args
+        assert pa.multi_workspace_bytes(B, B, 1, Hq, Hkv, D, L, bs, kd, part) == pa.workspace_bytes(*args)
+        assert pa.multi_partition_size_for(B, B, 1, Hq, Hkv, D, L, bs, kd, part) == pa.partition_size_for(*args)
     # the workspace holds one partial per query row and wave span: a matrix-core wave covers two 512-token
     # partitions and merges them itself
     B, T = 8, 24
-    w = pa.multi_workspace_bytes(B, T, 3, 8, 2, 64, 16, 4096, pa.PA_BF16, 512)
+    w = pa.multi_workspace_bytes(B, T, 3, 8, 2, 64, 4096, 16, pa.PA_BF16, 512)
     pm = 4096 // 1024
     assert w == (T * 8 * pm * 64 * 4 + 255) // 256 * 256 + T * 8 * pm * 2 * 4
 
@@ -178,25 +178,25 @@ def test_decode_with_no_sequences_is_a_no_op():
 def test_workspace_and_partition_plan():
     lib = pa.load_library()
     # single pass needs no workspace
-    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 0) == 0
-    assert pa.partition_size_for(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 0) == 0
+    assert pa.workspace_bytes(64, 32, 32, 128, 2048, 16, pa.PA_BF16, 0) == 0
+    assert pa.partition_size_for(64, 32, 32, 128, 2048, 16, pa.PA_BF16, 0) == 0
     # an explicit split: o [B, Hq, PM, D] fp32, then (m, l) pairs, 256-byte aligned; PM counts wave spans, and a
     # matrix-core wave covers two 512-token partitions
     B, Hq, D, P, L = 64, 64, 128, 512, 4096
     pm = L // (2 * P)
     o = B * Hq * pm * D * 4
     want = (o + 255) // 256 * 256 + B * Hq * pm * 2 * 4
-    assert pa.workspace_bytes(B, Hq, 8, D, 256, L, pa.PA_BF16, P) == want
-    assert pa.partition_size_for(B, Hq, 8, D, 256, L, pa.PA_BF16, P) == P
+    assert pa.workspace_bytes(B, Hq, 8, D, L, 256, pa.PA_BF16, P) == want
+    assert pa.partition_size_for(B, Hq, 8, D, L, 256, pa.PA_BF16, P) == P
     # a partition that covers the longest context is a single pass
-    assert pa.workspace_bytes(4, 4, 4, 64, 16, 64, pa.PA_F32, 64) == 0
+    assert pa.workspace_bytes(4, 4, 4, 64, 64, 16, pa.PA_F32, 64) == 0
     # the library's own choice is consistent with its workspace size
-    for args in ((64, 64, 8, 128, 256, 4096, pa.PA_BF16), (4, 4, 4, 64, 16, 64, pa.PA_F32)):
+    for args in ((64, 64, 8, 128, 4096, 256, pa.PA_BF16), (4, 4, 4, 64, 64, 16, pa.PA_F32)):
         p = pa.partition_size_for(*args, -1)
         assert p == 0 or p % 16 == 0
         assert (pa.workspace_bytes(*args, -1) > 0) == (p > 0)
-    assert lib.paged_attention_workspace_bytes(4, 8, 3, 128, 16, 64, 1, -1) == 0  # invalid -> 0
-    assert lib.paged_attention_partition_size(4, 8, 3, 128, 16, 64, 1, -1) == PA_ERR_SHAPE
+    assert lib.paged_attention_workspace_bytes(4, 8, 3, 128, 64, 16, 1, -1) == 0  # invalid -> 0
+    assert lib.paged_attention_partition_size(4, 8, 3, 128, 64, 16, 1, -1) == PA_ERR_SHAPE
 
 
 def test_grouped_query_default_counts_waves_per_span():
@@ -205,43 +205,43 @@ def test_grouped_query_default_counts_waves_per_span():
     # to a wave since that wave holds two accumulators): 1024 halves while the grid holds fewer than 2048 waves
     def multi(B, *args):
         return pa.multi_partition_size_for(B, 8 * B, 8, *args)
-    assert multi(32, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 256
-    assert multi(8, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 64
-    assert multi(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 512
+    assert multi(32, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == 256
+    assert multi(8, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == 64
+    assert multi(64, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == 512
     # 1024-token partitions that already give 2048 waves stay; 2048 (sequence, KV head, wave) triples run single
     # pass
-    assert multi(128, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 1024
-    assert multi(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+    assert multi(128, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == 1024
+    assert multi(256, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == 0
     # at head_dim 256 a wave serves one column group: 16 waves per sequence
-    assert multi(8, 32, 8, 256, 16, 2048, pa.PA_BF16, -1) == 128
+    assert multi(8, 32, 8, 256, 2048, 16, pa.PA_BF16, -1) == 128
     assert pa.load_library().paged_attention_multi_partition_size(
-        32, 256, 8, 32, 8, 128, 16, 2048, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == PA_ERR_UNSUPPORTED
+        32, 256, 8, 32, 8, 128, 2048, 16, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == PA_ERR_UNSUPPORTED
 
 
 def test_several_tokens_per_sequence_take_the_balanced_split_where_measured():
     B = pa.PA_PARTITION_BALANCED
     # one column group: beyond one round of partitions, as in decode
-    assert pa.multi_partition_size_for(64, 128, 2, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == B
+    assert pa.multi_partition_size_for(64, 128, 2, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == B
     # 64 sequences x 32 heads x 4 rows (MHA): a single pass of 2048 unequal waves -> balanced
-    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == B
-    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_FP8_E4M3, -1) == B
+    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 2048, 16, pa.PA_BF16, -1) == B
+    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 2048, 16, pa.PA_FP8_E4M3, -1) == B
     # 70B shape, 2 rows: one round of partitions keeps them (partitions measured faster there)
-    assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
+    assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 4096, 256, pa.PA_BF16, -1) == 1024
     # decode keeps its single pass where it fills a round
-    assert pa.partition_size_for(256, 32, 8, 128, 16, 1024, pa.PA_BF16, -1) == 0
+    assert pa.partition_size_for(256, 32, 8, 128, 1024, 16, pa.PA_BF16, -1) == 0
 
 
 def test_grouped_query_decode_default_takes_the_balanced_split_beyond_one_round():
     B = pa.PA_PARTITION_BALANCED
     # partitions of 256 tokens would launch 64 x 8 x 8 = 4096 waves, two rounds: balanced
-    assert pa.partition_size_for(64, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == B
-    assert pa.partition_size_for(128, 32, 8, 128, 16, 4096, pa.PA_FP8_E4M3, -1) == B
+    assert pa.partition_size_for(64, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == B
+    assert pa.partition_size_for(128, 32, 8, 128, 4096, 16, pa.PA_FP8_E4M3, -1) == B
     # one round of 2048 waves (64 x 8 x 4 spans of 1024 tokens) keeps its partitions; so does single pass
-    assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
-    assert pa.partition_size_for(16, 64, 8, 128, 16, 16384, pa.PA_BF16, -1) == 1024
-    assert pa.partition_size_for(256, 32, 8, 128, 16, 2048, pa.PA_BF16, -1) == 0
+    assert pa.partition_size_for(64, 64, 8, 128, 4096, 256, pa.PA_BF16, -1) == 1024
+    assert pa.partition_size_for(16, 64, 8, 128, 16384, 16, pa.PA_BF16, -1) == 1024
+    assert pa.partition_size_for(256, 32, 8, 128, 2048, 16, pa.PA_BF16, -1) == 0
     # more than 16 heads per KV head (two column groups): partitions
-    assert pa.partition_size_for(64, 64, 2, 128, 16, 2048, pa.PA_BF16, -1) % 16 == 0
+    assert pa.partition_size_for(64, 64, 2, 128, 2048, 16, pa.PA_BF16, -1) % 16 == 0
 
 
 def balanced_ws(T, Hq, D, hpw=1):
@@ -264,48 +264,48 @@ def test_balanced_split_plan():
     lib = pa.load_library()
     B = pa.PA_PARTITION_BALANCED
     # the library takes the balanced split where the single-head kernel would split its contexts
-    assert pa.partition_size_for(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == B
+    assert pa.partition_size_for(64, 32, 32, 128, 2048, 16, pa.PA_BF16, -1) == B
     # (bf16 rows of 256 bytes: two heads per wave, half the waves per run, twice the runs)
-    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) == balanced_ws(64, 32, 128, 2)
-    assert pa.workspace_bytes(7, 5, 5, 80, 16, 900, pa.PA_FP8_E4M3, B) == balanced_ws(7, 5, 80)
-    assert pa.workspace_bytes(3, 4096, 4096, 64, 16, 900, pa.PA_F32, B) == balanced_ws(3, 4096, 64)  # one run
+    assert pa.workspace_bytes(64, 32, 32, 128, 2048, 16, pa.PA_BF16, -1) == balanced_ws(64, 32, 128, 2)
+    assert pa.workspace_bytes(7, 5, 5, 80, 900, 16, pa.PA_FP8_E4M3, B) == balanced_ws(7, 5, 80)
+    assert pa.workspace_bytes(3, 4096, 4096, 64, 900, 16, pa.PA_F32, B) == balanced_ws(3, 4096, 64)  # one run
     # two heads per wave where head rows are 64 or 128 bytes (or 256 bytes of bf16) and every query head has its
     # own KV head: half the waves per run, twice the runs
-    assert pa.workspace_bytes(64, 32, 32, 128, 16, 2048, pa.PA_FP8_E4M3, B) == balanced_ws(64, 32, 128, 2)
-    assert pa.workspace_bytes(9, 5, 5, 64, 16, 900, pa.PA_BF16, B) == balanced_ws(9, 5, 64, 2)
-    assert pa.workspace_bytes(9, 8, 4, 64, 16, 900, pa.PA_F32, B) == balanced_ws(9, 8, 64)
+    assert pa.workspace_bytes(64, 32, 32, 128, 2048, 16, pa.PA_FP8_E4M3, B) == balanced_ws(64, 32, 128, 2)
+    assert pa.workspace_bytes(9, 5, 5, 64, 900, 16, pa.PA_BF16, B) == balanced_ws(9, 5, 64, 2)
+    assert pa.workspace_bytes(9, 8, 4, 64, 900, 16, pa.PA_F32, B) == balanced_ws(9, 8, 64)
     # several tokens per sequence (fp32: the per-head kernel): one tile count per query row
-    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == B
-    assert pa.multi_workspace_bytes(64, 256, 4, 32, 32, 128, 16, 2048, pa.PA_F32, -1) == balanced_ws(256, 32, 128)
+    assert pa.multi_partition_size_for(64, 256, 4, 32, 32, 128, 2048, 16, pa.PA_F32, -1) == B
+    assert pa.multi_workspace_bytes(64, 256, 4, 32, 32, 128, 2048, 16, pa.PA_F32, -1) == balanced_ws(256, 32, 128)
     # contexts that fit one partition stay single pass; grouped heads on the matrix cores whose partitions fit
     # one round of waves keep them by default ...
-    assert pa.partition_size_for(4, 4, 4, 64, 16, 64, pa.PA_F32, -1) == 0
-    assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
+    assert pa.partition_size_for(4, 4, 4, 64, 64, 16, pa.PA_F32, -1) == 0
+    assert pa.partition_size_for(64, 64, 8, 128, 4096, 256, pa.PA_BF16, -1) % 16 == 0
     # ... and take the balanced split when asked: runs = 2048 waves / (KV heads rounded to whole workgroups of
     # up to 8), partials per query head and run
-    assert pa.partition_size_for(64, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == B
-    assert pa.workspace_bytes(64, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == gqa_balanced_ws(64, 64, 8, 128)
-    assert pa.workspace_bytes(5, 24, 12, 64, 32, 4096, pa.PA_FP8_E4M3, B) == gqa_balanced_ws(5, 24, 12, 64)
-    assert pa.workspace_bytes(3, 16, 1, 128, 16, 900, pa.PA_BF16, B) == gqa_balanced_ws(3, 16, 1, 128)
+    assert pa.partition_size_for(64, 64, 8, 128, 4096, 256, pa.PA_BF16, B) == B
+    assert pa.workspace_bytes(64, 64, 8, 128, 4096, 256, pa.PA_BF16, B) == gqa_balanced_ws(64, 64, 8, 128)
+    assert pa.workspace_bytes(5, 24, 12, 64, 4096, 32, pa.PA_FP8_E4M3, B) == gqa_balanced_ws(5, 24, 12, 64)
+    assert pa.workspace_bytes(3, 16, 1, 128, 900, 16, pa.PA_BF16, B) == gqa_balanced_ws(3, 16, 1, 128)
     # beyond 2048 query rows, or 2^30 row-positions, the default falls back to partitions ...
-    assert pa.partition_size_for(4096, 32, 32, 128, 16, 2048, pa.PA_BF16, -1) % 16 == 0
-    assert pa.partition_size_for(2048, 32, 32, 128, 16, 1 << 20, pa.PA_BF16, -1) % 16 == 0
+    assert pa.partition_size_for(4096, 32, 32, 128, 2048, 16, pa.PA_BF16, -1) % 16 == 0
+    assert pa.partition_size_for(2048, 32, 32, 128, 1 << 20, 16, pa.PA_BF16, -1) % 16 == 0
     # ... and an explicit request is refused, on either kernel; so is one for the matrix-core kernel with more
     # than 16 (query row, head) columns per KV head
-    for args in ((2049, 32, 32, 128, 16, 2048, pa.PA_BF16), (2048, 32, 32, 128, 16, 1 << 20, pa.PA_BF16),
-                 (2049, 64, 8, 128, 256, 4096, pa.PA_BF16), (64, 64, 2, 128, 16, 2048, pa.PA_BF16)):
+    for args in ((2049, 32, 32, 128, 2048, 16, pa.PA_BF16), (2048, 32, 32, 128, 1 << 20, 16, pa.PA_BF16),
+                 (2049, 64, 8, 128, 4096, 256, pa.PA_BF16), (64, 64, 2, 128, 2048, 16, pa.PA_BF16)):
         assert lib.paged_attention_partition_size(*args, B) == PA_ERR_UNSUPPORTED
         assert lib.paged_attention_workspace_bytes(*args, B) == 0
     # several new tokens per sequence on the matrix cores: one column group takes it, with partial slots for
     # every row of a sequence; more columns are refused
-    assert lib.paged_attention_multi_partition_size(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == B
-    assert lib.paged_attention_multi_workspace_bytes(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, B) == \
+    assert lib.paged_attention_multi_partition_size(64, 128, 2, 64, 8, 128, 4096, 256, pa.PA_BF16, B) == B
+    assert lib.paged_attention_multi_workspace_bytes(64, 128, 2, 64, 8, 128, 4096, 256, pa.PA_BF16, B) == \
         gqa_balanced_ws(64, 64, 8, 128, ql=2)
-    assert lib.paged_attention_multi_partition_size(64, 192, 3, 64, 8, 128, 256, 4096, pa.PA_BF16,
+    assert lib.paged_attention_multi_partition_size(64, 192, 3, 64, 8, 128, 4096, 256, pa.PA_BF16,
                                                     B) == PA_ERR_UNSUPPORTED
-    assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) % 16 == 0
+    assert pa.multi_partition_size_for(64, 128, 2, 64, 8, 128, 4096, 256, pa.PA_BF16, -1) % 16 == 0
     # partition sizes between the balanced code and 16 are not multiples of 16
-    assert lib.paged_attention_partition_size(64, 32, 32, 128, 16, 2048, pa.PA_BF16, 2) == PA_ERR_SHAPE
+    assert lib.paged_attention_partition_size(64, 32, 32, 128, 2048, 16, pa.PA_BF16, 2) == PA_ERR_SHAPE
 
 
 @pytest.mark.parametrize("over,status", [
@@ -417,9 +417,9 @@ def test_noalloc_decode_rejects_before_launch(over, status):
 def test_noalloc_scratch_limit_matches_the_workspace_rule():
     lib = pa.load_library()
     # the largest plan that fits: the workspace size function gives the same bytes the no-alloc call needs
-    need = lib.paged_attention_workspace_bytes(256, 32, 32, 128, 16, 4096, pa.PA_BF16, 16)
+    need = lib.paged_attention_workspace_bytes(256, 32, 32, 128, 4096, 16, pa.PA_BF16, 16)
     assert need > pa.PA_STATIC_SCRATCH_BYTES
-    fits = lib.paged_attention_workspace_bytes(64, 64, 8, 128, 256, 4096, pa.PA_BF16, 512)
+    fits = lib.paged_attention_workspace_bytes(64, 64, 8, 128, 4096, 256, pa.PA_BF16, 512)
     assert 0 < fits <= pa.PA_STATIC_SCRATCH_BYTES
     assert "PA_STATIC_SCRATCH_BYTES" in pa.strerror(pa.PA_ERR_SCRATCH)
     assert noalloc_call(num_seqs=0) == 0  # nothing to do: no-op
@@ -429,15 +429,15 @@ def test_grouped_query_default_partitions_within_one_round():
     lib = pa.load_library()
     # 64 sequences of up to 4096 tokens, 32 query heads on 4 KV heads of 256 dims: 512-token partitions (one per
     # wave at head_dim > 128) fill one round of workgroups, which the kernel spreads over the XCDs by sequence
-    assert lib.paged_attention_partition_size(64, 32, 4, 256, 16, 4096, pa.PA_BF16, -1) == 512
+    assert lib.paged_attention_partition_size(64, 32, 4, 256, 4096, 16, pa.PA_BF16, -1) == 512
     # the 70B shape: 1024-token spans, one round of 2048 waves
-    assert lib.paged_attention_partition_size(64, 64, 8, 128, 256, 4096, pa.PA_BF16, -1) == 1024
+    assert lib.paged_attention_partition_size(64, 64, 8, 128, 4096, 256, pa.PA_BF16, -1) == 1024
     # grouped heads at every served head dim plan on the matrix cores (workspace of the balanced split with
     # one partial slot per query head and run, not per query row)
     for d in (64, 80, 96, 112, 128, 192, 256):
         for kd in (pa.PA_BF16, pa.PA_FP8_E4M3):
-            assert lib.paged_attention_partition_size(4, 16, 2, d, 16, 4096, kd, pa.PA_PARTITION_BALANCED) == 1
+            assert lib.paged_attention_partition_size(4, 16, 2, d, 4096, 16, kd, pa.PA_PARTITION_BALANCED) == 1
     # at head_dim > 128 a grouped-query wave covers one partition: 512-token partitions need a partial each
-    ws_128 = lib.paged_attention_workspace_bytes(8, 16, 2, 128, 16, 4096, pa.PA_BF16, 512)
-    ws_256 = lib.paged_attention_workspace_bytes(8, 16, 2, 256, 16, 4096, pa.PA_BF16, 512)
+    ws_128 = lib.paged_attention_workspace_bytes(8, 16, 2, 128, 4096, 16, pa.PA_BF16, 512)
+    ws_256 = lib.paged_attention_workspace_bytes(8, 16, 2, 256, 4096, 16, pa.PA_BF16, 512)
     assert ws_256 > 2 * ws_128 * 1.9

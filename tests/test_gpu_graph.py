@@ -52,7 +52,7 @@ def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, dt, what):
     kc0, vc0 = kc.clone(), vc.clone()
     tables, lens, slots = i32(st.block_tables_pre), i32(st.context_lens), i32(st.slot_mapping)
     kd = pa.PA_FP8_E4M3 if dt == "fp8" else pa.PA_BF16
-    need = pa.workspace_bytes(st.num_seqs, hq, hkv, st.head_dim, st.block_size, st.max_context_len, kd, part)
+    need = pa.workspace_bytes(st.num_seqs, hq, hkv, st.head_dim, st.max_context_len, st.block_size, kd, part)
     assert (need > 0) == (part != 0)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
     out = torch.empty((st.num_seqs, hq, st.head_dim), dtype=torch.float32, device=DEV)

@@ -97,7 +97,7 @@ def test_multi_parity(case):
     ref = oracle_multi(st, h, to_host(q), qs)
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[dt]
     balanced = pa.load_library().paged_attention_multi_partition_size(
-        st.num_seqs, q.shape[0], max(qls), hq, hkv, d, bs, st.max_context_len, kd, pa.PA_PARTITION_BALANCED) > 0
+        st.num_seqs, q.shape[0], max(qls), hq, hkv, d, st.max_context_len, bs, kd, pa.PA_PARTITION_BALANCED) > 0
     for part in (0, 16, 32, 64, 96, 512, -1) + ((pa.PA_PARTITION_BALANCED,) if balanced else ()):
         gpu = run_multi(st, t, q, qs, part)
         close(gpu, ref, dt, f"partition {part}")
@@ -142,7 +142,7 @@ def test_full_size_verification_batch(name, ql):
     err = close(gpu, ref, st.dtype, f"{name} x {ql}")
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
     launched = pa.multi_partition_size_for(st.num_seqs, q.shape[0], ql, st.num_q_heads, st.num_kv_heads, st.head_dim,
-                                           st.block_size, st.max_context_len, kd, st.partition_size)
+                                           st.max_context_len, st.block_size, kd, st.partition_size)
     sys.__stderr__.write(f"[{name} x {ql}] partition {launched}: max abs err {err:.3e} over all "
                          f"{gpu.shape[0] * gpu.shape[1]} (row, head) outputs\n")
 
@@ -161,7 +161,7 @@ def test_rows_past_max_query_len_are_clamped_alike(hq, hkv, d, dt):
     ref = oracle_multi(st, h, to_host(q)[keep], np.array([0, 1, 4, 6], np.int32))
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[dt]
     balanced = pa.load_library().paged_attention_multi_partition_size(
-        3, 8, 3, hq, hkv, d, 16, st.max_context_len, kd, pa.PA_PARTITION_BALANCED) > 0
+        3, 8, 3, hq, hkv, d, st.max_context_len, 16, kd, pa.PA_PARTITION_BALANCED) > 0
     for part in (0, 64, -1) + ((pa.PA_PARTITION_BALANCED,) if balanced else ()):
         out = torch.full((8, hq, d), float("nan"), dtype=torch.float32, device=DEV)
         pa.paged_attention_decode_multi(out, q, t["key_cache"], t["value_cache"], dev_i32(st.block_tables_pre),

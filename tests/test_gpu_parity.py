@@ -61,7 +61,7 @@ def balanced_ok(st) -> bool:
     """Whether the library runs the balanced split for these sizes (either kernel)."""
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
     return pa.load_library().paged_attention_partition_size(
-        st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size, st.max_context_len, kd,
+        st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len, st.block_size, kd,
         pa.PA_PARTITION_BALANCED) == pa.PA_PARTITION_BALANCED
 
 
@@ -439,9 +439,9 @@ def test_gqa_balanced_split_edge_cases():
     # refused beyond that
     lib = pa.load_library()
     assert lib.paged_attention_multi_partition_size(
-        5, 20, 4, 32, 8, 128, 16, 4096, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == pa.PA_PARTITION_BALANCED
+        5, 20, 4, 32, 8, 128, 4096, 16, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == pa.PA_PARTITION_BALANCED
     assert lib.paged_attention_multi_partition_size(
-        5, 40, 8, 32, 8, 128, 16, 4096, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == -4  # PA_ERR_UNSUPPORTED
+        5, 40, 8, 32, 8, 128, 4096, 16, pa.PA_BF16, pa.PA_PARTITION_BALANCED) == -4  # PA_ERR_UNSUPPORTED
 
 
 # --------------------------------------------------------------------------------------------------------

@@ -55,8 +55,8 @@ def run_both(st, t, part):
                               max_context_len=st.max_context_len, partition_size=part, k_scale=st.k_scale,
                               v_scale=st.v_scale)
     torch.cuda.synchronize()
-    launched = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.block_size,
-                                     st.max_context_len, kv_code(st), part)
+    launched = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len,
+                                     st.block_size, kv_code(st), part)
     return got, b.cpu().numpy(), launched
 
 
@@ -79,7 +79,7 @@ def test_noalloc_matches_workspace_call(big, small, part):
     np.testing.assert_array_equal(got, ref)
     assert np.isfinite(got).all()
     need = pa.workspace_bytes(st_big.num_seqs, st_big.num_q_heads, st_big.num_kv_heads, st_big.head_dim,
-                              st_big.block_size, st_big.max_context_len, kv_code(st_big), part)
+                              st_big.max_context_len, st_big.block_size, kv_code(st_big), part)
     sys.__stderr__.write(f"[{big}] partition {launched}, scratch {need} B: identical\n")
     del t_big
 
