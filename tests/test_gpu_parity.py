@@ -111,8 +111,8 @@ SMALL = [
     (217, [700, 45, 513, 9], 32, 8, 128, 8, "fp8"),
     (218, [33, 64, 7, 200], 4, 4, 64, 8, "f32"),
     (219, [1100, 24, 520], 64, 8, 128, 8, "bf16"),
-    # other head dims: row groups padded to a power of two of 16-byte chunks, tiles of 4..16 tokens; grouped
-    # queries at these dims take the per-head kernel
+    # other head dims: row groups padded to a power of two of 16-byte chunks, tiles of 4..16 tokens (per-head
+    # kernel); the grouped bf16 and E4M3 cases among them (222, 224) run on the matrix cores
     (220, [5, 17, 100, 300], 8, 8, 80, 16, "bf16"),
     (221, [33, 64, 129], 4, 2, 96, 16, "f32"),
     (222, [90, 513, 7], 16, 4, 112, 32, "fp8"),
