@@ -124,7 +124,8 @@ def test_one_row_per_sequence_is_decode(hq, hkv, dt, d):
 
 
 # every verification batch whose timing the benchmark reports (bench.py --query-len), at full size, in the launch
-# configuration the benchmark times; every element of the output is compared with the oracle
+# configuration the benchmark times and in the library's own plan where the workload states another; every element
+# of the output is compared with the oracle
 FULL_SIZE = [("llama2_7b", 4), ("llama2_70b_gqa", 2), ("llama2_70b_gqa", 4), ("mistral_gqa_prefix", 4),
              ("llama2_7b_fp8", 4), ("llama2_70b_gqa_fp8", 2)]
 
@@ -135,16 +136,18 @@ def test_full_size_verification_batch(name, ql):
     st = build_structure(name)
     t = materialize(st, DEV)
     q, qs = query_rows(st, np.full(st.num_seqs, ql), DEV)
-    gpu = run_multi(st, t, q, qs, st.partition_size)
+    parts = (st.partition_size,) + ((-1,) if st.partition_size != -1 else ())
+    gpus = [run_multi(st, t, q, qs, part) for part in parts]
     h = {k: to_host(v) for k, v in t.items()}
     del t
     ref = oracle_multi(st, h, to_host(q), qs)
-    err = close(gpu, ref, st.dtype, f"{name} x {ql}")
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
-    launched = pa.multi_partition_size_for(st.num_seqs, q.shape[0], ql, st.num_q_heads, st.num_kv_heads, st.head_dim,
-                                           st.max_context_len, st.block_size, kd, st.partition_size)
-    sys.__stderr__.write(f"[{name} x {ql}] partition {launched}: max abs err {err:.3e} over all "
-                         f"{gpu.shape[0] * gpu.shape[1]} (row, head) outputs\n")
+    for part, gpu in zip(parts, gpus):
+        err = close(gpu, ref, st.dtype, f"{name} x {ql}, partition_size {part}")
+        launched = pa.multi_partition_size_for(st.num_seqs, q.shape[0], ql, st.num_q_heads, st.num_kv_heads,
+                                               st.head_dim, st.max_context_len, st.block_size, kd, part)
+        sys.__stderr__.write(f"[{name} x {ql}] partition {launched}: max abs err {err:.3e} over all "
+                             f"{gpu.shape[0] * gpu.shape[1]} (row, head) outputs\n")
 
 
 @pytest.mark.parametrize("hq,hkv,d,dt", [(4, 4, 64, "f32"), (16, 4, 128, "bf16"), (8, 8, 128, "fp8")])
