@@ -126,8 +126,9 @@ def test_one_row_per_sequence_is_decode(hq, hkv, dt, d):
 # every verification batch whose timing the benchmark reports (bench.py --query-len), at full size, in the launch
 # configuration the benchmark times and in the library's own plan where the workload states another; every element
 # of the output is compared with the oracle
-FULL_SIZE = [("llama2_7b", 4), ("llama2_70b_gqa", 2), ("llama2_70b_gqa", 4), ("mistral_gqa_prefix", 4),
-             ("llama2_7b_fp8", 4), ("llama2_70b_gqa_fp8", 2)]
+FULL_SIZE = [("llama2_7b", 2), ("llama2_7b", 4), ("llama2_7b", 8), ("llama2_7b", 16), ("llama2_70b_gqa", 2),
+             ("llama2_70b_gqa", 4), ("llama2_70b_gqa", 8), ("mistral_gqa_prefix", 4), ("llama2_7b_fp8", 4),
+             ("llama2_70b_gqa_fp8", 2), ("llama2_70b_gqa_fp8", 4)]
 
 
 @pytest.mark.parametrize("name,ql", FULL_SIZE, ids=[f"{n}_q{q}" for n, q in FULL_SIZE])
