@@ -36,6 +36,36 @@ def test_library_exports_every_declared_function():
     assert lib.pa_abi_version() == pa.ABI_VERSION
 
 
+def header_prototypes():
+    """name -> list of parameter names, for every function the three headers declare."""
+    text = "".join(open(p).read() for p in (pa.HEADER_PATH, pa.DIAG_HEADER_PATH, pa.BM_HEADER_PATH))
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    protos = {}
+    for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        params = [q.strip() for q in m.group(2).replace("\n", " ").split(",") if q.strip() and q.strip() != "void"]
+        protos[m.group(1)] = [re.findall(r"(\w+)\s*$", q)[0] for q in params]
+    return protos
+
+
+def test_binding_matches_header_prototypes():
+    # every binding that sets argtypes passes as many arguments as the header declares; the sizing calls keep
+    # max_context_len before block_size (the order the decode call's documentation of them uses)
+    lib = pa.load_library()
+    protos = header_prototypes()
+    checked = 0
+    for name, params in protos.items():
+        fn = getattr(lib, name)
+        if fn.argtypes is not None:
+            assert len(fn.argtypes) == len(params), f"{name}: {len(fn.argtypes)} argtypes, header has {len(params)}"
+            checked += 1
+    assert checked >= 15
+    for name in ("paged_attention_workspace_bytes", "paged_attention_partition_size",
+                 "paged_attention_multi_workspace_bytes", "paged_attention_multi_partition_size"):
+        params = protos[name]
+        assert params.index("max_context_len") + 1 == params.index("block_size"), name
+        assert params[-1] == "partition_size" and params[-2] == "kv_dtype", name
+
+
 def test_strerror_names_every_status():
     for code in (0, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
                  PA_ERR_ALIGN, -10, pa.PA_ERR_SCRATCH):
