@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kWave * 4) void lse_reduce_kernel(const DecodeArgs 
 // first workgroup also publishes the prefix for the merge.
 // At least two waves per SIMD, which the grid's size assumes (without the bound the E4M3 kernels at head_dim 192
 // and 256 would take 256 VGPRs plus 12 AGPRs and one wave per SIMD).
-template <int KV, int D, bool kMulti, int HPW>
+template <int KV, int D, bool kMulti, int HPW, bool kAppend>
 __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balanced_kernel(const DecodeArgs a) {
   using S = Shape<KV, D, HPW>;
   constexpr int NL = S::kLoads;
@@ -437,6 +437,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   int32_t* __restrict__ P = lds_rows;           // P[r]: tiles of the rows before r; P[T]: all tiles
   int32_t* __restrict__ Ex = lds_rows + T + 1;  // positions row r attends over
   int32_t* __restrict__ Sq = Ex + T;            // sequence of row r (several-token batches only)
+  // appended decode (one row per sequence, so Sq is free): Sq[r] = the slot to write row r's new token into, -1
+  // for none; Sa[r] = 1 when that token is also the row's last position attended over
+  int32_t* __restrict__ Sa = Sq + T;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,6 +464,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
       Ex[q0 + j] = E;
       P[q0 + j + 1] = (E + TT - 1) / TT;
       if constexpr (kMulti) Sq[q0 + j] = s;
+    }
+    if constexpr (kAppend) {
+      const int raw = a.context_lens[s];
+      const int slot = a.slot_mapping[s];
+      const bool ok = raw >= 1 && slot >= 0 && (int64_t)slot < (a.num_blocks << a.bs_log2);
+      Sq[s] = ok ? slot : -1;
+      Sa[s] = ok && raw <= a.max_context_len ? 1 : 0;
     }
   }
   __syncthreads();
@@ -519,11 +529,28 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   // whether it opens (takes the row's query) or closes its row segment, whether that segment is the whole row
   // (written to out) or a partial and in which slot, a block id outside the pool, and the query row.
   constexpr uint32_t kRowsMask = 31u, kFirst = 1u << 5, kLast = 1u << 6, kWhole = 1u << 7, kSlot1 = 1u << 8,
-                     kBad = 1u << 9;
+                     kBad = 1u << 9, kNew = 1u << 10, kNewAttend = 1u << 11;
   constexpr int kRowShift = 12;
   auto table_of = [&](int row) {
     const int s = kMulti ? __builtin_amdgcn_readfirstlane(Sq[row]) : row;
     return as_constant(a.block_tables) + (int64_t)s * a.max_blocks_per_seq;
+  };
+
+  // Appended decode: sequence s's new token is its last position L - 1. It is not read from the pool (the same
+  // launch writes it there) but from the new rows, once, after the row's last tile, and the wave that reaches that
+  // tile writes it into the pools at its slot. A slot outside the pool is skipped, as the cache write skips it
+  // (the pool is then read as it was); a length beyond max_context_len clamps the positions attended over, so
+  // the token is written but not attended to, as the two separate calls would do. The returned value is the
+  // slot to write (-1: none); `attend` says whether the token is also the row's last position. Both come from
+  // the prologue's LDS arrays (global loads at every row switch would stall the next tile's issue).
+  auto new_slot_of = [&](int row, bool& attend) {
+    if constexpr (!kAppend) {
+      attend = false;
+      return -1;
+    } else {
+      attend = __builtin_amdgcn_readfirstlane(Sa[row]) != 0;
+      return __builtin_amdgcn_readfirstlane(Sq[row]);
+    }
   };
 
   // issue cursor: row, tile within the row, the row's first tile in the list and tile count, extent, table
@@ -533,6 +560,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   int i_ext = __builtin_amdgcn_readfirstlane(Ex[i_row]);
   int i_tile = g0 - i_p0;
   const ConstI32* i_table = table_of(i_row);
+  bool i_attend;
+  int i_slot = new_slot_of(i_row, i_attend);
 
   Words<S::kQWords> q;
   float m = -INFINITY, l = 0.f;
@@ -544,8 +573,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   U4 kb[kBalStages][NL], vb[kBalStages][NL];
   Words<S::kQWords> qb[kBalStages];
   uint32_t info[kBalStages];
+  U4 kn[kBalStages], vn[kBalStages];  // appended decode: the new token's K/V chunk (row group 0's lanes)
+  int nslot[kBalStages];
+  const char* __restrict__ nkbase = static_cast<const char*>(a.new_key);
+  const char* __restrict__ nvbase = static_cast<const char*>(a.new_value);
   constexpr bool kHalves = TT == kTile && S::kRows <= kTile / 2;
-  auto issue = [&](U4* kq, U4* vq, Words<S::kQWords>& qq, uint32_t& tinfo, int jj) {
+  auto issue = [&](U4* kq, U4* vq, Words<S::kQWords>& qq, uint32_t& tinfo, U4& kq_new, U4& vq_new, int& slot_new,
+                   int jj) {
     const bool live = jj < n;
     const int t = i_tile * TT;
     bool bad = false;
@@ -556,7 +590,22 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
                               ? tile_slot_bytes(i_table, min(t + kTile / 2, last8), a.bs_log2, a.num_blocks,
                                                 row_bytes, bad)
                               : base0 + (kTile / 2) * row_bytes;
-    const int rows = live ? min(TT, i_ext - t) : 0;
+    // appended decode: the row's last tile loads the new token from the new rows (row group 0's lanes, one
+    // 16-byte chunk each; the others read nothing) and, when the token is that tile's last position, reads one
+    // row less from the pool
+    const bool newtok = kAppend && live && i_tile == i_nt - 1 && i_slot >= 0;
+    const bool attend_new = newtok && i_attend;
+    // (taken through a scalar register: the descriptors below must stay wave-uniform)
+    const int rows = __builtin_amdgcn_readfirstlane(live ? min(TT, i_ext - t) - (attend_new ? 1 : 0) : 0);
+    if constexpr (kAppend) {
+      // issued for every tile (an empty descriptor reads nothing), so that the loads in flight are the same on
+      // every path and the waits for a tile's K/V stay as tight as without the append
+      const uint32_t noff = r == 0 && lane_ok ? lane_off[0] : kNowhere;
+      const uint32_t nbytes = newtok ? (uint32_t)row_bytes : 0u;
+      kq_new = load16<0>(make_rsrc(nkbase + (int64_t)i_row * row_bytes, nbytes), noff);
+      vq_new = load16<0>(make_rsrc(nvbase + (int64_t)i_row * row_bytes, nbytes), noff);
+      slot_new = i_slot;
+    }
     const uint32_t live0 = (uint32_t)(kHalves ? min(rows, kTile / 2) : rows) * (uint32_t)row_bytes;
     const uint32_t live1 = (uint32_t)max(rows - kTile / 2, 0) * (uint32_t)row_bytes;
     const __amdgpu_buffer_rsrc_t kr0 = make_rsrc(kbase + base0, live0), kr1 = make_rsrc(kbase + base1, live1);
@@ -580,13 +629,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     for (int i = 0; i < S::kQWords; ++i) qq.w[i] = load16<0>(qr, q_off[i]);
     tinfo = (uint32_t)rows | (first ? kFirst : 0u) | (i_tile == i_nt - 1 || jj == n - 1 ? kLast : 0u) |
             (i_p0 >= g0 && i_p0 + i_nt <= g1 ? kWhole : 0u) | (i_p0 > g0 ? kSlot1 : 0u) | (bad ? kBad : 0u) |
-            ((uint32_t)i_row << kRowShift);
+            (newtok ? kNew : 0u) | (attend_new ? kNewAttend : 0u) | ((uint32_t)i_row << kRowShift);
     if (live && jj + 1 < n && ++i_tile == i_nt) {
       i_row = next_row(i_row);
       i_p0 = __builtin_amdgcn_readfirstlane(P[i_row]);
       i_nt = __builtin_amdgcn_readfirstlane(P[i_row + 1]) - i_p0;
       i_ext = __builtin_amdgcn_readfirstlane(Ex[i_row]);
       i_table = table_of(i_row);
+      i_slot = new_slot_of(i_row, i_attend);
       i_tile = 0;
     }
   };
@@ -632,7 +682,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     seg_bad = false;
   };
 
-  auto consume = [&](const U4* kq, const U4* vq, const Words<S::kQWords>& qq, uint32_t tinfo) {
+  auto consume = [&](const U4* kq, const U4* vq, const Words<S::kQWords>& qq, uint32_t tinfo, const U4& kq_new,
+                     const U4& vq_new, int slot_new) {
     tinfo = __builtin_amdgcn_readfirstlane(tinfo);
     if (tinfo & kFirst) q = qq;
     seg_bad |= (tinfo & kBad) != 0;
@@ -662,23 +713,47 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
       axpy_chunk<KV>(acc, p, v);
     }
     m = mn;
+    if constexpr (kAppend) {
+      if (tinfo & kNewAttend) {
+        // the new token, one more position of row group 0 (the other groups' state does not move)
+        float sn = group_sum<S::kSumLanes>(dot_chunk<KV>(q, kq_new)) * a.scale_log2;
+        if (r != 0) sn = -INFINITY;
+        const float m2 = fmaxf(m, sn);
+        const float mref2 = m2 == -INFINITY ? 0.f : m2;
+        const float alpha2 = fast_exp2(m - mref2);
+        const float pn = fast_exp2(sn - mref2);
+        l = l * alpha2 + pn;
+#pragma unroll
+        for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha2;
+        axpy_chunk<KV>(acc, pn, vq_new);
+        m = m2;
+      }
+      if (tinfo & kNew) {
+        // its rows into the pools, by one wave per KV head
+        if (r == 0 && lane_ok && h % a.group == 0) {
+          const int64_t dst = (int64_t)slot_new * row_bytes + lane_off[0];
+          *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + dst) = kq_new;
+          *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + dst) = vq_new;
+        }
+      }
+    }
     if (tinfo & kLast) flush(tinfo);
   };
 
 #pragma unroll
-  for (int i = 0; i < kBalStages - 1; ++i) issue(kb[i], vb[i], qb[i], info[i], i);
+  for (int i = 0; i < kBalStages - 1; ++i) issue(kb[i], vb[i], qb[i], info[i], kn[i], vn[i], nslot[i], i);
   int j = 0;
   for (; j + kBalStages <= n; j += kBalStages) {
 #pragma unroll
     for (int i = 0; i < kBalStages; ++i) {
       const int w = (i + kBalStages - 1) % kBalStages;
-      issue(kb[w], vb[w], qb[w], info[w], j + i + kBalStages - 1);
-      consume(kb[i], vb[i], qb[i], info[i]);
+      issue(kb[w], vb[w], qb[w], info[w], kn[w], vn[w], nslot[w], j + i + kBalStages - 1);
+      consume(kb[i], vb[i], qb[i], info[i], kn[i], vn[i], nslot[i]);
     }
   }
 #pragma unroll
   for (int i = 0; i < kBalStages - 1; ++i)
-    if (j + i < n) consume(kb[i], vb[i], qb[i], info[i]);
+    if (j + i < n) consume(kb[i], vb[i], qb[i], info[i], kn[i], vn[i], nslot[i]);
 }
 
 // Merge of the balanced split's partials: one wave per (query row, head). The tile list holds query rows, or
@@ -784,30 +859,30 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t str
   return hipErrorInvalidValue;
 }
 
-template <int KV, bool kMulti>
+template <int KV, bool kMulti, bool kAppend>
 hipError_t launch_balanced_kv(const DecodeArgs& a, int hpw, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
   switch (a.head_dim) {
     case 64:
       if constexpr (KV != PA_F32)
         if (hpw == 2) {
-          decode_valu_balanced_kernel<KV, 64, kMulti, 2><<<grid, block, lds, stream>>>(a);
+          decode_valu_balanced_kernel<KV, 64, kMulti, 2, kAppend><<<grid, block, lds, stream>>>(a);
           break;
         }
-      decode_valu_balanced_kernel<KV, 64, kMulti, 1><<<grid, block, lds, stream>>>(a);
+      decode_valu_balanced_kernel<KV, 64, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a);
       break;
-    case 80: decode_valu_balanced_kernel<KV, 80, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
-    case 96: decode_valu_balanced_kernel<KV, 96, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
-    case 112: decode_valu_balanced_kernel<KV, 112, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
+    case 80: decode_valu_balanced_kernel<KV, 80, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a); break;
+    case 96: decode_valu_balanced_kernel<KV, 96, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a); break;
+    case 112: decode_valu_balanced_kernel<KV, 112, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a); break;
     case 128:
       if constexpr (KV != PA_F32)
         if (hpw == 2) {
-          decode_valu_balanced_kernel<KV, 128, kMulti, 2><<<grid, block, lds, stream>>>(a);
+          decode_valu_balanced_kernel<KV, 128, kMulti, 2, kAppend><<<grid, block, lds, stream>>>(a);
           break;
         }
-      decode_valu_balanced_kernel<KV, 128, kMulti, 1><<<grid, block, lds, stream>>>(a);
+      decode_valu_balanced_kernel<KV, 128, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a);
       break;
-    case 192: decode_valu_balanced_kernel<KV, 192, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
-    case 256: decode_valu_balanced_kernel<KV, 256, kMulti, 1><<<grid, block, lds, stream>>>(a); break;
+    case 192: decode_valu_balanced_kernel<KV, 192, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a); break;
+    case 256: decode_valu_balanced_kernel<KV, 256, kMulti, 1, kAppend><<<grid, block, lds, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -816,9 +891,17 @@ hipError_t launch_balanced_kv(const DecodeArgs& a, int hpw, dim3 grid, dim3 bloc
 template <int KV>
 hipError_t launch_balanced_dtype(const DecodeArgs& a, int hpw, dim3 grid, dim3 block, hipStream_t stream) {
   const bool multi = a.query_start != nullptr;
-  const size_t lds = (size_t)((multi ? 3 : 2) * (int64_t)a.num_tokens + 1) * sizeof(int32_t);
-  return multi ? launch_balanced_kv<KV, true>(a, hpw, grid, block, lds, stream)
-               : launch_balanced_kv<KV, false>(a, hpw, grid, block, lds, stream);
+  const size_t lds = (size_t)((multi ? 3 : a.new_key ? 4 : 2) * (int64_t)a.num_tokens + 1) * sizeof(int32_t);
+  if (a.new_key) {  // appended decode: one new token per sequence, caches of the new rows' dtype
+    if constexpr (KV == PA_FP8_E4M3) {
+      return hipErrorInvalidValue;
+    } else {
+      if (multi) return hipErrorInvalidValue;
+      return launch_balanced_kv<KV, false, true>(a, hpw, grid, block, lds, stream);
+    }
+  }
+  return multi ? launch_balanced_kv<KV, true, false>(a, hpw, grid, block, lds, stream)
+               : launch_balanced_kv<KV, false, false>(a, hpw, grid, block, lds, stream);
 }
 
 int valu_heads_per_wave(int kv_dtype, int head_dim, int group) {

@@ -326,15 +326,25 @@ int paged_attention_decode(float* out, const void* query, const void* key_cache,
 
 namespace {
 
+// The new tokens of paged_attention_decode_append: one K/V row per sequence and its slot, written into the pools.
+struct Append {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const int32_t* slot_mapping;
+};
+
 // Shared by the decode and multi-token entry points: query_start == nullptr means one query row per sequence.
-// With static_scratch the split-context partials go to this GPU's static scratch instead of `workspace`.
+// With static_scratch the split-context partials go to this GPU's static scratch instead of `workspace`. With
+// `app`, each sequence's new token is written into the pools as part of the call (paged_attention_decode_append).
 int attention(float* out, const void* query, const void* key_cache, const void* value_cache,
               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start, float scale,
               float k_scale, float v_scale, int32_t block_size, int32_t num_seqs, int32_t num_tokens,
               int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
               int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
-              bool static_scratch = false) {
+              bool static_scratch = false, const Append* app = nullptr) {
   const Plan plan = make_plan(num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
                               block_size, max_context_len, kv_dtype, partition_size);
   if (plan.status != PA_OK) return plan.status;
@@ -394,8 +404,29 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   a.tile_prefix =
       plan.balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_prefix_offset) : nullptr;
   a.seq_prefix = plan.balanced && plan.mfma ? 1 : 0;  // the matrix-core tile list is one of sequences
+  a.new_key = nullptr;
+  a.new_value = nullptr;
+  a.slot_mapping = nullptr;
+  a.key_out = nullptr;
+  a.value_out = nullptr;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (app) {
+    // The single-head balanced split appends the new tokens itself; every other plan writes them first, as
+    // reshape_and_cache would, and then attends.
+    if (plan.balanced && !plan.mfma && !query_start && (kv_dtype == PA_BF16 || kv_dtype == PA_F32)) {
+      a.new_key = app->key;
+      a.new_value = app->value;
+      a.slot_mapping = app->slot_mapping;
+      a.key_out = app->key_cache;
+      a.value_out = app->value_cache;
+    } else if (pa::launch_reshape_and_cache(app->key, app->value, app->key_cache, app->value_cache,
+                                            app->slot_mapping, num_seqs,
+                                            (int64_t)num_kv_heads * head_dim * esize_of(kv_dtype), block_size,
+                                            num_blocks, st) != hipSuccess) {
+      return PA_ERR_HIP;
+    }
+  }
   if (plan.balanced) {
     const hipError_t e = plan.mfma ? pa::launch_decode_gqa_mfma_balanced(a, kv_dtype, st)
                                    : pa::launch_decode_valu_balanced(a, kv_dtype, st);
@@ -435,6 +466,28 @@ int paged_attention_decode_noalloc(float* out, const void* query, const void* ke
                    block_size, num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks,
                    max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size, nullptr, 0, stream,
                    /*static_scratch=*/true);
+}
+
+int paged_attention_decode_append(float* out, const void* query, const void* key, const void* value, void* key_cache,
+                                  void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* slot_mapping, float scale, int32_t block_size, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
+                                  int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  // the cache write's own checks first (those of reshape_and_cache for num_seqs new rows), then the decode's
+  if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if ((int64_t)num_kv_heads * head_dim * esize_of(kv_dtype) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 0) {
+    if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned4(slot_mapping)) return PA_ERR_ALIGN;
+  }
+  const Append app{key, value, key_cache, value_cache, slot_mapping};
+  return attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr, scale, 1.0f, 1.0f,
+                   block_size, num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                   max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size, workspace, workspace_bytes,
+                   stream, /*static_scratch=*/false, &app);
 }
 
 int paged_attention_decode_multi(float* out, const void* query, const void* key_cache, const void* value_cache,

@@ -66,6 +66,34 @@ def test_binding_matches_header_prototypes():
         assert params[-1] == "partition_size" and params[-2] == "kv_dtype", name
 
 
+def append_call(**over):
+    args = dict(out=FAKE, query=FAKE, key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE,
+                context_lens=FAKE, slot_mapping=FAKE, scale=0.1, block_size=16, num_seqs=4, num_q_heads=8,
+                num_kv_heads=8, head_dim=128, num_blocks=100, max_blocks_per_seq=8, max_context_len=128,
+                q_dtype=pa.PA_BF16, kv_dtype=pa.PA_BF16, partition_size=-1, workspace=None, workspace_bytes=0,
+                stream=None)
+    args.update(over)
+    return pa.load_library().paged_attention_decode_append(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kv_dtype=pa.PA_FP8_E4M3), PA_ERR_DTYPE),     # E4M3 caches take the quantising write
+    (dict(kv_dtype=7), PA_ERR_DTYPE),
+    (dict(key=None), PA_ERR_NULL),
+    (dict(slot_mapping=None), PA_ERR_NULL),
+    (dict(value=FAKE + 8), PA_ERR_ALIGN),
+    (dict(num_kv_heads=0), PA_ERR_SHAPE),
+    (dict(head_dim=100), PA_ERR_UNSUPPORTED),           # the decode's own checks follow the cache write's
+    (dict(workspace=None, workspace_bytes=0, partition_size=64), PA_ERR_WORKSPACE),
+])
+def test_append_rejects_before_launch(over, status):
+    assert append_call(**over) == status
+
+
+def test_append_no_sequences_is_a_no_op():
+    assert append_call(num_seqs=0, key=None, value=None, slot_mapping=None) == 0
+
+
 def test_strerror_names_every_status():
     for code in (0, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
                  PA_ERR_ALIGN, -10, pa.PA_ERR_SCRATCH):

@@ -1,0 +1,141 @@
+"""paged_attention_decode_append: one decode step's cache write and attention in one call, against the two
+separate calls (reshape_and_cache, then paged_attention_decode) and the oracle.
+
+The pools must end byte for byte as the separate cache write leaves them. Where the single-head balanced split
+appends the new token itself, the output equals the separate calls' up to the order of floating-point
+additions (the new token is added to its row's state last); every other plan runs the two launches and must
+match them bit for bit. Both are also compared with the fp64 oracle over the updated pools."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_458_amd as pa
+from tests._host import to_host
+from tests.test_gpu_parity import assert_attention_close, decode, dev_i32, oracle_decode
+from workloads import build_structure, custom_structure, materialize
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+def appended(st, t, pools, tables, slots, partition_size, context_lens=None, max_context_len=None):
+    out = torch.empty((st.num_seqs, st.num_q_heads, st.head_dim), dtype=torch.float32, device=DEV)
+    cl = st.context_lens if context_lens is None else context_lens
+    pa.paged_attention_decode_append(out, t["query"], t["new_key"], t["new_value"], pools[0], pools[1],
+                                     dev_i32(tables), dev_i32(cl), dev_i32(slots), st.scale,
+                                     max_context_len=st.max_context_len if max_context_len is None
+                                     else max_context_len, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def fused_here(st, partition_size) -> bool:
+    """Whether the library appends in the decode launch itself (the single-head balanced split)."""
+    kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16}[st.dtype]
+    part = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len,
+                                 st.block_size, kd, partition_size)
+    mfma = st.dtype == "bf16" and st.num_q_heads != st.num_kv_heads
+    return part == pa.PA_PARTITION_BALANCED and not mfma
+
+
+def compare(st, fused, separate, ref, what, exact):
+    if exact:
+        np.testing.assert_array_equal(fused, separate, err_msg=what)
+    else:
+        np.testing.assert_allclose(fused, separate, rtol=1e-5, atol=1e-6, err_msg=what)
+    return assert_attention_close(fused, ref, st.dtype, what)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b", "mixed_len", "llama2_70b_gqa", "mistral_gqa_prefix"])
+def test_full_size_step(name):
+    # the benchmark's step: copy-on-write pairs, then the new tokens appended and attended over
+    st = build_structure(name)
+    t = materialize(st, DEV, include_new_token=False)
+    pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    h = {k: to_host(v) for k, v in t.items()}
+    # the separate calls, on the device and on the host copies
+    if len(st.copy_pairs):
+        pa.copy_blocks(t["key_cache"], t["value_cache"], dev_i32(st.copy_pairs))
+        pa.copy_blocks(pools[0], pools[1], dev_i32(st.copy_pairs))
+        oracle.copy_blocks(h["key_cache"], h["value_cache"], st.copy_pairs)
+    pa.reshape_and_cache(t["new_key"], t["new_value"], t["key_cache"], t["value_cache"], dev_i32(st.slot_mapping))
+    oracle.reshape_and_cache(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"], st.slot_mapping)
+    separate = decode(st, t, st.block_tables, st.partition_size)
+    fused = appended(st, t, pools, st.block_tables, st.slot_mapping, st.partition_size)
+    for got, want, which in ((pools[0], t["key_cache"], "key"), (pools[1], t["value_cache"], "value")):
+        assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"{name}: {which} pool differs"
+    del pools
+    ref = oracle_decode(st, h, st.block_tables)
+    err = compare(st, fused, separate, ref, name, exact=not fused_here(st, st.partition_size))
+    sys.__stderr__.write(f"[{name}] appended in the launch: {fused_here(st, st.partition_size)}, "
+                         f"max abs err {err:.3e}\n")
+
+
+# lengths with the new token alone in its tile (9 and 17 with 8- and 16-token tiles), a one-token context, rows
+# cut across the balanced split's runs; bf16 two heads per wave (head_dim 128 and 64), fp32 one head per wave,
+# grouped fp32 heads (one wave per KV head writes the rows), 8-slot blocks
+SMALL = [
+    # (seed, lens, Hq, Hkv, D, bs, dtype)
+    (601, [1, 8, 9, 16, 17, 300, 1000], 8, 8, 128, 16, "bf16"),
+    (602, [9, 1, 17, 2049, 33, 700], 4, 4, 64, 16, "bf16"),
+    (603, [1, 5, 16, 17, 129, 900], 4, 4, 128, 16, "f32"),
+    (604, [17, 1, 400, 9, 63], 8, 2, 64, 8, "f32"),
+    (605, [1000, 3, 8, 9, 250, 1], 16, 16, 128, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"seed{c[0]}" for c in SMALL])
+def test_small_cases(case):
+    seed, lens, hq, hkv, d, bs, dt = case
+    st = custom_structure(f"a{seed}", seed, lens, hq, hkv, d, bs, dt)
+    assert len(st.copy_pairs) == 0  # the tables before and after the step are the same
+    # the new tokens' slots hold data already (read where a token is not appended)
+    t = materialize(st, DEV, include_new_token=True)
+    tables = st.block_tables_pre
+    slots = st.slot_mapping.copy()
+    slots[1] = -1  # this sequence's token is not written: the pool is read as it was
+    for part in (-1, pa.PA_PARTITION_BALANCED, 0, 64):
+        ref_pools = (t["key_cache"].clone(), t["value_cache"].clone())
+        pools = (t["key_cache"].clone(), t["value_cache"].clone())
+        h = {k: to_host(v) for k, v in t.items()}
+        pa.reshape_and_cache(t["new_key"], t["new_value"], ref_pools[0], ref_pools[1], dev_i32(slots))
+        oracle.reshape_and_cache(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"], slots)
+        tref = dict(t, key_cache=ref_pools[0], value_cache=ref_pools[1])
+        separate = decode(st, tref, tables, part)
+        fused = appended(st, t, pools, tables, slots, part)
+        assert torch.equal(pools[0].view(torch.uint8), ref_pools[0].view(torch.uint8)), f"key pool, part {part}"
+        assert torch.equal(pools[1].view(torch.uint8), ref_pools[1].view(torch.uint8)), f"value pool, part {part}"
+        ref = oracle_decode(st, h, tables)
+        compare(st, fused, separate, ref, f"seed {seed} partition {part}", exact=not fused_here(st, part))
+
+
+def test_length_beyond_max_context_len_is_written_not_attended():
+    # the caller's max_context_len clamps the longest sequence: its new token is written (as the cache write
+    # does) but lies past the positions attended over, in both forms
+    st = custom_structure("a610", 610, [700, 33, 1200, 90], 8, 8, 128, 16, "bf16")
+    t = materialize(st, DEV, include_new_token=True)
+    mcl = 1100
+    cl = st.context_lens  # sequence 2 (1200 positions) is beyond it
+    pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    ref_pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    pa.reshape_and_cache(t["new_key"], t["new_value"], ref_pools[0], ref_pools[1], dev_i32(st.slot_mapping))
+    separate = decode(st, dict(t, key_cache=ref_pools[0], value_cache=ref_pools[1]), st.block_tables_pre, -1,
+                      context_lens=cl, max_context_len=mcl)
+    fused = appended(st, t, pools, st.block_tables_pre, st.slot_mapping, -1, context_lens=cl, max_context_len=mcl)
+    assert torch.equal(pools[0].view(torch.uint8), ref_pools[0].view(torch.uint8))
+    assert torch.equal(pools[1].view(torch.uint8), ref_pools[1].view(torch.uint8))
+    np.testing.assert_allclose(fused, separate, rtol=1e-5, atol=1e-6)
