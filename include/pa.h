@@ -171,8 +171,9 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
  *   other arguments as in paged_attention_decode; kv_dtype PA_F32 or PA_BF16 (E4M3 caches: reshape_and_cache_fp8
  *                  and paged_attention_decode_scaled)
  * Contract: for every s whose slot is written, position context_lens[s] - 1 of sequence s lies in that slot
- * through the block table (the new token is the last position the call attends over), and
- * 1 <= context_lens[s] <= max_context_len. Where the plan is the single-head balanced split, one launch does both:
+ * through the block table (the new token is the last position of the sequence) and context_lens[s] >= 1. As in
+ * paged_attention_decode, lengths beyond max_context_len are clamped: such a sequence's new token is written but
+ * not attended over. Where the plan is the single-head balanced split, one launch does both:
  * the last position of such a sequence is taken from `key` / `value` instead of the pool, and the wave that
  * reaches it writes it into the pools. Every other plan launches the cache write first. Either way the pools end
  * as reshape_and_cache leaves them, byte for byte, and the output equals that of the two calls up to the order
