@@ -237,7 +237,9 @@ def run_decode_loop(args) -> int:
         attn_s += e0.elapsed_time(e1) * 1e-3
         lens = lens.astype(np.int64)
         nb = int(((lens + bs - 1) // bs).sum())
-        other = len(lens) * hq * d * (2 + 4) + nb * 4 + 4 * len(lens)
+        # query in, fp32 out, live table entries, lengths; the new rows read from the input and written to the
+        # pools by the same call
+        other = len(lens) * hq * d * (2 + 4) + nb * 4 + 4 * len(lens) + 2 * row * len(lens)
         attn_bytes += int(lens.sum()) * row * 2 + other
         unique_bytes += unique_slots(tables, lens, bs) * row * 2 + other
         stepped += len(lens)
@@ -274,7 +276,7 @@ def run_decode_loop(args) -> int:
             "cow_copies": stats[-1]["cow_copies"],
         },
         # unique bytes: blocks shared by several sequences (prompt prefixes, forks) count once per call
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode within the loop",
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode_append within the loop",
                      "achieved": round(unique_bytes / attn_s / 1e9, 1),
                      "achieved_logical": round(attn_bytes / attn_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(unique_bytes / attn_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},

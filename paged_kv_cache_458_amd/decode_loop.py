@@ -3,8 +3,8 @@ the HIP kernels move and read the bytes.
 
 Each step appends one token to every running sequence (vLLM PagedAttention, page 3 section 2.1: forward,
 sample, update the KV cache, forward again): the block manager hands out the new tokens' slots and any
-copy-on-write pairs; copy_blocks applies the copies, reshape_and_cache writes the new K/V, and
-paged_attention_decode attends over each sequence's whole cache. Sequences join (with a prompt whose full
+copy-on-write pairs; copy_blocks applies the copies, and paged_attention_decode_append writes the new K/V
+into their slots and attends over each sequence's whole cache (in one launch where its plan allows). Sequences join (with a prompt whose full
 blocks may be shared with earlier prompts), fork (sharing every block, page 1 section 3.2) and finish
 (their blocks return to the pool) between steps. With a host pool (page 1 section 5: swap space; page 2
 section 7.2: inactive blocks to host memory) a step that runs out of blocks swaps the most recently admitted
@@ -19,8 +19,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (PA_BF16, PA_F32, PagedAttentionError, copy_blocks, paged_attention_decode, reshape_and_cache,
-               swap_blocks, workspace_bytes)
+from . import (PA_BF16, PA_F32, PagedAttentionError, copy_blocks, paged_attention_decode_append,
+               reshape_and_cache, swap_blocks, workspace_bytes)
 from .block_manager import PA_ERR_NOMEM, BlockManager
 
 
@@ -202,7 +202,9 @@ class DecodeLoop:
             return [], None, np.zeros((0, 2), np.int32)
         pairs = self._apply_copies()  # copy-on-write before the new tokens land in the copies
         k, v = self._rows(n) if new_kv is None else new_kv
-        self._write(k, v, slots)
+        slots_d = self._to_device(np.asarray(slots, dtype=np.int32))
+        if self.log is not None:
+            self.log.append(("write", slots.copy(), k.cpu(), v.cpu()))
         for s in ids:
             self.lengths[s] += 1
         if query is None:
@@ -220,9 +222,9 @@ class DecodeLoop:
         if self.attention_events is not None:
             ev = (t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
             ev[0].record(t.cuda.current_stream(self.dev))
-        paged_attention_decode(out, query, self.key_cache, self.value_cache, tables_d, lens_d, self.scale,
-                               self.bs, max_context_len=mcl, partition_size=self.partition_size,
-                               workspace=self._ws if need else None)
+        paged_attention_decode_append(out, query, k.contiguous(), v.contiguous(), self.key_cache, self.value_cache,
+                                      tables_d, lens_d, slots_d, self.scale, max_context_len=mcl,
+                                      partition_size=self.partition_size, workspace=self._ws if need else None)
         if ev is not None:
             ev[1].record(t.cuda.current_stream(self.dev))
             self.attention_events.append((ev, lens.copy(), tables.copy()))
