@@ -50,6 +50,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def step_appends(pa, st, query_len: int, launched_part: int, separate_write: bool = False) -> bool:
+    """Whether the benchmark's step writes the new tokens inside the decode launch: paged_attention_decode_append
+    does so under the single-head balanced split over an fp32 or bf16 cache (grouped bf16 heads run on the
+    matrix cores, where the call launches the cache write first, so the step keeps the two calls)."""
+    return (query_len == 1 and not separate_write and st.dtype in ("f32", "bf16") and
+            launched_part == pa.PA_PARTITION_BALANCED and (st.dtype == "f32" or st.num_q_heads == st.num_kv_heads))
+
+
+def appended_row_bytes(st) -> int:
+    """The new rows a decode step reads from its input and writes to both pools (sequences with a slot)."""
+    return 2 * int((st.slot_mapping >= 0).sum()) * st.num_kv_heads * st.head_dim * (st.q_esize + st.esize)
+
+
 TRAFFIC_TAG = "<!-- traffic "
 COPY_BYTES = 1 << 31  # bytes the calibration copy reads and writes per dispatch (stream_copy over 2 GiB)
 
@@ -113,9 +126,17 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
         f, w = fetch[kf][0] * f_scale, write[kw][0] * w_scale
         fb, wb = fb + f, wb + w
         rows.append((kf, fetch[kf][1], fetch[kf][0], write[kw][0], f, w))
+    import paged_kv_cache_458_amd as pa
     from workloads import algorithmic_bytes, build_structure
 
-    alg = algorithmic_bytes(build_structure(workload), query_len)["total"]
+    st = build_structure(workload)
+    alg = algorithmic_bytes(st, query_len)["total"]
+    if query_len == 1:
+        kv_code = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
+        part = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len,
+                                     st.block_size, kv_code, st.partition_size)
+        if step_appends(pa, st, 1, part):  # the counted call also reads and writes the new rows
+            alg += appended_row_bytes(st)
     label = workload if query_len == 1 else f"{workload}_q{query_len}"
     lines = [f"# HBM traffic per attention call: {label}", "",
              "Two counter runs of the benchmark (run from the repository root on one MI355X):", "", "```",
@@ -495,11 +516,7 @@ def main() -> int:
         launched_part = pa.partition_size_for(B, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
     else:
         launched_part = pa.multi_partition_size_for(B, T, Q, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
-    # The step calls paged_attention_decode_append where the library appends the new tokens inside its decode
-    # launch (the single-head balanced split over an fp32 or bf16 cache); elsewhere that call would launch the
-    # cache write first, so the step keeps the two calls and the attention call is timed alone.
-    append = (Q == 1 and not args.separate_write and st.dtype in ("f32", "bf16") and
-              launched_part == pa.PA_PARTITION_BALANCED and (st.dtype == "f32" or Hq == Hkv))
+    append = step_appends(pa, st, Q, launched_part, args.separate_write)
 
     t = materialize(st, dev, include_new_token=False)
     pools = [(t["key_cache"], t["value_cache"])]
