@@ -52,10 +52,14 @@ def kernel_source_hash() -> str:
 
 def step_appends(pa, st, query_len: int, launched_part: int, separate_write: bool = False) -> bool:
     """Whether the benchmark's step writes the new tokens inside the decode launch: paged_attention_decode_append
-    does so under the single-head balanced split over an fp32 or bf16 cache (grouped bf16 heads run on the
-    matrix cores, where the call launches the cache write first, so the step keeps the two calls)."""
-    return (query_len == 1 and not separate_write and st.dtype in ("f32", "bf16") and
-            launched_part == pa.PA_PARTITION_BALANCED and (st.dtype == "f32" or st.num_q_heads == st.num_kv_heads))
+    does so under the single-head balanced split over an fp32 or bf16 cache and in the matrix-core partition
+    kernel (grouped heads over bf16 or E4M3 caches). Elsewhere the call launches the cache write first, so the
+    step keeps the two calls and times the attention alone."""
+    if query_len != 1 or separate_write:
+        return False
+    mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
+    balanced = launched_part == pa.PA_PARTITION_BALANCED
+    return (mfma and not balanced) or (not mfma and balanced and st.dtype != "fp8")
 
 
 def appended_row_bytes(st) -> int:
@@ -572,8 +576,9 @@ def main() -> int:
         if append:
             attn = functools.partial(lib.paged_attention_decode_append, out.data_ptr(), query.data_ptr(),
                                      new_key.data_ptr(), new_value.data_ptr(), kc.data_ptr(), vc.data_ptr(),
-                                     tables.data_ptr(), lens.data_ptr(), slots.data_ptr(), st.scale, bs, B, Hq,
-                                     Hkv, D, NB, MB, mcl, qd, kv_code, part, ws.data_ptr(), ws.numel(), sp)
+                                     tables.data_ptr(), lens.data_ptr(), slots.data_ptr(), st.scale, st.k_scale,
+                                     st.v_scale, bs, B, Hq, Hkv, D, NB, MB, mcl, qd, kv_code, part, ws.data_ptr(),
+                                     ws.numel(), sp)
             return writes, attn
         if st.dtype == "fp8":
             writes.append(functools.partial(lib.reshape_and_cache_fp8, new_key.data_ptr(), new_value.data_ptr(),
@@ -719,8 +724,8 @@ def main() -> int:
         "device_stream_copy_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_attention_decode_append (balanced-split kernel appending the new tokens + "
-                       "log-sum-exp reduce)" if append else
+            "kernel": ("paged_attention_decode_append (decode kernel appending the new tokens + log-sum-exp "
+                       "reduce when split)" if append else
                        ("paged_attention_decode" if Q == 1 else "paged_attention_decode_multi") +
                        " (partition or balanced-split kernel + log-sum-exp reduce when split)"),
             # unique bytes (shared blocks once); the logical count of the metric's byte formula beside it

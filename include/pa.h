@@ -160,32 +160,36 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
                                   size_t workspace_bytes, void *stream);
 
 /*
- * One decode step's cache write and attention in one call: reshape_and_cache(key, value, key_cache, value_cache,
- * slot_mapping, num_seqs, ...) followed by paged_attention_decode(...) over the updated pools. Each new token is
- * appended where it is produced and attends at once (page 3 section 2.1: every decode step updates the KV cache;
- * page 1 section 3.1: the new token attends over every earlier K/V of its sequence, itself included).
+ * One decode step's cache write and attention in one call: the slot-mapped write of the new rows --
+ * reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_seqs, ...) for an fp32 or bf16 cache,
+ * reshape_and_cache_fp8(..., src_dtype = q_dtype, k_scale, v_scale, ...) for an E4M3 cache -- followed by
+ * paged_attention_decode_scaled(...) over the updated pools. Each new token is appended where it is produced
+ * and attends at once (page 3 section 2.1: every decode step updates the KV cache; page 1 section 3.1: the new
+ * token attends over every earlier K/V of its sequence, itself included).
  *
- *   key, value     [num_seqs][num_kv_heads][head_dim] kv_dtype: sequence s's new token, written unchanged into
- *                  slot slot_mapping[s] of both pools (updated in place; slots < 0 or >= num_blocks * block_size
- *                  are skipped, as in reshape_and_cache)
- *   other arguments as in paged_attention_decode; kv_dtype PA_F32 or PA_BF16 (E4M3 caches: reshape_and_cache_fp8
- *                  and paged_attention_decode_scaled)
+ *   key, value     [num_seqs][num_kv_heads][head_dim]: sequence s's new token, in kv_dtype for an fp32 or bf16
+ *                  cache (written unchanged), in q_dtype for an E4M3 cache (quantised with k_scale / v_scale as
+ *                  reshape_and_cache_fp8 does); written into slot slot_mapping[s] of both pools (updated in place;
+ *                  slots < 0 or >= num_blocks * block_size are skipped, as in the cache writes)
+ *   other arguments as in paged_attention_decode_scaled
  * Contract: for every s whose slot is written, position context_lens[s] - 1 of sequence s lies in that slot
  * through the block table (the new token is the last position of the sequence) and context_lens[s] >= 1. As in
  * paged_attention_decode, lengths beyond max_context_len are clamped: such a sequence's new token is written but
- * not attended over. Where the plan is the single-head balanced split, one launch does both:
- * the last position of such a sequence is taken from `key` / `value` instead of the pool, and the wave that
- * reaches it writes it into the pools. Every other plan launches the cache write first. Either way the pools end
- * as reshape_and_cache leaves them, byte for byte, and the output equals that of the two calls up to the order
- * of floating-point additions.
+ * not attended over. Where the plan is the single-head balanced split over an fp32 or bf16 cache, or the
+ * matrix-core partition kernel, one launch does both: the last position of such a sequence is taken from
+ * `key` / `value` (quantised first for E4M3) instead of the pool, and a wave of that sequence writes it into
+ * the pools. Every other plan launches the cache write first. Either way the pools end as the cache write
+ * leaves them, byte for byte. The output equals that of the two calls bit for bit, except under the
+ * single-head balanced split, where the new token enters its row's softmax after the pool rows of its tile (the
+ * same values, another order of floating-point additions).
  */
 int paged_attention_decode_append(float *out, const void *query, const void *key, const void *value, void *key_cache,
                                   void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
-                                  const int32_t *slot_mapping, float scale, int32_t block_size, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
-                                  int32_t kv_dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
-                                  void *stream);
+                                  const int32_t *slot_mapping, float scale, float k_scale, float v_scale,
+                                  int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t max_context_len, int32_t q_dtype, int32_t kv_dtype, int32_t partition_size,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * paged_attention_decode_scaled for callers that cannot allocate device memory or pass a workspace: code under

@@ -61,8 +61,8 @@ def load_library(path: str | None = None):
     lib.paged_attention_decode_noalloc.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i64,
                                                    i32, i32, i32, i32, i32, P]
     lib.paged_attention_decode_noalloc.restype = ctypes.c_int
-    lib.paged_attention_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, f32, i32, i32, i32, i32, i32, i64, i32,
-                                                  i32, i32, i32, i32, P, sz, P]
+    lib.paged_attention_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32,
+                                                  i64, i32, i32, i32, i32, i32, P, sz, P]
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_decode_multi.argtypes = [P, P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32, i32, i32,
                                                  i32, i64, i32, i32, i32, i32, i32, P, sz, P]
@@ -234,10 +234,12 @@ def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tab
 
 def paged_attention_decode_append(out, query, key, value, key_cache, value_cache, block_tables, context_lens,
                                   slot_mapping, scale: float, *, max_context_len: int | None = None,
-                                  partition_size: int = -1, workspace=None, stream=None):
-    """One decode step's cache write and attention: reshape_and_cache(key, value, ..., slot_mapping) then
-    paged_attention_decode over the updated pools, in one launch where the plan allows (see the C header).
-    key/value: [B, Hkv, D] in the caches' dtype (float32 or bfloat16); slot_mapping: int32 [B]."""
+                                  partition_size: int = -1, workspace=None, stream=None, k_scale: float = 1.0,
+                                  v_scale: float = 1.0):
+    """One decode step's cache write and attention: the slot-mapped write of key/value (reshape_and_cache, or
+    reshape_and_cache_fp8 for an E4M3 cache) then paged_attention_decode over the updated pools, in one launch
+    where the plan allows (see the C header). key/value: [B, Hkv, D] in the caches' dtype (float32 or bfloat16),
+    or in the query's dtype for an E4M3 cache; slot_mapping: int32 [B]."""
     torch = _torch()
     dev = _dev(out, query, key, value, key_cache, value_cache, block_tables, context_lens, slot_mapping)
     if out.dtype != torch.float32:
@@ -253,13 +255,15 @@ def paged_attention_decode_append(out, query, key, value, key_cache, value_cache
         raise ValueError("key/value must be [B, Hkv, D] and slot_mapping [B]")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
         raise ValueError("block_tables must be [B, MB] and context_lens [B]")
-    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
-        raise TypeError("key, value and the caches must share one dtype")
+    qd, kd = _dtype_code(query), _dtype_code(key_cache)
+    if value_cache.dtype != key_cache.dtype or key.dtype != value.dtype:
+        raise TypeError("the two caches, and key and value, must share their dtypes")
+    if key.dtype != (query.dtype if kd == PA_FP8_E4M3 else key_cache.dtype):
+        raise TypeError("key/value must have the caches' dtype (the query's for an E4M3 cache)")
     if not (key.is_contiguous() and value.is_contiguous()):
         raise ValueError("key and value must be contiguous")
     MB = block_tables.shape[1]
     mcl = MB * bs if max_context_len is None else int(max_context_len)
-    qd, kd = _dtype_code(query), _dtype_code(key_cache)
     lib = load_library()
     need = lib.paged_attention_workspace_bytes(B, Hq, Hkv, D, mcl, bs, kd, partition_size)
     if need and workspace is None:
@@ -269,8 +273,8 @@ def paged_attention_decode_append(out, query, key, value, key_cache, value_cache
     st = lib.paged_attention_decode_append(
         out.data_ptr(), query.data_ptr(), key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
         value_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), slot_mapping.data_ptr(),
-        float(scale), bs, B, Hq, Hkv, D, NB, MB, mcl, qd, kd, int(partition_size), ws_ptr, ws_len,
-        _stream(dev, stream))
+        float(scale), float(k_scale), float(v_scale), bs, B, Hq, Hkv, D, NB, MB, mcl, qd, kd, int(partition_size),
+        ws_ptr, ws_len, _stream(dev, stream))
     _check("paged_attention_decode_append", st)
     return out
 

@@ -31,43 +31,13 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(const U4* _
   }
 }
 
-// E4M3 code of x / scale: an fp32 division (correctly rounded), saturated to +-448, rounded to nearest with
-// ties to even by the hardware conversion (which would turn |y| >= 480 into NaN, hence the clamp); NaN is
-// stored as 0x7F. Four values packed into one word, first value in the lowest byte.
-__device__ __forceinline__ float e4m3_prepare(float x, float scale) {
-  const float y = x / scale;
-  return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
-}
-__device__ __forceinline__ uint32_t nan_to_7f(uint32_t word, float a, float b, float c, float d) {
-  if (a != a) word = (word & 0xffffff00u) | 0x7fu;
-  if (b != b) word = (word & 0xffff00ffu) | 0x7f00u;
-  if (c != c) word = (word & 0xff00ffffu) | 0x7f0000u;
-  if (d != d) word = (word & 0x00ffffffu) | 0x7f000000u;
-  return word;
-}
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float scale) {
-  a = e4m3_prepare(a, scale);
-  b = e4m3_prepare(b, scale);
-  c = e4m3_prepare(c, scale);
-  d = e4m3_prepare(d, scale);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return nan_to_7f((uint32_t)w, a, b, c, d);
-}
-
-// 16 consecutive source elements (float32 or bf16) -> 16 E4M3 codes.
+// 16 consecutive source elements (float32 or bf16) -> 16 E4M3 codes (e4m3_pack16 in pa_device.h).
 template <int SRC>
-__device__ __forceinline__ U4 e4m3_pack16(const char* src, float scale) {
-  float f[16];
+__device__ __forceinline__ U4 e4m3_pack16_from(const char* src, float scale) {
   if constexpr (SRC == PA_BF16) {
-    const U4 a = *reinterpret_cast<const U4*>(src), b = *reinterpret_cast<const U4*>(src + 16);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f[2 * i] = bf16_lo(w[i]);
-      f[2 * i + 1] = bf16_hi(w[i]);
-    }
+    return e4m3_pack16_bf16(*reinterpret_cast<const U4*>(src), *reinterpret_cast<const U4*>(src + 16), scale);
   } else {
+    float f[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const U4 v = reinterpret_cast<const U4*>(src)[i];
@@ -76,9 +46,8 @@ __device__ __forceinline__ U4 e4m3_pack16(const char* src, float scale) {
       f[4 * i + 2] = __uint_as_float(v.z);
       f[4 * i + 3] = __uint_as_float(v.w);
     }
+    return e4m3_pack16(f, scale);
   }
-  return U4{e4m3_pack4(f[0], f[1], f[2], f[3], scale), e4m3_pack4(f[4], f[5], f[6], f[7], scale),
-            e4m3_pack4(f[8], f[9], f[10], f[11], scale), e4m3_pack4(f[12], f[13], f[14], f[15], scale)};
 }
 
 // Quantising cache write: one workgroup per new token, one 16-element word per thread and step.
@@ -97,8 +66,8 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
   U4* kd = key_cache + (int64_t)slot * words;
   U4* vd = value_cache + (int64_t)slot * words;
   for (int64_t i = threadIdx.x; i < words; i += kThreads) {
-    kd[i] = e4m3_pack16<SRC>(ks + i * 16 * kSrcEsize, k_scale);
-    vd[i] = e4m3_pack16<SRC>(vs + i * 16 * kSrcEsize, v_scale);
+    kd[i] = e4m3_pack16_from<SRC>(ks + i * 16 * kSrcEsize, k_scale);
+    vd[i] = e4m3_pack16_from<SRC>(vs + i * 16 * kSrcEsize, v_scale);
   }
 }
 

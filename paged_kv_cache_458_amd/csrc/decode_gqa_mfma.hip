@@ -356,7 +356,7 @@ __device__ __forceinline__ void gqa_offsets(int rr, int rc, int64_t row_bytes, i
 // one (measured on MI355X with 4, 2 and 1 KV heads: 3-8% slower). A wave serves NCG consecutive groups of 16
 // columns (1, or 2 at head_dim <= 128 where the registers hold two accumulators): they share every K/V load and
 // every LDS operand read.
-template <int KV, int D, int W, int NCG>
+template <int KV, int D, int W, int NCG, bool kAppend>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const DecodeArgs a) {
   using S = GqaShape<KV, D>;
   constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
@@ -458,9 +458,60 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   gqa_offsets<KV, D>(rr, rc, row_bytes, head_off, off);
   const bool stage_lane = rc < S::kStageLanes;
 
+  // Decode with the sequence's new token appended in this launch (the cache write of page 3 section 2.1 and the
+  // attention over it in one pass). Every lane of a head row's lane group loads its piece of head g's new K/V
+  // row: 16 bytes as given, or 32 bytes of bf16 that become 16 E4M3 codes, quantised exactly as the quantising
+  // cache write does, where they are used. The loads are unconditional and their registers are read only where
+  // the row is used, so no wait for them holds back the first tile's loads. The wave of the first span and
+  // column-group slot stores the row into its slot of both pools, after its loop; the wave whose span holds the
+  // new position stages the row over the tile's pool row, which may or may not have been written yet. A token
+  // whose slot the cache write would skip (slot < 0 or past the pool) is neither written nor substituted.
+  constexpr int kNewPieces = S::kRaw ? 2 : 1;
+  int tj_new = -1, r_new = 0;
+  bool lane_new = false, lane_store = false;
+  int64_t store_at = 0;
+  U4 nk[kNewPieces], nv[kNewPieces];
+  if constexpr (kAppend) {
+    const bool piece = rc < S::kHeadLanes;
+    // this lane's piece of the input row (the first piece for lanes past the row), in 16-byte units
+    const int64_t src = (((int64_t)s * a.num_kv_heads + g) * D * (S::kRaw ? 2 : kEsize)) / 16 +
+                        (piece ? rc : 0) * kNewPieces;
+#pragma unroll
+    for (int e = 0; e < kNewPieces; ++e) {
+      nk[e] = static_cast<const U4*>(a.new_key)[src + e];
+      nv[e] = static_cast<const U4*>(a.new_value)[src + e];
+    }
+    const int Lraw = a.context_lens[s];
+    const int64_t slot = a.slot_mapping[s];
+    if (slot >= 0 && slot < (a.num_blocks << a.bs_log2) && Lraw >= 1) {
+      lane_store = cg == 0 && by == 0 && rr == 0 && piece;
+      store_at = slot * row_bytes + head_off + rc * 16;
+      const int p = Lraw - 1;
+      if (Lraw <= a.max_context_len && p >= u0 && p < u1) {
+        tj_new = (p - u0) / kTileTok;
+        r_new = (p - u0) % kTileTok;
+        lane_new = piece && rr == (r_new % kTile) % S::kRows;
+      }
+    }
+  }
+  // the lane's 16 bytes of the new K or V row as the pool holds them
+  auto new_piece = [&](const U4* raw, float scale) __attribute__((always_inline)) {
+    if constexpr (S::kRaw)
+      return e4m3_pack16_bf16(raw[0], raw[1], scale);
+    else
+      return raw[0];
+  };
+
   const char* __restrict__ kbase = static_cast<const char*>(a.key_cache);
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
-  const int32_t* __restrict__ table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  // with the pool stores of an appended decode, the table is read through the constant address space: only
+  // there do its loads stay scalar, and the tile descriptors wave-uniform
+  const auto* __restrict__ table = [&] {
+    if constexpr (kAppend)
+      return as_constant(a.block_tables);
+    else
+      return a.block_tables;
+  }() + (int64_t)s * a.max_blocks_per_seq;
 
   float m[NCG], l[NCG];
   f32x4 o[NCG][kNt];
@@ -547,11 +598,17 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     }
   };
 
+  // the appended row over the staged pool row: the same lane staged that piece, so its write lands after
+  auto substitute = [&](int tj, char* slice, const U4* raw, float scale) __attribute__((always_inline)) {
+    if constexpr (kAppend)
+      if (tj == tj_new && lane_new) *reinterpret_cast<U4*>(slice + r_new * kPitch + rc * 16) = new_piece(raw, scale);
+  };
   auto tile_step = [&](int tj) {
     const int t = u0 + tj * kTileTok;
     const bool full = t + kTileTok <= ufull;  // no column masks a position of a tile below ufull
     wave_lds_sync();  // the previous tile's reads come first
     gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
+    substitute(tj, kslice, nk, a.new_k_scale);
     if constexpr (S::kPhased) {
       wave_lds_sync();
       issue_v(tj);
@@ -559,11 +616,13 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
       gqa_scores<KV, D, NCG>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
       wave_lds_sync();
       gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
+      substitute(tj, vslice, nv, a.new_v_scale);
       wave_lds_sync();
       issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
       gqa_pv<KV, D, NCG>(rbase, pb, pl, o);
     } else {
       gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
+      substitute(tj, vslice, nv, a.new_v_scale);
       wave_lds_sync();
       issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
       gqa_compute<KV, D, NCG>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
@@ -595,6 +654,12 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // an empty context writes a zero row (l = 0)
 #pragma unroll
   for (int k = 0; k < NCG; ++k) write_rows(k, by, m[k], l[k], o[k]);
+  if constexpr (kAppend) {
+    if (lane_store) {
+      *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + store_at) = new_piece(nk, a.new_k_scale);
+      *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + store_at) = new_piece(nv, a.new_v_scale);
+    }
+  }
 }
 
 // Balanced split (one column group: the G heads of a KV head times at most 16 / G query rows per sequence). With
@@ -855,7 +920,12 @@ hipError_t launch_wc(const DecodeArgs& a, hipStream_t stream) {
   // the waves' column-group slots share the x dimension with the KV-head groups (the kernel unpacks them)
   const int nslots = (a.col_groups + NCG - 1) / NCG;
   const dim3 grid((a.num_kv_heads + W - 1) / W * nslots, groups, a.num_seqs);
-  decode_gqa_mfma_kernel<KV, D, W, NCG><<<grid, dim3(kWave * W), 0, stream>>>(a);
+  if (a.new_key) {  // appended decode: one new token (query row) per sequence
+    if (a.query_start) return hipErrorInvalidValue;
+    decode_gqa_mfma_kernel<KV, D, W, NCG, true><<<grid, dim3(kWave * W), 0, stream>>>(a);
+  } else {
+    decode_gqa_mfma_kernel<KV, D, W, NCG, false><<<grid, dim3(kWave * W), 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -944,7 +1014,7 @@ int32_t gqa_balanced_chunks(int32_t num_kv_heads) {
 
 hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   if (a.num_seqs > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix || a.col_groups != 1 ||
-      a.group * a.max_query_len > 16 || !a.seq_prefix)
+      a.group * a.max_query_len > 16 || !a.seq_prefix || a.new_key)
     return hipErrorInvalidValue;
   if (kv_dtype == PA_BF16) return dispatch_dim<PA_BF16, LaunchBalanced>(a, stream);
   if (kv_dtype == PA_FP8_E4M3) return dispatch_dim<PA_FP8_E4M3, LaunchBalanced>(a, stream);

@@ -850,6 +850,7 @@ hipError_t launch_kv(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t str
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
+  if (a.new_key) return hipErrorInvalidValue;  // the partition kernel does not append
   const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.split ? a.max_partitions : 1,
                   a.num_tokens);
   const dim3 block(kWave * kWavesPerGroup);

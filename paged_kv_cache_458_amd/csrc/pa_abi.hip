@@ -409,23 +409,34 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   a.slot_mapping = nullptr;
   a.key_out = nullptr;
   a.value_out = nullptr;
+  a.new_k_scale = k_scale;
+  a.new_v_scale = v_scale;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (app) {
-    // The single-head balanced split appends the new tokens itself; every other plan writes them first, as
-    // reshape_and_cache would, and then attends.
-    if (plan.balanced && !plan.mfma && !query_start && (kv_dtype == PA_BF16 || kv_dtype == PA_F32)) {
+    // The single-head balanced split (fp32 and bf16 caches) and the matrix-core partition kernel (bf16 caches,
+    // and E4M3 caches from bf16 rows) append the new tokens themselves; every other plan writes them first, as
+    // reshape_and_cache or reshape_and_cache_fp8 would, and then attends.
+    const bool fused =
+        !query_start && ((plan.balanced && !plan.mfma && (kv_dtype == PA_BF16 || kv_dtype == PA_F32)) ||
+                         (plan.mfma && !plan.balanced && (kv_dtype == PA_BF16 || q_dtype == PA_BF16)));
+    hipError_t e = hipSuccess;
+    if (fused) {
       a.new_key = app->key;
       a.new_value = app->value;
       a.slot_mapping = app->slot_mapping;
       a.key_out = app->key_cache;
       a.value_out = app->value_cache;
-    } else if (pa::launch_reshape_and_cache(app->key, app->value, app->key_cache, app->value_cache,
-                                            app->slot_mapping, num_seqs,
-                                            (int64_t)num_kv_heads * head_dim * esize_of(kv_dtype), block_size,
-                                            num_blocks, st) != hipSuccess) {
-      return PA_ERR_HIP;
+    } else if (kv_dtype == PA_FP8_E4M3) {
+      e = pa::launch_reshape_and_cache_fp8(app->key, app->value, app->key_cache, app->value_cache, app->slot_mapping,
+                                           num_seqs, (int64_t)num_kv_heads * head_dim, block_size, num_blocks,
+                                           q_dtype, k_scale, v_scale, st);
+    } else {
+      e = pa::launch_reshape_and_cache(app->key, app->value, app->key_cache, app->value_cache, app->slot_mapping,
+                                       num_seqs, (int64_t)num_kv_heads * head_dim * esize_of(kv_dtype), block_size,
+                                       num_blocks, st);
     }
+    if (e != hipSuccess) return PA_ERR_HIP;
   }
   if (plan.balanced) {
     const hipError_t e = plan.mfma ? pa::launch_decode_gqa_mfma_balanced(a, kv_dtype, st)
@@ -470,21 +481,25 @@ int paged_attention_decode_noalloc(float* out, const void* query, const void* ke
 
 int paged_attention_decode_append(float* out, const void* query, const void* key, const void* value, void* key_cache,
                                   void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
-                                  const int32_t* slot_mapping, float scale, int32_t block_size, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t q_dtype,
-                                  int32_t kv_dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-  // the cache write's own checks first (those of reshape_and_cache for num_seqs new rows), then the decode's
+                                  const int32_t* slot_mapping, float scale, float k_scale, float v_scale,
+                                  int32_t block_size, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t max_context_len, int32_t q_dtype, int32_t kv_dtype, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  // the cache write's own checks first (those of reshape_and_cache, or of reshape_and_cache_fp8 with the query's
+  // dtype as the source, for num_seqs new rows), then the decode's
   if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
-  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16) return PA_ERR_DTYPE;
-  if ((int64_t)num_kv_heads * head_dim * esize_of(kv_dtype) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  const bool quantise = kv_dtype == PA_FP8_E4M3;
+  if (quantise ? q_dtype != PA_BF16 && q_dtype != PA_F32 : kv_dtype != PA_F32 && kv_dtype != PA_BF16)
+    return PA_ERR_DTYPE;
+  if (quantise && (!finite_nonzero(k_scale) || !finite_nonzero(v_scale))) return PA_ERR_SHAPE;
+  if ((int64_t)num_kv_heads * head_dim * (quantise ? 1 : esize_of(kv_dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 0) {
     if (!key || !value || !slot_mapping) return PA_ERR_NULL;
     if (!aligned16(key) || !aligned16(value) || !aligned4(slot_mapping)) return PA_ERR_ALIGN;
   }
   const Append app{key, value, key_cache, value_cache, slot_mapping};
-  return attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr, scale, 1.0f, 1.0f,
+  return attention(out, query, key_cache, value_cache, block_tables, context_lens, nullptr, scale, k_scale, v_scale,
                    block_size, num_seqs, num_seqs, 1, num_q_heads, num_kv_heads, head_dim, num_blocks,
                    max_blocks_per_seq, max_context_len, q_dtype, kv_dtype, partition_size, workspace, workspace_bytes,
                    stream, /*static_scratch=*/false, &app);

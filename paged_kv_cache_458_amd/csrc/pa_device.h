@@ -56,6 +56,48 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint3
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// OCP E4M3 quantisation, shared by the quantising cache write and the decode kernels that append a new row
+// themselves, so both store the same codes. The code of x / scale: an fp32 division (correctly rounded),
+// saturated to +-448, rounded to nearest with ties to even by the hardware conversion (which would turn
+// |y| >= 480 into NaN, hence the clamp); NaN is stored as 0x7F. Four values packed into one word, first value in
+// the lowest byte.
+__device__ __forceinline__ float e4m3_prepare(float x, float scale) {
+  const float y = x / scale;
+  return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
+}
+__device__ __forceinline__ uint32_t nan_to_7f(uint32_t word, float a, float b, float c, float d) {
+  if (a != a) word = (word & 0xffffff00u) | 0x7fu;
+  if (b != b) word = (word & 0xffff00ffu) | 0x7f00u;
+  if (c != c) word = (word & 0xff00ffffu) | 0x7f0000u;
+  if (d != d) word = (word & 0x00ffffffu) | 0x7f000000u;
+  return word;
+}
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float scale) {
+  a = e4m3_prepare(a, scale);
+  b = e4m3_prepare(b, scale);
+  c = e4m3_prepare(c, scale);
+  d = e4m3_prepare(d, scale);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return nan_to_7f((uint32_t)w, a, b, c, d);
+}
+// 16 values -> 16 codes
+__device__ __forceinline__ U4 e4m3_pack16(const float* f, float scale) {
+  return U4{e4m3_pack4(f[0], f[1], f[2], f[3], scale), e4m3_pack4(f[4], f[5], f[6], f[7], scale),
+            e4m3_pack4(f[8], f[9], f[10], f[11], scale), e4m3_pack4(f[12], f[13], f[14], f[15], scale)};
+}
+// 16 consecutive bf16 values, as two 16-byte pieces -> 16 codes
+__device__ __forceinline__ U4 e4m3_pack16_bf16(U4 a, U4 b, float scale) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+  return e4m3_pack16(f, scale);
+}
+
 // ---------------------------------------------------------------------------------------------------------
 // Paged addressing (vLLM PagedAttention, page 1 section 3.2; page 3 section 2.2). Pools are
 // [num_blocks][block_size][num_kv_heads][head_dim]; one "row" is a slot: all KV heads of one position,

@@ -34,13 +34,15 @@ struct DecodeArgs {
   int32_t chunks;              // balanced split: runs of tiles per query head (0: partitions as above)
   int32_t* tile_prefix;        // balanced split: tiles of the rows before each row, [T + 1] (workspace) ...
   int32_t seq_prefix;          // ... or, when 1 (matrix-core kernel), of the sequences before each, [B + 1]
-  // Decode with each sequence's new token appended in the same launch (single-head balanced split): the new K/V
-  // rows [B][Hkv][D] in the cache's dtype, their slots [B], and the pools they are written to. Null otherwise.
+  // Decode with each sequence's new token appended in the same launch: the new K/V rows [B][Hkv][D] (in the
+  // cache's dtype, or bf16 for an E4M3 cache, quantised with the scales below as the cache write does), their
+  // slots [B], and the pools they are written to. Null otherwise.
   const void* new_key;
   const void* new_value;
   const int32_t* slot_mapping;
   void* key_out;
   void* value_out;
+  float new_k_scale, new_v_scale;
 };
 
 // The sequence that owns query row t: the last s with query_start[s] <= t (empty sequences are skipped since the

@@ -68,7 +68,8 @@ def test_binding_matches_header_prototypes():
 
 def append_call(**over):
     args = dict(out=FAKE, query=FAKE, key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE, block_tables=FAKE,
-                context_lens=FAKE, slot_mapping=FAKE, scale=0.1, block_size=16, num_seqs=4, num_q_heads=8,
+                context_lens=FAKE, slot_mapping=FAKE, scale=0.1, k_scale=1.0, v_scale=1.0, block_size=16,
+                num_seqs=4, num_q_heads=8,
                 num_kv_heads=8, head_dim=128, num_blocks=100, max_blocks_per_seq=8, max_context_len=128,
                 q_dtype=pa.PA_BF16, kv_dtype=pa.PA_BF16, partition_size=-1, workspace=None, workspace_bytes=0,
                 stream=None)
@@ -77,8 +78,12 @@ def append_call(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(kv_dtype=pa.PA_FP8_E4M3), PA_ERR_DTYPE),     # E4M3 caches take the quantising write
     (dict(kv_dtype=7), PA_ERR_DTYPE),
+    (dict(kv_dtype=pa.PA_FP8_E4M3, q_dtype=7), PA_ERR_DTYPE),          # the quantising write's source dtype
+    (dict(kv_dtype=pa.PA_FP8_E4M3, q_dtype=pa.PA_F32), PA_ERR_DTYPE),  # the decode takes E4M3 under bf16 only
+    (dict(kv_dtype=pa.PA_FP8_E4M3, k_scale=0.0), PA_ERR_SHAPE),
+    (dict(kv_dtype=pa.PA_FP8_E4M3, v_scale=float("inf")), PA_ERR_SHAPE),
+    (dict(kv_dtype=pa.PA_FP8_E4M3, key=None), PA_ERR_NULL),
     (dict(key=None), PA_ERR_NULL),
     (dict(slot_mapping=None), PA_ERR_NULL),
     (dict(value=FAKE + 8), PA_ERR_ALIGN),

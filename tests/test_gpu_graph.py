@@ -2,7 +2,7 @@
 
 The library allocates nothing, clears nothing with memsets and never synchronises, so a whole decode step --
 the slot-mapped write of the new token's K/V, then paged attention with its merge kernel -- can be captured
-once (torch.cuda.graph) and replayed. Each replay starts from the pristine pools and a NaN-filled output,
+once (torch.cuda.graph) and replayed. So can the call that does both, paged_attention_decode_append. Each replay starts from the pristine pools and a NaN-filled output,
 with eager work and host synchronisations between replays, and must reproduce the eager step bit for bit:
 output and both pools.
 """
@@ -41,11 +41,15 @@ CASES = [
     (32, 8, 512, "bf16", "matrix-core partitions, two per wave, + log-sum-exp merge"),
     (32, 8, pa.PA_PARTITION_BALANCED, "bf16", "matrix-core balanced split + merge"),
     (8, 8, -1, "fp8", "E4M3: quantising cache write, balanced split with two heads per wave + merge"),
+    (8, 8, -1, "bf16+append", "one call: new rows written by the balanced split's launch + merge"),
+    (32, 8, 512, "bf16+append", "one call: cache write launch, matrix-core partitions + merge"),
 ]
 
 
 @pytest.mark.parametrize("hq,hkv,part,dt,what", CASES, ids=[c[4] for c in CASES])
 def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, dt, what):
+    append = dt.endswith("+append")
+    dt = dt.split("+")[0]
     st = custom_structure("graph", 461, [700, 1500, 33, 2048, 1, 900], hq, hkv, 128, 16, dt)
     t = materialize(st, DEV, include_new_token=False)
     kc, vc = t["key_cache"], t["value_cache"]
@@ -58,6 +62,11 @@ def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, dt, what):
     out = torch.empty((st.num_seqs, hq, st.head_dim), dtype=torch.float32, device=DEV)
 
     def step():
+        if append:
+            pa.paged_attention_decode_append(out, t["query"], t["new_key"], t["new_value"], kc, vc, tables, lens,
+                                             slots, st.scale, max_context_len=st.max_context_len,
+                                             partition_size=part, workspace=ws)
+            return
         pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots, k_scale=st.k_scale, v_scale=st.v_scale)
         pa.paged_attention_decode(out, t["query"], kc, vc, tables, lens, st.scale, st.block_size,
                                   max_context_len=st.max_context_len, partition_size=part, workspace=ws,
