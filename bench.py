@@ -52,14 +52,14 @@ def kernel_source_hash() -> str:
 
 def step_appends(pa, st, query_len: int, launched_part: int, separate_write: bool = False) -> bool:
     """Whether the benchmark's step writes the new tokens inside the decode launch: paged_attention_decode_append
-    does so under the single-head balanced split over an fp32 or bf16 cache and in the matrix-core partition
-    kernel (grouped heads over bf16 or E4M3 caches). Elsewhere the call launches the cache write first, so the
-    step keeps the two calls and times the attention alone."""
+    does so under the single-head balanced split and in the matrix-core partition kernel (grouped heads over
+    bf16 or E4M3 caches). Elsewhere the call launches the cache write first, so the step keeps the two calls and
+    times the attention alone."""
     if query_len != 1 or separate_write:
         return False
     mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
     balanced = launched_part == pa.PA_PARTITION_BALANCED
-    return (mfma and not balanced) or (not mfma and balanced and st.dtype != "fp8")
+    return mfma != balanced
 
 
 def appended_row_bytes(st) -> int:

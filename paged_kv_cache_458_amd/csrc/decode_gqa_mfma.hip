@@ -461,8 +461,8 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // Decode with the sequence's new token appended in this launch (the cache write of page 3 section 2.1 and the
   // attention over it in one pass). Every lane of a head row's lane group loads its piece of head g's new K/V
   // row: 16 bytes as given, or 32 bytes of bf16 that become 16 E4M3 codes, quantised exactly as the quantising
-  // cache write does, where they are used. The loads are unconditional and their registers are read only where
-  // the row is used, so no wait for them holds back the first tile's loads. The wave of the first span and
+  // cache write does. The loads are unconditional, and their registers are first read once the first tile's
+  // loads are in flight, so no wait for them holds back those loads. The wave of the first span and
   // column-group slot stores the row into its slot of both pools, after its loop; the wave whose span holds the
   // new position stages the row over the tile's pool row, which may or may not have been written yet. A token
   // whose slot the cache write would skip (slot < 0 or past the pool) is neither written nor substituted.
@@ -471,6 +471,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   bool lane_new = false, lane_store = false;
   int64_t store_at = 0;
   U4 nk[kNewPieces], nv[kNewPieces];
+  U4 nkc{}, nvc{};  // the pieces as the pool holds them
   if constexpr (kAppend) {
     const bool piece = rc < S::kHeadLanes;
     // this lane's piece of the input row (the first piece for lanes past the row), in 16-byte units
@@ -599,16 +600,16 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   };
 
   // the appended row over the staged pool row: the same lane staged that piece, so its write lands after
-  auto substitute = [&](int tj, char* slice, const U4* raw, float scale) __attribute__((always_inline)) {
+  auto substitute = [&](int tj, char* slice, const U4& piece) __attribute__((always_inline)) {
     if constexpr (kAppend)
-      if (tj == tj_new && lane_new) *reinterpret_cast<U4*>(slice + r_new * kPitch + rc * 16) = new_piece(raw, scale);
+      if (tj == tj_new && lane_new) *reinterpret_cast<U4*>(slice + r_new * kPitch + rc * 16) = piece;
   };
   auto tile_step = [&](int tj) {
     const int t = u0 + tj * kTileTok;
     const bool full = t + kTileTok <= ufull;  // no column masks a position of a tile below ufull
     wave_lds_sync();  // the previous tile's reads come first
     gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
-    substitute(tj, kslice, nk, a.new_k_scale);
+    substitute(tj, kslice, nkc);
     if constexpr (S::kPhased) {
       wave_lds_sync();
       issue_v(tj);
@@ -616,13 +617,13 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
       gqa_scores<KV, D, NCG>(kread, qb, a.scale_log2, t, full, lim, j, m, l, o, pb, pl);
       wave_lds_sync();
       gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
-      substitute(tj, vslice, nv, a.new_v_scale);
+      substitute(tj, vslice, nvc);
       wave_lds_sync();
       issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
       gqa_pv<KV, D, NCG>(rbase, pb, pl, o);
     } else {
       gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
-      substitute(tj, vslice, nv, a.new_v_scale);
+      substitute(tj, vslice, nvc);
       wave_lds_sync();
       issue_kv(tj + 1);  // past the last tile every row is beyond the range: nothing is read
       gqa_compute<KV, D, NCG>(kread, rbase, qb, a.scale_log2, t, full, lim, j, m, l, o);
@@ -630,6 +631,10 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   };
   if (ntiles > 0) {
     issue_kv(0);
+    if constexpr (kAppend) {  // (computed inside the tile loop, it would be hoisted before the loads above)
+      nkc = new_piece(nk, a.new_k_scale);
+      nvc = new_piece(nv, a.new_v_scale);
+    }
     // The tiles of the first partition, the park, then the rest: two loops around one pipeline. (A park taken
     // conditionally inside a single loop made the compiler copy every accumulator and parked register on each
     // tile, about 100 moves per tile.)
@@ -656,8 +661,12 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   for (int k = 0; k < NCG; ++k) write_rows(k, by, m[k], l[k], o[k]);
   if constexpr (kAppend) {
     if (lane_store) {
-      *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + store_at) = new_piece(nk, a.new_k_scale);
-      *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + store_at) = new_piece(nv, a.new_v_scale);
+      if (ntiles <= 0) {
+        nkc = new_piece(nk, a.new_k_scale);
+        nvc = new_piece(nv, a.new_v_scale);
+      }
+      *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + store_at) = nkc;
+      *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + store_at) = nvc;
     }
   }
 }

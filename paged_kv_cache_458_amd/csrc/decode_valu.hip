@@ -573,7 +573,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
   U4 kb[kBalStages][NL], vb[kBalStages][NL];
   Words<S::kQWords> qb[kBalStages];
   uint32_t info[kBalStages];
-  U4 kn[kBalStages], vn[kBalStages];  // appended decode: the new token's K/V chunk (row group 0's lanes)
+  // appended decode: the new token's K/V chunk, as given (row group 0's lanes) or, for an E4M3 cache, as the 32
+  // bytes of bf16 that its 16 codes are quantised from, the first half in row group 0's lanes and the second in
+  // row group 1's (one 16-byte load per lane, as for the other dtypes)
+  constexpr bool kQuantNew = S::kEsize == 1;
+  static_assert(!kQuantNew || S::kRows >= 2, "an E4M3 row's new token takes two row groups");
+  U4 kn[kBalStages], vn[kBalStages];
   int nslot[kBalStages];
   const char* __restrict__ nkbase = static_cast<const char*>(a.new_key);
   const char* __restrict__ nvbase = static_cast<const char*>(a.new_value);
@@ -600,10 +605,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     if constexpr (kAppend) {
       // issued for every tile (an empty descriptor reads nothing), so that the loads in flight are the same on
       // every path and the waits for a tile's K/V stay as tight as without the append
-      const uint32_t noff = r == 0 && lane_ok ? lane_off[0] : kNowhere;
-      const uint32_t nbytes = newtok ? (uint32_t)row_bytes : 0u;
-      kq_new = load16<0>(make_rsrc(nkbase + (int64_t)i_row * row_bytes, nbytes), noff);
-      vq_new = load16<0>(make_rsrc(nvbase + (int64_t)i_row * row_bytes, nbytes), noff);
+      // (bf16 rows of an E4M3 cache take twice the bytes of the pool's rows, at twice the offsets)
+      constexpr int kW = kQuantNew ? 2 : 1;
+      const uint32_t noff = !lane_ok || r >= kW ? kNowhere : (lane_off[0] - (uint32_t)(r * row_bytes)) * kW + 16 * r;
+      const uint32_t nbytes = newtok ? (uint32_t)(row_bytes * kW) : 0u;
+      kq_new = load16<0>(make_rsrc(nkbase + (int64_t)i_row * row_bytes * kW, nbytes), noff);
+      vq_new = load16<0>(make_rsrc(nvbase + (int64_t)i_row * row_bytes * kW, nbytes), noff);
       slot_new = i_slot;
     }
     const uint32_t live0 = (uint32_t)(kHalves ? min(rows, kTile / 2) : rows) * (uint32_t)row_bytes;
@@ -682,6 +689,17 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     seg_bad = false;
   };
 
+  // the new token's 16 bytes as the pool holds them, in row group 0's lanes (E4M3: quantised exactly as the
+  // quantising cache write does, from the two halves; called by the whole wave)
+  auto new_piece = [&](const U4& mine, float scale) __attribute__((always_inline)) {
+    if constexpr (kQuantNew) {
+      const U4 hi{(uint32_t)__shfl_down((int)mine.x, S::kRowLanes), (uint32_t)__shfl_down((int)mine.y, S::kRowLanes),
+                  (uint32_t)__shfl_down((int)mine.z, S::kRowLanes), (uint32_t)__shfl_down((int)mine.w, S::kRowLanes)};
+      return e4m3_pack16_bf16(mine, hi, scale);
+    } else {
+      return mine;
+    }
+  };
   auto consume = [&](const U4* kq, const U4* vq, const Words<S::kQWords>& qq, uint32_t tinfo, const U4& kq_new,
                      const U4& vq_new, int slot_new) {
     tinfo = __builtin_amdgcn_readfirstlane(tinfo);
@@ -716,7 +734,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     if constexpr (kAppend) {
       if (tinfo & kNewAttend) {
         // the new token, one more position of row group 0 (the other groups' state does not move)
-        float sn = group_sum<S::kSumLanes>(dot_chunk<KV>(q, kq_new)) * a.scale_log2;
+        float sn = group_sum<S::kSumLanes>(dot_chunk<KV>(q, new_piece(kq_new, a.new_k_scale))) * a.scale_log2;
         if (r != 0) sn = -INFINITY;
         const float m2 = fmaxf(m, sn);
         const float mref2 = m2 == -INFINITY ? 0.f : m2;
@@ -725,15 +743,16 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
         l = l * alpha2 + pn;
 #pragma unroll
         for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha2;
-        axpy_chunk<KV>(acc, pn, vq_new);
+        axpy_chunk<KV>(acc, pn, new_piece(vq_new, a.new_v_scale));
         m = m2;
       }
       if (tinfo & kNew) {
         // its rows into the pools, by one wave per KV head
+        const U4 kp = new_piece(kq_new, a.new_k_scale), vp = new_piece(vq_new, a.new_v_scale);
         if (r == 0 && lane_ok && h % a.group == 0) {
           const int64_t dst = (int64_t)slot_new * row_bytes + lane_off[0];
-          *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + dst) = kq_new;
-          *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + dst) = vq_new;
+          *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + dst) = kp;
+          *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + dst) = vp;
         }
       }
     }
@@ -893,13 +912,9 @@ template <int KV>
 hipError_t launch_balanced_dtype(const DecodeArgs& a, int hpw, dim3 grid, dim3 block, hipStream_t stream) {
   const bool multi = a.query_start != nullptr;
   const size_t lds = (size_t)((multi ? 3 : a.new_key ? 4 : 2) * (int64_t)a.num_tokens + 1) * sizeof(int32_t);
-  if (a.new_key) {  // appended decode: one new token per sequence, caches of the new rows' dtype
-    if constexpr (KV == PA_FP8_E4M3) {
-      return hipErrorInvalidValue;
-    } else {
-      if (multi) return hipErrorInvalidValue;
-      return launch_balanced_kv<KV, false, true>(a, hpw, grid, block, lds, stream);
-    }
+  if (a.new_key) {  // appended decode: one new token per sequence (rows in the cache's dtype, bf16 for E4M3)
+    if (multi) return hipErrorInvalidValue;
+    return launch_balanced_kv<KV, false, true>(a, hpw, grid, block, lds, stream);
   }
   return multi ? launch_balanced_kv<KV, true, false>(a, hpw, grid, block, lds, stream)
                : launch_balanced_kv<KV, false, false>(a, hpw, grid, block, lds, stream);

@@ -414,12 +414,11 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (app) {
-    // The single-head balanced split (fp32 and bf16 caches) and the matrix-core partition kernel (bf16 caches,
-    // and E4M3 caches from bf16 rows) append the new tokens themselves; every other plan writes them first, as
+    // The single-head balanced split and the matrix-core partition kernel append the new tokens themselves (for
+    // an E4M3 cache from bf16 rows, which every E4M3 decode has); every other plan writes them first, as
     // reshape_and_cache or reshape_and_cache_fp8 would, and then attends.
-    const bool fused =
-        !query_start && ((plan.balanced && !plan.mfma && (kv_dtype == PA_BF16 || kv_dtype == PA_F32)) ||
-                         (plan.mfma && !plan.balanced && (kv_dtype == PA_BF16 || q_dtype == PA_BF16)));
+    const bool fused = !query_start && (kv_dtype != PA_FP8_E4M3 || q_dtype == PA_BF16) &&
+                       ((plan.balanced && !plan.mfma) || (plan.mfma && !plan.balanced));
     hipError_t e = hipSuccess;
     if (fused) {
       a.new_key = app->key;

@@ -67,7 +67,7 @@ def fused_here(st, partition_size) -> str | None:
                                  st.block_size, kd, partition_size)
     mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
     if part == pa.PA_PARTITION_BALANCED:
-        return None if mfma or st.dtype == "fp8" else "single-head balanced"
+        return None if mfma else "single-head balanced"
     return "matrix-core partitions" if mfma else None
 
 
@@ -127,8 +127,7 @@ SMALL = [
     (608, [700, 1, 65, 2048, 129], 16, 4, 256, 16, "bf16"),
     (609, [40, 1300, 1, 257], 64, 2, 64, 8, "bf16"),
     (611, [3000, 45, 800, 1], 32, 4, 112, 32, "bf16"),
-    # E4M3 caches from bf16 rows: grouped heads quantise the appended row in the matrix-core kernel, single
-    # heads write it with the quantising cache write first
+    # E4M3 caches from bf16 rows: the kernels that append quantise the new row where they use it
     (612, [1, 32, 33, 1024, 1025, 2000, 513], 32, 8, 128, 16, "fp8"),
     (613, [31, 97, 1500, 1, 600], 8, 2, 80, 16, "fp8"),
     (614, [700, 1, 65, 2048, 129], 16, 4, 256, 16, "fp8"),
