@@ -52,14 +52,13 @@ def kernel_source_hash() -> str:
 
 def step_appends(pa, st, query_len: int, launched_part: int, separate_write: bool = False) -> bool:
     """Whether the benchmark's step writes the new tokens inside the decode launch: paged_attention_decode_append
-    does so under the single-head balanced split and in the matrix-core partition kernel (grouped heads over
-    bf16 or E4M3 caches). Elsewhere the call launches the cache write first, so the step keeps the two calls and
-    times the attention alone."""
-    if query_len != 1 or separate_write:
+    does so under both kernels' balanced splits and in the matrix-core partition kernel (grouped heads over bf16
+    or E4M3 caches). Under the single-head partition kernel the call launches the cache write first, so the step
+    keeps the two calls and times the attention alone."""
+    if query_len != 1 or separate_write or st.max_context_len < 1:
         return False
     mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
-    balanced = launched_part == pa.PA_PARTITION_BALANCED
-    return mfma != balanced
+    return mfma or launched_part == pa.PA_PARTITION_BALANCED
 
 
 def appended_row_bytes(st) -> int:

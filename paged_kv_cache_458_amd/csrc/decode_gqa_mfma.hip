@@ -686,7 +686,12 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
 //
 // Every workgroup first derives the prefix of the sequences' tile counts in LDS; the first one also
 // publishes it for the merge.
-template <int KV, int D, int W>
+//
+// Decode with each sequence's new token appended in this launch (kAppend; one query row per sequence): as in the
+// partition kernel, every lane loads its piece of head g's new row, for each sequence when its query comes in,
+// and the wave whose run holds the sequence's last tile stages that row over the pool's and stores it into the
+// sequence's slot once the segment is done.
+template <int KV, int D, int W, bool kAppend>
 __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(const DecodeArgs a) {
   using S = GqaShape<KV, D>;
   constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
@@ -741,6 +746,29 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   const char* __restrict__ vbase = static_cast<const char*>(a.value_cache);
   const float poison = __uint_as_float(0x7fc00000u);
 
+  // appended decode: sequence s's new K/V piece of this lane (16 bytes as given, or 32 bytes of bf16 for 16 E4M3
+  // codes), loaded unconditionally (lanes past the head row take the first piece)
+  constexpr int kNewPieces = S::kRaw ? 2 : 1;
+  const bool piece = rc < S::kHeadLanes;
+  auto load_new = [&](int s, U4* k, U4* v) __attribute__((always_inline)) {
+    if constexpr (kAppend) {
+      const int64_t src = (((int64_t)s * a.num_kv_heads + g) * D * (S::kRaw ? 2 : kEsize)) / 16 +
+                          (piece ? rc : 0) * kNewPieces;
+#pragma unroll
+      for (int e = 0; e < kNewPieces; ++e) {
+        k[e] = static_cast<const U4*>(a.new_key)[src + e];
+        v[e] = static_cast<const U4*>(a.new_value)[src + e];
+      }
+    }
+  };
+  // the piece as the pool holds it (E4M3: quantised exactly as the quantising cache write does)
+  auto new_piece = [&](const U4* raw, float scale) __attribute__((always_inline)) {
+    if constexpr (S::kRaw)
+      return e4m3_pack16_bf16(raw[0], raw[1], scale);
+    else
+      return raw[0];
+  };
+
   // the run's first sequence: the first s with P[s + 1] > g0
   int lo = 0, hi = T - 1;
   while (lo < hi) {
@@ -788,6 +816,11 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   Seg cs = is;
   U4 qb[kChunks], qn[kChunks];
   load_query(cs.s, qb);
+  // appended decode: the issue cursor's sequence's new pieces as loaded, the compute cursor's as the pool holds
+  // them (converted once the next tile's loads are in flight, so that no wait for them holds those back)
+  U4 nkn[kNewPieces], nvn[kNewPieces];
+  U4 nkc{}, nvc{};
+  load_new(cs.s, nkn, nvn);
   // one register set (phased shapes: K or V of a tile at a time), as in the partition kernel
   U4 kR[2][kLoads], vR[2][S::kPhased ? 1 : kLoads];
   bool bad_staged = false, bad_issued = false;
@@ -806,7 +839,20 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   // per-segment state of the compute cursor
   int q0, ql, qrow, lim0, ufull;
   bool head_ok;
+  // appended decode: whether this run holds the sequence's last tile and writes its new token (slot), whether the
+  // token is attended over (the lane then stages its piece as row r_new of that tile)
+  bool seg_store = false, lane_new = false;
+  int64_t seg_slot = 0;
+  int r_new = 0;
   auto begin_segment = [&]() {
+    if constexpr (kAppend) {
+      const int Lraw = lens[cs.s];
+      const int64_t slot = as_constant(a.slot_mapping)[cs.s];
+      seg_store = cs.p1 <= g1 && Lraw >= 1 && slot >= 0 && slot < (a.num_blocks << a.bs_log2);
+      seg_slot = slot;
+      r_new = (Lraw - 1) % kTileTok;
+      lane_new = seg_store && Lraw <= a.max_context_len && piece && rr == (r_new % kTile) % S::kRows;
+    }
     q0 = cs.s;
     ql = 1;
     if (a.query_start) {
@@ -831,12 +877,22 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
       if (gi + 1 >= is.p1) {  // the next tile opens the next sequence: its query rows come in with it
         is = segment(next_seq(is.s));
         load_query(is.s, qn);
+        load_new(is.s, nkn, nvn);
       }
       issue_kv(gi + 1);
     }
   };
 
   issue_kv(g0);
+  if constexpr (kAppend) {
+    nkc = new_piece(nkn, a.new_k_scale);
+    nvc = new_piece(nvn, a.new_v_scale);
+  }
+  // the appended row over the staged pool row of the sequence's last tile (the lane staged that piece)
+  auto substitute = [&](int gi, char* slice, const U4& pc) __attribute__((always_inline)) {
+    if constexpr (kAppend)
+      if (gi == cs.p1 - 1 && lane_new) *reinterpret_cast<U4*>(slice + r_new * kPitch + rc * 16) = pc;
+  };
   // Segments in an outer loop, their tiles in an inner one. (Closing a segment conditionally inside one tile loop
   // made the compiler copy every accumulator on each tile, as in the partition kernel.)
   int gi = g0;
@@ -849,6 +905,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
       const bool full = t + kTileTok <= ufull;
       wave_lds_sync();  // the previous tile's reads come first
       gqa_stage<KV, D>(kR, kslice, wofs, stage_lane);
+      substitute(gi, kslice, nkc);
       bad_staged = bad_issued;
       bad_issued = false;
       if constexpr (S::kPhased) {
@@ -859,11 +916,13 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
                              (f32x4(*)[kNt])o, &pb, &pl);
         wave_lds_sync();
         gqa_stage<KV, D>(kR, vslice, wofs, stage_lane);
+        substitute(gi, vslice, nvc);
         wave_lds_sync();
         issue_next(gi);
         gqa_pv<KV, D, 1>(rbase, &pb, &pl, (f32x4(*)[kNt])o);
       } else {
         gqa_stage<KV, D>((U4(*)[kLoads])vR, vslice, wofs, stage_lane);
+        substitute(gi, vslice, nvc);
         wave_lds_sync();
         issue_next(gi);
         gqa_compute<KV, D, 1>(kread, rbase, (const U4(*)[kChunks])qb, a.scale_log2, t, full, &lim, j, &m, &l,
@@ -898,11 +957,22 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
                 : make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
       }
     }
+    if constexpr (kAppend) {
+      if (seg_store && rr == 0 && piece) {  // the sequence's new token into its slot of both pools
+        const int64_t dst = seg_slot * row_bytes + head_off + rc * 16;
+        *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + dst) = nkc;
+        *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + dst) = nvc;
+      }
+    }
     if (gi >= g1) break;
     // the next segment: the one the issue cursor opened
     cs = is;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) qb[c] = qn[c];
+    if constexpr (kAppend) {
+      nkc = new_piece(nkn, a.new_k_scale);
+      nvc = new_piece(nvn, a.new_v_scale);
+    }
     begin_segment();
     m = -INFINITY;
     l = 0.f;
@@ -994,7 +1064,12 @@ template <int KV, int D, int W>
 hipError_t launch_balanced_w(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((a.num_kv_heads + W - 1) / W, a.chunks, 1);
   const size_t lds = ((size_t)a.num_seqs + 1) * sizeof(int32_t);
-  decode_gqa_mfma_balanced_kernel<KV, D, W><<<grid, dim3(kWave * W), lds, stream>>>(a);
+  if (a.new_key) {  // appended decode: one new token (query row) per sequence
+    if (a.query_start) return hipErrorInvalidValue;
+    decode_gqa_mfma_balanced_kernel<KV, D, W, true><<<grid, dim3(kWave * W), lds, stream>>>(a);
+  } else {
+    decode_gqa_mfma_balanced_kernel<KV, D, W, false><<<grid, dim3(kWave * W), lds, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1023,7 +1098,7 @@ int32_t gqa_balanced_chunks(int32_t num_kv_heads) {
 
 hipError_t launch_decode_gqa_mfma_balanced(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
   if (a.num_seqs > kMaxBalancedRows || a.chunks <= 0 || !a.tile_prefix || a.col_groups != 1 ||
-      a.group * a.max_query_len > 16 || !a.seq_prefix || a.new_key)
+      a.group * a.max_query_len > 16 || !a.seq_prefix)
     return hipErrorInvalidValue;
   if (kv_dtype == PA_BF16) return dispatch_dim<PA_BF16, LaunchBalanced>(a, stream);
   if (kv_dtype == PA_FP8_E4M3) return dispatch_dim<PA_FP8_E4M3, LaunchBalanced>(a, stream);

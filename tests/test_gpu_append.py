@@ -3,9 +3,9 @@ separate calls (reshape_and_cache, then paged_attention_decode) and the oracle.
 
 The pools must end byte for byte as the separate cache write leaves them. Where the single-head balanced split
 appends the new token itself, the output equals the separate calls' up to the order of floating-point
-additions (the new token is added to its row's state last). The matrix-core partition kernel stages the new row
-in place of the pool's, and every other plan runs the two launches: both must match the separate calls bit for
-bit. All are also compared with the fp64 oracle over the updated pools."""
+additions (the new token is added to its row's state last). The matrix-core kernels stage the new row in place
+of the pool's, and the single-head partition kernel's plans run the two launches: both must match the separate
+calls bit for bit. All are also compared with the fp64 oracle over the updated pools."""
 
 from __future__ import annotations
 
@@ -60,14 +60,14 @@ def write_on_host(st, h, slots):
 
 
 def fused_here(st, partition_size) -> str | None:
-    """Which decode launch appends the new tokens itself: "single-head balanced", "matrix-core partitions", or
-    None where the call launches the cache write first."""
+    """Which decode launch appends the new tokens itself: "single-head balanced", "matrix-core balanced",
+    "matrix-core partitions", or None where the call launches the cache write first."""
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
     part = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len,
                                  st.block_size, kd, partition_size)
     mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
     if part == pa.PA_PARTITION_BALANCED:
-        return None if mfma else "single-head balanced"
+        return "matrix-core balanced" if mfma else "single-head balanced"
     return "matrix-core partitions" if mfma else None
 
 
@@ -186,3 +186,18 @@ def test_length_beyond_max_context_len_is_written_not_attended(hq, part):
         np.testing.assert_allclose(fused, separate, rtol=1e-5, atol=1e-6)
     else:
         np.testing.assert_array_equal(fused, separate)
+
+
+@pytest.mark.parametrize("hq,part", [(8, pa.PA_PARTITION_BALANCED), (32, pa.PA_PARTITION_BALANCED), (32, -1)],
+                         ids=["single-head balanced", "matrix-core balanced", "matrix-core default"])
+def test_zero_max_context_len_still_writes(hq, part):
+    # nothing is attended over (zero rows), and every new token still lands in its slot
+    st = custom_structure("a616", 616, [300, 1, 45, 1000], hq, 8, 128, 16, "bf16")
+    t = materialize(st, DEV, include_new_token=True)
+    pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    ref_pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    write_separately(st, t, ref_pools, st.slot_mapping)
+    fused = appended(st, t, pools, st.block_tables_pre, st.slot_mapping, part, max_context_len=0)
+    assert torch.equal(pools[0].view(torch.uint8), ref_pools[0].view(torch.uint8))
+    assert torch.equal(pools[1].view(torch.uint8), ref_pools[1].view(torch.uint8))
+    np.testing.assert_array_equal(fused, np.zeros_like(fused))
