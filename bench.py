@@ -50,15 +50,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def step_appends(pa, st, query_len: int, launched_part: int, separate_write: bool = False) -> bool:
+def step_appends(query_len: int, max_context_len: int, separate_write: bool = False) -> bool:
     """Whether the benchmark's step writes the new tokens inside the decode launch: paged_attention_decode_append
-    does so under both kernels' balanced splits and in the matrix-core partition kernel (grouped heads over bf16
-    or E4M3 caches). Under the single-head partition kernel the call launches the cache write first, so the step
-    keeps the two calls and times the attention alone."""
-    if query_len != 1 or separate_write or st.max_context_len < 1:
-        return False
-    mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
-    return mfma or launched_part == pa.PA_PARTITION_BALANCED
+    does so under every plan of a decode step, except with max_context_len 0 (where it launches the cache write
+    first)."""
+    return query_len == 1 and not separate_write and max_context_len >= 1
 
 
 def appended_row_bytes(st) -> int:
@@ -129,17 +125,12 @@ def write_traffic_summary(workload: str, fetch_db: str, write_db: str, cmd_fetch
         f, w = fetch[kf][0] * f_scale, write[kw][0] * w_scale
         fb, wb = fb + f, wb + w
         rows.append((kf, fetch[kf][1], fetch[kf][0], write[kw][0], f, w))
-    import paged_kv_cache_458_amd as pa
     from workloads import algorithmic_bytes, build_structure
 
     st = build_structure(workload)
     alg = algorithmic_bytes(st, query_len)["total"]
-    if query_len == 1:
-        kv_code = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
-        part = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len,
-                                     st.block_size, kv_code, st.partition_size)
-        if step_appends(pa, st, 1, part):  # the counted call also reads and writes the new rows
-            alg += appended_row_bytes(st)
+    if step_appends(query_len, st.max_context_len):  # the counted call also reads and writes the new rows
+        alg += appended_row_bytes(st)
     label = workload if query_len == 1 else f"{workload}_q{query_len}"
     lines = [f"# HBM traffic per attention call: {label}", "",
              "Two counter runs of the benchmark (run from the repository root on one MI355X):", "", "```",
@@ -519,7 +510,7 @@ def main() -> int:
         launched_part = pa.partition_size_for(B, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
     else:
         launched_part = pa.multi_partition_size_for(B, T, Q, Hq, Hkv, D, st.max_context_len, bs, kv_code, part)
-    append = step_appends(pa, st, Q, launched_part, args.separate_write)
+    append = step_appends(Q, st.max_context_len, args.separate_write)
 
     t = materialize(st, dev, include_new_token=False)
     pools = [(t["key_cache"], t["value_cache"])]

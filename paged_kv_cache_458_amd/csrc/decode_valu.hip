@@ -132,7 +132,11 @@ constexpr int kStages = 3;         // 16-token tiles in flight per wave
 // grouped-query kernels, congest the memory system less.
 constexpr int kBalStages = 2;
 
-template <int KV, int D>
+// kAppend: decode with each sequence's new token appended in this launch (one query row per sequence). The wave
+// whose partition holds the token's position reads one position less from the pool and adds the token from the
+// new rows after its tiles; the first partition's wave of the first query head of each KV head writes it into
+// the pools.
+template <int KV, int D, bool kAppend>
 __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(const DecodeArgs a) {
   using S = Shape<KV, D>;
   constexpr int NL = S::kLoads;
@@ -150,11 +154,34 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   if (part > 0 && t0 >= L) return;  // this sequence has fewer partitions
   const int E = row_extent(a, s, row, L);
   if (E < 0) return;  // not one of the sequence's query rows: left unwritten
-  const int t1 = max(t0, min(min(L, t0 + a.partition), E));
+  int t1 = max(t0, min(min(L, t0 + a.partition), E));
   const int g = h / a.group;
   const int r = lane / S::kRowLanes;  // row group
   const int c = lane % S::kRowLanes;  // 16-byte chunk of the head's row
   const bool lane_ok = c < S::kHeadLanes;  // false for the padding lanes of a row group
+
+  // appended decode: this lane's chunk of head g's new K/V row (16 bytes as given, or 32 bytes of bf16 for 16
+  // E4M3 codes), loaded unconditionally and first read after the tiles
+  constexpr int kNewPieces = S::kEsize == 1 ? 2 : 1;
+  U4 nk[kNewPieces], nv[kNewPieces];
+  bool attend_new = false, store_new = false;
+  int64_t new_slot = 0;
+  if constexpr (kAppend) {
+    const int64_t src = (((int64_t)s * a.num_kv_heads + g) * D * (kNewPieces == 2 ? 2 : S::kEsize)) / 16 +
+                        (lane_ok ? c : 0) * kNewPieces;
+#pragma unroll
+    for (int e = 0; e < kNewPieces; ++e) {
+      nk[e] = static_cast<const U4*>(a.new_key)[src + e];
+      nv[e] = static_cast<const U4*>(a.new_value)[src + e];
+    }
+    const int Lraw = a.context_lens[s];
+    new_slot = a.slot_mapping[s];
+    if (Lraw >= 1 && new_slot >= 0 && new_slot < (a.num_blocks << a.bs_log2)) {
+      store_new = part == 0 && h % a.group == 0;
+      attend_new = Lraw <= a.max_context_len && Lraw - 1 >= t0 && Lraw - 1 < t1;  // then Lraw - 1 == t1 - 1
+      if (attend_new) --t1;
+    }
+  }
 
   const int64_t row_bytes = (int64_t)a.num_kv_heads * D * S::kEsize;
   // padding lanes load at an offset above every descriptor's size (at most 16 rows < 2^30 bytes), so they read
@@ -267,6 +294,32 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
       if (j + i < ntiles) consume(kb[i], vb[i], j + i);
   }
 
+  // appended decode: the new token (exactly as the pool would hold it: quantised for E4M3), one more position
+  // of row group 0
+  U4 nkc{}, nvc{};
+  if constexpr (kAppend) {
+    if constexpr (kNewPieces == 2) {
+      nkc = e4m3_pack16_bf16(nk[0], nk[1], a.new_k_scale);
+      nvc = e4m3_pack16_bf16(nv[0], nv[1], a.new_v_scale);
+    } else {
+      nkc = nk[0];
+      nvc = nv[0];
+    }
+    if (attend_new) {
+      float sn = group_sum<S::kRowLanes>(dot_chunk<KV>(q, nkc)) * a.scale_log2;
+      if (r != 0) sn = -INFINITY;
+      const float m2 = fmaxf(m, sn);
+      const float mref2 = m2 == -INFINITY ? 0.f : m2;
+      const float alpha2 = fast_exp2(m - mref2);
+      const float pn = fast_exp2(sn - mref2);
+      l = l * alpha2 + pn;
+#pragma unroll
+      for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha2;
+      axpy_chunk<KV>(acc, pn, nvc);
+      m = m2;
+    }
+  }
+
   // merge the row groups: lanes l, l ^ kRowLanes, ... hold the same dims of different token subsets
 #pragma unroll
   for (int off = S::kRowLanes; off < kWave; off <<= 1) {
@@ -301,6 +354,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
 #pragma unroll
     for (int e = 0; e < S::kEpl; e += 4)
       *reinterpret_cast<float4*>(dst + e) = make_float4(res[e], res[e + 1], res[e + 2], res[e + 3]);
+  }
+  if constexpr (kAppend) {
+    if (store_new && r == 0 && lane_ok) {  // the new token into its slot of both pools
+      const int64_t dst = new_slot * row_bytes + (int64_t)g * D * S::kEsize + c * 16;
+      *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + dst) = nkc;
+      *reinterpret_cast<U4*>(static_cast<char*>(a.value_out) + dst) = nvc;
+    }
   }
 }
 
@@ -853,23 +913,29 @@ __global__ __launch_bounds__(kWave * 4) void balanced_reduce_kernel(const Decode
 
 }  // namespace
 
-template <int KV>
-hipError_t launch_kv(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+template <int KV, bool kAppend>
+hipError_t launch_kv_append(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: decode_valu_kernel<KV, 64><<<grid, block, 0, stream>>>(a); break;
-    case 80: decode_valu_kernel<KV, 80><<<grid, block, 0, stream>>>(a); break;
-    case 96: decode_valu_kernel<KV, 96><<<grid, block, 0, stream>>>(a); break;
-    case 112: decode_valu_kernel<KV, 112><<<grid, block, 0, stream>>>(a); break;
-    case 128: decode_valu_kernel<KV, 128><<<grid, block, 0, stream>>>(a); break;
-    case 192: decode_valu_kernel<KV, 192><<<grid, block, 0, stream>>>(a); break;
-    case 256: decode_valu_kernel<KV, 256><<<grid, block, 0, stream>>>(a); break;
+    case 64: decode_valu_kernel<KV, 64, kAppend><<<grid, block, 0, stream>>>(a); break;
+    case 80: decode_valu_kernel<KV, 80, kAppend><<<grid, block, 0, stream>>>(a); break;
+    case 96: decode_valu_kernel<KV, 96, kAppend><<<grid, block, 0, stream>>>(a); break;
+    case 112: decode_valu_kernel<KV, 112, kAppend><<<grid, block, 0, stream>>>(a); break;
+    case 128: decode_valu_kernel<KV, 128, kAppend><<<grid, block, 0, stream>>>(a); break;
+    case 192: decode_valu_kernel<KV, 192, kAppend><<<grid, block, 0, stream>>>(a); break;
+    case 256: decode_valu_kernel<KV, 256, kAppend><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int KV>
+hipError_t launch_kv(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (!a.new_key) return launch_kv_append<KV, false>(a, grid, block, stream);
+  if (a.query_start) return hipErrorInvalidValue;  // appended decode: one new token (query row) per sequence
+  return launch_kv_append<KV, true>(a, grid, block, stream);
+}
+
 hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, hipStream_t stream) {
-  if (a.new_key) return hipErrorInvalidValue;  // the partition kernel does not append
   const dim3 grid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.split ? a.max_partitions : 1,
                   a.num_tokens);
   const dim3 block(kWave * kWavesPerGroup);

@@ -414,12 +414,10 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (app) {
-    // The balanced splits of both kernels and the matrix-core partition kernel append the new tokens themselves
-    // (for an E4M3 cache from bf16 rows, which every E4M3 decode has); the single-head partition kernel's plans
-    // write them first, as reshape_and_cache or reshape_and_cache_fp8 would, and then attend. So do calls with
-    // max_context_len 0, whose sequences have no tile in which a balanced run could write the token.
-    const bool fused = !query_start && max_context_len > 0 && (kv_dtype != PA_FP8_E4M3 || q_dtype == PA_BF16) &&
-                       (plan.balanced || plan.mfma);
+    // Every decode kernel appends the new tokens itself (for an E4M3 cache from bf16 rows, which every E4M3
+    // decode has). A call with max_context_len 0 gives its sequences no tile in which a balanced run could write
+    // the token: it writes them first, as reshape_and_cache or reshape_and_cache_fp8 would, and then attends.
+    const bool fused = !query_start && max_context_len > 0 && (kv_dtype != PA_FP8_E4M3 || q_dtype == PA_BF16);
     hipError_t e = hipSuccess;
     if (fused) {
       a.new_key = app->key;

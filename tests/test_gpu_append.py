@@ -1,11 +1,11 @@
 """paged_attention_decode_append: one decode step's cache write and attention in one call, against the two
 separate calls (reshape_and_cache, then paged_attention_decode) and the oracle.
 
-The pools must end byte for byte as the separate cache write leaves them. Where the single-head balanced split
-appends the new token itself, the output equals the separate calls' up to the order of floating-point
-additions (the new token is added to its row's state last). The matrix-core kernels stage the new row in place
-of the pool's, and the single-head partition kernel's plans run the two launches: both must match the separate
-calls bit for bit. All are also compared with the fp64 oracle over the updated pools."""
+The pools must end byte for byte as the separate cache write leaves them. The single-head kernels add the new
+token to its row's softmax after the pool rows of its tile or partition, so their output equals the separate
+calls' up to the order of floating-point additions; the matrix-core kernels stage the new row in place of the
+pool's, and must match the separate calls bit for bit (as must a call with max_context_len 0, which launches
+the cache write first). All are also compared with the fp64 oracle over the updated pools."""
 
 from __future__ import annotations
 
@@ -59,21 +59,20 @@ def write_on_host(st, h, slots):
         oracle.reshape_and_cache(h["key_cache"], h["value_cache"], h["new_key"], h["new_value"], slots)
 
 
-def fused_here(st, partition_size) -> str | None:
-    """Which decode launch appends the new tokens itself: "single-head balanced", "matrix-core balanced",
-    "matrix-core partitions", or None where the call launches the cache write first."""
+def fused_here(st, partition_size) -> str:
+    """Which decode kernel appends the new tokens itself (each of them does)."""
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[st.dtype]
     part = pa.partition_size_for(st.num_seqs, st.num_q_heads, st.num_kv_heads, st.head_dim, st.max_context_len,
                                  st.block_size, kd, partition_size)
     mfma = st.dtype in ("bf16", "fp8") and st.num_q_heads != st.num_kv_heads
     if part == pa.PA_PARTITION_BALANCED:
         return "matrix-core balanced" if mfma else "single-head balanced"
-    return "matrix-core partitions" if mfma else None
+    return "matrix-core partitions" if mfma else "single-head partitions"
 
 
 def reordered(st, partition_size) -> bool:
     """Whether the appended output may differ from the separate calls' in the order of its additions."""
-    return fused_here(st, partition_size) == "single-head balanced"
+    return fused_here(st, partition_size).startswith("single-head")
 
 
 def compare(st, fused, separate, ref, what, exact):
