@@ -655,9 +655,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
                               ? tile_slot_bytes(i_table, min(t + kTile / 2, last8), a.bs_log2, a.num_blocks,
                                                 row_bytes, bad)
                               : base0 + (kTile / 2) * row_bytes;
-    // appended decode: the row's last tile loads the new token from the new rows (row group 0's lanes, one
-    // 16-byte chunk each; the others read nothing) and, when the token is that tile's last position, reads one
-    // row less from the pool
+    // appended decode: the row's last tile loads the new token from the new rows (row group 0's lanes, and for
+    // an E4M3 cache row group 1's, one 16-byte chunk each; the others read nothing) and, when the token is that
+    // tile's last position, reads one row less from the pool
     const bool newtok = kAppend && live && i_tile == i_nt - 1 && i_slot >= 0;
     const bool attend_new = newtok && i_attend;
     // (taken through a scalar register: the descriptors below must stay wave-uniform)
