@@ -109,13 +109,14 @@ __device__ __forceinline__ void axpy_chunk(float* acc, float p, const U4& v) {
     axpy_bf16x2(acc + 4, p, v.z);
     axpy_bf16x2(acc + 6, p, v.w);
   } else if constexpr (KV == PA_FP8_E4M3) {
+    // codes widened straight to fp32: one conversion per two values (through bf16 pairs it took three)
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t a, b;
-      e4m3x4_to_bf16x4(w[i], a, b);
-      axpy_bf16x2(acc + 4 * i, p, a);
-      axpy_bf16x2(acc + 4 * i + 2, p, b);
+      float f[4];
+      e4m3x4_to_f32x4(w[i], f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * i + e] = fmaf(p, f[e], acc[4 * i + e]);
     }
   } else {
     acc[0] = fmaf(p, __uint_as_float(v.x), acc[0]);

@@ -52,6 +52,18 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint3
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
 }
 
+// Four OCP E4M3 codes (first code in the lowest byte) -> four floats in order, exactly (gfx950
+// v_cvt_scalef32_pk_f32_fp8 with scale 1: each converts the codes of one half-word).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void e4m3x4_to_f32x4(uint32_t w, float* f) {
+  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w, 1.0f, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w, 1.0f, true);
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+}
+
 // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
