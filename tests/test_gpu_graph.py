@@ -2,7 +2,8 @@
 
 The library allocates nothing, clears nothing with memsets and never synchronises, so a whole decode step --
 the slot-mapped write of the new token's K/V, then paged attention with its merge kernel -- can be captured
-once (torch.cuda.graph) and replayed. So can the call that does both, paged_attention_decode_append. Each replay starts from the pristine pools and a NaN-filled output,
+once (torch.cuda.graph) and replayed; so can the call that does both, paged_attention_decode_append. Each replay
+starts from the pristine pools and a NaN-filled output,
 with eager work and host synchronisations between replays, and must reproduce the eager step bit for bit:
 output and both pools.
 """
@@ -42,7 +43,9 @@ CASES = [
     (32, 8, pa.PA_PARTITION_BALANCED, "bf16", "matrix-core balanced split + merge"),
     (8, 8, -1, "fp8", "E4M3: quantising cache write, balanced split with two heads per wave + merge"),
     (8, 8, -1, "bf16+append", "one call: new rows written by the balanced split's launch + merge"),
-    (32, 8, 512, "bf16+append", "one call: cache write launch, matrix-core partitions + merge"),
+    (32, 8, 512, "bf16+append", "one call: new rows written by the matrix-core partition kernel + merge"),
+    (32, 8, pa.PA_PARTITION_BALANCED, "fp8+append",
+     "one call, E4M3: new rows quantised by the matrix-core balanced split + merge"),
 ]
 
 
@@ -65,7 +68,8 @@ def test_captured_decode_step_replays_bit_for_bit(hq, hkv, part, dt, what):
         if append:
             pa.paged_attention_decode_append(out, t["query"], t["new_key"], t["new_value"], kc, vc, tables, lens,
                                              slots, st.scale, max_context_len=st.max_context_len,
-                                             partition_size=part, workspace=ws)
+                                             partition_size=part, workspace=ws, k_scale=st.k_scale,
+                                             v_scale=st.v_scale)
             return
         pa.reshape_and_cache(t["new_key"], t["new_value"], kc, vc, slots, k_scale=st.k_scale, v_scale=st.v_scale)
         pa.paged_attention_decode(out, t["query"], kc, vc, tables, lens, st.scale, st.block_size,
