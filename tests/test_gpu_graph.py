@@ -3,9 +3,8 @@
 The library allocates nothing, clears nothing with memsets and never synchronises, so a whole decode step --
 the slot-mapped write of the new token's K/V, then paged attention with its merge kernel -- can be captured
 once (torch.cuda.graph) and replayed; so can the call that does both, paged_attention_decode_append. Each replay
-starts from the pristine pools and a NaN-filled output,
-with eager work and host synchronisations between replays, and must reproduce the eager step bit for bit:
-output and both pools.
+starts from the pristine pools and a NaN-filled output, with eager work and host synchronisations between
+replays, and must reproduce the eager step bit for bit: output and both pools.
 """
 
 from __future__ import annotations
