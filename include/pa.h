@@ -175,13 +175,13 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
  * Contract: for every s whose slot is written, position context_lens[s] - 1 of sequence s lies in that slot
  * through the block table (the new token is the last position of the sequence) and context_lens[s] >= 1. As in
  * paged_attention_decode, lengths beyond max_context_len are clamped: such a sequence's new token is written but
- * not attended over. Where the plan is the single-head balanced split over an fp32 or bf16 cache, or the
- * matrix-core partition kernel, one launch does both: the last position of such a sequence is taken from
- * `key` / `value` (quantised first for E4M3) instead of the pool, and a wave of that sequence writes it into
- * the pools. Every other plan launches the cache write first. Either way the pools end as the cache write
- * leaves them, byte for byte. The output equals that of the two calls bit for bit, except under the
- * single-head balanced split, where the new token enters its row's softmax after the pool rows of its tile (the
- * same values, another order of floating-point additions).
+ * not attended over. The decode launch does both, whatever the plan: the last position of such a sequence is
+ * taken from `key` / `value` (quantised first for E4M3) instead of the pool, and a wave of that sequence writes
+ * it into the pools. Only a call with max_context_len 0 (no position attended anywhere) launches the cache write
+ * first. Either way the pools end as the cache write leaves them, byte for byte. The output equals that of the
+ * two calls bit for bit on the matrix-core kernels (grouped heads over bf16 or E4M3 caches); the single-head
+ * kernels add the new token to its row's softmax after the pool rows of its tile or partition (the same values,
+ * another order of floating-point additions).
  */
 int paged_attention_decode_append(float *out, const void *query, const void *key, const void *value, void *key_cache,
                                   void *value_cache, const int32_t *block_tables, const int32_t *context_lens,
