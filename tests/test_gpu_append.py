@@ -139,11 +139,16 @@ def test_small_cases(case):
     seed, lens, hq, hkv, d, bs, dt = case
     st = custom_structure(f"a{seed}", seed, lens, hq, hkv, d, bs, dt)
     assert len(st.copy_pairs) == 0  # the tables before and after the step are the same
-    # the new tokens' slots hold data already (read where a token is not appended)
+    # the new tokens' slots hold data already (read where a token is not appended) ...
     t = materialize(st, DEV, include_new_token=True)
     tables = st.block_tables_pre
     slots = st.slot_mapping.copy()
     slots[1] = -1  # this sequence's token is not written: the pool is read as it was
+    # ... and NaN where one is: a kernel that read such a slot instead of the new row would show it
+    for pool in (t["key_cache"], t["value_cache"]):
+        rows = pool.view(torch.uint8).view(-1, hkv * d * pool.element_size())
+        nan = torch.tensor([float("nan")], dtype=pool.dtype, device=DEV).view(torch.uint8)
+        rows[torch.from_numpy(slots[slots >= 0].astype(np.int64)).to(DEV)] = nan.repeat(hkv * d)
     kd = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3}[dt]
     for part in (-1, pa.PA_PARTITION_BALANCED, 0, 64):
         if part == pa.PA_PARTITION_BALANCED and not pa.workspace_bytes(st.num_seqs, hq, hkv, d, st.max_context_len,
