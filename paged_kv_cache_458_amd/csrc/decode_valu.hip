@@ -793,23 +793,24 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     }
     m = mn;
     if constexpr (kAppend) {
-      if (tinfo & kNewAttend) {
-        // the new token, one more position of row group 0 (the other groups' state does not move)
-        float sn = group_sum<S::kSumLanes>(dot_chunk<KV>(q, new_piece(kq_new, a.new_k_scale))) * a.scale_log2;
-        if (r != 0) sn = -INFINITY;
-        const float m2 = fmaxf(m, sn);
-        const float mref2 = m2 == -INFINITY ? 0.f : m2;
-        const float alpha2 = fast_exp2(m - mref2);
-        const float pn = fast_exp2(sn - mref2);
-        l = l * alpha2 + pn;
-#pragma unroll
-        for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha2;
-        axpy_chunk<KV>(acc, pn, new_piece(vq_new, a.new_v_scale));
-        m = m2;
-      }
       if (tinfo & kNew) {
-        // its rows into the pools, by one wave per KV head
+        // (a token attended over is always one that is written: its pieces are formed once, for both)
         const U4 kp = new_piece(kq_new, a.new_k_scale), vp = new_piece(vq_new, a.new_v_scale);
+        if (tinfo & kNewAttend) {
+          // the new token, one more position of row group 0 (the other groups' state does not move)
+          float sn = group_sum<S::kSumLanes>(dot_chunk<KV>(q, kp)) * a.scale_log2;
+          if (r != 0) sn = -INFINITY;
+          const float m2 = fmaxf(m, sn);
+          const float mref2 = m2 == -INFINITY ? 0.f : m2;
+          const float alpha2 = fast_exp2(m - mref2);
+          const float pn = fast_exp2(sn - mref2);
+          l = l * alpha2 + pn;
+#pragma unroll
+          for (int e = 0; e < S::kEpl; ++e) acc[e] *= alpha2;
+          axpy_chunk<KV>(acc, pn, vp);
+          m = m2;
+        }
+        // its rows into the pools, by one wave per KV head
         if (r == 0 && lane_ok && h % a.group == 0) {
           const int64_t dst = (int64_t)slot_new * row_bytes + lane_off[0];
           *reinterpret_cast<U4*>(static_cast<char*>(a.key_out) + dst) = kp;
