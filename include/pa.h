@@ -105,7 +105,8 @@ size_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
  *
  *   out            [num_seqs][num_q_heads][head_dim] fp32, written; must not alias any input
  *   query          [num_seqs][num_q_heads][head_dim] q_dtype
- *   key_cache      [num_blocks][block_size][num_kv_heads][head_dim] kv_dtype
+ *   key_cache      [num_blocks][block_size][num_kv_heads][head_dim] kv_dtype; at most 2^32 slots
+ *                  (num_blocks * block_size), else PA_ERR_UNSUPPORTED (paged_gather alike)
  *   value_cache    same layout as key_cache
  *   block_tables   int32 [num_seqs][max_blocks_per_seq]; only entries j < ceil(L / block_size) are read
  *   context_lens   int32 [num_seqs]; 0 <= L <= max_context_len (longer lengths are clamped)

@@ -12,6 +12,8 @@
 namespace {
 
 constexpr int kTileTokens = 16;
+// the readers of the pool address a slot by a 32-bit index (num_blocks * block_size slots at most)
+constexpr int64_t kMaxPoolSlots = (int64_t)1 << 32;
 constexpr int kMaxGridYZ = 65535;
 
 int esize_of(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : dtype == PA_FP8_E4M3 ? 1 : 0; }
@@ -356,6 +358,7 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   if (num_blocks <= 0 || num_blocks > INT32_MAX || max_blocks_per_seq <= 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return PA_ERR_SHAPE;
+  if (num_blocks * block_size > kMaxPoolSlots) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
@@ -617,7 +620,8 @@ int paged_gather(void* out_key, void* out_value, const void* key_cache, const vo
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return PA_ERR_SHAPE;
   if (esize_of(kv_dtype) == 0) return PA_ERR_DTYPE;
-  if (!supported_block_size(block_size) || num_seqs > kMaxGridYZ) return PA_ERR_UNSUPPORTED;
+  if (!supported_block_size(block_size) || num_seqs > kMaxGridYZ || num_blocks * block_size > kMaxPoolSlots)
+    return PA_ERR_UNSUPPORTED;
   const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * esize_of(kv_dtype);
   if (row_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_context_len == 0) return PA_OK;

@@ -125,8 +125,9 @@ __device__ __forceinline__ int64_t tile_slot_bytes(TablePtr table_row, int t, in
   const int32_t phys = table_row[t >> bs_log2];
   const bool ok = (uint32_t)phys < (uint64_t)num_blocks;
   bad |= !ok;
-  const int64_t block = ok ? (int64_t)phys : 0;
-  return ((block << bs_log2) + (t & ((1 << bs_log2) - 1))) * row_bytes;
+  // the slot index fits 32 bits (the host refuses pools of more than 2^32 slots): a 32 x 32-bit product
+  const uint32_t slot = ((ok ? (uint32_t)phys : 0u) << bs_log2) + (uint32_t)(t & ((1 << bs_log2) - 1));
+  return (int64_t)((uint64_t)slot * (uint32_t)row_bytes);
 }
 
 // Block tables are not written while a kernel runs. Read through the constant address space, a wave-uniform

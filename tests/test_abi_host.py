@@ -130,6 +130,8 @@ def decode_call(**over):
     (dict(max_context_len=129), PA_ERR_SHAPE),
     (dict(num_blocks=0), PA_ERR_SHAPE),
     (dict(num_blocks=1 << 31), PA_ERR_SHAPE),
+    (dict(num_blocks=(1 << 28) + 1), PA_ERR_UNSUPPORTED),  # 2^32 + 16 slots: beyond a 32-bit slot index
+    (dict(num_blocks=1 << 28, num_seqs=0), 0),           # exactly 2^32 slots
     (dict(partition_size=24), PA_ERR_SHAPE),
     (dict(partition_size=-2), PA_ERR_SHAPE),
     (dict(out=None), PA_ERR_NULL),
@@ -434,6 +436,9 @@ def test_gather_rejects():
     null = list(base)
     null[4] = None
     assert lib.paged_gather(*null) == PA_ERR_NULL
+    huge_pool = list(base)
+    huge_pool[10] = (1 << 28) + 1  # 16-slot blocks: 2^32 + 16 slots
+    assert lib.paged_gather(*huge_pool) == PA_ERR_UNSUPPORTED
 
 
 def test_missing_library_fails_loudly(tmp_path):
