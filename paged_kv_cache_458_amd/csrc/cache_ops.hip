@@ -33,9 +33,9 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(const U4* _
 
 // 16 consecutive source elements (float32 or bf16) -> 16 E4M3 codes (e4m3_pack16 in pa_device.h).
 template <int SRC>
-__device__ __forceinline__ U4 e4m3_pack16_from(const char* src, float scale) {
+__device__ __forceinline__ U4 e4m3_pack16_from(const char* src, const E4m3Div& dv) {
   if constexpr (SRC == PA_BF16) {
-    return e4m3_pack16_bf16(*reinterpret_cast<const U4*>(src), *reinterpret_cast<const U4*>(src + 16), scale);
+    return e4m3_pack16_bf16(*reinterpret_cast<const U4*>(src), *reinterpret_cast<const U4*>(src + 16), dv);
   } else {
     float f[16];
 #pragma unroll
@@ -46,7 +46,7 @@ __device__ __forceinline__ U4 e4m3_pack16_from(const char* src, float scale) {
       f[4 * i + 2] = __uint_as_float(v.z);
       f[4 * i + 3] = __uint_as_float(v.w);
     }
-    return e4m3_pack16(f, scale);
+    return e4m3_pack16(f, dv);
   }
 }
 
@@ -65,9 +65,10 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
   const char* vs = value + n * row_elems * kSrcEsize;
   U4* kd = key_cache + (int64_t)slot * words;
   U4* vd = value_cache + (int64_t)slot * words;
+  const E4m3Div kdiv = e4m3_div(k_scale), vdiv = e4m3_div(v_scale);
   for (int64_t i = threadIdx.x; i < words; i += kThreads) {
-    kd[i] = e4m3_pack16_from<SRC>(ks + i * 16 * kSrcEsize, k_scale);
-    vd[i] = e4m3_pack16_from<SRC>(vs + i * 16 * kSrcEsize, v_scale);
+    kd[i] = e4m3_pack16_from<SRC>(ks + i * 16 * kSrcEsize, kdiv);
+    vd[i] = e4m3_pack16_from<SRC>(vs + i * 16 * kSrcEsize, vdiv);
   }
 }
 

@@ -467,13 +467,15 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // attention over it in one pass). Every lane of a head row's lane group loads its piece of head g's new K/V
   // row: 16 bytes as given, or 32 bytes of bf16 that become 16 E4M3 codes, quantised exactly as the quantising
   // cache write does. The loads are unconditional, and their registers are first read once the first tile's
-  // loads are in flight, so no wait for them holds back those loads. The wave of the first span and
-  // column-group slot stores the row into its slot of both pools, after its loop; the wave whose span holds the
-  // new position stages the row over the tile's pool row, which may or may not have been written yet. A token
-  // whose slot the cache write would skip (slot < 0 or past the pool) is neither written nor substituted.
+  // loads are in flight, so no wait for them holds back those loads. The waves whose span holds the new
+  // position stage the row over the tile's pool row, which may or may not have been written yet, and the one of
+  // them in the first column-group slot stores it into its slot of both pools, after its loop (a position past
+  // max_context_len is not attended over, and the first span's wave stores it). Only these waves form the row
+  // as the pool holds it. A token whose slot the cache write would skip (slot < 0 or past the pool) is neither
+  // written nor substituted.
   constexpr int kNewPieces = S::kRaw ? 2 : 1;
   int tj_new = -1, r_new = 0;
-  bool lane_new = false, lane_store = false;
+  bool lane_new = false, lane_store = false, need_new = false;
   int64_t store_at = 0;
   U4 nk[kNewPieces], nv[kNewPieces];
   U4 nkc{}, nvc{};  // the pieces as the pool holds them
@@ -490,10 +492,14 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
     const int Lraw = a.context_lens[s];
     const int64_t slot = a.slot_mapping[s];
     if (slot >= 0 && slot < (a.num_blocks << a.bs_log2) && Lraw >= 1) {
-      lane_store = cg == 0 && by == 0 && rr == 0 && piece;
-      store_at = slot * row_bytes + head_off + rc * 16;
       const int p = Lraw - 1;
-      if (Lraw <= a.max_context_len && p >= u0 && p < u1) {
+      const bool attended = Lraw <= a.max_context_len;
+      const bool here = attended && p >= u0 && p < u1;
+      const bool stores = cg == 0 && (attended ? here : by == 0);
+      need_new = here || stores;
+      lane_store = stores && rr == 0 && piece;
+      store_at = slot * row_bytes + head_off + rc * 16;
+      if (here) {
         tj_new = (p - u0) / kTileTok;
         r_new = (p - u0) % kTileTok;
         lane_new = piece && rr == (r_new % kTile) % S::kRows;
@@ -503,7 +509,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // the lane's 16 bytes of the new K or V row as the pool holds them
   auto new_piece = [&](const U4* raw, float scale) __attribute__((always_inline)) {
     if constexpr (S::kRaw)
-      return e4m3_pack16_bf16(raw[0], raw[1], scale);
+      return e4m3_pack16_bf16(raw[0], raw[1], e4m3_div(scale));
     else
       return raw[0];
   };
@@ -636,9 +642,14 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   };
   if (ntiles > 0) {
     issue_kv(0);
-    if constexpr (kAppend) {  // (computed inside the tile loop, it would be hoisted before the loads above)
-      nkc = new_piece(nk, a.new_k_scale);
-      nvc = new_piece(nv, a.new_v_scale);
+    if constexpr (kAppend) {
+      // after every load of the first tile is out (computed inside the tile loop, it would be hoisted before
+      // them, and without the barrier the scheduler would wait for the new row between them)
+      __builtin_amdgcn_sched_barrier(0);
+      if (need_new) {
+        nkc = new_piece(nk, a.new_k_scale);
+        nvc = new_piece(nv, a.new_v_scale);
+      }
     }
     // The tiles of the first partition, the park, then the rest: two loops around one pipeline. (A park taken
     // conditionally inside a single loop made the compiler copy every accumulator and parked register on each
@@ -666,7 +677,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   for (int k = 0; k < NCG; ++k) write_rows(k, by, m[k], l[k], o[k]);
   if constexpr (kAppend) {
     if (lane_store) {
-      if (ntiles <= 0) {
+      if (ntiles <= 0) {  // (no tile loop: not formed above)
         nkc = new_piece(nk, a.new_k_scale);
         nvc = new_piece(nv, a.new_v_scale);
       }
@@ -769,7 +780,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   // the piece as the pool holds it (E4M3: quantised exactly as the quantising cache write does)
   auto new_piece = [&](const U4* raw, float scale) __attribute__((always_inline)) {
     if constexpr (S::kRaw)
-      return e4m3_pack16_bf16(raw[0], raw[1], scale);
+      return e4m3_pack16_bf16(raw[0], raw[1], e4m3_div(scale));
     else
       return raw[0];
   };
@@ -889,9 +900,12 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   };
 
   issue_kv(g0);
-  if constexpr (kAppend) {
-    nkc = new_piece(nkn, a.new_k_scale);
-    nvc = new_piece(nvn, a.new_v_scale);
+  if constexpr (kAppend) {  // only a segment that holds its sequence's last tile stages or stores the row
+    __builtin_amdgcn_sched_barrier(0);  // after the first tile's loads, as in the partition kernel
+    if (seg_store) {
+      nkc = new_piece(nkn, a.new_k_scale);
+      nvc = new_piece(nvn, a.new_v_scale);
+    }
   }
   // the appended row over the staged pool row of the sequence's last tile (the lane staged that piece)
   auto substitute = [&](int gi, char* slice, const U4& pc) __attribute__((always_inline)) {
@@ -974,11 +988,13 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
     cs = is;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) qb[c] = qn[c];
-    if constexpr (kAppend) {
-      nkc = new_piece(nkn, a.new_k_scale);
-      nvc = new_piece(nvn, a.new_v_scale);
-    }
     begin_segment();
+    if constexpr (kAppend) {
+      if (seg_store) {
+        nkc = new_piece(nkn, a.new_k_scale);
+        nvc = new_piece(nvn, a.new_v_scale);
+      }
+    }
     m = -INFINITY;
     l = 0.f;
 #pragma unroll

@@ -295,13 +295,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
       if (j + i < ntiles) consume(kb[i], vb[i], j + i);
   }
 
-  // appended decode: the new token (exactly as the pool would hold it: quantised for E4M3), one more position
-  // of row group 0
+  // appended decode: the new token (exactly as the pool would hold it: quantised for E4M3, by the waves that
+  // attend over it or store it), one more position of row group 0
   U4 nkc{}, nvc{};
   if constexpr (kAppend) {
     if constexpr (kNewPieces == 2) {
-      nkc = e4m3_pack16_bf16(nk[0], nk[1], a.new_k_scale);
-      nvc = e4m3_pack16_bf16(nv[0], nv[1], a.new_v_scale);
+      if (attend_new || store_new) {
+        nkc = e4m3_pack16_bf16(nk[0], nk[1], e4m3_div(a.new_k_scale));
+        nvc = e4m3_pack16_bf16(nv[0], nv[1], e4m3_div(a.new_v_scale));
+      }
     } else {
       nkc = nk[0];
       nvc = nv[0];
@@ -756,7 +758,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     if constexpr (kQuantNew) {
       const U4 hi{(uint32_t)__shfl_down((int)mine.x, S::kRowLanes), (uint32_t)__shfl_down((int)mine.y, S::kRowLanes),
                   (uint32_t)__shfl_down((int)mine.z, S::kRowLanes), (uint32_t)__shfl_down((int)mine.w, S::kRowLanes)};
-      return e4m3_pack16_bf16(mine, hi, scale);
+      return e4m3_pack16_bf16(mine, hi, e4m3_div(scale));
     } else {
       return mine;
     }

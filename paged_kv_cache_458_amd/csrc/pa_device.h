@@ -69,12 +69,35 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // OCP E4M3 quantisation, shared by the quantising cache write and the decode kernels that append a new row
-// themselves, so both store the same codes. The code of x / scale: an fp32 division (correctly rounded),
-// saturated to +-448, rounded to nearest with ties to even by the hardware conversion (which would turn
-// |y| >= 480 into NaN, hence the clamp); NaN is stored as 0x7F. Four values packed into one word, first value in
-// the lowest byte.
-__device__ __forceinline__ float e4m3_prepare(float x, float scale) {
-  const float y = x / scale;
+// themselves, so both store the same codes. The code of x / scale: the quotient rounded to nearest fp32 (as an
+// IEEE division), saturated to +-448, rounded to nearest with ties to even by the hardware conversion (which
+// would turn |y| >= 480 into NaN, hence the clamp); NaN is stored as 0x7F. Four values packed into one word,
+// first value in the lowest byte.
+//
+// The quotient without a division per value: with inv = RN(1 / scale) and q = RN(x * inv), the residual
+// x - q * scale is exact in one fma, and q + residual * inv rounded once is the correctly rounded quotient
+// whenever it is a normal number (Markstein's correction step for division with a fused multiply-add). For
+// |scale| in [2^-32, 2^32] every quotient that decides a code (|x / scale| in [2^-11, 512)) is normal, and so
+// is every x that gives one; a smaller quotient gives a zero code of its sign, a larger one saturates, either
+// way. Exact quotients and signed zeros keep q (zero residual), and so do infinite or NaN q. Other scales take
+// the division.
+struct E4m3Div {
+  float scale, inv;
+  bool fast;
+};
+__device__ __forceinline__ E4m3Div e4m3_div(float scale) {
+  const float a = fabsf(scale);
+  return E4m3Div{scale, 1.0f / scale, a >= 0x1p-32f && a <= 0x1p32f};
+}
+__device__ __forceinline__ float e4m3_quotient(float x, const E4m3Div& d) {
+  if (!d.fast) return x / d.scale;
+  const float q = x * d.inv;
+  const float r = __builtin_fmaf(-q, d.scale, x);
+  const float y = __builtin_fmaf(r, d.inv, q);
+  return r == 0.f || !__builtin_isfinite(q) ? q : y;
+}
+__device__ __forceinline__ float e4m3_prepare(float x, const E4m3Div& d) {
+  const float y = e4m3_quotient(x, d);
   return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
 }
 __device__ __forceinline__ uint32_t nan_to_7f(uint32_t word, float a, float b, float c, float d) {
@@ -84,22 +107,22 @@ __device__ __forceinline__ uint32_t nan_to_7f(uint32_t word, float a, float b, f
   if (d != d) word = (word & 0x00ffffffu) | 0x7f000000u;
   return word;
 }
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float scale) {
-  a = e4m3_prepare(a, scale);
-  b = e4m3_prepare(b, scale);
-  c = e4m3_prepare(c, scale);
-  d = e4m3_prepare(d, scale);
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, const E4m3Div& dv) {
+  a = e4m3_prepare(a, dv);
+  b = e4m3_prepare(b, dv);
+  c = e4m3_prepare(c, dv);
+  d = e4m3_prepare(d, dv);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return nan_to_7f((uint32_t)w, a, b, c, d);
 }
 // 16 values -> 16 codes
-__device__ __forceinline__ U4 e4m3_pack16(const float* f, float scale) {
-  return U4{e4m3_pack4(f[0], f[1], f[2], f[3], scale), e4m3_pack4(f[4], f[5], f[6], f[7], scale),
-            e4m3_pack4(f[8], f[9], f[10], f[11], scale), e4m3_pack4(f[12], f[13], f[14], f[15], scale)};
+__device__ __forceinline__ U4 e4m3_pack16(const float* f, const E4m3Div& dv) {
+  return U4{e4m3_pack4(f[0], f[1], f[2], f[3], dv), e4m3_pack4(f[4], f[5], f[6], f[7], dv),
+            e4m3_pack4(f[8], f[9], f[10], f[11], dv), e4m3_pack4(f[12], f[13], f[14], f[15], dv)};
 }
 // 16 consecutive bf16 values, as two 16-byte pieces -> 16 codes
-__device__ __forceinline__ U4 e4m3_pack16_bf16(U4 a, U4 b, float scale) {
+__device__ __forceinline__ U4 e4m3_pack16_bf16(U4 a, U4 b, const E4m3Div& dv) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   float f[16];
 #pragma unroll
@@ -107,7 +130,7 @@ __device__ __forceinline__ U4 e4m3_pack16_bf16(U4 a, U4 b, float scale) {
     f[2 * i] = bf16_lo(w[i]);
     f[2 * i + 1] = bf16_hi(w[i]);
   }
-  return e4m3_pack16(f, scale);
+  return e4m3_pack16(f, dv);
 }
 
 // ---------------------------------------------------------------------------------------------------------

@@ -210,6 +210,42 @@ def test_fp8_quantiser_special_values_bit_exact(src):
         np.testing.assert_array_equal(to_host(vc), hv, err_msg=f"v_scale {vs}")
 
 
+@pytest.mark.parametrize("scale", [0.0125, 1 / 3, 0.3, 7.0, -0.7, 1.37 * 2.0 ** -40, 2.0 ** -32, 1.999 * 2.0 ** 31,
+                                   1.5 * 2.0 ** 32])
+def test_fp8_quantiser_every_bf16_value(scale):
+    # the quantiser divides by the scale without a division per value (a reciprocal and one fma correction) for
+    # scales of magnitude 2^-32 .. 2^32 and divides outside that range: every finite and non-finite bf16 bit
+    # pattern as key, its negation as value, and for a float32 source the values whose quotient lies at or one
+    # ulp either side of every E4M3 code and every midpoint between neighbouring codes
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    x = bits.view(np.float32)
+    vals = oracle.e4m3_values()
+    pos = np.sort(vals[(vals >= 0) & ~np.isnan(vals)])
+    targets = np.concatenate([pos, (pos[:-1] + pos[1:]) / 2, [464.0, 480.0]])
+    targets = np.concatenate([targets, -targets])
+    near = (targets * np.float64(np.float32(scale))).astype(np.float32)
+    near = np.concatenate([near, np.nextafter(near, np.float32(np.inf)), np.nextafter(near, np.float32(-np.inf))])
+    hkv, d = 2, 32
+    for src, data in (("bf16", x), ("f32", near)):
+        data = np.concatenate([data, np.zeros((-data.size) % (hkv * d), np.float32)]).reshape(-1, hkv, d)
+        n = data.shape[0]
+        src_t = torch.from_numpy(data)
+        if src == "bf16":
+            src_t = src_t.to(torch.bfloat16)
+        host_src = to_host(src_t)
+        nb, bs = -(-n // 16) + 1, 16
+        slots = np.random.default_rng(503).permutation(nb * bs)[:n].astype(np.int32)
+        kc = torch.full((nb, bs, hkv, d), float("nan"), device=DEV).to(torch.float8_e4m3fn)
+        vc = kc.clone()
+        pa.reshape_and_cache(src_t.to(DEV), (-src_t).to(DEV), kc, vc, dev_i32(slots), k_scale=scale, v_scale=scale)
+        torch.cuda.synchronize()
+        hk = np.full((nb, bs, hkv, d), 0x7F, np.uint8)
+        hv = hk.copy()
+        oracle.reshape_and_cache_e4m3(hk, hv, host_src, to_host(-src_t), slots, scale, scale)
+        np.testing.assert_array_equal(to_host(kc), hk, err_msg=f"{src} scale {scale}")
+        np.testing.assert_array_equal(to_host(vc), hv, err_msg=f"{src} scale {scale}")
+
+
 def test_reshape_skips_padding_and_out_of_pool_slots():
     st = custom_structure("skip", 302, [20, 40, 9], 4, 4, 64, 16, "bf16")
     t = materialize(st, DEV, include_new_token=False)
