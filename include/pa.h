@@ -178,8 +178,9 @@ int paged_attention_decode_scaled(float *out, const void *query, const void *key
  * paged_attention_decode, lengths beyond max_context_len are clamped: such a sequence's new token is written but
  * not attended over. The decode launch does both, whatever the plan: the last position of such a sequence is
  * taken from `key` / `value` (quantised first for E4M3) instead of the pool, and a wave of that sequence writes
- * it into the pools. Only a call with max_context_len 0 (no position attended anywhere) launches the cache write
- * first. Either way the pools end as the cache write leaves them, byte for byte. The output equals that of the
+ * it into the pools. Only a call with max_context_len 0 (no position attended anywhere), or an E4M3 call with
+ * |k_scale| or |v_scale| outside [2^-32, 2^32] (where the decode kernels' quantiser would need a division per
+ * value), launches the cache write first. Either way the pools end as the cache write leaves them, byte for byte. The output equals that of the
  * two calls bit for bit on the matrix-core kernels (grouped heads over bf16 or E4M3 caches); the single-head
  * kernels add the new token to its row's softmax after the pool rows of its tile or partition (the same values,
  * another order of floating-point additions).

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(const U4* _
 template <int SRC>
 __device__ __forceinline__ U4 e4m3_pack16_from(const char* src, const E4m3Div& dv) {
   if constexpr (SRC == PA_BF16) {
-    return e4m3_pack16_bf16(*reinterpret_cast<const U4*>(src), *reinterpret_cast<const U4*>(src + 16), dv);
+    return e4m3_pack16_bf16<true>(*reinterpret_cast<const U4*>(src), *reinterpret_cast<const U4*>(src + 16), dv);
   } else {
     float f[16];
 #pragma unroll
@@ -46,7 +46,7 @@ __device__ __forceinline__ U4 e4m3_pack16_from(const char* src, const E4m3Div& d
       f[4 * i + 2] = __uint_as_float(v.z);
       f[4 * i + 3] = __uint_as_float(v.w);
     }
-    return e4m3_pack16(f, dv);
+    return e4m3_pack16<true>(f, dv);
   }
 }
 

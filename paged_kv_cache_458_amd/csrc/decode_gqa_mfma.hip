@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const Dec
   // the lane's 16 bytes of the new K or V row as the pool holds them
   auto new_piece = [&](const U4* raw, float scale) __attribute__((always_inline)) {
     if constexpr (S::kRaw)
-      return e4m3_pack16_bf16(raw[0], raw[1], e4m3_div(scale));
+      return e4m3_pack16_bf16<false>(raw[0], raw[1], e4m3_div(scale));
     else
       return raw[0];
   };
@@ -780,7 +780,7 @@ __global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_balanced_kernel(
   // the piece as the pool holds it (E4M3: quantised exactly as the quantising cache write does)
   auto new_piece = [&](const U4* raw, float scale) __attribute__((always_inline)) {
     if constexpr (S::kRaw)
-      return e4m3_pack16_bf16(raw[0], raw[1], e4m3_div(scale));
+      return e4m3_pack16_bf16<false>(raw[0], raw[1], e4m3_div(scale));
     else
       return raw[0];
   };

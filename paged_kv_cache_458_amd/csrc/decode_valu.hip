@@ -301,8 +301,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_valu_kernel(con
   if constexpr (kAppend) {
     if constexpr (kNewPieces == 2) {
       if (attend_new || store_new) {
-        nkc = e4m3_pack16_bf16(nk[0], nk[1], e4m3_div(a.new_k_scale));
-        nvc = e4m3_pack16_bf16(nv[0], nv[1], e4m3_div(a.new_v_scale));
+        nkc = e4m3_pack16_bf16<false>(nk[0], nk[1], e4m3_div(a.new_k_scale));
+        nvc = e4m3_pack16_bf16<false>(nv[0], nv[1], e4m3_div(a.new_v_scale));
       }
     } else {
       nkc = nk[0];
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, 2) void decode_valu_balance
     if constexpr (kQuantNew) {
       const U4 hi{(uint32_t)__shfl_down((int)mine.x, S::kRowLanes), (uint32_t)__shfl_down((int)mine.y, S::kRowLanes),
                   (uint32_t)__shfl_down((int)mine.z, S::kRowLanes), (uint32_t)__shfl_down((int)mine.w, S::kRowLanes)};
-      return e4m3_pack16_bf16(mine, hi, e4m3_div(scale));
+      return e4m3_pack16_bf16<false>(mine, hi, e4m3_div(scale));
     } else {
       return mine;
     }

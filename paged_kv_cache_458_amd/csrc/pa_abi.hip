@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "../../include/pa.h"
+#include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace {
@@ -418,9 +419,13 @@ int attention(float* out, const void* query, const void* key_cache, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (app) {
     // Every decode kernel appends the new tokens itself (for an E4M3 cache from bf16 rows, which every E4M3
-    // decode has). A call with max_context_len 0 gives its sequences no tile in which a balanced run could write
-    // the token: it writes them first, as reshape_and_cache or reshape_and_cache_fp8 would, and then attends.
-    const bool fused = !query_start && max_context_len > 0 && (kv_dtype != PA_FP8_E4M3 || q_dtype == PA_BF16);
+    // decode has, with scales whose quotients the kernels' quantiser forms without a division: magnitudes 2^-32 ..
+    // 2^32). A call with max_context_len 0 gives its sequences no tile in which a balanced run could write the
+    // token, and an E4M3 scale outside that range would need the division: such calls write the tokens first,
+    // as reshape_and_cache or reshape_and_cache_fp8 would, and then attend.
+    const bool fused = !query_start && max_context_len > 0 &&
+                       (kv_dtype != PA_FP8_E4M3 ||
+                        (q_dtype == PA_BF16 && pa::e4m3_fast_scale(k_scale) && pa::e4m3_fast_scale(v_scale)));
     hipError_t e = hipSuccess;
     if (fused) {
       a.new_key = app->key;

@@ -80,24 +80,28 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // |scale| in [2^-32, 2^32] every quotient that decides a code (|x / scale| in [2^-11, 512)) is normal, and so
 // is every x that gives one; a smaller quotient gives a zero code of its sign, a larger one saturates, either
 // way. Exact quotients and signed zeros keep q (zero residual), and so do infinite or NaN q. Other scales take
-// the division.
+// the division; kAnyScale = false leaves that path out (callers that only see scales in the range: the decode
+// kernels, which the host gives no other scale).
 struct E4m3Div {
   float scale, inv;
   bool fast;
 };
-__device__ __forceinline__ E4m3Div e4m3_div(float scale) {
-  const float a = fabsf(scale);
-  return E4m3Div{scale, 1.0f / scale, a >= 0x1p-32f && a <= 0x1p32f};
+__host__ __device__ __forceinline__ bool e4m3_fast_scale(float scale) {
+  const float a = scale < 0.f ? -scale : scale;
+  return a >= 0x1p-32f && a <= 0x1p32f;
 }
+__device__ __forceinline__ E4m3Div e4m3_div(float scale) { return E4m3Div{scale, 1.0f / scale, e4m3_fast_scale(scale)}; }
+template <bool kAnyScale>
 __device__ __forceinline__ float e4m3_quotient(float x, const E4m3Div& d) {
-  if (!d.fast) return x / d.scale;
+  if (kAnyScale && !d.fast) return x / d.scale;
   const float q = x * d.inv;
   const float r = __builtin_fmaf(-q, d.scale, x);
   const float y = __builtin_fmaf(r, d.inv, q);
   return r == 0.f || !__builtin_isfinite(q) ? q : y;
 }
+template <bool kAnyScale>
 __device__ __forceinline__ float e4m3_prepare(float x, const E4m3Div& d) {
-  const float y = e4m3_quotient(x, d);
+  const float y = e4m3_quotient<kAnyScale>(x, d);
   return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
 }
 __device__ __forceinline__ uint32_t nan_to_7f(uint32_t word, float a, float b, float c, float d) {
@@ -107,21 +111,25 @@ __device__ __forceinline__ uint32_t nan_to_7f(uint32_t word, float a, float b, f
   if (d != d) word = (word & 0x00ffffffu) | 0x7f000000u;
   return word;
 }
+template <bool kAnyScale>
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, const E4m3Div& dv) {
-  a = e4m3_prepare(a, dv);
-  b = e4m3_prepare(b, dv);
-  c = e4m3_prepare(c, dv);
-  d = e4m3_prepare(d, dv);
+  a = e4m3_prepare<kAnyScale>(a, dv);
+  b = e4m3_prepare<kAnyScale>(b, dv);
+  c = e4m3_prepare<kAnyScale>(c, dv);
+  d = e4m3_prepare<kAnyScale>(d, dv);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return nan_to_7f((uint32_t)w, a, b, c, d);
 }
 // 16 values -> 16 codes
+template <bool kAnyScale>
 __device__ __forceinline__ U4 e4m3_pack16(const float* f, const E4m3Div& dv) {
-  return U4{e4m3_pack4(f[0], f[1], f[2], f[3], dv), e4m3_pack4(f[4], f[5], f[6], f[7], dv),
-            e4m3_pack4(f[8], f[9], f[10], f[11], dv), e4m3_pack4(f[12], f[13], f[14], f[15], dv)};
+  return U4{e4m3_pack4<kAnyScale>(f[0], f[1], f[2], f[3], dv), e4m3_pack4<kAnyScale>(f[4], f[5], f[6], f[7], dv),
+            e4m3_pack4<kAnyScale>(f[8], f[9], f[10], f[11], dv),
+            e4m3_pack4<kAnyScale>(f[12], f[13], f[14], f[15], dv)};
 }
 // 16 consecutive bf16 values, as two 16-byte pieces -> 16 codes
+template <bool kAnyScale>
 __device__ __forceinline__ U4 e4m3_pack16_bf16(U4 a, U4 b, const E4m3Div& dv) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   float f[16];
@@ -130,7 +138,7 @@ __device__ __forceinline__ U4 e4m3_pack16_bf16(U4 a, U4 b, const E4m3Div& dv) {
     f[2 * i] = bf16_lo(w[i]);
     f[2 * i + 1] = bf16_hi(w[i]);
   }
-  return e4m3_pack16(f, dv);
+  return e4m3_pack16<kAnyScale>(f, dv);
 }
 
 // ---------------------------------------------------------------------------------------------------------

@@ -205,3 +205,40 @@ def test_zero_max_context_len_still_writes(hq, part):
     assert torch.equal(pools[0].view(torch.uint8), ref_pools[0].view(torch.uint8))
     assert torch.equal(pools[1].view(torch.uint8), ref_pools[1].view(torch.uint8))
     np.testing.assert_array_equal(fused, np.zeros_like(fused))
+
+
+@pytest.mark.parametrize("scale", [1 / 64, 0.3, 1.5 * 2.0 ** 33, 1.37 * 2.0 ** -40],
+                         ids=["2^-6", "0.3", "above the kernels' range", "below the kernels' range"])
+@pytest.mark.parametrize("hq,part", [(8, pa.PA_PARTITION_BALANCED), (32, 512)],
+                         ids=["single-head balanced", "matrix-core partitions"])
+def test_e4m3_scales_inside_and_outside_the_kernels_range(scale, hq, part):
+    # the decode kernels quantise an appended row without a division, for |scale| in [2^-32, 2^32]; a call with a
+    # scale outside that range writes the rows with the quantising cache write first and then attends. Either way
+    # the pools end as reshape_and_cache_fp8 leaves them, and the output is the two calls' (bit for bit where the
+    # cache write runs first, or on the matrix cores)
+    st = custom_structure("a617", 617, [700, 33, 1200, 90, 2], hq, 8, 128, 16, "fp8")
+    t = materialize(st, DEV, include_new_token=True)  # pool codes drawn for the default scale
+    # the same codes read with the scale under test (the logits as before, so that the softmax stays as peaked
+    # as the oracle comparison expects); the new rows are quantised with it
+    st.scale = st.scale * st.k_scale / scale
+    st.k_scale, st.v_scale = scale, scale * 0.75
+    pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    ref_pools = (t["key_cache"].clone(), t["value_cache"].clone())
+    write_separately(st, t, ref_pools, st.slot_mapping)
+    h = {k: to_host(v) for k, v in t.items()}
+    write_on_host(st, h, st.slot_mapping)
+    separate = decode(st, dict(t, key_cache=ref_pools[0], value_cache=ref_pools[1]), st.block_tables_pre, part)
+    fused = appended(st, t, pools, st.block_tables_pre, st.slot_mapping, part)
+    assert torch.equal(pools[0].view(torch.uint8), ref_pools[0].view(torch.uint8))
+    assert torch.equal(pools[1].view(torch.uint8), ref_pools[1].view(torch.uint8))
+    np.testing.assert_array_equal(to_host(pools[0]).view(np.uint8), h["key_cache"].view(np.uint8))
+    np.testing.assert_array_equal(to_host(pools[1]).view(np.uint8), h["value_cache"].view(np.uint8))
+    inside = 2.0 ** -32 <= scale * 0.75 and scale <= 2.0 ** 32
+    # the outputs scale with v_scale: compared in units of v_scale * 64, in which they are of order one (the unit
+    # is 1 at the default scale) as the tolerances expect
+    unit = st.v_scale * 64
+    if inside and reordered(st, part):
+        np.testing.assert_allclose(fused, separate, rtol=1e-5, atol=1e-6 * unit)
+    else:
+        np.testing.assert_array_equal(fused, separate)
+    assert_attention_close(fused / unit, oracle_decode(st, h, st.block_tables_pre) / unit, st.dtype, f"scale {scale}")
