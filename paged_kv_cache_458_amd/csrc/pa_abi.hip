@@ -172,8 +172,9 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   // On the matrix cores it takes it only where the partitions would launch more than one round of resident
   // waves: measured on MI355X over grouped-query batches (bf16 and E4M3), it then gained 5-21%, while partitions
   // that all start together won by 3-8% (70B-shaped batch, 16 sequences of 8k-16k tokens) -- their fewer
-  // concurrent read streams keep the memory system less congested. A shared prefix favours partitions
-  // slightly (278 against 274 us for 128 sequences sharing 1024 tokens), and the host cannot see sharing.
+  // concurrent read streams keep the memory system less congested. A shared prefix favours partitions (277
+  // against 267 us for 128 sequences of 4096 tokens sharing the first 1024, with 1024-token partitions), but
+  // the host cannot see sharing: a caller that knows of it asks for partitions.
   const bool split_default = partition_size == -1 && balanced_ok && part > 0 && part < whole;
   const bool more_than_a_round =
       gqa && part > 0 &&
