@@ -408,11 +408,14 @@ def run_config_children(args) -> dict:
     from workloads import CONFIG_NAMES
 
     res = {}
+    # at least 100 timed steps each: the shortest calls (about 70 us) are the noisiest, and a few milliseconds of
+    # timed work steady their means
+    steps, warmup = max(args.steps, 100), max(args.warmup, 10)
     for name in CONFIG_NAMES:
         if name == HEADLINE:
             continue
-        cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(args.steps),
-               "--warmup", str(args.warmup), "--replicas", str(args.replicas), "--cpu-seconds",
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps", str(steps),
+               "--warmup", str(warmup), "--replicas", str(args.replicas), "--cpu-seconds",
                str(args.config_cpu_seconds), "--no-configs"]
         log(f"configs: {name}")
         r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
