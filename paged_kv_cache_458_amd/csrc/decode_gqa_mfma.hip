@@ -362,7 +362,7 @@ __device__ __forceinline__ void gqa_offsets(int rr, int rc, int64_t row_bytes, i
 // columns (1, or 2 at head_dim <= 128 where the registers hold two accumulators): they share every K/V load and
 // every LDS operand read.
 template <int KV, int D, int W, int NCG, bool kAppend>
-__global__ __launch_bounds__(kWave * W, 2) void decode_gqa_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kWave * W, NCG >= 4 ? 1 : 2) void decode_gqa_mfma_kernel(const DecodeArgs a) {
   using S = GqaShape<KV, D>;
   constexpr int kEsize = S::kEsize, kChunks = S::kChunks, kNt = S::kNt, kPitch = S::kPitch, kSlice = S::kSlice;
   constexpr int kRowLanes = S::kRowLanes, kLoads = S::kLoads;
@@ -1033,6 +1033,8 @@ template <int KV, int D, int W>
 hipError_t launch_w(const DecodeArgs& a, hipStream_t stream) {
   if constexpr (D <= 128)
     if (a.cg_per_wave == 2) return launch_wc<KV, D, W, 2>(a, stream);
+  if constexpr (D <= 128 && W <= 4 && KV == PA_BF16)
+    if (a.cg_per_wave == 4) return launch_wc<KV, D, W, 4>(a, stream);
   if (a.cg_per_wave != 1) return hipErrorInvalidValue;
   return launch_wc<KV, D, W, 1>(a, stream);
 }
@@ -1045,7 +1047,8 @@ int waves_per_group(int32_t num_kv_heads) {
 
 template <int KV, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  switch (waves_per_group(a.num_kv_heads)) {
+  // four column groups per wave take one wave per SIMD: at most 4 waves to a workgroup
+  switch (a.cg_per_wave == 4 ? min(4, waves_per_group(a.num_kv_heads)) : waves_per_group(a.num_kv_heads)) {
     case 8: return launch_w<KV, D, 8>(a, stream);
     case 4: return launch_w<KV, D, 4>(a, stream);
     case 2: return launch_w<KV, D, 2>(a, stream);

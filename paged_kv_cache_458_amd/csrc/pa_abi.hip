@@ -148,7 +148,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_tokens, int32_t max_query_len, int3
   const bool gqa = pa::gqa_mfma_supported(kv_dtype, head_dim, num_q_heads / num_kv_heads, max_query_len);
   p.mfma = gqa;
   p.col_groups = gqa ? (num_q_heads / num_kv_heads * max_query_len + 15) / 16 : 1;
-  p.cg_per_wave = gqa ? pa::gqa_cg_per_wave(p.col_groups, head_dim) : 1;
+  p.cg_per_wave = gqa ? pa::gqa_cg_per_wave(p.col_groups, head_dim, kv_dtype) : 1;
   const int32_t slots = (p.col_groups + p.cg_per_wave - 1) / p.cg_per_wave;  // waves per (sequence, KV head)
   if ((int64_t)(num_kv_heads + 7) / 8 * p.col_groups > INT32_MAX) {
     p.status = PA_ERR_UNSUPPORTED;
