@@ -408,9 +408,9 @@ def run_config_children(args) -> dict:
     from workloads import CONFIG_NAMES
 
     res = {}
-    # at least 100 timed steps each: the shortest calls (about 70 us) are the noisiest, and a few milliseconds of
-    # timed work steady their means
-    steps, warmup = max(args.steps, 100), max(args.warmup, 10)
+    # at least 100 timed steps and 200 warmup steps each: the shortest calls (about 70 us) are the noisiest, and
+    # their means settle only after tens of milliseconds of work
+    steps, warmup = max(args.steps, 100), max(args.warmup, 200)
     for name in CONFIG_NAMES:
         if name == HEADLINE:
             continue
