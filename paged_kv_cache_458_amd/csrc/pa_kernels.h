@@ -99,13 +99,14 @@ hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, int kv_dtype, hipStream_t
 constexpr int kMaxColGroups = 64;
 bool gqa_mfma_supported(int kv_dtype, int head_dim, int group, int max_query_len);
 // Column groups one wave of the matrix-core partition kernel serves: 2 (two accumulators, every K/V load and LDS
-// operand read shared) where there are several and head_dim <= 128, else 1; over a bf16 cache with exactly four,
-// all four (one wave per SIMD, its accumulators in AGPRs, at most 4 waves to a workgroup). Measured on MI355X,
-// 70B-shaped batch with 8 new tokens per sequence (64 columns): bf16 277.5 -> 233.0 us; its E4M3 form went
-// 173 -> 212 us, and 16 tokens per sequence (8 groups, two such waves) 409 -> 437 us, so only that case takes it.
+// operand read shared) where there are several and head_dim <= 128, else 1; over a bf16 cache with three or four,
+// all of them (one wave per SIMD, its accumulators in AGPRs, at most 4 waves to a workgroup). Measured on MI355X,
+// 70B-shaped batch with 5, 6 and 8 new tokens per sequence (40, 48 and 64 columns): bf16 261 -> 210, 268 -> 219
+// and 277.5 -> 233.0 us; the E4M3 form with 8 went 173 -> 212 us, and 16 tokens per sequence (8 groups, two such
+// waves) 409 -> 437 us, so only those cases take it.
 inline int gqa_cg_per_wave(int col_groups, int head_dim, int kv_dtype) {
   if (head_dim > 128) return 1;
-  if (col_groups == 4 && kv_dtype == PA_BF16) return 4;
+  if ((col_groups == 3 || col_groups == 4) && kv_dtype == PA_BF16) return 4;
   return col_groups >= 2 ? 2 : 1;
 }
 constexpr int kGqaTileTokens = 32;  // tokens per tile of the GQA kernel

@@ -80,6 +80,7 @@ CASES = [
     (522, [700, 45, 3, 1300], [8, 8, 2, 7], 64, 8, 128, 16, "bf16"),   # G 8 x QL 8: four groups in one wave
     (523, [90, 600, 33], [7, 8, 6], 32, 4, 64, 32, "bf16"),            # the same at head_dim 64, 4 KV heads
     (524, [500, 20, 250], [7, 7, 3], 16, 2, 96, 16, "bf16"),           # 56 columns (four groups), 96 dims
+    (525, [800, 64, 5, 333], [5, 3, 5, 1], 64, 8, 128, 16, "bf16"),    # 40 columns: three groups in one wave
     # per-head kernel
     (506, [33, 150, 600], [5, 1, 4], 4, 4, 64, 16, "f32"),
     (510, [0, 8, 700, 30], [3, 12, 5, 1], 8, 8, 80, 16, "bf16"),      # QL > L, an empty context
